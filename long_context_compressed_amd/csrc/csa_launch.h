@@ -1,0 +1,94 @@
+// Internal launcher interface between the C ABI (csa_api.cpp) and the kernels (*.hip).
+// Every launcher assumes its arguments were validated on the host.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+// Shape and metadata common to the per-token kernels.
+struct Shape {
+  int B;          // samples
+  int T;          // capacity rows
+  int max_seqlen; // host bound on L_b
+  int r;          // ratio
+  int W;          // window
+  int k;          // top-k
+  int k_cap;      // idx row width
+  int H, D;       // heads, head dim
+  int HI, dI;     // indexer heads, indexer dim
+  float scale;
+  int mode;       // csa_mode_t
+  int teacher;    // csa_teacher_t
+  int dtype;      // csa_dtype_t main operands
+  int idx_dtype;  // csa_dtype_t indexer operands
+  const int32_t* cu;      // cu_seqlens [B+1]
+  const int32_t* cu_cmp;  // cu_cmp [B+1]
+};
+
+hipError_t launch_cmp_seqlens(const int32_t* cu, int B, int r, int32_t* cu_cmp, hipStream_t s);
+hipError_t launch_validate_metadata(const int32_t* cu, int B, int T, int max_seqlen,
+                                    int32_t* status, hipStream_t s);
+hipError_t launch_compress(const Shape& sh, int dtype, const void* x, int dim, void* x_cmp,
+                           hipStream_t s);
+hipError_t launch_compress_bwd(const Shape& sh, const float* d_cmp, int dim, float* dx,
+                               hipStream_t s);
+hipError_t launch_quantize_fp8(const void* x, int dtype, int64_t rows, int row_len,
+                               uint8_t* codes, float* scale, hipStream_t s);
+hipError_t launch_index_scores(const Shape& sh, const void* qI, const float* qI_scale,
+                               const float* w, const void* kI, const float* kI_scale,
+                               float* scores, int64_t ld, hipStream_t s);
+hipError_t launch_topk(const Shape& sh, const float* scores, int64_t ld, int32_t* idx,
+                       hipStream_t s);
+
+struct AttnIO {
+  const void* q;
+  const void* kv_cmp;
+  const void* kv;
+  const int32_t* idx;
+  const float* sink;
+  void* out;
+  float* lse;
+  // backward only
+  const void* o;
+  const void* dout;
+  void* dq;
+  float* dkv_cmp;
+  float* dkv;
+  float* dsink;
+  void* ws;
+  size_t ws_bytes;
+};
+
+size_t attn_fwd_workspace(const Shape& sh);
+size_t attn_bwd_workspace(const Shape& sh);
+hipError_t launch_attn_fwd(const Shape& sh, const AttnIO& io, hipStream_t s);
+hipError_t launch_attn_bwd(const Shape& sh, const AttnIO& io, hipStream_t s);
+
+struct KlIO {
+  const void* q;
+  const void* kv_cmp;
+  const float* scores;
+  int64_t ld;
+  const int32_t* idx;
+  const void* qI;
+  const float* qI_scale;
+  const float* w;
+  const void* kI;
+  const float* kI_scale;
+  float grad_scale;
+  float* kl;
+  float* loss;
+  float* dqI;
+  float* dw;
+  float* dkI;
+  void* ws;
+  size_t ws_bytes;
+};
+
+size_t indexer_kl_workspace(const Shape& sh);
+hipError_t launch_indexer_kl(const Shape& sh, const KlIO& io, hipStream_t s);
+
+}  // namespace csa

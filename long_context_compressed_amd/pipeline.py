@@ -1,0 +1,165 @@
+"""One CSA/HCA layer step (forward + backward) chained over the C ABI.
+
+`CsaLayer` preallocates every output, gradient and workspace buffer with torch once,
+so a step enqueues only library kernels (and torch fill kernels that zero the
+accumulated gradients) on the current stream.  The order follows the fused training
+flow of "DeepSeek-V4 Attention Training Systems", section 8.2: compress, indexer score
++ top-k, selected-attention forward, teacher recompute with the eager indexer-loss
+backward, then the attention backward and the compressor adjoints.
+"""
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import binding as B
+
+MODE = {"sparse": B.CSA_SPARSE, "dense": B.CSA_DENSE, "window": B.CSA_WINDOW}
+TEACHER = {"none": B.CSA_TEACHER_NONE, "selected": B.CSA_TEACHER_SELECTED,
+           "dense": B.CSA_TEACHER_DENSE}
+DTYPE = {"f32": B.CSA_F32, "bf16": B.CSA_BF16, "fp8": B.CSA_FP8_E4M3}
+
+
+@dataclass
+class LayerConfig:
+    heads: int
+    head_dim: int
+    ratio: int
+    window: int
+    topk: int
+    topk_cap: int
+    idx_heads: int
+    idx_dim: int
+    dtype: str
+    idx_dtype: str
+    mode: str
+    teacher: str
+    scale: float
+
+    @classmethod
+    def of(cls, w):
+        return cls(heads=w.heads, head_dim=w.head_dim, ratio=w.ratio, window=w.window,
+                   topk=w.topk, topk_cap=w.topk_cap, idx_heads=w.idx_heads, idx_dim=w.idx_dim,
+                   dtype=w.dtype, idx_dtype=w.idx_dtype, mode=w.mode, teacher=w.teacher,
+                   scale=w.scale)
+
+    @property
+    def has_indexer(self):
+        return self.idx_heads > 0 and self.mode == "sparse"
+
+
+class CsaLayer:
+    """Buffers and calls of one layer step for a fixed capacity (T rows, max_seqlen)."""
+
+    def __init__(self, cfg: LayerConfig, batch: int, total_tokens: int, max_seqlen: int,
+                 device="cuda", backward: bool = True, grad_scale: float = 1.0):
+        self.cfg = cfg
+        self.backward = backward
+        self.grad_scale = grad_scale
+        dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+        T, H, D, r = total_tokens, cfg.heads, cfg.head_dim, cfg.ratio
+        self.T, self.B = T, batch
+        self.n_cap = max_seqlen // r
+        self.tc_cap = max(1, T // r)
+        self.p = B.make_params(
+            batch=batch, total_tokens=T, max_seqlen=max_seqlen, ratio=r, window=cfg.window,
+            topk=max(1, cfg.topk), topk_cap=cfg.topk_cap, heads=H, head_dim=D,
+            idx_heads=cfg.idx_heads, idx_dim=cfg.idx_dim, scale=cfg.scale, mode=MODE[cfg.mode],
+            teacher=TEACHER[cfg.teacher], dtype=DTYPE[cfg.dtype],
+            idx_dtype=DTYPE[cfg.idx_dtype] if cfg.idx_heads else B.CSA_BF16)
+        z = lambda *s, dtype=torch.float32: torch.empty(*s, dtype=dtype, device=device)  # noqa
+        self.cu_cmp = z(batch + 1, dtype=torch.int32)
+        self.kv_cmp = z(self.tc_cap, D, dtype=dt)
+        self.out = z(T, H, D, dtype=dt)
+        self.lse = z(T, H)
+        self.ws_fwd = self._ws(B.CSA_OP_ATTN_FWD, device)
+        if cfg.has_indexer:
+            HI, dI = cfg.idx_heads, cfg.idx_dim
+            idt = torch.float32 if cfg.idx_dtype == "f32" else torch.bfloat16
+            self.kI_cmp = z(self.tc_cap, dI, dtype=idt)
+            if cfg.idx_dtype == "fp8":
+                self.qI8 = z(T, HI, dI, dtype=torch.uint8)
+                self.qI_scale = z(T, HI)
+                self.kI8 = z(self.tc_cap, dI, dtype=torch.uint8)
+                self.kI_scale = z(self.tc_cap)
+            self.scores = z(T, max(1, self.n_cap))
+            self.idx = z(T, cfg.topk_cap, dtype=torch.int32)
+            if cfg.teacher != "none":
+                self.kl = z(T)
+                self.loss = z(1)
+                self.ws_kl = self._ws(B.CSA_OP_INDEXER_KL, device)
+                if backward:
+                    self.dqI = z(T, HI, dI)
+                    self.dw = z(T, HI)
+                    self.dkI_cmp = z(self.tc_cap, dI)
+                    self.dkI_tok = z(T, dI)
+        if backward:
+            self.dq = z(T, H, D, dtype=dt)
+            self.dkv_cmp = z(self.tc_cap, D)
+            self.dkv = z(T, D)
+            self.dsink = z(H)
+            self.ws_bwd = self._ws(B.CSA_OP_ATTN_BWD, device)
+
+    def _ws(self, op, device):
+        n = B.csa_workspace_size(self.p, op)
+        return torch.empty(max(n, 1), dtype=torch.uint8, device=device) if n else None
+
+    # ------------------------------------------------------------------ steps
+    def metadata(self, cu_seqlens):
+        B.csa_cmp_seqlens(cu_seqlens, self.B, self.cfg.ratio, self.cu_cmp)
+
+    def forward(self, inp, cu_seqlens):
+        """inp: dict of device tensors q, kv, [qI, kI_tok, w], [sink]."""
+        cfg, p = self.cfg, self.p
+        B.csa_compress(p, inp["kv"], cu_seqlens, self.cu_cmp, self.kv_cmp)
+        idx = None
+        if cfg.has_indexer:
+            B.csa_compress(p, inp["kI_tok"], cu_seqlens, self.cu_cmp, self.kI_cmp)
+            if cfg.idx_dtype == "fp8":
+                B.csa_quantize_fp8(inp["qI"], self.qI8, self.qI_scale)
+                B.csa_quantize_fp8(self.kI_cmp, self.kI8, self.kI_scale)
+                qI, qs, kI, ks = self.qI8, self.qI_scale, self.kI8, self.kI_scale
+            else:
+                qI, qs, kI, ks = inp["qI"], None, self.kI_cmp, None
+            B.csa_index_scores(p, qI, qs, inp["w"], kI, ks, cu_seqlens, self.cu_cmp, self.scores)
+            B.csa_topk_select(p, self.scores, cu_seqlens, self.cu_cmp, self.idx)
+            idx = self.idx
+        B.csa_sparse_attn_fwd(p, inp["q"], self.kv_cmp, inp["kv"], idx, inp.get("sink"),
+                              cu_seqlens, self.cu_cmp, self.out, self.lse, self.ws_fwd)
+        if cfg.has_indexer and cfg.teacher != "none":
+            grads = self.backward
+            if grads:
+                self.dkI_cmp.zero_()
+            B.csa_indexer_kl(p, inp["q"], self.kv_cmp, self.scores, self.idx, qI, qs, inp["w"],
+                             kI, ks, cu_seqlens, self.cu_cmp, self.grad_scale, self.kl, self.loss,
+                             self.dqI if grads else None, self.dw if grads else None,
+                             self.dkI_cmp if grads else None, self.ws_kl)
+
+    def backward_step(self, inp, cu_seqlens):
+        cfg, p = self.cfg, self.p
+        self.dkv_cmp.zero_()
+        self.dkv.zero_()
+        sink = inp.get("sink")
+        if sink is not None:
+            self.dsink.zero_()
+        B.csa_sparse_attn_bwd(p, inp["q"], self.kv_cmp, inp["kv"],
+                              self.idx if cfg.has_indexer else None, sink, cu_seqlens,
+                              self.cu_cmp, self.out, self.lse, inp["dO"], self.dq, self.dkv_cmp,
+                              self.dkv, self.dsink if sink is not None else None, self.ws_bwd)
+        B.csa_compress_bwd(p, self.dkv_cmp, cu_seqlens, self.cu_cmp, self.dkv)
+        if cfg.has_indexer and cfg.teacher != "none":
+            self.dkI_tok.zero_()
+            B.csa_compress_bwd(p, self.dkI_cmp, cu_seqlens, self.cu_cmp, self.dkI_tok)
+
+    def step(self, inp, cu_seqlens):
+        self.metadata(cu_seqlens)
+        self.forward(inp, cu_seqlens)
+        if self.backward:
+            self.backward_step(inp, cu_seqlens)
+
+
+def to_device(host, device="cuda", keys=("q", "kv", "qI", "kI_tok", "w", "dO", "sink")):
+    """Copy the seeded host tensors of a workload to the device."""
+    out = {k: host[k].to(device) for k in keys if k in host}
+    out["cu_seqlens"] = torch.tensor(host["cu_seqlens"], dtype=torch.int32, device=device)
+    return out

@@ -411,7 +411,9 @@ def layer_step(inp, cfg, rows=None, backward=None, grad_scale=1.0):
     kv_cmp = compress(inp["kv"], cu, r)
     res["kv_cmp"] = kv_cmp
     idx = None
-    if cfg.has_indexer:
+    if cfg.mode == "window":          # ratio-0 layer: no compressed candidates at all
+        idx = np.full((rows.size, 1), -1, dtype=np.int64)
+    if cfg.has_indexer and cfg.mode == "sparse":
         kI_cmp = compress(inp["kI_tok"], cu, r)
         qI = inp["qI"]
         if cfg.idx_dtype == "fp8":
@@ -424,13 +426,12 @@ def layer_step(inp, cfg, rows=None, backward=None, grad_scale=1.0):
         n_cap = int(inp["max_seqlen"]) // r
         scores = index_scores(qI, inp["w"], kI_cmp, cu, r, n_cap, rows=rows)
         res["scores"] = scores
-        if cfg.mode == "sparse":
-            idx = topk_select(scores, cu, r, cfg.topk, cfg.topk_cap, T, rows=rows)
-            res["idx"] = idx
+        idx = topk_select(scores, cu, r, cfg.topk, cfg.topk_cap, T, rows=rows)
+        res["idx"] = idx
     O, LSE = sparse_attn_fwd(q, kv_cmp, inp["kv"], idx, inp.get("sink"), cu, r, cfg.window,
                              cfg.scale, rows=rows)
     res["O"], res["LSE"] = O, LSE
-    if cfg.has_indexer and cfg.teacher != "none":
+    if cfg.has_indexer and cfg.mode == "sparse" and cfg.teacher != "none":
         kl, loss, dqI, dw, dkI = indexer_kl(q, kv_cmp, res["scores"], idx, qI, inp["w"], kI_cmp,
                                             cu, r, cfg.scale, cfg.teacher, grad_scale, rows=rows)
         res.update(kl=kl, loss=loss, dqI=dqI, dw=dw, dkI_cmp=dkI)

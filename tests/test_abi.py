@@ -1,0 +1,139 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol,
+and rejects invalid arguments before launching anything (no GPU needed)."""
+import ctypes
+
+import pytest
+
+from long_context_compressed_amd import binding as B
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.lib()
+
+
+def _params(**kw):
+    base = dict(batch=1, total_tokens=256, max_seqlen=256, ratio=4, window=16, topk=16,
+                topk_cap=64, heads=4, head_dim=64, idx_heads=2, idx_dim=32, scale=0.125,
+                mode=B.CSA_SPARSE, teacher=B.CSA_TEACHER_DENSE, dtype=B.CSA_F32,
+                idx_dtype=B.CSA_F32)
+    base.update(kw)
+    return B.make_params(**base)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = B.header_functions()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B._SIGS)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.csa_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5):
+        assert lib.csa_status_string(st)
+    assert lib.csa_status_string(7) == b"unknown status"
+
+
+def test_workspace_sizes(lib):
+    p = _params()
+    assert B.csa_workspace_size(p, B.CSA_OP_ATTN_BWD) == 256 * 4 * 4
+    assert B.csa_workspace_size(p, B.CSA_OP_ATTN_FWD) >= 0
+    n = ctypes.c_size_t(0)
+    assert lib.csa_workspace_size(ctypes.byref(p), 99, ctypes.byref(n)) == B.CSA_ERR_ARG
+    assert lib.csa_workspace_size(None, 1, ctypes.byref(n)) == B.CSA_ERR_NULL
+
+
+FAKE = 4096  # a non-null pointer value; every call below fails validation before any use
+
+
+def test_compress_validation(lib):
+    p = _params()
+    f = lib.csa_compress
+    assert f(ctypes.byref(p), 0, None, 64, FAKE, FAKE, FAKE, None) == B.CSA_ERR_NULL
+    assert f(None, 0, FAKE, 64, FAKE, FAKE, FAKE, None) == B.CSA_ERR_NULL
+    assert f(ctypes.byref(p), 0, FAKE, 4, FAKE, FAKE, FAKE, None) == B.CSA_ERR_ARG
+    assert f(ctypes.byref(p), 0, FAKE, 60, FAKE, FAKE, FAKE, None) == B.CSA_ERR_UNSUPPORTED
+    assert f(ctypes.byref(p), 2, FAKE, 64, FAKE, FAKE, FAKE, None) == B.CSA_ERR_UNSUPPORTED
+    bad = _params(ratio=0)
+    assert f(ctypes.byref(bad), 0, FAKE, 64, FAKE, FAKE, FAKE, None) == B.CSA_ERR_ARG
+    bad = _params(batch=-1)
+    assert f(ctypes.byref(bad), 0, FAKE, 64, FAKE, FAKE, FAKE, None) == B.CSA_ERR_ARG
+    g = lib.csa_compress_bwd
+    assert g(ctypes.byref(p), FAKE, 64, FAKE, FAKE, None, None) == B.CSA_ERR_NULL
+    assert g(ctypes.byref(p), FAKE, 12, FAKE, FAKE, FAKE, None) == B.CSA_ERR_UNSUPPORTED
+
+
+def test_cmp_seqlens_and_quantize_validation(lib):
+    assert lib.csa_cmp_seqlens(None, 1, 4, FAKE, None) == B.CSA_ERR_NULL
+    assert lib.csa_cmp_seqlens(FAKE, -1, 4, FAKE, None) == B.CSA_ERR_ARG
+    assert lib.csa_cmp_seqlens(FAKE, 1, 0, FAKE, None) == B.CSA_ERR_ARG
+    q = lib.csa_quantize_fp8
+    assert q(None, 1, 10, 128, FAKE, FAKE, None) == B.CSA_ERR_NULL
+    assert q(FAKE, 1, -1, 128, FAKE, FAKE, None) == B.CSA_ERR_ARG
+    assert q(FAKE, 1, 10, 100, FAKE, FAKE, None) == B.CSA_ERR_UNSUPPORTED
+    assert q(FAKE, 1, 10, 2048, FAKE, FAKE, None) == B.CSA_ERR_UNSUPPORTED
+    assert q(FAKE, 2, 10, 128, FAKE, FAKE, None) == B.CSA_ERR_UNSUPPORTED
+    v = lib.csa_validate_metadata
+    assert v(None, FAKE, FAKE, None) == B.CSA_ERR_NULL
+
+
+def test_scores_and_topk_validation(lib):
+    p = _params()
+    s = lib.csa_index_scores
+    args = [FAKE, None, FAKE, FAKE, None, FAKE, FAKE, FAKE]
+    assert s(ctypes.byref(p), *args[:7], None, 64, None) == B.CSA_ERR_NULL
+    assert s(ctypes.byref(p), *args, 63, None) == B.CSA_ERR_ARG            # ld < n_cap = 64
+    fp8 = _params(idx_dtype=B.CSA_FP8_E4M3)
+    assert s(ctypes.byref(fp8), *args, 64, None) == B.CSA_ERR_NULL         # scales missing
+    big = _params(idx_dim=512)
+    assert s(ctypes.byref(big), *args, 64, None) == B.CSA_ERR_UNSUPPORTED
+    odd = _params(idx_dim=36)
+    assert s(ctypes.byref(odd), *args, 64, None) == B.CSA_ERR_UNSUPPORTED
+    t = lib.csa_topk_select
+    assert t(ctypes.byref(p), FAKE, 64, FAKE, FAKE, None, None) == B.CSA_ERR_NULL
+    assert t(ctypes.byref(_params(topk_cap=48)), FAKE, 64, FAKE, FAKE, FAKE, None) == B.CSA_ERR_ARG
+    assert t(ctypes.byref(_params(topk=0)), FAKE, 64, FAKE, FAKE, FAKE, None) == B.CSA_ERR_ARG
+    assert t(ctypes.byref(_params(topk=100)), FAKE, 64, FAKE, FAKE, FAKE, None) == B.CSA_ERR_ARG
+    assert t(ctypes.byref(p), FAKE, 10, FAKE, FAKE, FAKE, None) == B.CSA_ERR_ARG
+    huge = _params(total_tokens=1 << 20, max_seqlen=1 << 20)
+    assert t(ctypes.byref(huge), FAKE, 1 << 18, FAKE, FAKE, FAKE, None) == B.CSA_ERR_UNSUPPORTED
+
+
+def test_attention_validation(lib):
+    p = _params()
+    f = lib.csa_sparse_attn_fwd
+    a = [FAKE] * 9
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, None, 0,
+             None) == B.CSA_ERR_NULL                                          # idx for sparse
+    assert f(ctypes.byref(_params(window=0)), *a, None, 0, None) == B.CSA_ERR_ARG
+    assert f(ctypes.byref(_params(scale=0.0)), *a, None, 0, None) == B.CSA_ERR_ARG
+    assert f(ctypes.byref(_params(mode=3)), *a, None, 0, None) == B.CSA_ERR_ARG
+    assert f(ctypes.byref(_params(head_dim=1024)), *a, None, 0, None) == B.CSA_ERR_UNSUPPORTED
+    assert f(ctypes.byref(_params(dtype=B.CSA_FP8_E4M3)), *a, None, 0, None) == B.CSA_ERR_UNSUPPORTED
+    assert f(ctypes.byref(_params(mode=B.CSA_DENSE)), FAKE, None, FAKE, None, None, FAKE, FAKE,
+             FAKE, FAKE, None, 0, None) == B.CSA_ERR_NULL                    # kv_cmp for dense
+    b = lib.csa_sparse_attn_bwd
+    args = [FAKE] * 14
+    assert b(ctypes.byref(p), *args, None, 0, None) == B.CSA_ERR_WORKSPACE
+    assert b(ctypes.byref(p), *args, FAKE, 100, None) == B.CSA_ERR_WORKSPACE
+    args[11] = None                                                          # dq
+    assert b(ctypes.byref(p), *args, FAKE, 1 << 20, None) == B.CSA_ERR_NULL
+
+
+def test_indexer_kl_validation(lib):
+    p = _params()
+    f = lib.csa_indexer_kl
+
+    def call(pp, idx=FAKE, grads=(FAKE, FAKE, FAKE), ld=64, gs=1.0):
+        return f(ctypes.byref(pp), FAKE, FAKE, FAKE, ld, idx, FAKE, None, FAKE, FAKE, None,
+                 FAKE, FAKE, gs, FAKE, FAKE, *grads, None, 0, None)
+
+    assert call(_params(teacher=B.CSA_TEACHER_NONE)) == B.CSA_ERR_ARG
+    assert call(_params(teacher=B.CSA_TEACHER_SELECTED), idx=None) == B.CSA_ERR_NULL
+    assert call(p, grads=(FAKE, None, FAKE)) == B.CSA_ERR_NULL
+    assert call(p, ld=10) == B.CSA_ERR_ARG
+    assert call(p, gs=float("nan")) == B.CSA_ERR_ARG
+    assert call(_params(heads=128)) == B.CSA_ERR_UNSUPPORTED
+    assert call(_params(idx_dtype=B.CSA_FP8_E4M3)) == B.CSA_ERR_NULL
