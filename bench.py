@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Throughput of one CSA/HCA attention-layer step (forward + backward) on one MI355X.
+
+A step is one pass of the whole hot path over one packed THD batch of synthetic
+input (seeded, resident in HBM before timing): compressor (main KV and indexer key),
+[fp8 quantization], indexer scores, top-k, sparse attention forward, indexer KL with
+its eager backward, sparse attention backward and the compressor adjoints.
+Default workload: 8 ragged samples summing to 65536 tokens, ratio-4 CSA, 64 heads,
+KV width 512, top-k 1024, window 128, selected-set KL teacher.
+
+Prints ONE JSON line.  Every ABI call is bracketed by HIP events on the stream it runs
+on, so the line also carries a per-call breakdown and the roofline of the dominant
+kernel; the fp64 CPU oracle is timed on a bounded sample of query rows for the CPU
+baseline (rank 0, N = 1 only).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from synth import configs, inputs  # noqa: E402
+
+PEAK = {"bf16": 2.5e15, "fp8": 5.0e15, "f32": 157.3e12, "hbm": 8.0e12}
+METRIC = "CSA fwd+bwd tokens/s at L=64K THD (with TFLOP/s, % MFMA peak, top-k GB/s)"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="thd64k_csa_bf16", choices=sorted(configs.WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class EventTimer:
+    """HIP events around each ABI call, on torch's current stream (the library's stream)."""
+
+    def __init__(self):
+        self.open = {}
+        self.pairs = {}
+
+    def mark(self, name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.open[name] = e
+
+    def done(self, name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.setdefault(name, []).append((self.open.pop(name), e))
+
+    def mean_ms(self):
+        return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in self.pairs.items()}
+
+
+def work_counts(w, lengths):
+    """Per-step algorithmic work from the packed lengths (no device data needed)."""
+    r, W, k = w.ratio, w.window, w.topk
+    cand = 0          # sum_t |X_t|: attended rows per query (compressed + window)
+    vis = 0           # sum_t n_vis(t)
+    vis_read = 0      # visible scores top-k must read (rows with n_vis > k)
+    sel = 0           # sum_t |S_t| (or all visible in dense mode)
+    tcmp = 0
+    for L in lengths:
+        p = np.arange(L, dtype=np.int64)
+        nv = (p + 1) // r
+        win = np.minimum(W, p + 1)
+        if w.mode == "sparse":
+            s = np.minimum(k, nv)
+        elif w.mode == "dense":
+            s = nv
+        else:
+            s = np.zeros_like(nv)
+        cand += int((s + win).sum())
+        vis += int(nv.sum())
+        vis_read += int(nv[nv > k].sum()) if w.mode == "sparse" else 0
+        sel += int(s.sum())
+        tcmp += L // r
+    return dict(cand=cand, vis=vis, vis_read=vis_read, sel=sel, tcmp=tcmp,
+                tokens=int(sum(lengths)))
+
+
+def roofline_table(w, c, T):
+    """(bound, algorithmic amount per launch, unit, peak) per ABI call."""
+    H, D, HI, dI = w.heads, w.head_dim, w.idx_heads, w.idx_dim
+    e = 4 if w.dtype == "f32" else 2
+    ei = 1 if w.idx_dtype == "fp8" else (4 if w.idx_dtype == "f32" else 2)
+    mm = "bf16" if w.dtype == "bf16" else "f32"
+    teach = c["vis"] if w.teacher == "dense" else c["sel"]
+    kl_flops = 2 * D * H * teach * (2 if w.teacher == "dense" else 1) + 4 * dI * HI * teach
+    tab = {
+        "compress_kv": ("hbm", c["tokens"] * D * e + c["tcmp"] * D * e),
+        "compress_kI": ("hbm", c["tokens"] * dI * 2 + c["tcmp"] * dI * 2),
+        "quantize_qI": ("hbm", c["tokens"] * HI * dI * (2 + 1) + c["tokens"] * HI * 4),
+        "quantize_kI": ("hbm", c["tcmp"] * dI * (2 + 1) + c["tcmp"] * 4),
+        "index_scores": ("fp8" if w.idx_dtype == "fp8" else mm, 2 * dI * HI * c["vis"]),
+        "topk_select": ("hbm", 4 * c["vis_read"] + 4 * T * max(w.topk_cap, 1)),
+        "attn_fwd": (mm, 4 * D * H * c["cand"]),
+        "indexer_kl": (mm, kl_flops),
+        "attn_bwd": (mm, 10 * D * H * c["cand"]),
+        "compress_bwd_kv": ("hbm", c["tcmp"] * D * 4 + 2 * c["tcmp"] * w.ratio * D * 4),
+        "compress_bwd_kI": ("hbm", c["tcmp"] * dI * 4 + 2 * c["tcmp"] * w.ratio * dI * 4),
+    }
+    _ = ei
+    return tab
+
+
+def cpu_baseline(w, host, budget_s):
+    """The fp64 oracle, as it stands, on evenly spaced query rows of the same workload."""
+    from oracle import csa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    n_real = int(host["cu_seqlens"][-1])
+    T = w.total_tokens
+    h64 = {"cu_seqlens": host["cu_seqlens"], "max_seqlen": host["max_seqlen"]}
+    # full-size arrays are only touched on the sampled rows (zero pages stay unallocated)
+    for key in ("kv", "kI_tok"):
+        if key in host:
+            h64[key] = inputs.to_f64(host[key])
+    if "sink" in host:
+        h64["sink"] = inputs.to_f64(host["sink"])
+
+    def rows_view(sample):
+        for key in ("q", "qI", "w", "dO"):
+            if key in host:
+                a = np.zeros(tuple(host[key].shape), dtype=np.float64)
+                a[sample] = inputs.to_f64(host[key][torch.as_tensor(sample)])
+                h64[key] = a
+
+    def run(n):
+        sample = np.unique(np.linspace(0, n_real - 1, n).astype(np.int64))
+        rows_view(sample)
+        t0 = time.perf_counter()
+        O.layer_step(h64, w, rows=sample)
+        return time.perf_counter() - t0, sample.size
+
+    t_fixed, _ = run(1)                      # one row + the full-size compressor passes
+    t2, n2 = run(min(64, n_real))
+    per_row = max((t2 - t_fixed) / max(n2 - 1, 1), 1e-5)
+    # sample size: fill the budget, bounded so the sampled rows stay a few GB of host memory
+    n = int(min(n_real, 4096, max(64, (budget_s - t_fixed) / per_row)))
+    t, n = run(n)
+    per_row = max((t - t_fixed) / max(n - 1, 1), 1e-9)
+    est = t_fixed + per_row * (n_real - 1)
+    return {"value": n_real / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} of {n_real} query rows, evenly spaced, plus the full-size compressor "
+                      f"and compressor-adjoint passes ({t:.1f} s measured); whole-step time "
+                      f"extrapolated linearly in the number of query rows"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (no collectives or "
+              "sharding); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    from long_context_compressed_amd import binding
+    from long_context_compressed_amd.pipeline import CsaLayer, LayerConfig, to_device
+    binding.lib()
+    w = configs.workload(args.workload)
+    t0 = time.time()
+    host = inputs.make_inputs(w)
+    dev = to_device(host)
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s workload={w.name} "
+          f"lengths={host['lengths']}", file=sys.stderr, flush=True)
+    layer = CsaLayer(LayerConfig.of(w), len(host["lengths"]), w.total_tokens,
+                     host["max_seqlen"], backward=w.backward)
+    cu = dev["cu_seqlens"]
+    for i in range(args.warmup):
+        layer.step(dev, cu)
+        torch.cuda.synchronize()
+        print(f"[bench] warmup step {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+    timer = EventTimer()
+    layer.timer = timer
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        layer.step(dev, cu)
+    end.record()
+    torch.cuda.synchronize()
+    layer.timer = None
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / max(args.steps, 1)
+    per_call = timer.mean_ms()
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    c = work_counts(w, host["lengths"])
+    tab = roofline_table(w, c, w.total_tokens)
+    breakdown = {}
+    for name, t in per_call.items():
+        bound, amount = tab.get(name, ("", 0))
+        ent = {"ms": round(t, 4)}
+        if bound == "hbm" and t > 0:
+            ent["GB/s"] = round(amount / (t * 1e-3) / 1e9, 1)
+            ent["frac_hbm"] = round(amount / (t * 1e-3) / PEAK["hbm"], 4)
+        elif bound and t > 0:
+            ent["TFLOP/s"] = round(amount / (t * 1e-3) / 1e12, 2)
+            ent["frac_mfma"] = round(amount / (t * 1e-3) / PEAK[bound], 4)
+        breakdown[name] = ent
+    dom = max(per_call, key=per_call.get)
+    bound, amount = tab[dom]
+    tdom = per_call[dom] * 1e-3
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": amount / tdom / 1e9, "peak": PEAK["hbm"] / 1e9,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": amount / tdom / 1e12, "peak": PEAK[bound] / 1e12,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["algorithmic_per_launch"] = amount
+    tokens = c["tokens"]
+    value = tokens / (ms * 1e-3)
+    attn_ms = per_call.get("attn_fwd", 0) + per_call.get("attn_bwd", 0)
+    attn_flops = tab["attn_fwd"][1] + (tab["attn_bwd"][1] if w.backward else 0)
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "tokens": tokens, "samples": len(host["lengths"]),
+                   "lengths": host["lengths"], "heads": w.heads, "head_dim": w.head_dim,
+                   "ratio": w.ratio, "window": w.window, "topk": w.topk, "mode": w.mode,
+                   "idx_heads": w.idx_heads, "idx_dim": w.idx_dim, "idx_dtype": w.idx_dtype,
+                   "teacher": w.teacher, "pass": "fwd+bwd" if w.backward else "fwd"},
+        "roofline": roof,
+        "attention_tflops": attn_flops / max(attn_ms * 1e-3, 1e-12) / 1e12 if attn_ms else None,
+        "topk_gbps": breakdown.get("topk_select", {}).get("GB/s"),
+        "breakdown": breakdown,
+        "work": c,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

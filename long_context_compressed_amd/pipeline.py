@@ -54,6 +54,7 @@ class CsaLayer:
     def __init__(self, cfg: LayerConfig, batch: int, total_tokens: int, max_seqlen: int,
                  device="cuda", backward: bool = True, grad_scale: float = 1.0):
         self.cfg = cfg
+        self.timer = None          # optional object with mark(name) / done(name) around calls
         self.backward = backward
         self.grad_scale = grad_scale
         dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
@@ -105,35 +106,47 @@ class CsaLayer:
         return torch.empty(max(n, 1), dtype=torch.uint8, device=device) if n else None
 
     # ------------------------------------------------------------------ steps
+    def _call(self, name, fn, *args):
+        if self.timer is not None:
+            self.timer.mark(name)
+        fn(*args)
+        if self.timer is not None:
+            self.timer.done(name)
+
     def metadata(self, cu_seqlens):
-        B.csa_cmp_seqlens(cu_seqlens, self.B, self.cfg.ratio, self.cu_cmp)
+        self._call("cmp_seqlens", B.csa_cmp_seqlens, cu_seqlens, self.B, self.cfg.ratio,
+                   self.cu_cmp)
 
     def forward(self, inp, cu_seqlens):
         """inp: dict of device tensors q, kv, [qI, kI_tok, w], [sink]."""
         cfg, p = self.cfg, self.p
-        B.csa_compress(p, inp["kv"], cu_seqlens, self.cu_cmp, self.kv_cmp)
+        self._call("compress_kv", B.csa_compress, p, inp["kv"], cu_seqlens, self.cu_cmp,
+                   self.kv_cmp)
         idx = None
         if cfg.has_indexer:
-            B.csa_compress(p, inp["kI_tok"], cu_seqlens, self.cu_cmp, self.kI_cmp)
+            self._call("compress_kI", B.csa_compress, p, inp["kI_tok"], cu_seqlens, self.cu_cmp,
+                       self.kI_cmp)
             if cfg.idx_dtype == "fp8":
-                B.csa_quantize_fp8(inp["qI"], self.qI8, self.qI_scale)
-                B.csa_quantize_fp8(self.kI_cmp, self.kI8, self.kI_scale)
+                self._call("quantize_qI", B.csa_quantize_fp8, inp["qI"], self.qI8, self.qI_scale)
+                self._call("quantize_kI", B.csa_quantize_fp8, self.kI_cmp, self.kI8, self.kI_scale)
                 qI, qs, kI, ks = self.qI8, self.qI_scale, self.kI8, self.kI_scale
             else:
                 qI, qs, kI, ks = inp["qI"], None, self.kI_cmp, None
-            B.csa_index_scores(p, qI, qs, inp["w"], kI, ks, cu_seqlens, self.cu_cmp, self.scores)
-            B.csa_topk_select(p, self.scores, cu_seqlens, self.cu_cmp, self.idx)
+            self._call("index_scores", B.csa_index_scores, p, qI, qs, inp["w"], kI, ks, cu_seqlens,
+                       self.cu_cmp, self.scores)
+            self._call("topk_select", B.csa_topk_select, p, self.scores, cu_seqlens, self.cu_cmp,
+                       self.idx)
             idx = self.idx
-        B.csa_sparse_attn_fwd(p, inp["q"], self.kv_cmp, inp["kv"], idx, inp.get("sink"),
-                              cu_seqlens, self.cu_cmp, self.out, self.lse, self.ws_fwd)
+        self._call("attn_fwd", B.csa_sparse_attn_fwd, p, inp["q"], self.kv_cmp, inp["kv"], idx,
+                   inp.get("sink"), cu_seqlens, self.cu_cmp, self.out, self.lse, self.ws_fwd)
         if cfg.has_indexer and cfg.teacher != "none":
             grads = self.backward
             if grads:
                 self.dkI_cmp.zero_()
-            B.csa_indexer_kl(p, inp["q"], self.kv_cmp, self.scores, self.idx, qI, qs, inp["w"],
-                             kI, ks, cu_seqlens, self.cu_cmp, self.grad_scale, self.kl, self.loss,
-                             self.dqI if grads else None, self.dw if grads else None,
-                             self.dkI_cmp if grads else None, self.ws_kl)
+            self._call("indexer_kl", B.csa_indexer_kl, p, inp["q"], self.kv_cmp, self.scores,
+                       self.idx, qI, qs, inp["w"], kI, ks, cu_seqlens, self.cu_cmp,
+                       self.grad_scale, self.kl, self.loss, self.dqI if grads else None,
+                       self.dw if grads else None, self.dkI_cmp if grads else None, self.ws_kl)
 
     def backward_step(self, inp, cu_seqlens):
         cfg, p = self.cfg, self.p
@@ -142,14 +155,16 @@ class CsaLayer:
         sink = inp.get("sink")
         if sink is not None:
             self.dsink.zero_()
-        B.csa_sparse_attn_bwd(p, inp["q"], self.kv_cmp, inp["kv"],
-                              self.idx if cfg.has_indexer else None, sink, cu_seqlens,
-                              self.cu_cmp, self.out, self.lse, inp["dO"], self.dq, self.dkv_cmp,
-                              self.dkv, self.dsink if sink is not None else None, self.ws_bwd)
-        B.csa_compress_bwd(p, self.dkv_cmp, cu_seqlens, self.cu_cmp, self.dkv)
+        self._call("attn_bwd", B.csa_sparse_attn_bwd, p, inp["q"], self.kv_cmp, inp["kv"],
+                   self.idx if cfg.has_indexer else None, sink, cu_seqlens, self.cu_cmp, self.out,
+                   self.lse, inp["dO"], self.dq, self.dkv_cmp, self.dkv,
+                   self.dsink if sink is not None else None, self.ws_bwd)
+        self._call("compress_bwd_kv", B.csa_compress_bwd, p, self.dkv_cmp, cu_seqlens,
+                   self.cu_cmp, self.dkv)
         if cfg.has_indexer and cfg.teacher != "none":
             self.dkI_tok.zero_()
-            B.csa_compress_bwd(p, self.dkI_cmp, cu_seqlens, self.cu_cmp, self.dkI_tok)
+            self._call("compress_bwd_kI", B.csa_compress_bwd, p, self.dkI_cmp, cu_seqlens,
+                       self.cu_cmp, self.dkI_tok)
 
     def step(self, inp, cu_seqlens):
         self.metadata(cu_seqlens)

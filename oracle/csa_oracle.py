@@ -417,7 +417,7 @@ def layer_step(inp, cfg, rows=None, backward=None, grad_scale=1.0):
         kI_cmp = compress(inp["kI_tok"], cu, r)
         qI = inp["qI"]
         if cfg.idx_dtype == "fp8":
-            qI = np.zeros_like(qI)
+            qI = np.zeros(qI.shape)          # untouched pages stay unallocated
             qc, qs = quantize_fp8(inp["qI"][rows].astype(np.float32))
             qI[rows] = dequantize_fp8(qc, qs)
             kc, ks = quantize_fp8(kI_cmp.astype(np.float32))

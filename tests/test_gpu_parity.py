@@ -432,4 +432,5 @@ def test_forward_deterministic(name):
         torch.cuda.synchronize()
         outs.append([t.clone() for t in (L.kv_cmp, L.kI_cmp, L.scores, L.idx, L.out, L.lse)])
     for a, b in zip(*outs):
-        assert torch.equal(a, b)
+        # bitwise: unwritten capacity rows hold arbitrary bits (NaN included)
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
