@@ -1,20 +1,637 @@
-// Matrix-core (MFMA) sparse attention for bf16, H = 64 heads, D = 512 on gfx950.
-// (Filled in by the MFMA kernels; until a shape is covered here the scalar kernels run.)
+// Matrix-core (MFMA) sparse attention for bf16 operands, H = 64 heads sharing one
+// D = 512 K=V row (MQA), on gfx950.
+//
+// Method ("DeepSeek-V4 Attention Training Systems", sections 2 and 8.2): each query
+// attends its selected (or all visible) compressed rows plus its local raw window;
+// forward returns O and the log-sum-exp.
+//
+// Forward design: one workgroup (4 waves) per query token; the 64 heads form the M
+// dimension of every product, so each gathered 1 KiB row feeds 64 x 512 x 4 FLOP.
+// Wave w owns the 128-wide slice D_w of the row:
+//   1. it loads K[c, D_w] for a block of 64 candidates straight from HBM/L2 into MFMA
+//      A-operand registers (16-byte loads, one row segment per lane);
+//   2. S^T_w = K[:, D_w] Q[:, D_w]^T on v_mfma_f32_16x16x32_bf16 (Q slice resident in
+//      registers for the whole token);
+//   3. the four partial S_w are summed through LDS; wave w runs the online softmax of
+//      heads 16w..16w+15 and publishes P (bf16) and the per-head rescale factors;
+//   4. the same K registers, written once to a wave-private transposed LDS tile, are
+//      the B operand of O[:, D_w] += P V[:, D_w].
+// Every gathered byte is read from memory once per token.  Tokens are mapped to
+// workgroups so that each XCD walks contiguous 256-token chunks (its L2 then holds the
+// compressed rows of one sample).
+#include <math.h>
+
 #include "csa_device.h"
 #include "csa_launch.h"
 
 namespace csa {
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int kH = 64;
+constexpr int kD = 512;
+constexpr int kDW = 128;    // d per wave
+constexpr int kNB = 64;     // candidates per block
+constexpr int kSPS = 68;    // row stride (floats) of the partial-S tiles
+constexpr int kPS = 72;     // row stride (bf16) of the P tile
+constexpr int kVTS = 72;    // row stride (bf16) of the transposed V tiles
+constexpr int kChunk = 256; // tokens per XCD chunk
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* kv_cmp;
+  const uint16_t* kv;
+  const int32_t* idx;
+  const float* sink;
+  const int32_t* cu;
+  const int32_t* cu_cmp;
+  uint16_t* out;
+  float* lse;
+  int B, T, r, n_cap, W, k_cap, mode;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+__device__ __forceinline__ bf16x8 ld16(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Workgroup -> token: XCD x = bid % 8 takes 256-token chunks x, x+8, x+16, ...
+__device__ __forceinline__ int token_of_block(int bid) {
+  const int x = bid & 7, j = bid >> 3;
+  return (j / kChunk) * (8 * kChunk) + x * kChunk + (j % kChunk);
+}
+
+// First -1 of an idx row; every lane gets it.
+__device__ int leading_valid(const int32_t* __restrict__ row, int k_cap, int* s_tmp) {
+  if (threadIdx.x == 0) *s_tmp = k_cap;
+  __syncthreads();
+  for (int c = threadIdx.x; c < k_cap; c += blockDim.x)
+    if (row[c] < 0) atomicMin(s_tmp, c);
+  __syncthreads();
+  const int n = *s_tmp;
+  __syncthreads();
+  return n;
+}
+
+struct CandSet {
+  int n_c, n_w, row0, nv, win0;
+};
+
+// Pointer to the row of candidate slot c, or nullptr for a masked / absent slot.
+__device__ __forceinline__ const uint16_t* cand_ptr(const FwdArgs& a, int t, const CandSet& cs,
+                                                    int c) {
+  if (c < cs.n_c) {
+    const int g = a.mode == 1 ? cs.row0 + c : a.idx[(int64_t)t * a.k_cap + c];
+    return (g >= cs.row0 && g < cs.row0 + cs.nv) ? a.kv_cmp + (int64_t)g * kD : nullptr;
+  }
+  if (c < cs.n_c + cs.n_w) return a.kv + (int64_t)(cs.win0 + (c - cs.n_c)) * kD;
+  return nullptr;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_attn_fwd_mfma(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float Sp[4][kH][kSPS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[kH][kPS];
+  __shared__ __attribute__((aligned(16))) uint16_t VT[4][kDW][kVTS];
+  __shared__ float alpha_s[kH];
+  __shared__ float fin_s[kH];
+  __shared__ int valid_s[kNB];
+  __shared__ int s_tmp;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;     // lane group (k-slot of the MFMA operands)
+  const int c16 = lane & 15;   // row / column within a 16-wide tile
+  const int t = token_of_block(blockIdx.x);
+  if (t >= a.T) return;
+
+  TokenInfo ti;
+  if (!token_info(a.cu, a.B, t, ti)) {
+    uint4* o = reinterpret_cast<uint4*>(a.out + (int64_t)t * kH * kD);
+    for (int e = threadIdx.x; e < kH * kD / 8; e += 256) o[e] = make_uint4(0, 0, 0, 0);
+    if (threadIdx.x < kH) a.lse[(int64_t)t * kH + threadIdx.x] = 0.f;
+    return;
+  }
+  CandSet cs;
+  cs.row0 = a.cu_cmp[ti.b];
+  cs.nv = min((ti.p + 1) / a.r, a.n_cap);
+  cs.n_w = min(a.W, ti.p + 1);
+  cs.win0 = t - cs.n_w + 1;
+  if (a.mode == 1) cs.n_c = cs.nv;
+  else if (a.mode == 2) cs.n_c = 0;
+  else cs.n_c = leading_valid(a.idx + (int64_t)t * a.k_cap, a.k_cap, &s_tmp);
+  const int n_tot = cs.n_c + cs.n_w;
+  const int dw = wave * kDW;
+
+  // Q^T as the B operand: qb[nt][ks] = Q[16nt + c16][dw + 32ks + 8g .. +7]
+  bf16x8 qb[4][4];
+  const uint16_t* qt = a.q + (int64_t)t * kH * kD;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[nt][ks] = ld16(qt + (16 * nt + c16) * kD + dw + 32 * ks + 8 * g);
+
+  f32x4 o[4][8];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) o[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int hl = lane >> 2, cq = lane & 3;   // softmax lane: head 16*wave+hl, candidates 16cq..
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int c0 = 0; c0 < n_tot; c0 += kNB) {
+    // ---- gather K[c, D_w] for the 64 candidates of this block
+    bf16x8 kr[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int c = c0 + 16 * mt + c16;
+      const uint16_t* src = cand_ptr(a, t, cs, c);
+      if (wave == 0 && g == 0) valid_s[16 * mt + c16] = src != nullptr;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (src) kr[mt][ks] = ld16(src + dw + 32 * ks + 8 * g);
+        else kr[mt][ks] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+      }
+    }
+    // ---- partial S^T over this wave's d slice
+    f32x4 st[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma16(kr[mt][ks], qb[nt][ks], acc);
+        st[mt][nt] = acc;
+      }
+    // ---- K slice -> wave-private transposed tile VT[d][c] (column swizzle 16*((d/8)%4))
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 bits = __builtin_bit_cast(uint4, kr[mt][ks]);
+        const uint32_t w4[4] = {bits.x, bits.y, bits.z, bits.w};
+        const int col = (16 * mt + c16) ^ (16 * g);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int d = 32 * ks + 8 * g + i;
+          VT[wave][d][col] = (uint16_t)((i & 1) ? (w4[i >> 1] >> 16) : (w4[i >> 1] & 0xffffu));
+        }
+      }
+    // ---- publish partial S as [h][c]
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        *reinterpret_cast<f32x4*>(&Sp[wave][16 * nt + c16][16 * mt + 4 * g]) = st[mt][nt];
+    __syncthreads();
+
+    // ---- reduce the four partials; online softmax of head 16*wave+hl
+    {
+      const int h = 16 * wave + hl;
+      float s[16];
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        f32x4 acc = *reinterpret_cast<const f32x4*>(&Sp[0][h][16 * cq + 4 * j4]);
+#pragma unroll
+        for (int w2 = 1; w2 < 4; ++w2) acc += *reinterpret_cast<const f32x4*>(&Sp[w2][h][16 * cq + 4 * j4]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[4 * j4 + i] = acc[i];
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        s[j] = valid_s[16 * cq + j] ? s[j] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, s[j]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+      const float m_new = fmaxf(m_run, mx);
+      float alpha = 1.f, sum = 0.f;
+      uint32_t pw[8];
+      if (m_new == -INFINITY) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pw[j] = 0u;
+      } else {
+        alpha = exp2f(m_run - m_new);
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+          const float p0 = exp2f(s[j] - m_new), p1 = exp2f(s[j + 1] - m_new);
+          sum += p0 + p1;
+          pw[j >> 1] = (uint32_t)f32_to_bf16_bits(p0) | ((uint32_t)f32_to_bf16_bits(p1) << 16);
+        }
+      }
+      sum += __shfl_xor(sum, 1, 64);
+      sum += __shfl_xor(sum, 2, 64);
+      l_run = l_run * alpha + sum;
+      m_run = m_new;
+      *reinterpret_cast<uint4*>(&Ps[h][16 * cq]) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+      *reinterpret_cast<uint4*>(&Ps[h][16 * cq + 8]) = make_uint4(pw[4], pw[5], pw[6], pw[7]);
+      if (cq == 0) alpha_s[h] = alpha;
+    }
+    __syncthreads();
+
+    // ---- O[:, D_w] = alpha * O + P V[:, D_w]
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float al = alpha_s[16 * mt + 4 * g + i];
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) o[mt][nt][i] *= al;
+      }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 pa[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) pa[mt] = ld16(&Ps[16 * mt + c16][32 * kk + 8 * g]);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const int d = 16 * nt + c16;
+        const bf16x8 vb = ld16(&VT[wave][d][(32 * kk + 8 * g) ^ (16 * ((d >> 3) & 3))]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) o[mt][nt] = mfma16(pa[mt], vb, o[mt][nt]);
+      }
+    }
+  }
+
+  // ---- finalize: lse and 1/l (with the optional sink), then store O
+  if (cq == 0) {
+    const int h = 16 * wave + hl;
+    const float ln2 = 0.69314718055994531f;
+    float mf = m_run, lf = l_run;
+    if (a.sink) {
+      const float sk = a.sink[h] * 1.44269504088896341f;
+      mf = fmaxf(m_run, sk);
+      lf = l_run * exp2f(m_run - mf) + exp2f(sk - mf);
+    }
+    a.lse[(int64_t)t * kH + h] = (mf + log2f(lf)) * ln2;
+    fin_s[h] = exp2f(m_run - mf) / lf;
+  }
+  __syncthreads();
+  uint16_t* op = a.out + (int64_t)t * kH * kD + dw;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 16 * mt + 4 * g + i;
+      const float f = fin_s[h];
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) op[h * kD + 16 * nt + c16] = f32_to_bf16_bits(o[mt][nt][i] * f);
+    }
+}
+
 hipError_t launch_attn_fwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s, bool* handled) {
-  (void)sh; (void)io; (void)s;
   *handled = false;
-  return hipSuccess;
+  if (sh.dtype != 1 || sh.H != kH || sh.D != kD) return hipSuccess;
+  *handled = true;
+  FwdArgs a;
+  a.q = (const uint16_t*)io.q;
+  a.kv_cmp = (const uint16_t*)io.kv_cmp;
+  a.kv = (const uint16_t*)io.kv;
+  a.idx = io.idx;
+  a.sink = io.sink;
+  a.cu = sh.cu;
+  a.cu_cmp = sh.cu_cmp;
+  a.out = (uint16_t*)io.out;
+  a.lse = io.lse;
+  a.B = sh.B;
+  a.T = sh.T;
+  a.r = sh.r;
+  a.n_cap = sh.max_seqlen / sh.r;
+  a.W = sh.W;
+  a.k_cap = sh.k_cap;
+  a.mode = sh.mode;
+  a.scale_log2 = sh.scale * 1.44269504088896341f;
+  const int64_t chunks = ((int64_t)sh.T + 8 * kChunk - 1) / (8 * kChunk);
+  const int64_t grid = chunks * 8 * kChunk;
+  hipLaunchKernelGGL(k_attn_fwd_mfma, dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ======================================================================== backward
+//
+// Kernel 1 (k_attn_bwd_dq_mfma): one workgroup per query token, wave w owns heads
+// 16w..16w+15 over the whole row.  Per block of 32 candidates the rows are staged once in
+// LDS (row-major); each wave recomputes S^T and dP^T for its heads on MFMA (A = rows from
+// LDS, B = its Q / dO slice resident in registers), forms P = e^{S - LSE} and
+// dS = P (dP - Dt) in fp32, stores scale*dS and P (bf16) for kernel 2, and accumulates
+// dq += (scale dS) K with the row tile as a transposed B operand (ds_read_b64_tr_b16).
+// The S^T result layout (lane = head, 4 candidates per m-tile) is reused directly as the
+// A operand of the dq product by ordering the 32 candidates of a k-step as
+// {4g..4g+3, 16+4g..16+4g+3} for lane group g.
+//
+// Kernel 2 (k_attn_bwd_dkv_mfma): one workgroup per query token, wave w owns d-slice
+// 128w..128w+127.  Q and dO of the token are staged once in LDS and read transposed into
+// registers as the B operand [scale Q... ; dO] (k = 64 heads of dS then 64 heads of P);
+// per block of 64 candidates d row = [scale dS | P]^T [Q; dO] on MFMA, then the fp32
+// result is scatter-added into dkv_cmp (compressed rows) or dkv (window rows).
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int kNB1 = 32;          // candidates per block, kernel 1
+constexpr int kKS = kD + 16;      // row stride (bf16) of LDS row tiles
+constexpr int kNB2 = 64;          // candidates per block, kernel 2
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* kv_cmp;
+  const uint16_t* kv;
+  const int32_t* idx;
+  const float* sink;
+  const int32_t* cu;
+  const int32_t* cu_cmp;
+  const uint16_t* o;
+  const float* lse;
+  const uint16_t* dout;
+  uint16_t* dq;
+  float* dkv_cmp;
+  float* dkv;
+  float* dsink;
+  uint16_t* pds;     // workspace [T][n_slots][128]: scale*dS (64 heads) then P (64 heads)
+  int64_t n_slots;
+  int B, T, r, n_cap, W, k_cap, mode;
+  float scale, scale_log2;
+};
+
+__device__ __forceinline__ FwdArgs as_fwd(const BwdArgs& b) {
+  FwdArgs a;
+  a.q = b.q; a.kv_cmp = b.kv_cmp; a.kv = b.kv; a.idx = b.idx; a.sink = b.sink; a.cu = b.cu;
+  a.cu_cmp = b.cu_cmp; a.out = nullptr; a.lse = nullptr; a.B = b.B; a.T = b.T; a.r = b.r;
+  a.n_cap = b.n_cap; a.W = b.W; a.k_cap = b.k_cap; a.mode = b.mode; a.scale_log2 = b.scale_log2;
+  return a;
+}
+
+__device__ __forceinline__ v4i16 ld_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(p));
+}
+
+__device__ __forceinline__ bf16x8 join8(v4i16 lo, v4i16 hi) {
+  const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+__device__ __forceinline__ CandSet make_cands(const FwdArgs& a, int t, const TokenInfo& ti,
+                                              int* s_tmp) {
+  CandSet cs;
+  cs.row0 = a.cu_cmp[ti.b];
+  cs.nv = min((ti.p + 1) / a.r, a.n_cap);
+  cs.n_w = min(a.W, ti.p + 1);
+  cs.win0 = t - cs.n_w + 1;
+  if (a.mode == 1) cs.n_c = cs.nv;
+  else if (a.mode == 2) cs.n_c = 0;
+  else cs.n_c = leading_valid(a.idx + (int64_t)t * a.k_cap, a.k_cap, s_tmp);
+  return cs;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_attn_bwd_dq_mfma(BwdArgs b) {
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][kNB1][kKS];
+  __shared__ int valid_s[2][kNB1];
+  __shared__ int s_tmp;
+  const FwdArgs a = as_fwd(b);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int t = token_of_block(blockIdx.x);
+  if (t >= b.T) return;
+  TokenInfo ti;
+  if (!token_info(b.cu, b.B, t, ti)) {
+    uint4* o = reinterpret_cast<uint4*>(b.dq + (int64_t)t * kH * kD);
+    for (int e = tid; e < kH * kD / 8; e += 256) o[e] = make_uint4(0, 0, 0, 0);
+    return;
+  }
+  const CandSet cs = make_cands(a, t, ti, &s_tmp);
+  const int n_tot = cs.n_c + cs.n_w;
+  const int h = 16 * wave + c16;  // this lane's head for S^T / dP^T (n index)
+
+  // B operands: Q[h][32ks + 8g ..] and dO[h][...]; Dt = dO . O for head h
+  bf16x8 qb[16], gb[16];
+  const int64_t rowq = ((int64_t)t * kH + h) * kD;
+  float dt = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) {
+    qb[ks] = ld16(b.q + rowq + 32 * ks + 8 * g);
+    gb[ks] = ld16(b.dout + rowq + 32 * ks + 8 * g);
+    float ov[8], gv[8];
+    load8(b.o + rowq + 32 * ks + 8 * g, ov);
+    load8(b.dout + rowq + 32 * ks + 8 * g, gv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dt = fmaf(ov[i], gv[i], dt);
+  }
+  dt += __shfl_xor(dt, 16, 64);
+  dt += __shfl_xor(dt, 32, 64);
+  const float lse_t = b.lse[(int64_t)t * kH + h];
+  const float lse2 = lse_t * 1.44269504088896341f;
+
+  f32x4 dq[32];
+#pragma unroll
+  for (int nt = 0; nt < 32; ++nt) dq[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // cooperative row loads: 8 x 16 B per lane, one full row per wave instruction
+  auto load_block = [&](int c0, int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 4 * i + wave;
+      const uint16_t* src = cand_ptr(a, t, cs, c0 + row);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (src) v = *reinterpret_cast<const uint4*>(src + 8 * lane);
+      *reinterpret_cast<uint4*>(&Kt[buf][row][8 * lane]) = v;
+      if (lane == 0) valid_s[buf][row] = src != nullptr;
+    }
+  };
+
+  uint16_t* pds_t = b.pds + (int64_t)t * b.n_slots * 128;
+  int buf = 0;
+  if (n_tot > 0) load_block(0, 0);
+  for (int c0 = 0; c0 < n_tot; c0 += kNB1, buf ^= 1) {
+    __syncthreads();
+    if (c0 + kNB1 < n_tot) load_block(c0 + kNB1, buf ^ 1);
+    // S^T, dP^T for 32 candidates x this wave's 16 heads
+    f32x4 st[2], gt[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      gt[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const bf16x8 av = ld16(&Kt[buf][16 * mt + c16][32 * ks + 8 * g]);
+        st[mt] = mfma16(av, qb[ks], st[mt]);
+        gt[mt] = mfma16(av, gb[ks], gt[mt]);
+      }
+    }
+    // P, scale*dS for candidates c = c0 + 16mt + 4g + i, head h
+    uint32_t dsw[4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int cl = 16 * mt + 4 * g + i;
+        float p = 0.f, ds = 0.f;
+        if (valid_s[buf][cl]) {
+          p = exp2f(st[mt][i] * b.scale_log2 - lse2);
+          ds = b.scale * p * (gt[mt][i] - dt);
+        }
+        const uint16_t pb = f32_to_bf16_bits(p), db = f32_to_bf16_bits(ds);
+        uint16_t* dst = pds_t + (int64_t)(c0 + cl) * 128;
+        dst[h] = db;
+        dst[64 + h] = pb;
+        const int k = 4 * mt + i;   // k-slot of the dq product
+        if (k & 1) dsw[k >> 1] |= (uint32_t)db << 16;
+        else dsw[k >> 1] = db;
+      }
+    const bf16x8 dsa = __builtin_bit_cast(bf16x8, make_uint4(dsw[0], dsw[1], dsw[2], dsw[3]));
+    // dq[h'][d] += sum_c dS[h'][c] K[c][d]; B = rows {4g..4g+3, 16+4g..16+4g+3} of the tile
+    const int jr = c16 >> 2, jc = 4 * (c16 & 3);
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) {
+      const v4i16 lo = ld_tr(&Kt[buf][4 * g + jr][16 * nt + jc]);
+      const v4i16 hi = ld_tr(&Kt[buf][16 + 4 * g + jr][16 * nt + jc]);
+      dq[nt] = mfma16(dsa, join8(lo, hi), dq[nt]);
+    }
+  }
+  // dq rows h' = 16 wave + 4g + i, columns 16nt + c16
+  uint16_t* dqp = b.dq + (int64_t)t * kH * kD;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = 16 * wave + 4 * g + i;
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) dqp[hh * kD + 16 * nt + c16] = f32_to_bf16_bits(dq[nt][i]);
+  }
+  if (b.sink && b.dsink && g == 0)
+    atomicAdd(b.dsink + h, -expf(b.sink[h] - lse_t) * dt);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_attn_bwd_dkv_mfma(BwdArgs b) {
+  __shared__ __attribute__((aligned(16))) uint16_t QO[2 * kH][kKS];
+  __shared__ int s_tmp;
+  const FwdArgs a = as_fwd(b);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int t = token_of_block(blockIdx.x);
+  if (t >= b.T) return;
+  TokenInfo ti;
+  if (!token_info(b.cu, b.B, t, ti)) return;
+  const CandSet cs = make_cands(a, t, ti, &s_tmp);
+  const int n_tot = cs.n_c + cs.n_w;
+  // stage Q (rows 0..63) and dO (rows 64..127) of the token
+  const uint16_t* qt = b.q + (int64_t)t * kH * kD;
+  const uint16_t* gt = b.dout + (int64_t)t * kH * kD;
+  for (int e = tid; e < 2 * kH * (kD / 8); e += 256) {
+    const int row = e / (kD / 8), ch = e % (kD / 8);
+    const uint16_t* src = row < kH ? qt + row * kD : gt + (row - kH) * kD;
+    *reinterpret_cast<uint4*>(&QO[row][8 * ch]) = *reinterpret_cast<const uint4*>(src + 8 * ch);
+  }
+  __syncthreads();
+  const int dw = wave * kDW;
+  const int jr = c16 >> 2, jc = 4 * (c16 & 3);
+  bf16x8 bo[8][4];   // [n-tile of d][k-step of h']
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const v4i16 lo = ld_tr(&QO[32 * ks + 8 * g + jr][dw + 16 * nt + jc]);
+      const v4i16 hi = ld_tr(&QO[32 * ks + 8 * g + 4 + jr][dw + 16 * nt + jc]);
+      bo[nt][ks] = join8(lo, hi);
+    }
+  const uint16_t* pds_t = b.pds + (int64_t)t * b.n_slots * 128;
+  for (int c0 = 0; c0 < n_tot; c0 += kNB2) {
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      bf16x8 av[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        av[ks] = ld16(pds_t + (int64_t)(c0 + 16 * mt + c16) * 128 + 32 * ks + 8 * g);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) x = mfma16(av[ks], bo[nt][ks], x);
+        acc[mt][nt] = x;
+      }
+    }
+    // scatter-add rows c = c0 + 16mt + 4g + i, columns dw + 16nt + c16
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = c0 + 16 * mt + 4 * g + i;
+        float* dst = nullptr;
+        if (c < cs.n_c) {
+          const int gr = a.mode == 1 ? cs.row0 + c : a.idx[(int64_t)t * a.k_cap + c];
+          if (gr >= cs.row0 && gr < cs.row0 + cs.nv) dst = b.dkv_cmp + (int64_t)gr * kD;
+        } else if (c < n_tot) {
+          dst = b.dkv + (int64_t)(cs.win0 + (c - cs.n_c)) * kD;
+        }
+        if (dst) {
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) atomicAdd(dst + dw + 16 * nt + c16, acc[mt][nt][i]);
+        }
+      }
+  }
+}
+
+size_t attn_bwd_workspace_mfma(const Shape& sh) {
+  if (sh.dtype != 1 || sh.H != kH || sh.D != kD) return 0;
+  const int64_t n_c = sh.mode == 0 ? sh.k_cap : (sh.mode == 1 ? sh.max_seqlen / sh.r : 0);
+  const int64_t slots = ((n_c + sh.W + kNB2 - 1) / kNB2) * kNB2;
+  return (size_t)sh.T * slots * 128 * sizeof(uint16_t);
 }
 
 hipError_t launch_attn_bwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s, bool* handled) {
-  (void)sh; (void)io; (void)s;
   *handled = false;
-  return hipSuccess;
+  if (sh.dtype != 1 || sh.H != kH || sh.D != kD) return hipSuccess;
+  *handled = true;
+  BwdArgs b;
+  b.q = (const uint16_t*)io.q;
+  b.kv_cmp = (const uint16_t*)io.kv_cmp;
+  b.kv = (const uint16_t*)io.kv;
+  b.idx = io.idx;
+  b.sink = io.sink;
+  b.cu = sh.cu;
+  b.cu_cmp = sh.cu_cmp;
+  b.o = (const uint16_t*)io.o;
+  b.lse = io.lse;
+  b.dout = (const uint16_t*)io.dout;
+  b.dq = (uint16_t*)io.dq;
+  b.dkv_cmp = io.dkv_cmp;
+  b.dkv = io.dkv;
+  b.dsink = io.dsink;
+  b.pds = (uint16_t*)io.ws;
+  const int64_t n_c = sh.mode == 0 ? sh.k_cap : (sh.mode == 1 ? sh.max_seqlen / sh.r : 0);
+  b.n_slots = ((n_c + sh.W + kNB2 - 1) / kNB2) * kNB2;
+  b.B = sh.B;
+  b.T = sh.T;
+  b.r = sh.r;
+  b.n_cap = sh.max_seqlen / sh.r;
+  b.W = sh.W;
+  b.k_cap = sh.k_cap;
+  b.mode = sh.mode;
+  b.scale = sh.scale;
+  b.scale_log2 = sh.scale * 1.44269504088896341f;
+  const int64_t chunks = ((int64_t)sh.T + 8 * kChunk - 1) / (8 * kChunk);
+  const int64_t grid = chunks * 8 * kChunk;
+  hipLaunchKernelGGL(k_attn_bwd_dq_mfma, dim3((unsigned)grid), dim3(256), 0, s, b);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_attn_bwd_dkv_mfma, dim3((unsigned)grid), dim3(256), 0, s, b);
+  return hipGetLastError();
 }
 
 }  // namespace csa

@@ -38,8 +38,13 @@ def test_version_and_status_strings(lib):
 
 def test_workspace_sizes(lib):
     p = _params()
-    assert B.csa_workspace_size(p, B.CSA_OP_ATTN_BWD) == 256 * 4 * 4
-    assert B.csa_workspace_size(p, B.CSA_OP_ATTN_FWD) >= 0
+    assert B.csa_workspace_size(p, B.CSA_OP_ATTN_BWD) == 0          # scalar path: none
+    assert B.csa_workspace_size(p, B.CSA_OP_ATTN_FWD) == 0
+    # bf16 H=64 D=512 backward: [scale*dS | P] per (token, candidate slot), slots = k_cap + W
+    # rounded up to 64
+    big = _params(heads=64, head_dim=512, dtype=B.CSA_BF16, topk=1024, topk_cap=1024,
+                  window=128, total_tokens=1000, max_seqlen=1000)
+    assert B.csa_workspace_size(big, B.CSA_OP_ATTN_BWD) == 1000 * 1152 * 128 * 2
     n = ctypes.c_size_t(0)
     assert lib.csa_workspace_size(ctypes.byref(p), 99, ctypes.byref(n)) == B.CSA_ERR_ARG
     assert lib.csa_workspace_size(None, 1, ctypes.byref(n)) == B.CSA_ERR_NULL
@@ -116,8 +121,9 @@ def test_attention_validation(lib):
              FAKE, FAKE, None, 0, None) == B.CSA_ERR_NULL                    # kv_cmp for dense
     b = lib.csa_sparse_attn_bwd
     args = [FAKE] * 14
-    assert b(ctypes.byref(p), *args, None, 0, None) == B.CSA_ERR_WORKSPACE
-    assert b(ctypes.byref(p), *args, FAKE, 100, None) == B.CSA_ERR_WORKSPACE
+    bf = _params(heads=64, head_dim=512, dtype=B.CSA_BF16)
+    assert b(ctypes.byref(bf), *args, None, 0, None) == B.CSA_ERR_WORKSPACE
+    assert b(ctypes.byref(bf), *args, FAKE, 100, None) == B.CSA_ERR_WORKSPACE
     args[11] = None                                                          # dq
     assert b(ctypes.byref(p), *args, FAKE, 1 << 20, None) == B.CSA_ERR_NULL
 
