@@ -321,21 +321,29 @@ hipError_t launch_attn_fwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s
 
 // ======================================================================== backward
 //
+// The backward is processed in chunks of query tokens (so the workspace stays bounded);
+// per chunk:
 // Kernel 1 (k_attn_bwd_dq_mfma): one workgroup per query token, wave w owns heads
 // 16w..16w+15 over the whole row.  Per block of 32 candidates the rows are staged once in
-// LDS (row-major); each wave recomputes S^T and dP^T for its heads on MFMA (A = rows from
+// LDS (row-major; the next block's rows are fetched into registers while the current
+// block computes); each wave recomputes S^T and dP^T for its heads on MFMA (A = rows from
 // LDS, B = its Q / dO slice resident in registers), forms P = e^{S - LSE} and
 // dS = P (dP - Dt) in fp32, stores scale*dS and P (bf16) for kernel 2, and accumulates
 // dq += (scale dS) K with the row tile as a transposed B operand (ds_read_b64_tr_b16).
 // The S^T result layout (lane = head, 4 candidates per m-tile) is reused directly as the
 // A operand of the dq product by ordering the 32 candidates of a k-step as
 // {4g..4g+3, 16+4g..16+4g+3} for lane group g.
-//
 // Kernel 2 (k_attn_bwd_dkv_mfma): one workgroup per query token, wave w owns d-slice
 // 128w..128w+127.  Q and dO of the token are staged once in LDS and read transposed into
-// registers as the B operand [scale Q... ; dO] (k = 64 heads of dS then 64 heads of P);
-// per block of 64 candidates d row = [scale dS | P]^T [Q; dO] on MFMA, then the fp32
-// result is scatter-added into dkv_cmp (compressed rows) or dkv (window rows).
+// registers; per block of 64 candidates the row gradients
+// (d row)^T = [Q; dO]^T [scale dS | P]^T are formed on MFMA (lane = candidate, 4
+// consecutive d) and stored as bf16 to a staging buffer, one 1 KiB vector per
+// (query, candidate) pair, with plain stores.
+// Then the owner of each shared row sums its staged vectors in fp32: a CSR of the
+// compressed rows (row -> contributing (query, slot) pairs) is built from the candidate
+// lists, and window rows find their contributors directly (the next W-1 queries).
+// Stores + an owner-side gather replace fp32 atomics, which run at a fraction of the
+// store bandwidth on this part.
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
@@ -344,6 +352,7 @@ namespace {
 constexpr int kNB1 = 32;          // candidates per block, kernel 1
 constexpr int kKS = kD + 16;      // row stride (bf16) of LDS row tiles
 constexpr int kNB2 = 64;          // candidates per block, kernel 2
+constexpr int64_t kStageBudget = 24ll << 30;   // bytes of pds + staging per chunk
 
 struct BwdArgs {
   const uint16_t* q;
@@ -360,8 +369,15 @@ struct BwdArgs {
   float* dkv_cmp;
   float* dkv;
   float* dsink;
-  uint16_t* pds;     // workspace [T][n_slots][128]: scale*dS (64 heads) then P (64 heads)
+  uint16_t* pds;     // [chunk][n_slots][128]: scale*dS (64 heads) then P (64 heads)
+  uint16_t* stage;   // [chunk][n_slots][512]: bf16 row gradient of each (query, slot)
+  int32_t* nc;       // [T] compressed candidate count of each query
+  int32_t* cnt;      // [Tc_cap] contributors per compressed row (this chunk)
+  int32_t* off;      // [Tc_cap] CSR offsets
+  int32_t* cur;      // [Tc_cap] CSR fill cursors
+  int32_t* list;     // [chunk * n_c_max] (query - t0) * n_slots + slot
   int64_t n_slots;
+  int t0, nT, Tc_cap;
   int B, T, r, n_cap, W, k_cap, mode;
   float scale, scale_log2;
 };
@@ -397,6 +413,12 @@ __device__ __forceinline__ CandSet make_cands(const FwdArgs& a, int t, const Tok
   return cs;
 }
 
+// Global compressed row of slot c (< n_c) of query t, or -1 if it is outside the visible range.
+__device__ __forceinline__ int cmp_row(const BwdArgs& b, int t, int row0, int nv, int c) {
+  const int gr = b.mode == 1 ? row0 + c : b.idx[(int64_t)t * b.k_cap + c];
+  return (gr >= row0 && gr < row0 + nv) ? gr : -1;
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -407,15 +429,18 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
   const FwdArgs a = as_fwd(b);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int t = token_of_block(blockIdx.x);
-  if (t >= b.T) return;
+  const int tl = token_of_block(blockIdx.x);
+  if (tl >= b.nT) return;
+  const int t = b.t0 + tl;
   TokenInfo ti;
   if (!token_info(b.cu, b.B, t, ti)) {
     uint4* o = reinterpret_cast<uint4*>(b.dq + (int64_t)t * kH * kD);
     for (int e = tid; e < kH * kD / 8; e += 256) o[e] = make_uint4(0, 0, 0, 0);
+    if (tid == 0) b.nc[t] = 0;
     return;
   }
   const CandSet cs = make_cands(a, t, ti, &s_tmp);
+  if (tid == 0) b.nc[t] = cs.n_c;
   const int n_tot = cs.n_c + cs.n_w;
   const int h = 16 * wave + c16;  // this lane's head for S^T / dP^T (n index)
 
@@ -442,25 +467,38 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
 #pragma unroll
   for (int nt = 0; nt < 32; ++nt) dq[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // cooperative row loads: 8 x 16 B per lane, one full row per wave instruction
-  auto load_block = [&](int c0, int buf) {
+  // row fetch split in two halves: issue (global -> registers) early, commit (-> LDS) late,
+  // so the loads of block c+1 are in flight while block c computes
+  uint4 pre[8];
+  int pre_ok = 0;
+  auto issue = [&](int c0) {
+    pre_ok = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int row = 4 * i + wave;
-      const uint16_t* src = cand_ptr(a, t, cs, c0 + row);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (src) v = *reinterpret_cast<const uint4*>(src + 8 * lane);
-      *reinterpret_cast<uint4*>(&Kt[buf][row][8 * lane]) = v;
-      if (lane == 0) valid_s[buf][row] = src != nullptr;
+      const uint16_t* src = cand_ptr(a, t, cs, c0 + 4 * i + wave);
+      pre[i] = src ? *reinterpret_cast<const uint4*>(src + 8 * lane) : make_uint4(0, 0, 0, 0);
+      pre_ok |= (src != nullptr) << i;
+    }
+  };
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      *reinterpret_cast<uint4*>(&Kt[buf][4 * i + wave][8 * lane]) = pre[i];
+      if (lane == 0) valid_s[buf][4 * i + wave] = (pre_ok >> i) & 1;
     }
   };
 
-  uint16_t* pds_t = b.pds + (int64_t)t * b.n_slots * 128;
+  uint16_t* pds_t = b.pds + (int64_t)tl * b.n_slots * 128;
+  const int jr = c16 >> 2, jc = 4 * (c16 & 3);
   int buf = 0;
-  if (n_tot > 0) load_block(0, 0);
+  if (n_tot > 0) {
+    issue(0);
+    commit(0);
+  }
   for (int c0 = 0; c0 < n_tot; c0 += kNB1, buf ^= 1) {
     __syncthreads();
-    if (c0 + kNB1 < n_tot) load_block(c0 + kNB1, buf ^ 1);
+    const bool more = c0 + kNB1 < n_tot;
+    if (more) issue(c0 + kNB1);
     // S^T, dP^T for 32 candidates x this wave's 16 heads
     f32x4 st[2], gt[2];
 #pragma unroll
@@ -496,13 +534,13 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
       }
     const bf16x8 dsa = __builtin_bit_cast(bf16x8, make_uint4(dsw[0], dsw[1], dsw[2], dsw[3]));
     // dq[h'][d] += sum_c dS[h'][c] K[c][d]; B = rows {4g..4g+3, 16+4g..16+4g+3} of the tile
-    const int jr = c16 >> 2, jc = 4 * (c16 & 3);
 #pragma unroll
     for (int nt = 0; nt < 32; ++nt) {
       const v4i16 lo = ld_tr(&Kt[buf][4 * g + jr][16 * nt + jc]);
       const v4i16 hi = ld_tr(&Kt[buf][16 + 4 * g + jr][16 * nt + jc]);
       dq[nt] = mfma16(dsa, join8(lo, hi), dq[nt]);
     }
+    if (more) commit(buf ^ 1);
   }
   // dq rows h' = 16 wave + 4g + i, columns 16nt + c16
   uint16_t* dqp = b.dq + (int64_t)t * kH * kD;
@@ -519,16 +557,14 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_attn_bwd_dkv_mfma(BwdArgs b) {
   __shared__ __attribute__((aligned(16))) uint16_t QO[2 * kH][kKS];
-  __shared__ int s_tmp;
-  const FwdArgs a = as_fwd(b);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int t = token_of_block(blockIdx.x);
-  if (t >= b.T) return;
+  const int tl = token_of_block(blockIdx.x);
+  if (tl >= b.nT) return;
+  const int t = b.t0 + tl;
   TokenInfo ti;
   if (!token_info(b.cu, b.B, t, ti)) return;
-  const CandSet cs = make_cands(a, t, ti, &s_tmp);
-  const int n_tot = cs.n_c + cs.n_w;
+  const int n_tot = b.nc[t] + min(b.W, ti.p + 1);
   // stage Q (rows 0..63) and dO (rows 64..127) of the token
   const uint16_t* qt = b.q + (int64_t)t * kH * kD;
   const uint16_t* gt = b.dout + (int64_t)t * kH * kD;
@@ -540,7 +576,8 @@ void k_attn_bwd_dkv_mfma(BwdArgs b) {
   __syncthreads();
   const int dw = wave * kDW;
   const int jr = c16 >> 2, jc = 4 * (c16 & 3);
-  bf16x8 bo[8][4];   // [n-tile of d][k-step of h']
+  // [Q; dO] read transposed: MFMA A operand with m = d, k = head slot
+  bf16x8 bo[8][4];   // [tile of d][k-step over the 128 head slots]
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
@@ -549,55 +586,204 @@ void k_attn_bwd_dkv_mfma(BwdArgs b) {
       const v4i16 hi = ld_tr(&QO[32 * ks + 8 * g + 4 + jr][dw + 16 * nt + jc]);
       bo[nt][ks] = join8(lo, hi);
     }
-  const uint16_t* pds_t = b.pds + (int64_t)t * b.n_slots * 128;
-  for (int c0 = 0; c0 < n_tot; c0 += kNB2) {
-    f32x4 acc[4][8];
+  const uint16_t* pds_t = b.pds + (int64_t)tl * b.n_slots * 128;
+  uint16_t* stg_t = b.stage + (int64_t)tl * b.n_slots * kD;
+  bf16x8 av[4][4], nx[4][4];
+  auto fetch = [&](int c0, bf16x8 (&dst)[4][4]) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      bf16x8 av[4];
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        av[ks] = ld16(pds_t + (int64_t)(c0 + 16 * mt + c16) * 128 + 32 * ks + 8 * g);
+        dst[mt][ks] = ld16(pds_t + (int64_t)(c0 + 16 * mt + c16) * 128 + 32 * ks + 8 * g);
+  };
+  if (n_tot > 0) fetch(0, av);
+  for (int c0 = 0; c0 < n_tot; c0 += kNB2) {
+    const bool more = c0 + kNB2 < n_tot;
+    if (more) fetch(c0 + kNB2, nx);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int c = c0 + 16 * mt + c16;       // this lane's candidate (output column)
+      uint16_t* dst = stg_t + (int64_t)c * kD + dw + 4 * g;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) x = mfma16(av[ks], bo[nt][ks], x);
-        acc[mt][nt] = x;
+        for (int ks = 0; ks < 4; ++ks) x = mfma16(bo[nt][ks], av[mt][ks], x);
+        // lane holds d = dw + 16nt + 4g .. +3 of candidate c
+        if (c < n_tot) {
+          const uint32_t lo = (uint32_t)f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
+          *reinterpret_cast<uint2*>(dst + 16 * nt) = make_uint2(lo, hi);
+        }
       }
     }
-    // scatter-add rows c = c0 + 16mt + 4g + i, columns dw + 16nt + c16
+    if (more) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = c0 + 16 * mt + 4 * g + i;
-        float* dst = nullptr;
-        if (c < cs.n_c) {
-          const int gr = a.mode == 1 ? cs.row0 + c : a.idx[(int64_t)t * a.k_cap + c];
-          if (gr >= cs.row0 && gr < cs.row0 + cs.nv) dst = b.dkv_cmp + (int64_t)gr * kD;
-        } else if (c < n_tot) {
-          dst = b.dkv + (int64_t)(cs.win0 + (c - cs.n_c)) * kD;
-        }
-        if (dst) {
-#pragma unroll
-          for (int nt = 0; nt < 8; ++nt) atomicAdd(dst + dw + 16 * nt + c16, acc[mt][nt][i]);
-        }
-      }
+        for (int ks = 0; ks < 4; ++ks) av[mt][ks] = nx[mt][ks];
+    }
   }
 }
 
+// ---- CSR of the compressed rows of a chunk: count, scan, fill
+__global__ __launch_bounds__(256) void k_bwd_fill_zero(int32_t* __restrict__ p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
+template <bool FILL>
+__global__ __launch_bounds__(256) void k_bwd_csr_pass(BwdArgs b) {
+  const int tl = blockIdx.x;
+  if (tl >= b.nT) return;
+  const int t = b.t0 + tl;
+  TokenInfo ti;
+  if (!token_info(b.cu, b.B, t, ti)) return;
+  const int row0 = b.cu_cmp[ti.b];
+  const int nv = min((ti.p + 1) / b.r, b.n_cap);
+  const int n_c = b.nc[t];
+  for (int c = threadIdx.x; c < n_c; c += 256) {
+    const int gr = cmp_row(b, t, row0, nv, c);
+    if (gr < 0) continue;
+    if (!FILL) {
+      atomicAdd(&b.cnt[gr], 1);
+    } else {
+      const int pos = atomicAdd(&b.cur[gr], 1);
+      b.list[pos] = tl * (int32_t)b.n_slots + c;
+    }
+  }
+}
+
+// exclusive scan of cnt[0 .. n) into off and cur (one workgroup of 1024 lanes)
+__global__ __launch_bounds__(1024) void k_bwd_csr_scan(BwdArgs b, int n) {
+  __shared__ int part[1024];
+  const int per = (n + 1023) / 1024;
+  const int lo = threadIdx.x * per, hi = min(n, lo + per);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += b.cnt[i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int run = part[threadIdx.x] - s;
+  for (int i = lo; i < hi; ++i) {
+    b.off[i] = run;
+    b.cur[i] = run;
+    run += b.cnt[i];
+  }
+}
+
+// ---- owner-side reductions: 4 groups of 64 lanes, each lane owns 8 consecutive floats
+__device__ __forceinline__ void add_staged(const uint16_t* src, float (&acc)[8]) {
+  float v[8];
+  load8(src, v);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] += v[i];
+}
+
+__device__ __forceinline__ void finish_row(float (&acc)[8], float* __restrict__ dst, float* red) {
+  const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[(q * 64 + lane) * 9 + i] = acc[i];
+  __syncthreads();
+  if (q == 0) {
+    float o[8];
+    load8(dst + 8 * lane, o);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      o[i] += (acc[i] + red[(64 + lane) * 9 + i]) + (red[(128 + lane) * 9 + i] + red[(192 + lane) * 9 + i]);
+    store8(dst + 8 * lane, o);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_bwd_reduce_cmp(BwdArgs b) {
+  __shared__ float red[256 * 9];
+  const int j = blockIdx.x;
+  const int n = b.cnt[j];
+  if (n == 0) return;
+  const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int* lst = b.list + b.off[j];
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  int e = q;
+  for (; e + 4 < n; e += 8) {
+    add_staged(b.stage + (int64_t)lst[e] * kD + 8 * lane, acc);
+    add_staged(b.stage + (int64_t)lst[e + 4] * kD + 8 * lane, acc);
+  }
+  for (; e < n; e += 4) add_staged(b.stage + (int64_t)lst[e] * kD + 8 * lane, acc);
+  finish_row(acc, b.dkv_cmp + (int64_t)j * kD, red);
+}
+
+// raw rows u in [u_lo, u_lo + gridDim.x): contributors are the queries t in [u, u + W - 1]
+// of u's sample that lie in this chunk; u is slot nc[t] + (u - first window row of t)
+__global__ __launch_bounds__(256) void k_bwd_reduce_win(BwdArgs b, int u_lo) {
+  __shared__ float red[256 * 9];
+  const int u = u_lo + blockIdx.x;
+  TokenInfo ti;
+  if (!token_info(b.cu, b.B, u, ti)) return;
+  const int t_lo = max(u, b.t0);
+  const int t_hi = min(min(u + b.W - 1, ti.start + ti.len - 1), b.t0 + b.nT - 1);
+  if (t_lo > t_hi) return;
+  const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int t = t_lo + q; t <= t_hi; t += 4) {
+    const int p = t - ti.start;
+    const int win0 = t - min(b.W, p + 1) + 1;
+    const int64_t slot = (int64_t)(t - b.t0) * b.n_slots + b.nc[t] + (u - win0);
+    add_staged(b.stage + slot * kD + 8 * lane, acc);
+  }
+  finish_row(acc, b.dkv + (int64_t)u * kD, red);
+}
+
+namespace {
+
+struct BwdPlan {
+  int64_t n_slots, n_c_max, chunk, Tc_cap;
+  size_t off_pds, off_stage, off_nc, off_cnt, off_off, off_cur, off_list, total;
+};
+
+BwdPlan bwd_plan(const Shape& sh) {
+  BwdPlan p;
+  p.n_c_max = sh.mode == 0 ? sh.k_cap : (sh.mode == 1 ? sh.max_seqlen / sh.r : 0);
+  p.n_slots = ((p.n_c_max + sh.W + kNB2 - 1) / kNB2) * kNB2;
+  const int64_t per_tok = p.n_slots * (128 + kD) * 2;
+  int64_t ch = kStageBudget / per_tok;
+  ch = (ch / (8 * kChunk)) * (8 * kChunk);
+  if (ch < 8 * kChunk) ch = 8 * kChunk;
+  p.chunk = ch < sh.T ? ch : sh.T;
+  p.Tc_cap = sh.r > 0 ? sh.T / sh.r + 1 : 1;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t o = 0;
+  p.off_pds = o;   o = al(o + (size_t)p.chunk * p.n_slots * 128 * 2);
+  p.off_stage = o; o = al(o + (size_t)p.chunk * p.n_slots * kD * 2);
+  p.off_nc = o;    o = al(o + (size_t)sh.T * 4);
+  p.off_cnt = o;   o = al(o + (size_t)p.Tc_cap * 4);
+  p.off_off = o;   o = al(o + (size_t)p.Tc_cap * 4);
+  p.off_cur = o;   o = al(o + (size_t)p.Tc_cap * 4);
+  p.off_list = o;  o = al(o + (size_t)p.chunk * (p.n_c_max > 0 ? p.n_c_max : 1) * 4);
+  p.total = o;
+  return p;
+}
+
+}  // namespace
+
 size_t attn_bwd_workspace_mfma(const Shape& sh) {
   if (sh.dtype != 1 || sh.H != kH || sh.D != kD) return 0;
-  const int64_t n_c = sh.mode == 0 ? sh.k_cap : (sh.mode == 1 ? sh.max_seqlen / sh.r : 0);
-  const int64_t slots = ((n_c + sh.W + kNB2 - 1) / kNB2) * kNB2;
-  return (size_t)sh.T * slots * 128 * sizeof(uint16_t);
+  return bwd_plan(sh).total;
 }
 
 hipError_t launch_attn_bwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s, bool* handled) {
   *handled = false;
   if (sh.dtype != 1 || sh.H != kH || sh.D != kD) return hipSuccess;
   *handled = true;
+  const BwdPlan pl = bwd_plan(sh);
+  char* ws = (char*)io.ws;
   BwdArgs b;
   b.q = (const uint16_t*)io.q;
   b.kv_cmp = (const uint16_t*)io.kv_cmp;
@@ -613,9 +799,15 @@ hipError_t launch_attn_bwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s
   b.dkv_cmp = io.dkv_cmp;
   b.dkv = io.dkv;
   b.dsink = io.dsink;
-  b.pds = (uint16_t*)io.ws;
-  const int64_t n_c = sh.mode == 0 ? sh.k_cap : (sh.mode == 1 ? sh.max_seqlen / sh.r : 0);
-  b.n_slots = ((n_c + sh.W + kNB2 - 1) / kNB2) * kNB2;
+  b.pds = (uint16_t*)(ws + pl.off_pds);
+  b.stage = (uint16_t*)(ws + pl.off_stage);
+  b.nc = (int32_t*)(ws + pl.off_nc);
+  b.cnt = (int32_t*)(ws + pl.off_cnt);
+  b.off = (int32_t*)(ws + pl.off_off);
+  b.cur = (int32_t*)(ws + pl.off_cur);
+  b.list = (int32_t*)(ws + pl.off_list);
+  b.n_slots = pl.n_slots;
+  b.Tc_cap = (int)pl.Tc_cap;
   b.B = sh.B;
   b.T = sh.T;
   b.r = sh.r;
@@ -625,13 +817,26 @@ hipError_t launch_attn_bwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s
   b.mode = sh.mode;
   b.scale = sh.scale;
   b.scale_log2 = sh.scale * 1.44269504088896341f;
-  const int64_t chunks = ((int64_t)sh.T + 8 * kChunk - 1) / (8 * kChunk);
-  const int64_t grid = chunks * 8 * kChunk;
-  hipLaunchKernelGGL(k_attn_bwd_dq_mfma, dim3((unsigned)grid), dim3(256), 0, s, b);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_bwd_dkv_mfma, dim3((unsigned)grid), dim3(256), 0, s, b);
-  return hipGetLastError();
+  for (int64_t t0 = 0; t0 < sh.T; t0 += pl.chunk) {
+    b.t0 = (int)t0;
+    b.nT = (int)(sh.T - t0 < pl.chunk ? sh.T - t0 : pl.chunk);
+    const int64_t grid = ((b.nT + 8 * kChunk - 1) / (8 * kChunk)) * 8 * kChunk;
+    hipLaunchKernelGGL(k_attn_bwd_dq_mfma, dim3((unsigned)grid), dim3(256), 0, s, b);
+    hipLaunchKernelGGL(k_attn_bwd_dkv_mfma, dim3((unsigned)grid), dim3(256), 0, s, b);
+    if (sh.mode != 2) {
+      hipLaunchKernelGGL(k_bwd_fill_zero, dim3(64), dim3(256), 0, s, b.cnt, b.Tc_cap);
+      hipLaunchKernelGGL(k_bwd_csr_pass<false>, dim3(b.nT), dim3(256), 0, s, b);
+      hipLaunchKernelGGL(k_bwd_csr_scan, dim3(1), dim3(1024), 0, s, b, b.Tc_cap);
+      hipLaunchKernelGGL(k_bwd_csr_pass<true>, dim3(b.nT), dim3(256), 0, s, b);
+      hipLaunchKernelGGL(k_bwd_reduce_cmp, dim3(b.Tc_cap), dim3(256), 0, s, b);
+    }
+    const int u_lo = b.t0 - sh.W + 1 > 0 ? b.t0 - sh.W + 1 : 0;
+    const int u_hi = b.t0 + b.nT;          // exclusive
+    hipLaunchKernelGGL(k_bwd_reduce_win, dim3(u_hi - u_lo), dim3(256), 0, s, b, u_lo);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace csa

@@ -40,11 +40,12 @@ def test_workspace_sizes(lib):
     p = _params()
     assert B.csa_workspace_size(p, B.CSA_OP_ATTN_BWD) == 0          # scalar path: none
     assert B.csa_workspace_size(p, B.CSA_OP_ATTN_FWD) == 0
-    # bf16 H=64 D=512 backward: [scale*dS | P] per (token, candidate slot), slots = k_cap + W
-    # rounded up to 64
+    # bf16 H=64 D=512 backward: [scale*dS | P] (128 bf16) and a staged row gradient (512
+    # bf16) per (token, candidate slot) of a token chunk, slots = k_cap + W rounded up to 64
     big = _params(heads=64, head_dim=512, dtype=B.CSA_BF16, topk=1024, topk_cap=1024,
                   window=128, total_tokens=1000, max_seqlen=1000)
-    assert B.csa_workspace_size(big, B.CSA_OP_ATTN_BWD) == 1000 * 1152 * 128 * 2
+    n = B.csa_workspace_size(big, B.CSA_OP_ATTN_BWD)
+    assert 1000 * 1152 * (128 + 512) * 2 <= n <= 1000 * 1152 * (128 + 512) * 2 + 8 * 2**20
     n = ctypes.c_size_t(0)
     assert lib.csa_workspace_size(ctypes.byref(p), 99, ctypes.byref(n)) == B.CSA_ERR_ARG
     assert lib.csa_workspace_size(None, 1, ctypes.byref(n)) == B.CSA_ERR_NULL
