@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="also run one plain device-to-device copy of this many bytes before "
+                         "the timed steps (a known-traffic reference for HBM counters)")
     return ap.parse_args()
 
 
@@ -182,6 +185,13 @@ def main():
     layer = CsaLayer(LayerConfig.of(w), len(host["lengths"]), w.total_tokens,
                      host["max_seqlen"], backward=w.backward)
     cu = dev["cu_seqlens"]
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         layer.step(dev, cu)
         torch.cuda.synchronize()

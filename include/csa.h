@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 typedef int32_t csa_status_t;
 enum {
@@ -170,12 +170,18 @@ csa_status_t csa_topk_select(const csa_params_t* p, const float* scores, int64_t
  * window rows of kv.  One row is both key and value (MQA).  For each head h:
  *   l_x = scale q[t,h].row_x,  lse[t,h] = log([e^{sink_h}] + sum_x e^{l_x}),
  *   out[t,h] = sum_x e^{l_x - lse[t,h]} row_x.
+ * Optionally also lse_cmp[t,h] = log(sum over the compressed candidates only of e^{l_x})
+ * (no window, no sink; -inf for a query without compressed candidates): with a
+ * selected-set teacher this is the teacher's per-head normalizer, which csa_indexer_kl
+ * then need not recompute (section 8.2, teacher score recomputation).
  * q, out: [T, H, D]; kv_cmp: [Tc, D]; kv: [T, D] (dtype); idx: int32 [T, topk_cap] or NULL
- * unless CSA_SPARSE; sink: fp32 [H] or NULL; lse: fp32 [T, H] (natural log). */
+ * unless CSA_SPARSE; sink: fp32 [H] or NULL; lse, lse_cmp: fp32 [T, H] (natural log);
+ * lse_cmp may be NULL. */
 csa_status_t csa_sparse_attn_fwd(const csa_params_t* p, const void* q, const void* kv_cmp,
                                  const void* kv, const int32_t* idx, const float* sink,
                                  const int32_t* cu_seqlens, const int32_t* cu_cmp, void* out,
-                                 float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+                                 float* lse, float* lse_cmp, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
 
 /* Sparse attention backward (section 8.2: consumes saved O, LSE, dO; no dense matrix).
  * With P = e^{l_x - lse}, dP = dO.row_x, Dt = dO.O, dS = P (dP - Dt):
@@ -201,10 +207,14 @@ csa_status_t csa_sparse_attn_bwd(const csa_params_t* p, const void* q, const voi
  *   dw[t,h] = sum_j g relu(z); dqI[t,h,:] = sum_j g w[t,h] 1[z>0] kI[j,:]     (overwrite)
  *   dkI_cmp[j,:] += sum_{t,h} g w[t,h] 1[z>0] qI[t,h,:]                        (+=)
  * For CSA_FP8_E4M3 the gradients are taken with respect to the dequantized operands.
+ * teacher_lse: NULL, or (CSA_TEACHER_SELECTED only) the lse_cmp [T, H] that
+ * csa_sparse_attn_fwd returned for the same q, kv_cmp and idx; it is then used as the
+ * teacher's per-head log-normalizer instead of being recomputed.
  * kl: fp32 [T]; loss: fp32 [1]; dqI: fp32 [T, H_I, d_I]; dw: fp32 [T, H_I];
  * dkI_cmp: fp32 [Tc, d_I].  dqI, dw and dkI_cmp all NULL => loss only. */
 csa_status_t csa_indexer_kl(const csa_params_t* p, const void* q, const void* kv_cmp,
                             const float* scores, int64_t ld_scores, const int32_t* idx,
+                            const float* teacher_lse,
                             const void* qI, const float* qI_scale, const float* w,
                             const void* kI_cmp, const float* kI_scale,
                             const int32_t* cu_seqlens, const int32_t* cu_cmp, float grad_scale,

@@ -56,9 +56,9 @@ _SIGS = {
     "csa_quantize_fp8": ([_P, _I32, _I64, _I32, _P, _P, _P], _I32),
     "csa_index_scores": ([_PP, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _P], _I32),
     "csa_topk_select": ([_PP, _P, _I64, _P, _P, _P, _P], _I32),
-    "csa_sparse_attn_fwd": ([_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
+    "csa_sparse_attn_fwd": ([_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
     "csa_sparse_attn_bwd": ([_PP] + [_P] * 14 + [_P, _SZ, _P], _I32),
-    "csa_indexer_kl": ([_PP, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _F,
+    "csa_indexer_kl": ([_PP, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F,
                         _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
 }
 
@@ -175,11 +175,11 @@ def csa_topk_select(p, scores, cu_seqlens, cu_cmp, idx, stream=None):
         _ptr(idx), _stream(stream)))
 
 
-def csa_sparse_attn_fwd(p, q, kv_cmp, kv, idx, sink, cu_seqlens, cu_cmp, out, lse, ws=None,
-                        stream=None):
+def csa_sparse_attn_fwd(p, q, kv_cmp, kv, idx, sink, cu_seqlens, cu_cmp, out, lse, lse_cmp=None,
+                        ws=None, stream=None):
     _check("csa_sparse_attn_fwd", lib().csa_sparse_attn_fwd(
         ctypes.byref(p), _ptr(q), _ptr(kv_cmp), _ptr(kv), _ptr(idx), _ptr(sink), _ptr(cu_seqlens),
-        _ptr(cu_cmp), _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws),
+        _ptr(cu_cmp), _ptr(out), _ptr(lse), _ptr(lse_cmp), _ptr(ws), _nbytes(ws),
         _stream(stream)))
 
 
@@ -193,9 +193,9 @@ def csa_sparse_attn_bwd(p, q, kv_cmp, kv, idx, sink, cu_seqlens, cu_cmp, out, ls
 
 def csa_indexer_kl(p, q, kv_cmp, scores, idx, qI, qI_scale, w, kI_cmp, kI_scale, cu_seqlens,
                    cu_cmp, grad_scale, kl, loss, dqI=None, dw=None, dkI_cmp=None, ws=None,
-                   stream=None):
+                   teacher_lse=None, stream=None):
     _check("csa_indexer_kl", lib().csa_indexer_kl(
         ctypes.byref(p), _ptr(q), _ptr(kv_cmp), _ptr(scores), scores.shape[-1], _ptr(idx),
-        _ptr(qI), _ptr(qI_scale), _ptr(w), _ptr(kI_cmp), _ptr(kI_scale), _ptr(cu_seqlens),
+        _ptr(teacher_lse), _ptr(qI), _ptr(qI_scale), _ptr(w), _ptr(kI_cmp), _ptr(kI_scale), _ptr(cu_seqlens),
         _ptr(cu_cmp), float(grad_scale), _ptr(kl), _ptr(loss), _ptr(dqI), _ptr(dw), _ptr(dkI_cmp),
         _ptr(ws), _nbytes(ws), _stream(stream)))

@@ -28,6 +28,7 @@ struct AttnK {
   const int32_t* cu_cmp;
   void* out;
   float* lse;
+  float* lse_cmp;
   const void* o;
   const void* dout;
   void* dq;
@@ -40,9 +41,10 @@ struct AttnK {
 
 constexpr int kNB = 16;  // candidates per block
 
-// Candidate bookkeeping of one query: compressed slots first, then window rows.
+// Candidate bookkeeping of one query: compressed slots [0, n_c), masked padding
+// [n_c, n_cs), then window rows.
 struct Cands {
-  int n_c, n_w, row0, nv, win0;
+  int n_c, n_cs, n_w, row0, nv, win0;
 };
 
 // First -1 of an idx row (the number of leading selected entries); every lane returns it.
@@ -66,18 +68,20 @@ __device__ Cands make_cands(const AttnK& a, int t, const TokenInfo& ti, int* s_t
   if (a.mode == 1) c.n_c = c.nv;
   else if (a.mode == 2) c.n_c = 0;
   else c.n_c = leading_entries(a.idx + (int64_t)t * a.k_cap, a.k_cap, s_tmp);
+  c.n_cs = ((c.n_c + kNB - 1) / kNB) * kNB;   // whole blocks of compressed slots
   return c;
 }
 
 // Row id of candidate slot c: >= 0 compressed row, <= -2 window row -(id+2), -1 masked.
 __device__ __forceinline__ int cand_row(const AttnK& a, int t, const Cands& cd, int c) {
-  const int n = cd.n_c + cd.n_w;
+  const int n = cd.n_cs + cd.n_w;
   if (c >= n) return -1;
   if (c < cd.n_c) {
     const int g = a.mode == 1 ? cd.row0 + c : a.idx[(int64_t)t * a.k_cap + c];
     return (g >= cd.row0 && g < cd.row0 + cd.nv) ? g : -1;
   }
-  return -2 - (cd.win0 + (c - cd.n_c));
+  if (c < cd.n_cs) return -1;
+  return -2 - (cd.win0 + (c - cd.n_cs));
 }
 
 template <typename T>
@@ -115,6 +119,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd_generic(AttnK a) {
   if (!token_info(a.cu, a.B, t, ti)) {
     for (int e = tid; e < HG * D; e += 256) store1(outp + e, 0.f);
     if (tid < HG) a.lse[(int64_t)t * a.H + h0 + tid] = 0.f;
+    if (a.lse_cmp && tid < HG) a.lse_cmp[(int64_t)t * a.H + h0 + tid] = -INFINITY;
     return;
   }
   const Cands cd = make_cands(a, t, ti, &s_tmp);
@@ -124,7 +129,8 @@ __global__ __launch_bounds__(256) void k_attn_fwd_generic(AttnK a) {
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  const int n = cd.n_c + cd.n_w;
+  float lse_c = -INFINITY;
+  const int n = cd.n_cs + cd.n_w;
   for (int c0 = 0; c0 < n; c0 += kNB) {
     if (tid < kNB) rowid[tid] = cand_row(a, t, cd, c0 + tid);
     __syncthreads();
@@ -163,6 +169,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd_generic(AttnK a) {
       lh[tid] = lh[tid] * alpha + sum;
       mh[tid] = mnew;
       al[tid] = alpha;
+      if (c0 + kNB == cd.n_cs && lh[tid] > 0.f) lse_c = mnew + logf(lh[tid]);
     }
     __syncthreads();
 #pragma unroll
@@ -192,6 +199,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd_generic(AttnK a) {
       f = 1.f / l;
     }
     a.lse[(int64_t)t * a.H + h0 + tid] = lse;
+    if (a.lse_cmp) a.lse_cmp[(int64_t)t * a.H + h0 + tid] = lse_c;
     al[tid] = f;
   }
   __syncthreads();
@@ -242,7 +250,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_generic(AttnK a) {
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  const int n = cd.n_c + cd.n_w;
+  const int n = cd.n_cs + cd.n_w;
   for (int c0 = 0; c0 < n; c0 += kNB) {
     if (tid < kNB) rowid[tid] = cand_row(a, t, cd, c0 + tid);
     __syncthreads();
@@ -313,7 +321,8 @@ static int head_group(int H, int D) {
 static AttnK make_k(const Shape& sh, const AttnIO& io) {
   AttnK a;
   a.q = io.q; a.kv_cmp = io.kv_cmp; a.kv = io.kv; a.idx = io.idx; a.sink = io.sink;
-  a.cu = sh.cu; a.cu_cmp = sh.cu_cmp; a.out = io.out; a.lse = io.lse; a.o = io.o;
+  a.cu = sh.cu; a.cu_cmp = sh.cu_cmp; a.out = io.out; a.lse = io.lse; a.lse_cmp = io.lse_cmp;
+  a.o = io.o;
   a.dout = io.dout; a.dq = io.dq; a.dkv_cmp = io.dkv_cmp; a.dkv = io.dkv; a.dsink = io.dsink;
   a.B = sh.B; a.H = sh.H; a.D = sh.D; a.r = sh.r; a.n_cap = sh.r > 0 ? sh.max_seqlen / sh.r : 0;
   a.W = sh.W; a.k_cap = sh.k_cap; a.mode = sh.mode; a.HG = head_group(sh.H, sh.D);

@@ -50,6 +50,7 @@ struct FwdArgs {
   const int32_t* cu_cmp;
   uint16_t* out;
   float* lse;
+  float* lse_cmp;    // optional log-sum-exp over the compressed candidates only
   int B, T, r, n_cap, W, k_cap, mode;
   float scale_log2;  // softmax scale * log2(e)
 };
@@ -80,8 +81,10 @@ __device__ int leading_valid(const int32_t* __restrict__ row, int k_cap, int* s_
   return n;
 }
 
+// Candidate slots of a query: compressed candidates in [0, n_c), masked padding in
+// [n_c, n_cs), window rows in [n_cs, n_cs + n_w).
 struct CandSet {
-  int n_c, n_w, row0, nv, win0;
+  int n_c, n_cs, n_w, row0, nv, win0;
 };
 
 // Pointer to the row of candidate slot c, or nullptr for a masked / absent slot.
@@ -91,7 +94,8 @@ __device__ __forceinline__ const uint16_t* cand_ptr(const FwdArgs& a, int t, con
     const int g = a.mode == 1 ? cs.row0 + c : a.idx[(int64_t)t * a.k_cap + c];
     return (g >= cs.row0 && g < cs.row0 + cs.nv) ? a.kv_cmp + (int64_t)g * kD : nullptr;
   }
-  if (c < cs.n_c + cs.n_w) return a.kv + (int64_t)(cs.win0 + (c - cs.n_c)) * kD;
+  if (c < cs.n_cs) return nullptr;
+  if (c < cs.n_cs + cs.n_w) return a.kv + (int64_t)(cs.win0 + (c - cs.n_cs)) * kD;
   return nullptr;
 }
 
@@ -119,6 +123,7 @@ void k_attn_fwd_mfma(FwdArgs a) {
     uint4* o = reinterpret_cast<uint4*>(a.out + (int64_t)t * kH * kD);
     for (int e = threadIdx.x; e < kH * kD / 8; e += 256) o[e] = make_uint4(0, 0, 0, 0);
     if (threadIdx.x < kH) a.lse[(int64_t)t * kH + threadIdx.x] = 0.f;
+    if (a.lse_cmp && threadIdx.x < kH) a.lse_cmp[(int64_t)t * kH + threadIdx.x] = -INFINITY;
     return;
   }
   CandSet cs;
@@ -129,8 +134,12 @@ void k_attn_fwd_mfma(FwdArgs a) {
   if (a.mode == 1) cs.n_c = cs.nv;
   else if (a.mode == 2) cs.n_c = 0;
   else cs.n_c = leading_valid(a.idx + (int64_t)t * a.k_cap, a.k_cap, &s_tmp);
-  const int n_tot = cs.n_c + cs.n_w;
+  // compressed slots padded to whole blocks, so a block never mixes compressed and window
+  // rows and the compressed-only normalizer can be read off after the last compressed block
+  cs.n_cs = ((cs.n_c + kNB - 1) / kNB) * kNB;
+  const int n_tot = cs.n_cs + cs.n_w;
   const int dw = wave * kDW;
+  float lse_c = -INFINITY;
 
   // Q^T as the B operand: qb[nt][ks] = Q[16nt + c16][dw + 32ks + 8g .. +7]
   bf16x8 qb[4][4];
@@ -238,6 +247,8 @@ void k_attn_fwd_mfma(FwdArgs a) {
       *reinterpret_cast<uint4*>(&Ps[h][16 * cq]) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
       *reinterpret_cast<uint4*>(&Ps[h][16 * cq + 8]) = make_uint4(pw[4], pw[5], pw[6], pw[7]);
       if (cq == 0) alpha_s[h] = alpha;
+      if (c0 + kNB == cs.n_cs && l_run > 0.f)
+        lse_c = (m_run + log2f(l_run)) * 0.69314718055994531f;
     }
     __syncthreads();
 
@@ -276,6 +287,7 @@ void k_attn_fwd_mfma(FwdArgs a) {
       lf = l_run * exp2f(m_run - mf) + exp2f(sk - mf);
     }
     a.lse[(int64_t)t * kH + h] = (mf + log2f(lf)) * ln2;
+    if (a.lse_cmp) a.lse_cmp[(int64_t)t * kH + h] = lse_c;
     fin_s[h] = exp2f(m_run - mf) / lf;
   }
   __syncthreads();
@@ -305,6 +317,7 @@ hipError_t launch_attn_fwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s
   a.cu_cmp = sh.cu_cmp;
   a.out = (uint16_t*)io.out;
   a.lse = io.lse;
+  a.lse_cmp = io.lse_cmp;
   a.B = sh.B;
   a.T = sh.T;
   a.r = sh.r;
@@ -385,7 +398,7 @@ struct BwdArgs {
 __device__ __forceinline__ FwdArgs as_fwd(const BwdArgs& b) {
   FwdArgs a;
   a.q = b.q; a.kv_cmp = b.kv_cmp; a.kv = b.kv; a.idx = b.idx; a.sink = b.sink; a.cu = b.cu;
-  a.cu_cmp = b.cu_cmp; a.out = nullptr; a.lse = nullptr; a.B = b.B; a.T = b.T; a.r = b.r;
+  a.cu_cmp = b.cu_cmp; a.out = nullptr; a.lse = nullptr; a.lse_cmp = nullptr; a.B = b.B; a.T = b.T; a.r = b.r;
   a.n_cap = b.n_cap; a.W = b.W; a.k_cap = b.k_cap; a.mode = b.mode; a.scale_log2 = b.scale_log2;
   return a;
 }
@@ -410,6 +423,7 @@ __device__ __forceinline__ CandSet make_cands(const FwdArgs& a, int t, const Tok
   if (a.mode == 1) cs.n_c = cs.nv;
   else if (a.mode == 2) cs.n_c = 0;
   else cs.n_c = leading_valid(a.idx + (int64_t)t * a.k_cap, a.k_cap, s_tmp);
+  cs.n_cs = cs.n_c;
   return cs;
 }
 

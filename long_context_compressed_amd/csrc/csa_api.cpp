@@ -166,7 +166,8 @@ csa_status_t csa_topk_select(const csa_params_t* p, const float* scores, int64_t
 csa_status_t csa_sparse_attn_fwd(const csa_params_t* p, const void* q, const void* kv_cmp,
                                  const void* kv, const int32_t* idx, const float* sink,
                                  const int32_t* cu_seqlens, const int32_t* cu_cmp, void* out,
-                                 float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+                                 float* lse, float* lse_cmp, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
   csa_status_t st = check_attn(p);
   if (st) return st;
   if (!q || !kv || !cu_seqlens || !cu_cmp || !out || !lse) return CSA_ERR_NULL;
@@ -177,7 +178,8 @@ csa_status_t csa_sparse_attn_fwd(const csa_params_t* p, const void* q, const voi
   if (need > 0 && (!ws || ws_bytes < need)) return CSA_ERR_WORKSPACE;
   csa::AttnIO io = {};
   io.q = q; io.kv_cmp = kv_cmp; io.kv = kv; io.idx = p->mode == CSA_SPARSE ? idx : nullptr;
-  io.sink = sink; io.out = out; io.lse = lse; io.ws = ws; io.ws_bytes = ws_bytes;
+  io.sink = sink; io.out = out; io.lse = lse; io.lse_cmp = lse_cmp; io.ws = ws;
+  io.ws_bytes = ws_bytes;
   return launched(csa::launch_attn_fwd(sh, io, stream));
 }
 
@@ -206,8 +208,8 @@ csa_status_t csa_sparse_attn_bwd(const csa_params_t* p, const void* q, const voi
 
 csa_status_t csa_indexer_kl(const csa_params_t* p, const void* q, const void* kv_cmp,
                             const float* scores, int64_t ld_scores, const int32_t* idx,
-                            const void* qI, const float* qI_scale, const float* w,
-                            const void* kI_cmp, const float* kI_scale,
+                            const float* teacher_lse, const void* qI, const float* qI_scale,
+                            const float* w, const void* kI_cmp, const float* kI_scale,
                             const int32_t* cu_seqlens, const int32_t* cu_cmp, float grad_scale,
                             float* kl, float* loss, float* dqI, float* dw, float* dkI_cmp,
                             void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -237,6 +239,7 @@ csa_status_t csa_indexer_kl(const csa_params_t* p, const void* q, const void* kv
   csa::KlIO io = {};
   io.q = q; io.kv_cmp = kv_cmp; io.scores = scores; io.ld = ld_scores;
   io.idx = p->teacher == CSA_TEACHER_SELECTED ? idx : nullptr; io.qI = qI;
+  io.teacher_lse = p->teacher == CSA_TEACHER_SELECTED ? teacher_lse : nullptr;
   io.qI_scale = fp8 ? qI_scale : nullptr; io.w = w; io.kI = kI_cmp;
   io.kI_scale = fp8 ? kI_scale : nullptr; io.grad_scale = grad_scale; io.kl = kl; io.loss = loss;
   io.dqI = dqI; io.dw = dw; io.dkI = dkI_cmp; io.ws = ws; io.ws_bytes = ws_bytes;

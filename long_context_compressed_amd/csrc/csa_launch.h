@@ -51,6 +51,7 @@ struct AttnIO {
   const float* sink;
   void* out;
   float* lse;
+  float* lse_cmp;    // optional: log-sum-exp over the compressed candidates only
   // backward only
   const void* o;
   const void* dout;
@@ -73,6 +74,7 @@ struct KlIO {
   const float* scores;
   int64_t ld;
   const int32_t* idx;
+  const float* teacher_lse;   // optional per-head teacher normalizer (selected teacher)
   const void* qI;
   const float* qI_scale;
   const float* w;

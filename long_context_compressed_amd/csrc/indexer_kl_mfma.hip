@@ -49,6 +49,7 @@ struct KlArgs {
   const float* scores;
   int64_t ld;
   const int32_t* idx;
+  const float* teacher_lse;
   const void* qI;
   const float* qI_scale;
   const float* w;
@@ -201,19 +202,23 @@ void k_indexer_kl_mfma(KlArgs a) {
     }
   }
 
-  // ---- block loader: KV rows (and in pass 2 indexer keys, scores, row ids)
-  auto load_block = [&](int c0, int buf, bool second) {
+  // ---- block loader, split in two halves: issue (global -> registers) right after the
+  // barrier that starts a block, commit (registers -> LDS tiles) after the block computes,
+  // so the loads of block c+1 overlap the MFMA work of block c
+  uint4 pre_kv[8];
+  int pre_j[8];
+  float pre_I[8];
+  uint4 pre_ki[2];
+  float pre_sc[2];
+  int pre_kj[2];
+  auto issue = [&](int c0, bool second) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int row = 4 * i + wave;
-      const int j = slot_local(c0 + row);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (j >= 0) v = *reinterpret_cast<const uint4*>(a.kv_cmp + (int64_t)(row0 + j) * kD + 8 * lane);
-      *reinterpret_cast<uint4*>(&Kt[buf][row][8 * lane]) = v;
-      if (lane == 0) {
-        rowid_s[buf][row] = j >= 0 ? row0 + j : -1;
-        I_s[buf][row] = j >= 0 ? srow[j] : 0.f;
-      }
+      const int j = slot_local(c0 + 4 * i + wave);
+      pre_j[i] = j;
+      pre_kv[i] = j >= 0 ? *reinterpret_cast<const uint4*>(a.kv_cmp + (int64_t)(row0 + j) * kD + 8 * lane)
+                         : make_uint4(0, 0, 0, 0);
+      pre_I[i] = (j >= 0 && lane == 0) ? srow[j] : 0.f;
     }
     if (second && a.grads) {
 #pragma unroll
@@ -221,42 +226,69 @@ void k_indexer_kl_mfma(KlArgs a) {
         const int e = tid + 256 * i;
         const int row = e >> 4, ch = e & 15;
         const int j = slot_local(c0 + row);
-        uint4 v = make_uint4(0, 0, 0, 0);
+        pre_kj[i] = j;
+        pre_ki[i] = make_uint4(0, 0, 0, 0);
+        pre_sc[i] = 0.f;
         if (j >= 0) {
           if (!a.fp8) {
-            v = *reinterpret_cast<const uint4*>((const uint16_t*)a.kI + (int64_t)(row0 + j) * kDI + 8 * ch);
+            pre_ki[i] = *reinterpret_cast<const uint4*>((const uint16_t*)a.kI + (int64_t)(row0 + j) * kDI + 8 * ch);
           } else {
             const uint2 cw = *reinterpret_cast<const uint2*>((const uint8_t*)a.kI + (int64_t)(row0 + j) * kDI + 8 * ch);
-            const float sc = a.kI_scale[row0 + j];
-            *reinterpret_cast<uint2*>(&KI8[buf][row][8 * ch]) = cw;
-            if (ch == 0) ksc_s[buf][row] = sc;
-            uint32_t o[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const uint32_t wd = q < 2 ? cw.x : cw.y;
-              const uint32_t b0 = (wd >> (16 * (q & 1))) & 0xffu, b1 = (wd >> (16 * (q & 1) + 8)) & 0xffu;
-              o[q] = (uint32_t)f32_to_bf16_bits(e4m3_to_f32(b0) * sc) |
-                     ((uint32_t)f32_to_bf16_bits(e4m3_to_f32(b1) * sc) << 16);
-            }
-            v = make_uint4(o[0], o[1], o[2], o[3]);
+            pre_ki[i] = make_uint4(cw.x, cw.y, 0, 0);
+            pre_sc[i] = a.kI_scale[row0 + j];
           }
-        }
-        *reinterpret_cast<uint4*>(&KIt[buf][row][8 * ch]) = v;
-        if (a.fp8 && j < 0) {
-          *reinterpret_cast<uint2*>(&KI8[buf][row][8 * ch]) = make_uint2(0, 0);
-          if (ch == 0) ksc_s[buf][row] = 0.f;
         }
       }
     }
   };
+  auto commit = [&](int buf, bool second) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 4 * i + wave;
+      *reinterpret_cast<uint4*>(&Kt[buf][row][8 * lane]) = pre_kv[i];
+      if (lane == 0) {
+        rowid_s[buf][row] = pre_j[i] >= 0 ? row0 + pre_j[i] : -1;
+        I_s[buf][row] = pre_I[i];
+      }
+    }
+    if (second && a.grads) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int e = tid + 256 * i;
+        const int row = e >> 4, ch = e & 15;
+        uint4 v = pre_ki[i];
+        if (a.fp8) {
+          const uint2 cw = make_uint2(pre_ki[i].x, pre_ki[i].y);
+          *reinterpret_cast<uint2*>(&KI8[buf][row][8 * ch]) = cw;
+          if (ch == 0) ksc_s[buf][row] = pre_sc[i];
+          uint32_t o[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t wd = q < 2 ? cw.x : cw.y;
+            const uint32_t b0 = (wd >> (16 * (q & 1))) & 0xffu, b1 = (wd >> (16 * (q & 1) + 8)) & 0xffu;
+            o[q] = (uint32_t)f32_to_bf16_bits(e4m3_to_f32(b0) * pre_sc[i]) |
+                   ((uint32_t)f32_to_bf16_bits(e4m3_to_f32(b1) * pre_sc[i]) << 16);
+          }
+          v = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+        *reinterpret_cast<uint4*>(&KIt[buf][row][8 * ch]) = v;
+        (void)pre_kj;
+      }
+    }
+  };
 
-  // ---- pass 1: per-head teacher log-sum-exp over C_t
+  // ---- pass 1: per-head teacher log-sum-exp over C_t (skipped when the forward supplied it)
   float m_h = -INFINITY, l_h = 0.f;
   int buf = 0;
-  load_block(0, 0, false);
-  for (int c0 = 0; c0 < n_c; c0 += kNB, buf ^= 1) {
+  const bool have_lse = a.teacher_lse != nullptr;
+  if (!have_lse) {
+    issue(0, false);
+    commit(0, false);
+  }
+  for (int c0 = 0; c0 < (have_lse ? 0 : n_c); c0 += kNB, buf ^= 1) {
     __syncthreads();
-    if (c0 + kNB < n_c) load_block(c0 + kNB, buf ^ 1, false);
+    const bool more = c0 + kNB < n_c;
+    if (more) issue(c0 + kNB, false);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -274,6 +306,7 @@ void k_indexer_kl_mfma(KlArgs a) {
         }
       }
     }
+    if (more) commit(buf ^ 1, false);
   }
   {  // merge the 4 lane groups of head h
 #pragma unroll
@@ -286,7 +319,11 @@ void k_indexer_kl_mfma(KlArgs a) {
       }
     }
   }
-  const float lse2 = l_h > 0.f ? m_h + log2f(l_h) : INFINITY;
+  float lse2 = l_h > 0.f ? m_h + log2f(l_h) : INFINITY;
+  if (have_lse) {
+    const float v = a.teacher_lse[(int64_t)t * kH + h];
+    lse2 = v > -INFINITY ? v * 1.44269504088896341f : INFINITY;
+  }
 
   // ---- pass 2
   bf16x8 qib[4];
@@ -310,10 +347,12 @@ void k_indexer_kl_mfma(KlArgs a) {
   for (int nt = 0; nt < 8; ++nt) dqa[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int jr = c16 >> 2, jc = 4 * (c16 & 3);
   buf = 0;
-  load_block(0, 0, true);
+  issue(0, true);
+  commit(0, true);
   for (int c0 = 0; c0 < n_c; c0 += kNB, buf ^= 1) {
     __syncthreads();
-    if (c0 + kNB < n_c) load_block(c0 + kNB, buf ^ 1, true);
+    const bool more = c0 + kNB < n_c;
+    if (more) issue(c0 + kNB, true);
     // teacher probabilities of head h, summed over the wave's 16 heads
     float ps[2][4];
 #pragma unroll
@@ -412,6 +451,7 @@ void k_indexer_kl_mfma(KlArgs a) {
           }
         }
     }
+    if (more) commit(buf ^ 1, true);
   }
   // ---- outputs
   if (a.grads) {
@@ -445,6 +485,7 @@ hipError_t launch_indexer_kl_mfma(const Shape& sh, const KlIO& io, hipStream_t s
   a.scores = io.scores;
   a.ld = io.ld;
   a.idx = io.idx;
+  a.teacher_lse = sh.teacher == 1 ? io.teacher_lse : nullptr;
   a.qI = io.qI;
   a.qI_scale = io.qI_scale;
   a.w = io.w;

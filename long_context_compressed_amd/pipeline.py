@@ -73,6 +73,8 @@ class CsaLayer:
         self.kv_cmp = z(self.tc_cap, D, dtype=dt)
         self.out = z(T, H, D, dtype=dt)
         self.lse = z(T, H)
+        # selected-set teacher: the forward also returns the compressed-only normalizer
+        self.lse_cmp = z(T, H) if (cfg.has_indexer and cfg.teacher == "selected") else None
         self.ws_fwd = self._ws(B.CSA_OP_ATTN_FWD, device)
         if cfg.has_indexer:
             HI, dI = cfg.idx_heads, cfg.idx_dim
@@ -138,7 +140,8 @@ class CsaLayer:
                        self.idx)
             idx = self.idx
         self._call("attn_fwd", B.csa_sparse_attn_fwd, p, inp["q"], self.kv_cmp, inp["kv"], idx,
-                   inp.get("sink"), cu_seqlens, self.cu_cmp, self.out, self.lse, self.ws_fwd)
+                   inp.get("sink"), cu_seqlens, self.cu_cmp, self.out, self.lse, self.lse_cmp,
+                   self.ws_fwd)
         if cfg.has_indexer and cfg.teacher != "none":
             grads = self.backward
             if grads:
@@ -146,7 +149,8 @@ class CsaLayer:
             self._call("indexer_kl", B.csa_indexer_kl, p, inp["q"], self.kv_cmp, self.scores,
                        self.idx, qI, qs, inp["w"], kI, ks, cu_seqlens, self.cu_cmp,
                        self.grad_scale, self.kl, self.loss, self.dqI if grads else None,
-                       self.dw if grads else None, self.dkI_cmp if grads else None, self.ws_kl)
+                       self.dw if grads else None, self.dkI_cmp if grads else None, self.ws_kl,
+                       self.lse_cmp)
 
     def backward_step(self, inp, cu_seqlens):
         cfg, p = self.cfg, self.p

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 1
+    assert lib.csa_abi_version() == 2
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.csa_status_string(st)
     assert lib.csa_status_string(7) == b"unknown status"
@@ -110,8 +110,8 @@ def test_scores_and_topk_validation(lib):
 def test_attention_validation(lib):
     p = _params()
     f = lib.csa_sparse_attn_fwd
-    a = [FAKE] * 9
-    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, None, 0,
+    a = [FAKE] * 10
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, None, None, 0,
              None) == B.CSA_ERR_NULL                                          # idx for sparse
     assert f(ctypes.byref(_params(window=0)), *a, None, 0, None) == B.CSA_ERR_ARG
     assert f(ctypes.byref(_params(scale=0.0)), *a, None, 0, None) == B.CSA_ERR_ARG
@@ -119,7 +119,7 @@ def test_attention_validation(lib):
     assert f(ctypes.byref(_params(head_dim=1024)), *a, None, 0, None) == B.CSA_ERR_UNSUPPORTED
     assert f(ctypes.byref(_params(dtype=B.CSA_FP8_E4M3)), *a, None, 0, None) == B.CSA_ERR_UNSUPPORTED
     assert f(ctypes.byref(_params(mode=B.CSA_DENSE)), FAKE, None, FAKE, None, None, FAKE, FAKE,
-             FAKE, FAKE, None, 0, None) == B.CSA_ERR_NULL                    # kv_cmp for dense
+             FAKE, FAKE, None, None, 0, None) == B.CSA_ERR_NULL              # kv_cmp for dense
     b = lib.csa_sparse_attn_bwd
     args = [FAKE] * 14
     bf = _params(heads=64, head_dim=512, dtype=B.CSA_BF16)
@@ -134,7 +134,7 @@ def test_indexer_kl_validation(lib):
     f = lib.csa_indexer_kl
 
     def call(pp, idx=FAKE, grads=(FAKE, FAKE, FAKE), ld=64, gs=1.0):
-        return f(ctypes.byref(pp), FAKE, FAKE, FAKE, ld, idx, FAKE, None, FAKE, FAKE, None,
+        return f(ctypes.byref(pp), FAKE, FAKE, FAKE, ld, idx, None, FAKE, None, FAKE, FAKE, None,
                  FAKE, FAKE, gs, FAKE, FAKE, *grads, None, 0, None)
 
     assert call(_params(teacher=B.CSA_TEACHER_NONE)) == B.CSA_ERR_ARG

@@ -275,9 +275,10 @@ def test_attn_fwd(name):
     kvc = G.dev(kv_cmp_r if kv_cmp_r.size else np.zeros((1, w.head_dim)), dt)
     idx_d = torch.from_numpy(idx.astype(np.int32)).cuda() if w.mode == "sparse" else None
     sink = host.get("sink")
+    lse_cmp = torch.empty_like(L.lse)
     B.csa_sparse_attn_fwd(L.p, host["q"].cuda(), kvc, host["kv"].cuda(), idx_d,
                           None if sink is None else sink.cuda(), cu, L.cu_cmp, L.out, L.lse,
-                          L.ws_fwd)
+                          lse_cmp, ws=L.ws_fwd)
     n = int(host["cu_seqlens"][-1])
     rows = np.arange(n)
     Oref, Lref = O.sparse_attn_fwd(h64["q"], kv_cmp_r, h64["kv"], _mode_idx(w, idx),
@@ -286,6 +287,22 @@ def test_attn_fwd(name):
     torch.cuda.synchronize()
     G.check("O", G.back(L.out)[:n], Oref, w.dtype)
     G.check("LSE", G.back(L.lse)[:n], Lref, w.dtype)
+    # compressed-only normalizer: the same attention with an empty window and no sink
+    bb, pp = O.token_positions(host["cu_seqlens"], w.total_tokens)
+    if w.mode == "sparse":
+        has_c = np.array([(idx[t] >= 0).any() for t in rows])
+    elif w.mode == "dense":
+        has_c = (pp[rows] + 1) // w.ratio > 0
+    else:
+        has_c = np.zeros(n, dtype=bool)
+    got_c = G.back(lse_cmp)[:n]
+    assert np.all(np.isneginf(got_c[~has_c])), "queries without compressed candidates"
+    rc = rows[has_c]
+    if rc.size:
+        mi = None if _mode_idx(w, idx) is None else idx[rc]
+        _, Lc = O.sparse_attn_fwd(h64["q"], kv_cmp_r, h64["kv"], mi, None, host["cu_seqlens"],
+                                  w.ratio, 0, w.scale, rows=rc)
+        G.check("LSE(compressed only)", got_c[has_c], Lc, w.dtype)
     if n < w.total_tokens:
         assert torch.all(L.out[n:] == 0) and torch.all(L.lse[n:] == 0)
 
@@ -339,12 +356,21 @@ def test_attn_bwd(name):
 
 
 # ------------------------------------------------------------------------- indexer KL
-@pytest.mark.parametrize("name", _kl_cases())
-@pytest.mark.parametrize("grads", [True, False])
-def test_indexer_kl(name, grads):
+def _kl_variants():
+    out = []
+    for n in _kl_cases():
+        w = configs.workload(CASES[n][0], **CASES[n][1])
+        out += [(n, True, False), (n, False, False)]
+        if w.teacher == "selected":
+            out.append((n, True, True))
+    return out
+
+
+@pytest.mark.parametrize("name,grads,fwd_lse", _kl_variants())
+def test_indexer_kl(name, grads, fwd_lse):
     from long_context_compressed_amd import binding as B
     w, host, h64 = _case(name)
-    _announce(name, f"indexer_kl grads={grads}")
+    _announce(name, f"indexer_kl grads={grads} fwd_lse={fwd_lse}")
     L = _layer(w, host, backward=True)
     cu = _cu(host)
     L.metadata(cu)
@@ -354,12 +380,19 @@ def test_indexer_kl(name, grads):
     sc = O.index_scores(qI64, h64["w"], kI64, host["cu_seqlens"], w.ratio, L.n_cap)
     s32 = np.where(np.isfinite(sc), sc, 0.0).astype(np.float32)
     gs = 0.5
+    teacher_lse = None
+    if fwd_lse:
+        # the selected-set teacher normalizer taken from the GPU forward on the same inputs
+        teacher_lse = torch.empty_like(L.lse)
+        B.csa_sparse_attn_fwd(L.p, host["q"].cuda(), G.dev(kv_cmp_r, dt), host["kv"].cuda(),
+                              torch.from_numpy(idx.astype(np.int32)).cuda(), None, cu, L.cu_cmp,
+                              L.out, L.lse, teacher_lse, ws=L.ws_fwd)
     L.dkI_cmp.zero_()
     B.csa_indexer_kl(L.p, host["q"].cuda(), G.dev(kv_cmp_r, dt), torch.from_numpy(s32).cuda(),
                      torch.from_numpy(idx.astype(np.int32)).cuda(), d["qI"], d["qI_scale"],
                      host["w"].cuda(), d["kI"], d["kI_scale"], cu, L.cu_cmp, gs, L.kl, L.loss,
                      L.dqI if grads else None, L.dw if grads else None,
-                     L.dkI_cmp if grads else None, L.ws_kl)
+                     L.dkI_cmp if grads else None, L.ws_kl, teacher_lse)
     n = int(host["cu_seqlens"][-1])
     rows = np.arange(n)
     kl, loss, dqI, dw, dkI = O.indexer_kl(h64["q"], kv_cmp_r, s32[:n], idx[:n], qI64, h64["w"],
