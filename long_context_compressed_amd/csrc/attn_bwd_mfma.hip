@@ -1,339 +1,19 @@
-// Matrix-core (MFMA) sparse attention for bf16 operands, H = 64 heads sharing one
+// Matrix-core (MFMA) sparse attention backward for bf16 operands, H = 64 heads sharing one
 // D = 512 K=V row (MQA), on gfx950.
 //
-// Method ("DeepSeek-V4 Attention Training Systems", sections 2 and 8.2): each query
-// attends its selected (or all visible) compressed rows plus its local raw window;
-// forward returns O and the log-sum-exp.
-//
-// Forward design: one workgroup (4 waves) per query token; the 64 heads form the M
-// dimension of every product, so each gathered 1 KiB row feeds 64 x 512 x 4 FLOP.
-// Wave w owns the 128-wide slice D_w of the row:
-//   1. it loads K[c, D_w] for a block of 64 candidates straight from HBM/L2 into MFMA
-//      A-operand registers (16-byte loads, one row segment per lane);
-//   2. S^T_w = K[:, D_w] Q[:, D_w]^T on v_mfma_f32_16x16x32_bf16 (Q slice resident in
-//      registers for the whole token);
-//   3. the four partial S_w are summed through LDS; wave w runs the online softmax of
-//      heads 16w..16w+15 and publishes P (bf16) and the per-head rescale factors;
-//   4. the same K registers, written once to a wave-private transposed LDS tile, are
-//      the B operand of O[:, D_w] += P V[:, D_w].
-// Every gathered byte is read from memory once per token.  Tokens are mapped to
-// workgroups so that each XCD walks contiguous 256-token chunks (its L2 then holds the
-// compressed rows of one sample).
+// Method ("DeepSeek-V4 Attention Training Systems", section 8.2): from the saved O and
+// log-sum-exp, recompute P over each query's candidates and return dq, the gradients of
+// the shared compressed rows and raw window rows (key and value contributions summed, as
+// one row is both), and the optional sink gradient.
 #include <math.h>
 
-#include "csa_device.h"
+#include "attn_common.h"
 #include "csa_launch.h"
 
 namespace csa {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+using namespace attn;
 
-namespace {
-
-constexpr int kH = 64;
-constexpr int kD = 512;
-constexpr int kDW = 128;    // d per wave
-constexpr int kNB = 64;     // candidates per block
-constexpr int kSPS = 68;    // row stride (floats) of the partial-S tiles
-constexpr int kPS = 72;     // row stride (bf16) of the P tile
-constexpr int kVTS = 72;    // row stride (bf16) of the transposed V tiles
-constexpr int kChunk = 256; // tokens per XCD chunk
-
-struct FwdArgs {
-  const uint16_t* q;
-  const uint16_t* kv_cmp;
-  const uint16_t* kv;
-  const int32_t* idx;
-  const float* sink;
-  const int32_t* cu;
-  const int32_t* cu_cmp;
-  uint16_t* out;
-  float* lse;
-  float* lse_cmp;    // optional log-sum-exp over the compressed candidates only
-  int B, T, r, n_cap, W, k_cap, mode;
-  float scale_log2;  // softmax scale * log2(e)
-};
-
-__device__ __forceinline__ bf16x8 ld16(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
-}
-
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Workgroup -> token: XCD x = bid % 8 takes 256-token chunks x, x+8, x+16, ...
-__device__ __forceinline__ int token_of_block(int bid) {
-  const int x = bid & 7, j = bid >> 3;
-  return (j / kChunk) * (8 * kChunk) + x * kChunk + (j % kChunk);
-}
-
-// First -1 of an idx row; every lane gets it.
-__device__ int leading_valid(const int32_t* __restrict__ row, int k_cap, int* s_tmp) {
-  if (threadIdx.x == 0) *s_tmp = k_cap;
-  __syncthreads();
-  for (int c = threadIdx.x; c < k_cap; c += blockDim.x)
-    if (row[c] < 0) atomicMin(s_tmp, c);
-  __syncthreads();
-  const int n = *s_tmp;
-  __syncthreads();
-  return n;
-}
-
-// Candidate slots of a query: compressed candidates in [0, n_c), masked padding in
-// [n_c, n_cs), window rows in [n_cs, n_cs + n_w).
-struct CandSet {
-  int n_c, n_cs, n_w, row0, nv, win0;
-};
-
-// Pointer to the row of candidate slot c, or nullptr for a masked / absent slot.
-__device__ __forceinline__ const uint16_t* cand_ptr(const FwdArgs& a, int t, const CandSet& cs,
-                                                    int c) {
-  if (c < cs.n_c) {
-    const int g = a.mode == 1 ? cs.row0 + c : a.idx[(int64_t)t * a.k_cap + c];
-    return (g >= cs.row0 && g < cs.row0 + cs.nv) ? a.kv_cmp + (int64_t)g * kD : nullptr;
-  }
-  if (c < cs.n_cs) return nullptr;
-  if (c < cs.n_cs + cs.n_w) return a.kv + (int64_t)(cs.win0 + (c - cs.n_cs)) * kD;
-  return nullptr;
-}
-
-}  // namespace
-
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_attn_fwd_mfma(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) float Sp[4][kH][kSPS];
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[kH][kPS];
-  __shared__ __attribute__((aligned(16))) uint16_t VT[4][kDW][kVTS];
-  __shared__ float alpha_s[kH];
-  __shared__ float fin_s[kH];
-  __shared__ int valid_s[kNB];
-  __shared__ int s_tmp;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int g = lane >> 4;     // lane group (k-slot of the MFMA operands)
-  const int c16 = lane & 15;   // row / column within a 16-wide tile
-  const int t = token_of_block(blockIdx.x);
-  if (t >= a.T) return;
-
-  TokenInfo ti;
-  if (!token_info(a.cu, a.B, t, ti)) {
-    uint4* o = reinterpret_cast<uint4*>(a.out + (int64_t)t * kH * kD);
-    for (int e = threadIdx.x; e < kH * kD / 8; e += 256) o[e] = make_uint4(0, 0, 0, 0);
-    if (threadIdx.x < kH) a.lse[(int64_t)t * kH + threadIdx.x] = 0.f;
-    if (a.lse_cmp && threadIdx.x < kH) a.lse_cmp[(int64_t)t * kH + threadIdx.x] = -INFINITY;
-    return;
-  }
-  CandSet cs;
-  cs.row0 = a.cu_cmp[ti.b];
-  cs.nv = min((ti.p + 1) / a.r, a.n_cap);
-  cs.n_w = min(a.W, ti.p + 1);
-  cs.win0 = t - cs.n_w + 1;
-  if (a.mode == 1) cs.n_c = cs.nv;
-  else if (a.mode == 2) cs.n_c = 0;
-  else cs.n_c = leading_valid(a.idx + (int64_t)t * a.k_cap, a.k_cap, &s_tmp);
-  // compressed slots padded to whole blocks, so a block never mixes compressed and window
-  // rows and the compressed-only normalizer can be read off after the last compressed block
-  cs.n_cs = ((cs.n_c + kNB - 1) / kNB) * kNB;
-  const int n_tot = cs.n_cs + cs.n_w;
-  const int dw = wave * kDW;
-  float lse_c = -INFINITY;
-
-  // Q^T as the B operand: qb[nt][ks] = Q[16nt + c16][dw + 32ks + 8g .. +7]
-  bf16x8 qb[4][4];
-  const uint16_t* qt = a.q + (int64_t)t * kH * kD;
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qb[nt][ks] = ld16(qt + (16 * nt + c16) * kD + dw + 32 * ks + 8 * g);
-
-  f32x4 o[4][8];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) o[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int hl = lane >> 2, cq = lane & 3;   // softmax lane: head 16*wave+hl, candidates 16cq..
-  float m_run = -INFINITY, l_run = 0.f;
-
-  for (int c0 = 0; c0 < n_tot; c0 += kNB) {
-    // ---- gather K[c, D_w] for the 64 candidates of this block
-    bf16x8 kr[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int c = c0 + 16 * mt + c16;
-      const uint16_t* src = cand_ptr(a, t, cs, c);
-      if (wave == 0 && g == 0) valid_s[16 * mt + c16] = src != nullptr;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (src) kr[mt][ks] = ld16(src + dw + 32 * ks + 8 * g);
-        else kr[mt][ks] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-      }
-    }
-    // ---- partial S^T over this wave's d slice
-    f32x4 st[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma16(kr[mt][ks], qb[nt][ks], acc);
-        st[mt][nt] = acc;
-      }
-    // ---- K slice -> wave-private transposed tile VT[d][c] (column swizzle 16*((d/8)%4))
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 bits = __builtin_bit_cast(uint4, kr[mt][ks]);
-        const uint32_t w4[4] = {bits.x, bits.y, bits.z, bits.w};
-        const int col = (16 * mt + c16) ^ (16 * g);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int d = 32 * ks + 8 * g + i;
-          VT[wave][d][col] = (uint16_t)((i & 1) ? (w4[i >> 1] >> 16) : (w4[i >> 1] & 0xffffu));
-        }
-      }
-    // ---- publish partial S as [h][c]
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        *reinterpret_cast<f32x4*>(&Sp[wave][16 * nt + c16][16 * mt + 4 * g]) = st[mt][nt];
-    __syncthreads();
-
-    // ---- reduce the four partials; online softmax of head 16*wave+hl
-    {
-      const int h = 16 * wave + hl;
-      float s[16];
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        f32x4 acc = *reinterpret_cast<const f32x4*>(&Sp[0][h][16 * cq + 4 * j4]);
-#pragma unroll
-        for (int w2 = 1; w2 < 4; ++w2) acc += *reinterpret_cast<const f32x4*>(&Sp[w2][h][16 * cq + 4 * j4]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[4 * j4 + i] = acc[i];
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        s[j] = valid_s[16 * cq + j] ? s[j] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, s[j]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-      const float m_new = fmaxf(m_run, mx);
-      float alpha = 1.f, sum = 0.f;
-      uint32_t pw[8];
-      if (m_new == -INFINITY) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pw[j] = 0u;
-      } else {
-        alpha = exp2f(m_run - m_new);
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) {
-          const float p0 = exp2f(s[j] - m_new), p1 = exp2f(s[j + 1] - m_new);
-          sum += p0 + p1;
-          pw[j >> 1] = (uint32_t)f32_to_bf16_bits(p0) | ((uint32_t)f32_to_bf16_bits(p1) << 16);
-        }
-      }
-      sum += __shfl_xor(sum, 1, 64);
-      sum += __shfl_xor(sum, 2, 64);
-      l_run = l_run * alpha + sum;
-      m_run = m_new;
-      *reinterpret_cast<uint4*>(&Ps[h][16 * cq]) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-      *reinterpret_cast<uint4*>(&Ps[h][16 * cq + 8]) = make_uint4(pw[4], pw[5], pw[6], pw[7]);
-      if (cq == 0) alpha_s[h] = alpha;
-      if (c0 + kNB == cs.n_cs && l_run > 0.f)
-        lse_c = (m_run + log2f(l_run)) * 0.69314718055994531f;
-    }
-    __syncthreads();
-
-    // ---- O[:, D_w] = alpha * O + P V[:, D_w]
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float al = alpha_s[16 * mt + 4 * g + i];
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) o[mt][nt][i] *= al;
-      }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 pa[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) pa[mt] = ld16(&Ps[16 * mt + c16][32 * kk + 8 * g]);
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int d = 16 * nt + c16;
-        const bf16x8 vb = ld16(&VT[wave][d][(32 * kk + 8 * g) ^ (16 * ((d >> 3) & 3))]);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) o[mt][nt] = mfma16(pa[mt], vb, o[mt][nt]);
-      }
-    }
-  }
-
-  // ---- finalize: lse and 1/l (with the optional sink), then store O
-  if (cq == 0) {
-    const int h = 16 * wave + hl;
-    const float ln2 = 0.69314718055994531f;
-    float mf = m_run, lf = l_run;
-    if (a.sink) {
-      const float sk = a.sink[h] * 1.44269504088896341f;
-      mf = fmaxf(m_run, sk);
-      lf = l_run * exp2f(m_run - mf) + exp2f(sk - mf);
-    }
-    a.lse[(int64_t)t * kH + h] = (mf + log2f(lf)) * ln2;
-    if (a.lse_cmp) a.lse_cmp[(int64_t)t * kH + h] = lse_c;
-    fin_s[h] = exp2f(m_run - mf) / lf;
-  }
-  __syncthreads();
-  uint16_t* op = a.out + (int64_t)t * kH * kD + dw;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 16 * mt + 4 * g + i;
-      const float f = fin_s[h];
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) op[h * kD + 16 * nt + c16] = f32_to_bf16_bits(o[mt][nt][i] * f);
-    }
-}
-
-hipError_t launch_attn_fwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s, bool* handled) {
-  *handled = false;
-  if (sh.dtype != 1 || sh.H != kH || sh.D != kD) return hipSuccess;
-  *handled = true;
-  FwdArgs a;
-  a.q = (const uint16_t*)io.q;
-  a.kv_cmp = (const uint16_t*)io.kv_cmp;
-  a.kv = (const uint16_t*)io.kv;
-  a.idx = io.idx;
-  a.sink = io.sink;
-  a.cu = sh.cu;
-  a.cu_cmp = sh.cu_cmp;
-  a.out = (uint16_t*)io.out;
-  a.lse = io.lse;
-  a.lse_cmp = io.lse_cmp;
-  a.B = sh.B;
-  a.T = sh.T;
-  a.r = sh.r;
-  a.n_cap = sh.max_seqlen / sh.r;
-  a.W = sh.W;
-  a.k_cap = sh.k_cap;
-  a.mode = sh.mode;
-  a.scale_log2 = sh.scale * 1.44269504088896341f;
-  const int64_t chunks = ((int64_t)sh.T + 8 * kChunk - 1) / (8 * kChunk);
-  const int64_t grid = chunks * 8 * kChunk;
-  hipLaunchKernelGGL(k_attn_fwd_mfma, dim3((unsigned)grid), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-// ======================================================================== backward
-//
 // The backward is processed in chunks of query tokens (so the workspace stays bounded);
 // per chunk:
 // Kernel 1 (k_attn_bwd_dq_mfma): one workgroup per query token, wave w owns heads
@@ -358,10 +38,9 @@ hipError_t launch_attn_fwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s
 // Stores + an owner-side gather replace fp32 atomics, which run at a fraction of the
 // store bandwidth on this part.
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
 namespace {
 
+constexpr int kDW = 128;          // d per wave, kernel 2
 constexpr int kNB1 = 32;          // candidates per block, kernel 1
 constexpr int kKS = kD + 16;      // row stride (bf16) of LDS row tiles
 constexpr int kNB2 = 64;          // candidates per block, kernel 2
@@ -395,36 +74,26 @@ struct BwdArgs {
   float scale, scale_log2;
 };
 
-__device__ __forceinline__ FwdArgs as_fwd(const BwdArgs& b) {
-  FwdArgs a;
-  a.q = b.q; a.kv_cmp = b.kv_cmp; a.kv = b.kv; a.idx = b.idx; a.sink = b.sink; a.cu = b.cu;
-  a.cu_cmp = b.cu_cmp; a.out = nullptr; a.lse = nullptr; a.lse_cmp = nullptr; a.B = b.B; a.T = b.T; a.r = b.r;
-  a.n_cap = b.n_cap; a.W = b.W; a.k_cap = b.k_cap; a.mode = b.mode; a.scale_log2 = b.scale_log2;
-  return a;
-}
-
-__device__ __forceinline__ v4i16 ld_tr(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(p));
-}
-
-__device__ __forceinline__ bf16x8 join8(v4i16 lo, v4i16 hi) {
-  const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
-  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
-}
-
-__device__ __forceinline__ CandSet make_cands(const FwdArgs& a, int t, const TokenInfo& ti,
+__device__ __forceinline__ CandSet make_cands(const BwdArgs& b, int t, const TokenInfo& ti,
                                               int* s_tmp) {
   CandSet cs;
-  cs.row0 = a.cu_cmp[ti.b];
-  cs.nv = min((ti.p + 1) / a.r, a.n_cap);
-  cs.n_w = min(a.W, ti.p + 1);
+  cs.row0 = b.cu_cmp[ti.b];
+  cs.nv = min((ti.p + 1) / b.r, b.n_cap);
+  cs.n_w = min(b.W, ti.p + 1);
   cs.win0 = t - cs.n_w + 1;
-  if (a.mode == 1) cs.n_c = cs.nv;
-  else if (a.mode == 2) cs.n_c = 0;
-  else cs.n_c = leading_valid(a.idx + (int64_t)t * a.k_cap, a.k_cap, s_tmp);
+  if (b.mode == 1) cs.n_c = cs.nv;
+  else if (b.mode == 2) cs.n_c = 0;
+  else cs.n_c = leading_valid(b.idx + (int64_t)t * b.k_cap, b.k_cap, s_tmp);
   cs.n_cs = cs.n_c;
   return cs;
+}
+
+// Pointer to the row of candidate slot c, or nullptr for a masked / absent slot.
+__device__ __forceinline__ const uint16_t* cand_ptr(const BwdArgs& b, int t, const CandSet& cs,
+                                                    int c) {
+  const int id = slot_row(b.mode == 0 ? b.idx + (int64_t)t * b.k_cap : nullptr, b.mode, cs, c);
+  if (id == -1) return nullptr;
+  return id >= 0 ? b.kv_cmp + (int64_t)id * kD : b.kv + (int64_t)(-2 - id) * kD;
 }
 
 // Global compressed row of slot c (< n_c) of query t, or -1 if it is outside the visible range.
@@ -440,7 +109,6 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
   __shared__ __attribute__((aligned(16))) uint16_t Kt[2][kNB1][kKS];
   __shared__ int valid_s[2][kNB1];
   __shared__ int s_tmp;
-  const FwdArgs a = as_fwd(b);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int tl = token_of_block(blockIdx.x);
@@ -453,7 +121,7 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
     if (tid == 0) b.nc[t] = 0;
     return;
   }
-  const CandSet cs = make_cands(a, t, ti, &s_tmp);
+  const CandSet cs = make_cands(b, t, ti, &s_tmp);
   if (tid == 0) b.nc[t] = cs.n_c;
   const int n_tot = cs.n_c + cs.n_w;
   const int h = 16 * wave + c16;  // this lane's head for S^T / dP^T (n index)
@@ -489,7 +157,7 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
     pre_ok = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint16_t* src = cand_ptr(a, t, cs, c0 + 4 * i + wave);
+      const uint16_t* src = cand_ptr(b, t, cs, c0 + 4 * i + wave);
       pre[i] = src ? *reinterpret_cast<const uint4*>(src + 8 * lane) : make_uint4(0, 0, 0, 0);
       pre_ok |= (src != nullptr) << i;
     }
@@ -834,7 +502,7 @@ hipError_t launch_attn_bwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s
   for (int64_t t0 = 0; t0 < sh.T; t0 += pl.chunk) {
     b.t0 = (int)t0;
     b.nT = (int)(sh.T - t0 < pl.chunk ? sh.T - t0 : pl.chunk);
-    const int64_t grid = ((b.nT + 8 * kChunk - 1) / (8 * kChunk)) * 8 * kChunk;
+    const int64_t grid = token_grid(b.nT);
     hipLaunchKernelGGL(k_attn_bwd_dq_mfma, dim3((unsigned)grid), dim3(256), 0, s, b);
     hipLaunchKernelGGL(k_attn_bwd_dkv_mfma, dim3((unsigned)grid), dim3(256), 0, s, b);
     if (sh.mode != 2) {

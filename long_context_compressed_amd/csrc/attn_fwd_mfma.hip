@@ -1,0 +1,422 @@
+// Matrix-core (MFMA) sparse attention forward for bf16 operands, H = 64 heads sharing one
+// D = 512 K=V row (MQA), on gfx950.
+//
+// Method ("DeepSeek-V4 Attention Training Systems", sections 2 and 8.2): each query
+// attends its selected (or all visible) compressed rows plus its local raw window; the
+// forward returns O, the log-sum-exp and, optionally, the log-sum-exp over the compressed
+// candidates alone (the normalizer of the selected-set indexer teacher, section 3).
+//
+// Design: one workgroup of 4 waves per query token (one per SIMD, 512 registers each);
+// candidates are processed in blocks of 64 rows, double-buffered in LDS.
+//   * Rows are gathered with direct global->LDS loads (global_load_lds_dwordx4, one 1 KiB
+//     row per wave instruction) one block ahead, so they land while the current block
+//     computes; the idx entries of a block are loaded a block before that.  LDS rows are 1 KiB with a 16-byte chunk swizzle, so both the row-segment
+//     reads of S = Q K^T and the transposed reads of P V are bank-conflict free.
+//   * S^T: wave (hh, ch) computes heads 32hh..32hh+31 against candidates 32ch..32ch+31 of
+//     the block on v_mfma_f32_16x16x32_bf16 (A = row segments from LDS, B = the query's Q
+//     resident in registers); every row segment read from LDS feeds two MFMAs.
+//   * Online softmax per head with a lazily rescaled running max: the max is only moved
+//     when it grows by more than 2^8, so most blocks skip the O rescale.  P (bf16) goes to
+//     LDS.
+//   * O^T: wave w owns d = 128w..128w+127 for all 64 heads: A = the row tile read transposed
+//     (ds_read_b64_tr_b16), B = P^T from LDS.
+//   * O is normalised, transposed through LDS and written with full-row 16-byte stores.
+// Tokens map to workgroups so that each XCD walks contiguous 256-token chunks (its L2 then
+// holds the compressed rows of one sample).
+#include <math.h>
+
+#include "attn_common.h"
+#include "csa_launch.h"
+
+// M0 is named as clobbered by the LDS-DMA asm below; the compiler keeps no value in it here.
+#pragma clang diagnostic ignored "-Winline-asm"
+
+namespace csa {
+
+using namespace attn;
+
+namespace {
+
+constexpr int kNB = 64;        // candidates per block
+constexpr int kPS = 72;        // P tile row stride (bf16)
+constexpr float kLazy = 8.f;
+constexpr int kFwdWaves = 4;     // one wave per SIMD: each wave holds Q (32 heads) and 1/4 of O   // growth (log2 units) of the running max tolerated before rescaling
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* kv_cmp;
+  const uint16_t* kv;
+  const int32_t* idx;
+  const float* sink;
+  const int32_t* cu;
+  const int32_t* cu_cmp;
+  uint16_t* out;
+  float* lse;
+  float* lse_cmp;    // optional log-sum-exp over the compressed candidates only
+  int B, T, r, n_cap, W, k_cap, mode;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// One 16-byte-per-lane global -> LDS load (global_load_lds_dwordx4); lane l's 16 bytes land
+// at LDS byte offset lds + 16 l.  Issued through asm so that the compiler does not order the
+// LDS reads of the other tile buffer behind it: completion is awaited explicitly with
+// wait_vmem() before the barrier that publishes the tile.
+__device__ __forceinline__ void dma_row16(const void* src, const void* lds_row) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_row);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(src) : "memory", "m0");
+}
+
+}  // namespace
+
+// NW waves per query: NW/2 candidate groups of CPW = 128/NW candidates for S^T, and d slices
+// of DPW = 512/NW columns for O^T.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+void k_attn_fwd_mfma(FwdArgs a) {
+  constexpr int NT = NW * 64, NCH = NW / 2, CPW = kNB / NCH, MQ = CPW / 16, DPW = kD / NW,
+                MP = DPW / 16, RPW = kNB / NW;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kNB][kD];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[kH][kPS];
+  __shared__ float mx_s[NCH][kH];
+  __shared__ float alpha_s[kH];
+  __shared__ float lsum_s[NCH][kH], lsnap_s[NCH][kH];
+  __shared__ float mrun_s[kH], msnap_s[kH], fin_s[kH];
+  __shared__ int resc_s[2];
+  __shared__ int s_tmp;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int hh = wave & 1, ch = wave >> 1;
+  const int t = token_of_block(blockIdx.x);
+  if (t >= a.T) return;
+
+  TokenInfo ti;
+  if (!token_info_wave(a.cu, a.B, t, ti)) {
+    uint4* o = reinterpret_cast<uint4*>(a.out + (int64_t)t * kH * kD);
+    for (int e = tid; e < kH * kD / 8; e += NT) o[e] = make_uint4(0, 0, 0, 0);
+    if (tid < kH) a.lse[(int64_t)t * kH + tid] = 0.f;
+    if (a.lse_cmp && tid < kH) a.lse_cmp[(int64_t)t * kH + tid] = -INFINITY;
+    return;
+  }
+  // Q^T as the B operand: qb[nt][ks] = Q[32hh + 16nt + c16][32ks + 8g .. +7] (loads issued
+  // first so they overlap the metadata loads below)
+  bf16x8 qb[2][16];
+  {
+    const uint16_t* qt = a.q + ((int64_t)t * kH + 32 * hh + c16) * kD + 8 * g;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) qb[nt][ks] = ld16(qt + 16 * nt * kD + 32 * ks);
+  }
+  const int32_t* idx_t = a.mode == 0 ? a.idx + (int64_t)t * a.k_cap : nullptr;
+  // raw idx entries of slot 64 b + lane; converted to row ids once the candidate counts are known
+  auto raw_of = [&](int b) {
+    const int c = kNB * b + lane;
+    return (a.mode == 0 && c < a.k_cap) ? idx_t[c] : 0;
+  };
+  int raw_cur = raw_of(0);
+  int raw_nxt = raw_of(1);
+
+  CandSet cs;
+  cs.row0 = a.cu_cmp[ti.b];
+  cs.nv = min((ti.p + 1) / a.r, a.n_cap);
+  cs.n_w = min(a.W, ti.p + 1);
+  cs.win0 = t - cs.n_w + 1;
+  if (a.mode == 1) cs.n_c = cs.nv;
+  else if (a.mode == 2) cs.n_c = 0;
+  else cs.n_c = leading_valid(idx_t, a.k_cap, &s_tmp);
+  // compressed slots padded to whole blocks, so a block never mixes compressed and window
+  // rows and the compressed-only normalizer can be read off after the last compressed block
+  cs.n_cs = ((cs.n_c + kNB - 1) / kNB) * kNB;
+  const int nblk = (cs.n_cs + cs.n_w + kNB - 1) / kNB;
+
+  f32x4 o[MP][4];   // O^T: d = DPW wave + 16 mt + 4g + i, head = 16 nt + c16
+#pragma unroll
+  for (int mt = 0; mt < MP; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) o[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  float m_run[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
+  float m_snap[2] = {-INFINITY, -INFINITY}, l_snap[2] = {0.f, 0.f};
+
+  // row-segment reads of S^T: logical chunk 4ks + g of row CPW ch + 16 mq + c16 sits at
+  // physical chunk 16 (ks / 4) + ((4 (ks % 4) + g) ^ swz(c16))
+  int eq[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) eq[q] = 8 * ((4 * q + g) ^ swz(c16));
+  // transposed reads of P V: logical chunk DPW/8 wave + 2 mt + (c16 & 3) / 2 of rows
+  // 32ks + 8g + c16/4 (lo) and +4 (hi); 8 ((2 mt + e) ^ s) = 16 mt ^ 8 (e ^ s)
+  const int tr_e = (c16 & 3) >> 1, tr_off = 4 * (c16 & 1);
+  const int klo = 8 * (tr_e ^ swz(8 * (g & 1) + (c16 >> 2)));
+  const int khi = 8 * (tr_e ^ swz(8 * (g & 1) + 4 + (c16 >> 2)));
+
+  // row id of slot 64 b + lane: >= 0 compressed row, <= -2 raw row -2 - id, -1 none
+  auto rid_of = [&](int b, int raw) {
+    const int c = kNB * b + lane;
+    if (b >= nblk) return -1;
+    if (c < cs.n_c) {
+      const int gr = a.mode == 1 ? cs.row0 + c : raw;
+      return (gr >= cs.row0 && gr < cs.row0 + cs.nv) ? gr : -1;
+    }
+    if (c < cs.n_cs) return -1;
+    if (c < cs.n_cs + cs.n_w) return -2 - (cs.win0 + (c - cs.n_cs));
+    return -1;
+  };
+  // gather block rows RPW wave .. RPW wave + RPW - 1 into tile[buf] (lane l fills physical
+  // chunk l); an absent slot loads the query's own raw row (finite, masked out by the softmax)
+  auto issue_row = [&](int rid, int buf, int j) {
+    const int r = RPW * wave + j;
+    const int id = __builtin_amdgcn_readlane(rid, r);
+    const uint16_t* src = id >= 0 ? a.kv_cmp + (int64_t)id * kD
+                                  : a.kv + (int64_t)(id == -1 ? t : -2 - id) * kD;
+    dma_row16(src + 8 * (lane ^ swz(r)), &tile[buf][r][0]);
+  };
+  auto issue = [&](int rid, int buf) {
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) issue_row(rid, buf, j);
+  };
+
+  int rid_cur = rid_of(0, raw_cur);
+  int rid_nxt = rid_of(1, raw_nxt);
+  if (nblk > 0) issue(rid_cur, 0);
+  wait_vmem();
+  __syncthreads();
+
+  for (int b = 0; b < nblk; ++b) {
+    const int buf = b & 1;
+    const uint64_t valid = __ballot(rid_cur != -1);
+    if (b + 1 < nblk) issue(rid_nxt, buf ^ 1);
+    const int raw_nn = raw_of(b + 2);   // consumed after this block's final wait
+
+    // ---- S^T: candidates CPW ch + 16 mq + 4g + i, heads 32hh + 16nt + c16
+    f32x4 st[MQ][2];
+#pragma unroll
+    for (int mq = 0; mq < MQ; ++mq) st[mq][0] = st[mq][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      // operands read kPre k-steps ahead of the MFMAs that consume them
+      const uint16_t* rb = &tile[buf][CPW * ch + c16][0];
+      auto seg = [&](int ks, int mq) { return ld16(rb + 16 * mq * kD + 128 * (ks >> 2) + eq[ks & 3]); };
+      constexpr int kPre = 3;
+      bf16x8 av[kPre][MQ];
+#pragma unroll
+      for (int j = 0; j < kPre; ++j)
+#pragma unroll
+        for (int mq = 0; mq < MQ; ++mq) av[j][mq] = seg(j, mq);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mq = 0; mq < MQ; ++mq) {
+          st[mq][0] = mfma16(av[ks % kPre][mq], qb[0][ks], st[mq][0]);
+          st[mq][1] = mfma16(av[ks % kPre][mq], qb[1][ks], st[mq][1]);
+        }
+        if (ks + kPre < 16) {
+#pragma unroll
+          for (int mq = 0; mq < MQ; ++mq) av[ks % kPre][mq] = seg(ks + kPre, mq);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // candidate validity of this lane's slots
+    const uint32_t vbits = (uint32_t)(valid >> (CPW * ch + 4 * g));
+    float s[2][4 * MQ];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4 * MQ; ++j) {
+        const int bit = 16 * (j >> 2) + (j & 3);
+        s[nt][j] = ((vbits >> bit) & 1) ? st[j >> 2][nt][j & 3] * a.scale_log2 : -INFINITY;
+        mloc = fmaxf(mloc, s[nt][j]);
+      }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      if (g == 0) mx_s[ch][32 * hh + 16 * nt + c16] = mloc;
+    }
+    __syncthreads();
+
+    // ---- softmax of this block: P (bf16) and the per-head rescale factors
+    bool any_resc = false;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int h = 32 * hh + 16 * nt + c16;
+      float mb = mx_s[0][h];
+#pragma unroll
+      for (int c = 1; c < NCH; ++c) mb = fmaxf(mb, mx_s[c][h]);
+      float alpha = 1.f;
+      if (mb > m_run[nt] + kLazy) {
+        alpha = __builtin_amdgcn_exp2f(m_run[nt] - mb);
+        m_run[nt] = mb;
+        any_resc = true;
+      }
+      float p[4 * MQ], sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4 * MQ; ++j) {
+        const int bit = 16 * (j >> 2) + (j & 3);
+        p[j] = ((vbits >> bit) & 1) ? __builtin_amdgcn_exp2f(s[nt][j] - m_run[nt]) : 0.f;
+        sum += p[j];
+      }
+      l_part[nt] = l_part[nt] * alpha + sum;
+#pragma unroll
+      for (int mq = 0; mq < MQ; ++mq)
+        *reinterpret_cast<uint2*>(&Ps[h][CPW * ch + 16 * mq + 4 * g]) =
+            make_uint2(pack_bf16x2(p[4 * mq], p[4 * mq + 1]), pack_bf16x2(p[4 * mq + 2], p[4 * mq + 3]));
+      if (ch == 0 && g == 0) alpha_s[h] = alpha;
+      if (kNB * (b + 1) == cs.n_cs) {
+        m_snap[nt] = m_run[nt];
+        l_snap[nt] = l_part[nt];
+      }
+    }
+    if (ch == 0) {
+      const uint64_t r = __ballot(any_resc);
+      if (lane == 0) resc_s[hh] = r != 0;
+    }
+    __syncthreads();
+
+    // ---- O^T[d, h] = alpha_h O^T + V^T P^T over this block
+    if (resc_s[0] | resc_s[1]) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float al = alpha_s[16 * nt + c16];
+#pragma unroll
+        for (int mt = 0; mt < MP; ++mt) o[mt][nt] *= al;
+      }
+    }
+    {
+      // unit u = (ks, mt) = (u / MP, u % MP); its transposed row reads are issued two units
+      // ahead of its MFMAs, the P^T operands of k-step 1 during unit 0
+      const uint16_t* vb = &tile[buf][8 * g + (c16 >> 2)][DPW * wave + tr_off];
+      static_assert(DPW <= 128, "the transposed-read swizzle covers 16 chunks of a d slice");
+      auto tr_lo = [&](int u) { return ld_tr(vb + 32 * (u / MP) * kD + ((16 * (u % MP)) ^ klo)); };
+      auto tr_hi = [&](int u) { return ld_tr(vb + (32 * (u / MP) + 4) * kD + ((16 * (u % MP)) ^ khi)); };
+      bf16x8 pb[2][4];
+      v4i16 vlo[2], vhi[2];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) pb[0][nt] = ld16(&Ps[16 * nt + c16][8 * g]);
+      vlo[0] = tr_lo(0);
+      vhi[0] = tr_hi(0);
+      vlo[1] = tr_lo(1);
+      vhi[1] = tr_hi(1);
+#pragma unroll
+      for (int u = 0; u < 2 * MP; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int ks = u / MP, mt = u % MP;
+        const bf16x8 va = join8(vlo[u & 1], vhi[u & 1]);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) o[mt][nt] = mfma16(va, pb[ks][nt], o[mt][nt]);
+        if (u + 2 < 2 * MP) {
+          vlo[u & 1] = tr_lo(u + 2);
+          vhi[u & 1] = tr_hi(u + 2);
+        }
+        if (u == 0) {
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) pb[1][nt] = ld16(&Ps[16 * nt + c16][32 + 8 * g]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmem();
+    __syncthreads();
+    rid_cur = rid_nxt;
+    rid_nxt = rid_of(b + 2, raw_nn);
+  }
+
+  // ---- finalize: per-head normalizers (with the optional sink), lse, lse_cmp
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    float lt = l_part[nt], ls = l_snap[nt];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    if (g == 0) {
+      const int h = 32 * hh + 16 * nt + c16;
+      lsum_s[ch][h] = lt;
+      lsnap_s[ch][h] = ls;
+      if (ch == 0) {
+        mrun_s[h] = m_run[nt];
+        msnap_s[h] = m_snap[nt];
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < kH) {
+    const int h = tid;
+    const float ln2 = 0.69314718055994531f;
+    const float m = mrun_s[h];
+    float l = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) l += lsum_s[c][h];
+    float mf = m, lf = l;
+    if (a.sink) {
+      const float sk = a.sink[h] * 1.44269504088896341f;
+      mf = fmaxf(m, sk);
+      lf = (l > 0.f ? l * exp2f(m - mf) : 0.f) + exp2f(sk - mf);
+    }
+    a.lse[(int64_t)t * kH + h] = (mf + log2f(lf)) * ln2;
+    fin_s[h] = l > 0.f ? exp2f(m - mf) / lf : 0.f;
+    if (a.lse_cmp) {
+      float lc = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) lc += lsnap_s[c][h];
+      a.lse_cmp[(int64_t)t * kH + h] = lc > 0.f ? (msnap_s[h] + log2f(lc)) * ln2 : -INFINITY;
+    }
+  }
+  __syncthreads();
+  // O (bf16) -> LDS as [h][d] with the row swizzle, then full-row stores
+  uint16_t* ot = &tile[0][0][0];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int h = 16 * nt + c16;
+    const float f = fin_s[h];
+#pragma unroll
+    for (int mt = 0; mt < MP; ++mt) {
+      const int d = DPW * wave + 16 * mt + 4 * g;
+      *reinterpret_cast<uint2*>(&ot[h * kD + 8 * ((d >> 3) ^ swz(h)) + (d & 7)]) =
+          make_uint2(pack_bf16x2(o[mt][nt][0] * f, o[mt][nt][1] * f),
+                     pack_bf16x2(o[mt][nt][2] * f, o[mt][nt][3] * f));
+    }
+  }
+  __syncthreads();
+  uint16_t* op = a.out + (int64_t)t * kH * kD;
+#pragma unroll
+  for (int k = 0; k < kH * kD / 8 / NT; ++k) {
+    const int e = tid + NT * k;        // 16-byte chunk of the 64 x 512 output
+    const int h = e >> 6, cc = e & 63;
+    *reinterpret_cast<uint4*>(op + h * kD + 8 * cc) =
+        *reinterpret_cast<const uint4*>(&ot[h * kD + 8 * (cc ^ swz(h))]);
+  }
+}
+
+hipError_t launch_attn_fwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s, bool* handled) {
+  *handled = false;
+  if (sh.dtype != 1 || sh.H != kH || sh.D != kD) return hipSuccess;
+  *handled = true;
+  FwdArgs a;
+  a.q = (const uint16_t*)io.q;
+  a.kv_cmp = (const uint16_t*)io.kv_cmp;
+  a.kv = (const uint16_t*)io.kv;
+  a.idx = io.idx;
+  a.sink = io.sink;
+  a.cu = sh.cu;
+  a.cu_cmp = sh.cu_cmp;
+  a.out = (uint16_t*)io.out;
+  a.lse = io.lse;
+  a.lse_cmp = io.lse_cmp;
+  a.B = sh.B;
+  a.T = sh.T;
+  a.r = sh.r;
+  a.n_cap = sh.max_seqlen / sh.r;
+  a.W = sh.W;
+  a.k_cap = sh.k_cap;
+  a.mode = sh.mode;
+  a.scale_log2 = sh.scale * 1.44269504088896341f;
+  hipLaunchKernelGGL(k_attn_fwd_mfma<kFwdWaves>, dim3((unsigned)token_grid(sh.T)),
+                     dim3(kFwdWaves * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace csa
