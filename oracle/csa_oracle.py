@@ -285,6 +285,30 @@ def sparse_attn_fwd(q, kv_cmp, kv, idx, sink, cu_seqlens, ratio, window, scale, 
     return O, LSE
 
 
+def compressed_logits(q, kv_cmp, idx, cu_seqlens, ratio, scale, rows=None):
+    """Main-attention logits of the compressed candidates of each query, in the order the
+    attention takes them: l[h, c] = scale q[t,h] . kv_cmp[row_c], row_c the c-th valid entry
+    of the idx row (idx given) or the c-th visible compressed row (idx None).  With C_t equal
+    to that set these are the indexer teacher's logits (section 3 with R9).
+    Returns a list (one entry per row) of [H, n_c] arrays."""
+    q = np.asarray(q, dtype=np.float64)
+    kv_cmp = np.asarray(kv_cmp, dtype=np.float64)
+    T = q.shape[0]
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    bb, pp = token_positions(cu_seqlens, T)
+    starts, _ = sample_table(cu_seqlens)
+    cu_cmp = cmp_seqlens(cu_seqlens, ratio)
+    out = []
+    for i, t in enumerate(rows):
+        if bb[t] < 0:
+            out.append(np.zeros((q.shape[1], 0)))
+            continue
+        cr, _ = attn_candidates(t, bb, pp, starts, cu_cmp, ratio, 0,
+                                None if idx is None else idx[i])
+        out.append(scale * (q[t] @ kv_cmp[cr].T))
+    return out
+
+
 def sparse_attn_bwd(q, kv_cmp, kv, idx, sink, cu_seqlens, ratio, window, scale, O, LSE, dO,
                     rows=None):
     """Gradients of the sparse attention given the saved O, LSE and the incoming dO.

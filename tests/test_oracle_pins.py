@@ -592,3 +592,35 @@ def test_packing_invariance_whole_layer():
         sel_p = packed["idx"][s:s + L]
         sel_a = alone["idx"]
         np.testing.assert_array_equal(np.where(sel_p >= 0, sel_p - c0, -1), sel_a)
+
+
+def test_compressed_logits_normalize_to_compressed_lse_and_feed_the_teacher():
+    # the cached-teacher path of the loss reads these logits: their log-sum-exp is the
+    # attention's compressed-only normalizer (window 0, no sink), and the head-averaged
+    # softmax of them reproduces the loss the oracle forms from q and kv_cmp
+    cu, q, kc, qI, w, kI, sc, idx = _kl_case([17, 12])
+    r, scale = 2, 0.4
+    logits = O.compressed_logits(q, kc, idx, cu, r, scale)
+    kv_raw = RNG.standard_normal((q.shape[0], q.shape[2]))
+    rc = np.array([t for t, l in enumerate(logits) if l.shape[1] > 0])
+    _, lse0 = O.sparse_attn_fwd(q, kc, kv_raw, idx[rc], None, cu, r, 0, scale, rows=rc)
+    lse0 = dict(zip(rc.tolist(), lse0))
+    kl, *_ = O.indexer_kl(q, kc, sc, idx, qI, w, kI, cu, r, scale, "selected")
+    cu_cmp = O.cmp_seqlens(cu, r)
+    bb, _ = O.token_positions(cu, q.shape[0])
+    for t, l in enumerate(logits):
+        if l.shape[1] == 0:
+            assert kl[t] == 0
+            continue
+        assert np.allclose(logsumexp(l, axis=1), lse0[t], rtol=0, atol=1e-12)
+        C = idx[t][idx[t] >= 0] - cu_cmp[bb[t]]
+        P = torch.softmax(torch.tensor(l), dim=1).mean(0)
+        logQ = torch.log_softmax(torch.tensor(sc[t, C]), dim=0)
+        ref = torch.nn.functional.kl_div(logQ, P, reduction="sum").item()
+        assert abs(kl[t] - ref) < 1e-12
+    # dense order: visible rows 0 .. n_vis - 1
+    dl = O.compressed_logits(q, kc, None, cu, r, scale)
+    rd = np.array([t for t, l in enumerate(dl) if l.shape[1] > 0])
+    _, lsed = O.sparse_attn_fwd(q, kc, kv_raw, None, None, cu, r, 0, scale, rows=rd)
+    for i, t in enumerate(rd):
+        assert np.allclose(logsumexp(dl[t], axis=1), lsed[i], rtol=0, atol=1e-12)
