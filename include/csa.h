@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+#define CSA_ABI_VERSION 3
 
 typedef int32_t csa_status_t;
 enum {
@@ -103,7 +103,8 @@ typedef struct csa_params {
 } csa_params_t;
 
 /* Workspace-using operations, for csa_workspace_size. */
-enum { CSA_OP_ATTN_FWD = 1, CSA_OP_ATTN_BWD = 2, CSA_OP_INDEXER_KL = 3 };
+enum { CSA_OP_ATTN_FWD = 1, CSA_OP_ATTN_BWD = 2, CSA_OP_INDEXER_KL = 3,
+       CSA_OP_INDEXER_KL_CACHED = 4 /* csa_indexer_kl with teacher_logits */ };
 
 int csa_abi_version(void);
 const char* csa_status_string(csa_status_t status);
@@ -174,14 +175,24 @@ csa_status_t csa_topk_select(const csa_params_t* p, const float* scores, int64_t
  * (no window, no sink; -inf for a query without compressed candidates): with a
  * selected-set teacher this is the teacher's per-head normalizer, which csa_indexer_kl
  * then need not recompute (section 8.2, teacher score recomputation).
+ * Optionally also the compressed-candidate logits themselves, t_logits[t, h, c] = l_x of
+ * compressed slot c (slot order of the idx row for CSA_SPARSE, visible order for
+ * CSA_DENSE) for c < the query's compressed count; other entries are unspecified.  They
+ * are the teacher logits csa_indexer_kl needs when its candidate set equals the
+ * attention's (selected teacher with CSA_SPARSE, dense teacher with CSA_DENSE).
  * q, out: [T, H, D]; kv_cmp: [Tc, D]; kv: [T, D] (dtype); idx: int32 [T, topk_cap] or NULL
  * unless CSA_SPARSE; sink: fp32 [H] or NULL; lse, lse_cmp: fp32 [T, H] (natural log);
- * lse_cmp may be NULL. */
+ * t_logits: fp32 [T, H, csa_teacher_logits_stride(p)].  lse_cmp and t_logits may be NULL. */
 csa_status_t csa_sparse_attn_fwd(const csa_params_t* p, const void* q, const void* kv_cmp,
                                  const void* kv, const int32_t* idx, const float* sink,
                                  const int32_t* cu_seqlens, const int32_t* cu_cmp, void* out,
-                                 float* lse, float* lse_cmp, void* ws, size_t ws_bytes,
-                                 hipStream_t stream);
+                                 float* lse, float* lse_cmp, float* t_logits, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/* Row stride (in elements) of the t_logits cache: the compressed-slot capacity (topk_cap
+ * for CSA_SPARSE, max_seqlen / ratio for CSA_DENSE) rounded up to a multiple of 64; 0 for
+ * CSA_WINDOW or invalid parameters. */
+int64_t csa_teacher_logits_stride(const csa_params_t* p);
 
 /* Sparse attention backward (section 8.2: consumes saved O, LSE, dO; no dense matrix).
  * With P = e^{l_x - lse}, dP = dO.row_x, Dt = dO.O, dS = P (dP - Dt):
@@ -210,11 +221,16 @@ csa_status_t csa_sparse_attn_bwd(const csa_params_t* p, const void* q, const voi
  * teacher_lse: NULL, or (CSA_TEACHER_SELECTED only) the lse_cmp [T, H] that
  * csa_sparse_attn_fwd returned for the same q, kv_cmp and idx; it is then used as the
  * teacher's per-head log-normalizer instead of being recomputed.
+ * teacher_logits: NULL, or the t_logits cache csa_sparse_attn_fwd wrote for the same
+ * q, kv_cmp, idx and params (allowed for CSA_TEACHER_SELECTED with CSA_SPARSE and for
+ * CSA_TEACHER_DENSE with CSA_DENSE; else CSA_ERR_ARG).  Teacher logits may then be read
+ * from it instead of recomputed; results agree up to floating-point rounding.  With a
+ * cache the workspace must be csa_workspace_size(p, CSA_OP_INDEXER_KL_CACHED) bytes.
  * kl: fp32 [T]; loss: fp32 [1]; dqI: fp32 [T, H_I, d_I]; dw: fp32 [T, H_I];
  * dkI_cmp: fp32 [Tc, d_I].  dqI, dw and dkI_cmp all NULL => loss only. */
 csa_status_t csa_indexer_kl(const csa_params_t* p, const void* q, const void* kv_cmp,
                             const float* scores, int64_t ld_scores, const int32_t* idx,
-                            const float* teacher_lse,
+                            const float* teacher_lse, const float* teacher_logits,
                             const void* qI, const float* qI_scale, const float* w,
                             const void* kI_cmp, const float* kI_scale,
                             const int32_t* cu_seqlens, const int32_t* cu_cmp, float grad_scale,

@@ -19,7 +19,7 @@ CSA_OK, CSA_ERR_NULL, CSA_ERR_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_E
 CSA_F32, CSA_BF16, CSA_FP8_E4M3 = 0, 1, 2
 CSA_SPARSE, CSA_DENSE, CSA_WINDOW = 0, 1, 2
 CSA_TEACHER_NONE, CSA_TEACHER_SELECTED, CSA_TEACHER_DENSE = 0, 1, 2
-CSA_OP_ATTN_FWD, CSA_OP_ATTN_BWD, CSA_OP_INDEXER_KL = 1, 2, 3
+CSA_OP_ATTN_FWD, CSA_OP_ATTN_BWD, CSA_OP_INDEXER_KL, CSA_OP_INDEXER_KL_CACHED = 1, 2, 3, 4
 
 _DT = {torch.float32: CSA_F32, torch.bfloat16: CSA_BF16, torch.uint8: CSA_FP8_E4M3}
 
@@ -56,9 +56,10 @@ _SIGS = {
     "csa_quantize_fp8": ([_P, _I32, _I64, _I32, _P, _P, _P], _I32),
     "csa_index_scores": ([_PP, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _P], _I32),
     "csa_topk_select": ([_PP, _P, _I64, _P, _P, _P, _P], _I32),
-    "csa_sparse_attn_fwd": ([_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
+    "csa_sparse_attn_fwd": ([_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
+    "csa_teacher_logits_stride": ([_PP], _I64),
     "csa_sparse_attn_bwd": ([_PP] + [_P] * 14 + [_P, _SZ, _P], _I32),
-    "csa_indexer_kl": ([_PP, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F,
+    "csa_indexer_kl": ([_PP, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F,
                         _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
 }
 
@@ -83,7 +84,7 @@ def header_functions():
     """Names of the functions include/csa.h declares."""
     with open(HEADER) as f:
         text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:csa_status_t|int|const char\*)\s+(csa_\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:csa_status_t|int64_t|int|const char\*)\s+(csa_\w+)\s*\(",
                                  text, re.M)))
 
 
@@ -176,11 +177,15 @@ def csa_topk_select(p, scores, cu_seqlens, cu_cmp, idx, stream=None):
 
 
 def csa_sparse_attn_fwd(p, q, kv_cmp, kv, idx, sink, cu_seqlens, cu_cmp, out, lse, lse_cmp=None,
-                        ws=None, stream=None):
+                        ws=None, stream=None, t_logits=None):
     _check("csa_sparse_attn_fwd", lib().csa_sparse_attn_fwd(
         ctypes.byref(p), _ptr(q), _ptr(kv_cmp), _ptr(kv), _ptr(idx), _ptr(sink), _ptr(cu_seqlens),
-        _ptr(cu_cmp), _ptr(out), _ptr(lse), _ptr(lse_cmp), _ptr(ws), _nbytes(ws),
+        _ptr(cu_cmp), _ptr(out), _ptr(lse), _ptr(lse_cmp), _ptr(t_logits), _ptr(ws), _nbytes(ws),
         _stream(stream)))
+
+
+def csa_teacher_logits_stride(p) -> int:
+    return int(lib().csa_teacher_logits_stride(ctypes.byref(p)))
 
 
 def csa_sparse_attn_bwd(p, q, kv_cmp, kv, idx, sink, cu_seqlens, cu_cmp, out, lse, d_out, dq,
@@ -193,9 +198,9 @@ def csa_sparse_attn_bwd(p, q, kv_cmp, kv, idx, sink, cu_seqlens, cu_cmp, out, ls
 
 def csa_indexer_kl(p, q, kv_cmp, scores, idx, qI, qI_scale, w, kI_cmp, kI_scale, cu_seqlens,
                    cu_cmp, grad_scale, kl, loss, dqI=None, dw=None, dkI_cmp=None, ws=None,
-                   teacher_lse=None, stream=None):
+                   teacher_lse=None, stream=None, teacher_logits=None):
     _check("csa_indexer_kl", lib().csa_indexer_kl(
         ctypes.byref(p), _ptr(q), _ptr(kv_cmp), _ptr(scores), scores.shape[-1], _ptr(idx),
-        _ptr(teacher_lse), _ptr(qI), _ptr(qI_scale), _ptr(w), _ptr(kI_cmp), _ptr(kI_scale), _ptr(cu_seqlens),
+        _ptr(teacher_lse), _ptr(teacher_logits), _ptr(qI), _ptr(qI_scale), _ptr(w), _ptr(kI_cmp), _ptr(kI_scale), _ptr(cu_seqlens),
         _ptr(cu_cmp), float(grad_scale), _ptr(kl), _ptr(loss), _ptr(dqI), _ptr(dw), _ptr(dkI_cmp),
         _ptr(ws), _nbytes(ws), _stream(stream)))

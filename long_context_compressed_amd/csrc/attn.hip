@@ -29,6 +29,8 @@ struct AttnK {
   void* out;
   float* lse;
   float* lse_cmp;
+  float* t_logits;
+  int64_t ld_t;
   const void* o;
   const void* dout;
   void* dq;
@@ -147,6 +149,8 @@ __global__ __launch_bounds__(256) void k_attn_fwd_generic(AttnK a) {
         s = z * a.scale;
       }
       sl[pr] = s;
+      if (a.t_logits && c0 + cc < cd.n_c)
+        a.t_logits[((int64_t)t * a.H + h0 + h) * a.ld_t + c0 + cc] = s;
     }
     __syncthreads();
     if (tid < HG) {
@@ -322,6 +326,7 @@ static AttnK make_k(const Shape& sh, const AttnIO& io) {
   AttnK a;
   a.q = io.q; a.kv_cmp = io.kv_cmp; a.kv = io.kv; a.idx = io.idx; a.sink = io.sink;
   a.cu = sh.cu; a.cu_cmp = sh.cu_cmp; a.out = io.out; a.lse = io.lse; a.lse_cmp = io.lse_cmp;
+  a.t_logits = io.t_logits; a.ld_t = teacher_logits_ld(sh);
   a.o = io.o;
   a.dout = io.dout; a.dq = io.dq; a.dkv_cmp = io.dkv_cmp; a.dkv = io.dkv; a.dsink = io.dsink;
   a.B = sh.B; a.H = sh.H; a.D = sh.D; a.r = sh.r; a.n_cap = sh.r > 0 ? sh.max_seqlen / sh.r : 0;

@@ -53,7 +53,10 @@ struct FwdArgs {
   uint16_t* out;
   float* lse;
   float* lse_cmp;    // optional log-sum-exp over the compressed candidates only
+  float* t_logits;   // optional compressed-candidate logits [T, H, ld_t]
+  int64_t ld_t;
   int B, T, r, n_cap, W, k_cap, mode;
+  float scale;
   float scale_log2;  // softmax scale * log2(e)
 };
 
@@ -219,6 +222,18 @@ void k_attn_fwd_mfma(FwdArgs a) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+    // compressed blocks: keep the logits for the indexer teacher (16-byte stores of four
+    // consecutive slots of one head)
+    if (a.t_logits && kNB * b < cs.n_cs) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float* dst = a.t_logits + ((int64_t)t * kH + 32 * hh + 16 * nt + c16) * a.ld_t +
+                     kNB * b + CPW * ch + 4 * g;
+#pragma unroll
+        for (int mq = 0; mq < MQ; ++mq)
+          *reinterpret_cast<f32x4*>(dst + 16 * mq) = st[mq][nt] * a.scale;
+      }
     }
     // candidate validity of this lane's slots
     const uint32_t vbits = (uint32_t)(valid >> (CPW * ch + 4 * g));
@@ -406,6 +421,9 @@ hipError_t launch_attn_fwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s
   a.out = (uint16_t*)io.out;
   a.lse = io.lse;
   a.lse_cmp = io.lse_cmp;
+  a.t_logits = io.t_logits;
+  a.ld_t = teacher_logits_ld(sh);
+  a.scale = sh.scale;
   a.B = sh.B;
   a.T = sh.T;
   a.r = sh.r;

@@ -82,6 +82,7 @@ csa_status_t csa_workspace_size(const csa_params_t* p, int32_t op, size_t* bytes
     case CSA_OP_ATTN_FWD: *bytes = csa::attn_fwd_workspace(sh); return CSA_OK;
     case CSA_OP_ATTN_BWD: *bytes = csa::attn_bwd_workspace(sh); return CSA_OK;
     case CSA_OP_INDEXER_KL: *bytes = csa::indexer_kl_workspace(sh); return CSA_OK;
+    case CSA_OP_INDEXER_KL_CACHED: *bytes = csa::indexer_kl_cached_workspace(sh); return CSA_OK;
     default: return CSA_ERR_ARG;
   }
 }
@@ -166,8 +167,8 @@ csa_status_t csa_topk_select(const csa_params_t* p, const float* scores, int64_t
 csa_status_t csa_sparse_attn_fwd(const csa_params_t* p, const void* q, const void* kv_cmp,
                                  const void* kv, const int32_t* idx, const float* sink,
                                  const int32_t* cu_seqlens, const int32_t* cu_cmp, void* out,
-                                 float* lse, float* lse_cmp, void* ws, size_t ws_bytes,
-                                 hipStream_t stream) {
+                                 float* lse, float* lse_cmp, float* t_logits, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
   csa_status_t st = check_attn(p);
   if (st) return st;
   if (!q || !kv || !cu_seqlens || !cu_cmp || !out || !lse) return CSA_ERR_NULL;
@@ -178,9 +179,14 @@ csa_status_t csa_sparse_attn_fwd(const csa_params_t* p, const void* q, const voi
   if (need > 0 && (!ws || ws_bytes < need)) return CSA_ERR_WORKSPACE;
   csa::AttnIO io = {};
   io.q = q; io.kv_cmp = kv_cmp; io.kv = kv; io.idx = p->mode == CSA_SPARSE ? idx : nullptr;
-  io.sink = sink; io.out = out; io.lse = lse; io.lse_cmp = lse_cmp; io.ws = ws;
-  io.ws_bytes = ws_bytes;
+  io.sink = sink; io.out = out; io.lse = lse; io.lse_cmp = lse_cmp;
+  io.t_logits = p->mode == CSA_WINDOW ? nullptr : t_logits; io.ws = ws; io.ws_bytes = ws_bytes;
   return launched(csa::launch_attn_fwd(sh, io, stream));
+}
+
+int64_t csa_teacher_logits_stride(const csa_params_t* p) {
+  if (check_attn(p) != CSA_OK) return 0;
+  return csa::teacher_logits_ld(make_shape(p, nullptr, nullptr));
 }
 
 csa_status_t csa_sparse_attn_bwd(const csa_params_t* p, const void* q, const void* kv_cmp,
@@ -208,7 +214,8 @@ csa_status_t csa_sparse_attn_bwd(const csa_params_t* p, const void* q, const voi
 
 csa_status_t csa_indexer_kl(const csa_params_t* p, const void* q, const void* kv_cmp,
                             const float* scores, int64_t ld_scores, const int32_t* idx,
-                            const float* teacher_lse, const void* qI, const float* qI_scale,
+                            const float* teacher_lse, const float* teacher_logits,
+                            const void* qI, const float* qI_scale,
                             const float* w, const void* kI_cmp, const float* kI_scale,
                             const int32_t* cu_seqlens, const int32_t* cu_cmp, float grad_scale,
                             float* kl, float* loss, float* dqI, float* dw, float* dkI_cmp,
@@ -233,10 +240,17 @@ csa_status_t csa_indexer_kl(const csa_params_t* p, const void* q, const void* kv
   const bool fp8 = p->idx_dtype == CSA_FP8_E4M3;
   if (fp8 && (!qI_scale || !kI_scale)) return CSA_ERR_NULL;
   if (ld_scores < n_cap_of(p)) return CSA_ERR_ARG;
+  if (teacher_logits) {
+    const bool same_set = (p->teacher == CSA_TEACHER_SELECTED && p->mode == CSA_SPARSE) ||
+                          (p->teacher == CSA_TEACHER_DENSE && p->mode == CSA_DENSE);
+    if (!same_set || check_attn(p) != CSA_OK) return CSA_ERR_ARG;
+  }
   const Shape sh = make_shape(p, cu_seqlens, cu_cmp);
-  const size_t need = csa::indexer_kl_workspace(sh);
+  const size_t need = teacher_logits ? csa::indexer_kl_cached_workspace(sh)
+                                     : csa::indexer_kl_workspace(sh);
   if (need > 0 && (!ws || ws_bytes < need)) return CSA_ERR_WORKSPACE;
   csa::KlIO io = {};
+  io.t_logits = teacher_logits;
   io.q = q; io.kv_cmp = kv_cmp; io.scores = scores; io.ld = ld_scores;
   io.idx = p->teacher == CSA_TEACHER_SELECTED ? idx : nullptr; io.qI = qI;
   io.teacher_lse = p->teacher == CSA_TEACHER_SELECTED ? teacher_lse : nullptr;

@@ -52,6 +52,7 @@ struct AttnIO {
   void* out;
   float* lse;
   float* lse_cmp;    // optional: log-sum-exp over the compressed candidates only
+  float* t_logits;   // optional: compressed-candidate logits [T, H, ld_t]
   // backward only
   const void* o;
   const void* dout;
@@ -75,6 +76,7 @@ struct KlIO {
   int64_t ld;
   const int32_t* idx;
   const float* teacher_lse;   // optional per-head teacher normalizer (selected teacher)
+  const float* t_logits;      // optional teacher logits cache [T, H, ld_t]
   const void* qI;
   const float* qI_scale;
   const float* w;
@@ -91,6 +93,13 @@ struct KlIO {
 };
 
 size_t indexer_kl_workspace(const Shape& sh);
+size_t indexer_kl_cached_workspace(const Shape& sh);
+
+// Row stride of the teacher-logit cache: compressed-slot capacity rounded up to 64.
+inline int64_t teacher_logits_ld(const Shape& sh) {
+  const int64_t n = sh.mode == 0 ? sh.k_cap : (sh.mode == 1 ? sh.max_seqlen / sh.r : 0);
+  return ((n + 63) / 64) * 64;
+}
 hipError_t launch_indexer_kl(const Shape& sh, const KlIO& io, hipStream_t s);
 
 }  // namespace csa

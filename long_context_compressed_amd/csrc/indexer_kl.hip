@@ -261,6 +261,7 @@ __global__ __launch_bounds__(256) void k_sum(const float* __restrict__ x, int n,
 }
 
 hipError_t launch_indexer_kl_mfma(const Shape& sh, const KlIO& io, hipStream_t s, bool* handled);
+hipError_t launch_indexer_kl_cached(const Shape& sh, const KlIO& io, hipStream_t s, bool* handled);
 
 size_t indexer_kl_workspace(const Shape& sh) { (void)sh; return 0; }
 
@@ -270,7 +271,8 @@ hipError_t launch_indexer_kl(const Shape& sh, const KlIO& io, hipStream_t s) {
     return hipGetLastError();
   }
   bool handled = false;
-  hipError_t e = launch_indexer_kl_mfma(sh, io, s, &handled);
+  hipError_t e = launch_indexer_kl_cached(sh, io, s, &handled);
+  if (!handled) e = launch_indexer_kl_mfma(sh, io, s, &handled);
   if (!handled) {
     KlK a;
     a.q = io.q; a.kv_cmp = io.kv_cmp; a.scores = io.scores; a.ld = io.ld; a.idx = io.idx;

@@ -1,0 +1,622 @@
+// Indexer KL loss and its eager backward from cached teacher logits (gfx950, 64 teacher
+// heads, bf16 64 x 128 indexer).
+//
+// "DeepSeek-V4 Attention Training Systems", section 3: L_I = sum_t KL(P_t || Q_t) over the
+// candidate set C_t; the teacher is detached and gradients reach the indexer query, head
+// weights and indexer keys only.  Section 8.2 recomputes the teacher logits inside the
+// loss; when C_t is exactly the attention's compressed candidate set, the attention
+// forward already formed those logits, and on a part with 288 GB of HBM keeping them
+// (4 bytes per head and candidate) is cheaper than gathering every 1 KiB row again and
+// repeating the QK product.  Teacher reading: P_t = mean over heads of the per-head
+// softmax over C_t.
+//
+// Per query token one workgroup of 4 waves; candidate slots in blocks of 64:
+//   * P_j: each thread reads 4 heads x 4 slots of the cached logits (16-byte loads),
+//     forms e^{l - lse_h} and the head sum is finished across lanes and waves;
+//   * Q_j from the index scores, KL_t, g_j = grad_scale (Q_j - P_j);
+//   * z^T = kI qI^T on v_mfma_f32_16x16x32_bf16 (wave = 32 indexer heads x 32 slots; key
+//     rows gathered into swizzled LDS by direct global->LDS loads one block ahead);
+//   * E = g w 1[z>0], dw += g relu(z); dqI += E kI (E reused from registers as the A
+//     operand, key rows read transposed);
+//   * dkI^T = qI^T E^T over all 64 heads (both operands read transposed from LDS) is
+//     written as one bf16 row per (query, slot) to a staging buffer; a CSR of the
+//     compressed rows then sums each row's staged vectors in fp32.  Plain stores and an
+//     owner-side sum replace fp32 atomics, which run at a fraction of the store bandwidth.
+#include <math.h>
+
+#include "attn_common.h"
+#include "csa_launch.h"
+
+#pragma clang diagnostic ignored "-Winline-asm"
+
+namespace csa {
+
+using namespace attn;
+
+namespace {
+
+constexpr int kHT = 64;     // teacher heads
+constexpr int kHI = 64;     // indexer heads
+constexpr int kDI = 128;    // indexer width
+constexpr int kNB = 64;     // slots per block
+constexpr int kES = 72;     // bf16 row stride of the E tile
+constexpr int64_t kStageBudget = 8ll << 30;   // bytes of staging per chunk
+
+struct KlcArgs {
+  const float* tl;          // cached teacher logits [T, 64, ld_t]
+  int64_t ld_t;
+  const float* tlse;        // teacher lse [T, 64] (natural log) or null
+  const float* scores;
+  int64_t ld;
+  const int32_t* idx;       // null for the dense teacher
+  const uint16_t* qI;
+  const float* w;
+  const uint16_t* kI;
+  const int32_t* cu;
+  const int32_t* cu_cmp;
+  float gs;
+  float* kl;
+  float* dqI;
+  float* dw;
+  uint16_t* stage;          // [chunk][k_slots][128] bf16
+  int32_t* nc;              // [T] candidate count
+  int64_t k_slots;
+  int t0, nT;
+  int B, T, r, n_cap, k_cap, grads;
+};
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void dma_rows16(const void* src, const void* lds) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(a), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float u = __shfl_xor(v, o, 64);
+    v = is_max ? fmaxf(v, u) : v + u;
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))
+                         : (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return r;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_kl_cached(KlcArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t KIt[2][kNB][kDI];   // swizzled 256-byte rows
+  __shared__ __attribute__((aligned(16))) uint16_t QIt[kHI][kDI];      // swizzled 256-byte rows
+  __shared__ __attribute__((aligned(16))) uint16_t Es[kHI][kES];
+  __shared__ float Pp[4][kNB];
+  __shared__ float gw_s[4][kNB];
+  __shared__ float lse2_s[kHT];
+  __shared__ float red[4];
+  __shared__ int s_tmp;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int hh = wave & 1, ch = wave >> 1;
+  const int tl = token_of_block(blockIdx.x);
+  if (tl >= a.nT) return;
+  const int t = a.t0 + tl;
+
+  TokenInfo ti;
+  const bool real = token_info_wave(a.cu, a.B, t, ti);
+  int row0 = 0, nv = 0, n_c = 0;
+  const int32_t* idx_t = a.idx ? a.idx + (int64_t)t * a.k_cap : nullptr;
+  if (real) {
+    row0 = a.cu_cmp[ti.b];
+    nv = min((ti.p + 1) / a.r, a.n_cap);
+    n_c = idx_t ? leading_valid(idx_t, a.k_cap, &s_tmp) : nv;
+  }
+  if (tid == 0) a.nc[t] = n_c;
+  if (n_c == 0) {
+    if (tid == 0) a.kl[t] = 0.f;
+    if (a.grads) {
+      float4* d = reinterpret_cast<float4*>(a.dqI + (int64_t)t * kHI * kDI);
+      for (int e = tid; e < kHI * kDI / 4; e += 256) d[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (tid < kHI) a.dw[(int64_t)t * kHI + tid] = 0.f;
+    }
+    return;
+  }
+  const float* srow = a.scores + (int64_t)t * a.ld;
+  // local visible index of slot c, or -1 (outside C_t or the visible range)
+  auto slot_local = [&](int c) -> int {
+    if (c >= n_c) return -1;
+    if (!idx_t) return c;
+    const int gr = idx_t[c];
+    return (gr >= row0 && gr < row0 + nv) ? gr - row0 : -1;
+  };
+
+  // ---- student log-sum-exp over C_t
+  float mx = -INFINITY;
+  for (int c = tid; c < n_c; c += 256) {
+    const int j = slot_local(c);
+    if (j >= 0) mx = fmaxf(mx, srow[j]);
+  }
+  const float mS = block_reduce(mx, red, true);
+  float sm = 0.f;
+  for (int c = tid; c < n_c; c += 256) {
+    const int j = slot_local(c);
+    if (j >= 0) sm += expf(srow[j] - mS);
+  }
+  const float sS = block_reduce(sm, red, false);
+  // all slots out of the visible range (an invalid idx row): Q_t = 0 instead of NaN
+  const float lseS = sS > 0.f ? mS + logf(sS) : INFINITY;
+
+  // ---- teacher log-normalizer per head (log2 domain), from the forward or the cache
+  const float* tl_t = a.tl + (int64_t)t * kHT * a.ld_t;
+  if (a.tlse) {
+    if (tid < kHT) {
+      const float v = a.tlse[(int64_t)t * kHT + tid];
+      lse2_s[tid] = v > -INFINITY ? v * 1.44269504088896341f : INFINITY;
+    }
+  } else {
+    // wave w: heads 16w..16w+15, one head at a time over all slots
+    for (int hq = 0; hq < 16; ++hq) {
+      const int h = 16 * wave + hq;
+      float m = -INFINITY, l = 0.f;
+      for (int c = lane; c < n_c; c += 64) {
+        if (slot_local(c) < 0) continue;
+        const float s2 = tl_t[(int64_t)h * a.ld_t + c] * 1.44269504088896341f;
+        if (s2 > m) { l = l * exp2f(m - s2) + 1.f; m = s2; } else { l += exp2f(s2 - m); }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float mo = __shfl_xor(m, o, 64), lo = __shfl_xor(l, o, 64);
+        const float mn = fmaxf(m, mo);
+        if (mn != -INFINITY) { l = l * exp2f(m - mn) + lo * exp2f(mo - mn); m = mn; }
+      }
+      if (lane == 0) lse2_s[h] = l > 0.f ? m + log2f(l) : INFINITY;
+    }
+  }
+
+  // ---- resident indexer operands: qI^T B operand of z, qI tile for dkI
+  bf16x8 qib[2][4];   // heads 32hh + 16nt + c16, d = 32ks + 8g .. +7
+  float wv[2];
+  if (a.grads) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const uint16_t* src = a.qI + ((int64_t)t * kHI + 32 * hh + 16 * nt + c16) * kDI + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qib[nt][ks] = ld16(src + 32 * ks);
+      wv[nt] = a.w[(int64_t)t * kHI + 32 * hh + 16 * nt + c16];
+    }
+    // QIt[h][chunk ^ swz(h)] (16-byte chunks of 256-byte rows)
+    for (int e = tid; e < kHI * 16; e += 256) {
+      const int h = e >> 4, cc = e & 15;
+      *reinterpret_cast<uint4*>(&QIt[h][8 * (cc ^ swz(h))]) =
+          *reinterpret_cast<const uint4*>(a.qI + ((int64_t)t * kHI + h) * kDI + 8 * cc);
+    }
+  }
+
+  // key-row ids of a block: lane l <-> slot 64 b + l (global compressed row or -1)
+  const int nblk = (n_c + kNB - 1) / kNB;
+  auto row_of = [&](int b) {
+    const int j = b < nblk ? slot_local(kNB * b + lane) : -1;
+    return j >= 0 ? row0 + j : -1;
+  };
+  auto score_of = [&](int b) {
+    const int j = b < nblk ? slot_local(kNB * b + lane) : -1;
+    return j >= 0 ? srow[j] : 0.f;
+  };
+  // wave w gathers rows 16w .. 16w+15 (4 rows of 256 bytes per instruction, lane l fills
+  // physical chunk l % 16 of row 4i + l / 16); an absent slot's row is zero-filled
+  auto issue = [&](int rid, int buf) {
+    if (!a.grads) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * wave + 4 * i + (lane >> 4);
+      const int id = __shfl(rid, r, 64);
+      if (id >= 0)
+        dma_rows16(a.kI + (int64_t)id * kDI + 8 * ((lane & 15) ^ swz(r)),
+                   &KIt[buf][16 * wave + 4 * i][0]);
+      else
+        *reinterpret_cast<uint4*>(&KIt[buf][r][8 * (lane & 15)]) = make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  f32x4 dq[2][8];   // dqI partial over this wave's slots: heads 32hh + 16nt + 4g + i, d 16nd + c16
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int nd = 0; nd < 8; ++nd) dq[nt][nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dw_acc[2] = {0.f, 0.f};
+  float kl_acc = 0.f;
+
+  // per-lane LDS offsets (elements) of the swizzled 256-byte key rows
+  //  z^T A operand: row 32ch + 16mt + c16, logical chunk 4ks + g
+  int za[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) za[ks] = 8 * ((4 * ks + g) ^ swz(c16));
+  //  dqI B operand (transposed): rows 32ch + 4g + c16/4 (lo) and +16 (hi), logical chunk
+  //  2 nd + (c16 & 3) / 2, element 4 (c16 & 1) within it; row bits 0-3 = 4g + c16/4 (mod 16)
+  const int trr = 4 * g + (c16 >> 2);
+  const int tre = (c16 & 3) >> 1, troff = 4 * (c16 & 1);
+  //  dkI^T operands: qI^T A (rows = heads 32ks + 8g + c16/4 (+4), chunk 2 md + e),
+  //  E B (rows = heads, columns = slots 16 wave + 4 (c16 & 3))
+  const int rq_lo = 8 * g + (c16 >> 2);
+
+  int rid_cur = row_of(0), rid_nxt = row_of(1);
+  float sc_cur = score_of(0), sc_nxt = score_of(1);
+  issue(rid_cur, 0);
+  wait_vmem();
+  __syncthreads();
+
+  for (int b = 0; b < nblk; ++b) {
+    const int buf = b & 1;
+    const int rid_nn = row_of(b + 2);
+    const float sc_nn = score_of(b + 2);
+
+    // ---- teacher probabilities: thread = (heads 4 hq .. +3, slots 4 sq .. +3)
+    {
+      const int hq = tid >> 4, sq = tid & 15;
+      float pj[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int h = 4 * hq + k;
+        const float l2 = lse2_s[h];
+        const f32x4 v = *reinterpret_cast<const f32x4*>(tl_t + (int64_t)h * a.ld_t + kNB * b + 4 * sq);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pj[i] += __builtin_amdgcn_exp2f(v[i] * 1.44269504088896341f - l2);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pj[i] += __shfl_xor(pj[i], 16, 64);
+        pj[i] += __shfl_xor(pj[i], 32, 64);
+      }
+      if (g == 0) *reinterpret_cast<f32x4*>(&Pp[wave][4 * sq]) = f32x4{pj[0], pj[1], pj[2], pj[3]};
+    }
+    wait_vmem();        // key rows of this block (issued during the previous block)
+    __syncthreads();
+    // the other key buffer was last read before the previous block's second barrier
+    if (b + 1 < nblk) issue(rid_nxt, buf ^ 1);
+
+    // ---- per slot (lane l = slot 64 b + l): P, Q, KL and g; g w per wave in LDS
+    float gl;
+    {
+      const bool in = rid_cur >= 0;
+      const float P = ((Pp[0][lane] + Pp[1][lane]) + (Pp[2][lane] + Pp[3][lane])) * (1.f / kHT);
+      const float logQ = sc_cur - lseS;
+      const float Q = in ? expf(logQ) : 0.f;
+      if (in && P > 0.f && wave == 0) kl_acc += P * (logf(P) - logQ);
+      gl = in ? a.gs * (Q - P) : 0.f;
+      gw_s[wave][lane] = gl;
+    }
+    if (a.grads) {
+      // ---- z^T: slots 32ch + 16mt + 4g + i, indexer heads 32hh + 16nt + c16
+      f32x4 z[2][2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        z[mt][0] = z[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint16_t* rp = &KIt[buf][32 * ch + 16 * mt + c16][0];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 av = ld16(rp + za[ks]);
+          z[mt][0] = mfma16(av, qib[0][ks], z[mt][0]);
+          z[mt][1] = mfma16(av, qib[1][ks], z[mt][1]);
+        }
+      }
+      // ---- E = g w 1[z > 0]; dw += g relu(z); E (bf16) to LDS as [head][slot]
+      uint32_t ew[2][4];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          float e[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gv = gw_s[wave][32 * ch + 16 * mt + 4 * g + i];
+            const float zz = z[mt][nt][i];
+            dw_acc[nt] = fmaf(gv, fmaxf(zz, 0.f), dw_acc[nt]);
+            e[i] = zz > 0.f ? gv * wv[nt] : 0.f;
+          }
+          ew[nt][2 * mt] = pack_bf16x2(e[0], e[1]);
+          ew[nt][2 * mt + 1] = pack_bf16x2(e[2], e[3]);
+          *reinterpret_cast<uint2*>(&Es[32 * hh + 16 * nt + c16][32 * ch + 16 * mt + 4 * g]) =
+              make_uint2(ew[nt][2 * mt], ew[nt][2 * mt + 1]);
+        }
+      }
+      // ---- dqI[h][d] += sum_c E[h][c] kI[c][d]: k-slot order {4g..4g+3, 16+4g..16+4g+3}
+      {
+        const uint16_t* klo = &KIt[buf][32 * ch + trr][troff];
+        const uint16_t* khi = &KIt[buf][32 * ch + 16 + trr][troff];
+        const int s_lo = swz(trr), s_hi = swz(16 + trr);
+#pragma unroll
+        for (int nd = 0; nd < 8; ++nd) {
+          const int kq = 2 * nd + tre;
+          const bf16x8 kb = join8(ld_tr(klo + 8 * (kq ^ s_lo)), ld_tr(khi + 8 * (kq ^ s_hi)));
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            const bf16x8 ea = __builtin_bit_cast(bf16x8, make_uint4(ew[nt][0], ew[nt][1], ew[nt][2], ew[nt][3]));
+            dq[nt][nd] = mfma16(ea, kb, dq[nt][nd]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (a.grads) {
+      // ---- dkI^T[d][c] = sum_h qI[h][d] E[h][c]: wave w takes slots 16w .. 16w+15, all d
+      f32x4 dk[8];
+#pragma unroll
+      for (int md = 0; md < 8; ++md) dk[md] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int r_lo = 32 * ks + rq_lo, r_hi = r_lo + 4;
+        const bf16x8 eb = join8(ld_tr(&Es[r_lo][16 * wave + 4 * (c16 & 3)]),
+                                ld_tr(&Es[r_hi][16 * wave + 4 * (c16 & 3)]));
+#pragma unroll
+        for (int md = 0; md < 8; ++md) {
+          const int kq = 2 * md + tre;
+          const bf16x8 qa = join8(ld_tr(&QIt[r_lo][8 * (kq ^ swz(r_lo)) + troff]),
+                                  ld_tr(&QIt[r_hi][8 * (kq ^ swz(r_hi)) + troff]));
+          dk[md] = mfma16(qa, eb, dk[md]);
+        }
+      }
+      // lane: slot 16 wave + c16, d = 16 md + 4g .. +3 -> bf16 staging row of (t, slot)
+      const int slot = kNB * b + 16 * wave + c16;
+      if (slot < n_c) {
+        uint16_t* dst = a.stage + ((int64_t)tl * a.k_slots + slot) * kDI + 4 * g;
+#pragma unroll
+        for (int md = 0; md < 8; ++md)
+          *reinterpret_cast<uint2*>(dst + 16 * md) =
+              make_uint2(pack_bf16x2(dk[md][0], dk[md][1]), pack_bf16x2(dk[md][2], dk[md][3]));
+      }
+    }
+    rid_cur = rid_nxt;
+    rid_nxt = rid_nn;
+    sc_cur = sc_nxt;
+    sc_nxt = sc_nn;
+  }
+
+  // ---- outputs: kl, dw, dqI (the two slot halves ch = 0, 1 summed through LDS)
+  if (wave == 0) {
+    float v = kl_acc;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) a.kl[t] = v;
+  }
+  if (!a.grads) return;
+  __syncthreads();
+  float* dqs = reinterpret_cast<float*>(&KIt[0][0][0]);   // [64][128] fp32 = 32 KiB
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    float d2 = dw_acc[nt];
+    d2 += __shfl_xor(d2, 16, 64);
+    d2 += __shfl_xor(d2, 32, 64);
+    if (g == 0) Pp[ch][32 * hh + 16 * nt + c16] = d2;
+  }
+  if (ch == 0) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int nd = 0; nd < 8; ++nd)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dqs[(32 * hh + 16 * nt + 4 * g + i) * kDI + 16 * nd + c16] = dq[nt][nd][i];
+  }
+  __syncthreads();
+  if (ch == 1) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int nd = 0; nd < 8; ++nd)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dqs[(32 * hh + 16 * nt + 4 * g + i) * kDI + 16 * nd + c16] += dq[nt][nd][i];
+  }
+  __syncthreads();
+  if (tid < kHI) a.dw[(int64_t)t * kHI + tid] = Pp[0][tid] + Pp[1][tid];
+  float4* dst = reinterpret_cast<float4*>(a.dqI + (int64_t)t * kHI * kDI);
+  const float4* src = reinterpret_cast<const float4*>(dqs);
+  for (int e = tid; e < kHI * kDI / 4; e += 256) dst[e] = src[e];
+}
+
+// ---- CSR of the compressed rows over a chunk's (query, slot) pairs, and the owner sums
+namespace {
+
+struct CsrArgs {
+  const int32_t* idx;
+  const int32_t* cu;
+  const int32_t* cu_cmp;
+  const int32_t* nc;
+  int32_t* cnt;
+  int32_t* off;
+  int32_t* cur;
+  int32_t* list;
+  const uint16_t* stage;
+  float* dst;
+  int64_t k_slots;
+  int t0, nT, B, r, n_cap, k_cap, n_rows;
+};
+
+template <bool FILL>
+__global__ __launch_bounds__(256) void k_csr_pairs(CsrArgs c) {
+  const int tl = blockIdx.x;
+  const int t = c.t0 + tl;
+  const int n = c.nc[t];
+  if (n == 0) return;
+  TokenInfo ti;
+  if (!token_info_wave(c.cu, c.B, t, ti)) return;
+  const int row0 = c.cu_cmp[ti.b];
+  const int nv = min((ti.p + 1) / c.r, c.n_cap);
+  for (int s = threadIdx.x; s < n; s += 256) {
+    int gr = c.idx ? c.idx[(int64_t)t * c.k_cap + s] : row0 + s;
+    if (gr < row0 || gr >= row0 + nv) continue;
+    if (!FILL) {
+      atomicAdd(&c.cnt[gr], 1);
+    } else {
+      const int pos = atomicAdd(&c.cur[gr], 1);
+      c.list[pos] = tl * (int32_t)c.k_slots + s;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fill_zero_i32(int32_t* __restrict__ p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
+// exclusive scan of cnt into off and cur (one workgroup of 1024 lanes)
+__global__ __launch_bounds__(1024) void k_csr_scan(CsrArgs c) {
+  __shared__ int part[1024];
+  const int n = c.n_rows;
+  const int per = (n + 1023) / 1024;
+  const int lo = threadIdx.x * per, hi = min(n, lo + per);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += c.cnt[i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int run = part[threadIdx.x] - s;
+  for (int i = lo; i < hi; ++i) {
+    c.off[i] = run;
+    c.cur[i] = run;
+    run += c.cnt[i];
+  }
+}
+
+// dst[j, :] += sum of the staged bf16 rows listed for j; one wave per row, 2 floats per lane,
+// four waves per workgroup
+__global__ __launch_bounds__(256) void k_csr_reduce(CsrArgs c) {
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (j >= c.n_rows) return;
+  const int n = c.cnt[j];
+  if (n == 0) return;
+  const int32_t* lst = c.list + c.off[j];
+  float s0 = 0.f, s1 = 0.f, u0 = 0.f, u1 = 0.f;
+  int e = 0;
+  for (; e + 1 < n; e += 2) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(c.stage + (int64_t)lst[e] * kDI + 2 * lane);
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(c.stage + (int64_t)lst[e + 1] * kDI + 2 * lane);
+    s0 += __uint_as_float(v << 16);
+    s1 += __uint_as_float(v & 0xffff0000u);
+    u0 += __uint_as_float(w << 16);
+    u1 += __uint_as_float(w & 0xffff0000u);
+  }
+  if (e < n) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(c.stage + (int64_t)lst[e] * kDI + 2 * lane);
+    s0 += __uint_as_float(v << 16);
+    s1 += __uint_as_float(v & 0xffff0000u);
+  }
+  float2* d = reinterpret_cast<float2*>(c.dst + (int64_t)j * kDI + 2 * lane);
+  const float2 o = *d;
+  *d = make_float2(o.x + (s0 + u0), o.y + (s1 + u1));
+}
+
+struct KlcPlan {
+  int64_t k_slots, chunk, rows_cap;
+  size_t off_stage, off_nc, off_cnt, off_off, off_cur, off_list, total;
+};
+
+bool klc_handles(const Shape& sh) {
+  return sh.H == kHT && sh.HI == kHI && sh.dI == kDI && sh.idx_dtype == 1 && sh.r > 0 &&
+         ((sh.teacher == 1 && sh.mode == 0) || (sh.teacher == 2 && sh.mode == 1));
+}
+
+KlcPlan klc_plan(const Shape& sh) {
+  KlcPlan p;
+  p.k_slots = sh.mode == 0 ? sh.k_cap : sh.max_seqlen / sh.r;
+  if (p.k_slots < 1) p.k_slots = 1;
+  const int64_t per_tok = p.k_slots * kDI * 2;
+  int64_t ch = kStageBudget / per_tok;
+  ch = (ch / (8 * kChunk)) * (8 * kChunk);
+  if (ch < 8 * kChunk) ch = 8 * kChunk;
+  p.chunk = ch < sh.T ? ch : sh.T;
+  p.rows_cap = sh.T / sh.r + 1;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t o = 0;
+  p.off_stage = o; o = al(o + (size_t)p.chunk * p.k_slots * kDI * 2);
+  p.off_nc = o;    o = al(o + (size_t)sh.T * 4);
+  p.off_cnt = o;   o = al(o + (size_t)p.rows_cap * 4);
+  p.off_off = o;   o = al(o + (size_t)p.rows_cap * 4);
+  p.off_cur = o;   o = al(o + (size_t)p.rows_cap * 4);
+  p.off_list = o;  o = al(o + (size_t)p.chunk * p.k_slots * 4);
+  p.total = o;
+  return p;
+}
+
+}  // namespace
+
+size_t indexer_kl_cached_workspace(const Shape& sh) {
+  return klc_handles(sh) ? klc_plan(sh).total : 0;
+}
+
+hipError_t launch_indexer_kl_cached(const Shape& sh, const KlIO& io, hipStream_t s, bool* handled) {
+  *handled = false;
+  if (!io.t_logits || !klc_handles(sh)) return hipSuccess;
+  *handled = true;
+  const KlcPlan pl = klc_plan(sh);
+  char* ws = (char*)io.ws;
+  KlcArgs a;
+  a.tl = io.t_logits;
+  a.ld_t = teacher_logits_ld(sh);
+  a.tlse = io.teacher_lse;
+  a.scores = io.scores;
+  a.ld = io.ld;
+  a.idx = sh.teacher == 1 ? io.idx : nullptr;
+  a.qI = (const uint16_t*)io.qI;
+  a.w = io.w;
+  a.kI = (const uint16_t*)io.kI;
+  a.cu = sh.cu;
+  a.cu_cmp = sh.cu_cmp;
+  a.gs = io.grad_scale;
+  a.kl = io.kl;
+  a.dqI = io.dqI;
+  a.dw = io.dw;
+  a.stage = (uint16_t*)(ws + pl.off_stage);
+  a.nc = (int32_t*)(ws + pl.off_nc);
+  a.k_slots = pl.k_slots;
+  a.B = sh.B;
+  a.T = sh.T;
+  a.r = sh.r;
+  a.n_cap = sh.max_seqlen / sh.r;
+  a.k_cap = sh.k_cap;
+  a.grads = io.dqI != nullptr;
+  CsrArgs c;
+  c.idx = a.idx;
+  c.cu = sh.cu;
+  c.cu_cmp = sh.cu_cmp;
+  c.nc = a.nc;
+  c.cnt = (int32_t*)(ws + pl.off_cnt);
+  c.off = (int32_t*)(ws + pl.off_off);
+  c.cur = (int32_t*)(ws + pl.off_cur);
+  c.list = (int32_t*)(ws + pl.off_list);
+  c.stage = a.stage;
+  c.dst = io.dkI;
+  c.k_slots = pl.k_slots;
+  c.B = sh.B;
+  c.r = sh.r;
+  c.n_cap = a.n_cap;
+  c.k_cap = sh.k_cap;
+  c.n_rows = (int)pl.rows_cap;
+  for (int64_t t0 = 0; t0 < sh.T; t0 += pl.chunk) {
+    a.t0 = c.t0 = (int)t0;
+    a.nT = c.nT = (int)(sh.T - t0 < pl.chunk ? sh.T - t0 : pl.chunk);
+    hipLaunchKernelGGL(k_kl_cached, dim3((unsigned)token_grid(a.nT)), dim3(256), 0, s, a);
+    if (a.grads) {
+      hipLaunchKernelGGL(k_fill_zero_i32, dim3(64), dim3(256), 0, s, c.cnt, c.n_rows);
+      hipLaunchKernelGGL(k_csr_pairs<false>, dim3(c.nT), dim3(256), 0, s, c);
+      hipLaunchKernelGGL(k_csr_scan, dim3(1), dim3(1024), 0, s, c);
+      hipLaunchKernelGGL(k_csr_pairs<true>, dim3(c.nT), dim3(256), 0, s, c);
+      hipLaunchKernelGGL(k_csr_reduce, dim3((c.n_rows + 3) / 4), dim3(256), 0, s, c);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace csa

@@ -76,6 +76,7 @@ class CsaLayer:
         # selected-set teacher: the forward also returns the compressed-only normalizer
         self.lse_cmp = z(T, H) if (cfg.has_indexer and cfg.teacher == "selected") else None
         self.ws_fwd = self._ws(B.CSA_OP_ATTN_FWD, device)
+        self.t_logits = None
         if cfg.has_indexer:
             HI, dI = cfg.idx_heads, cfg.idx_dim
             idt = torch.float32 if cfg.idx_dtype == "f32" else torch.bfloat16
@@ -90,7 +91,16 @@ class CsaLayer:
             if cfg.teacher != "none":
                 self.kl = z(T)
                 self.loss = z(1)
-                self.ws_kl = self._ws(B.CSA_OP_INDEXER_KL, device)
+                # teacher-logit cache: the forward keeps the compressed-candidate logits it
+                # forms anyway and the loss reads them instead of gathering the rows again;
+                # used where the library has a kernel for it (nonzero cached workspace)
+                n_cached = B.csa_workspace_size(self.p, B.CSA_OP_INDEXER_KL_CACHED)
+                if n_cached > 0 and backward:
+                    ld_t = B.csa_teacher_logits_stride(self.p)
+                    self.t_logits = z(T, H, ld_t)
+                    self.ws_kl = self._ws(B.CSA_OP_INDEXER_KL_CACHED, device)
+                else:
+                    self.ws_kl = self._ws(B.CSA_OP_INDEXER_KL, device)
                 if backward:
                     self.dqI = z(T, HI, dI)
                     self.dw = z(T, HI)
@@ -141,7 +151,7 @@ class CsaLayer:
             idx = self.idx
         self._call("attn_fwd", B.csa_sparse_attn_fwd, p, inp["q"], self.kv_cmp, inp["kv"], idx,
                    inp.get("sink"), cu_seqlens, self.cu_cmp, self.out, self.lse, self.lse_cmp,
-                   self.ws_fwd)
+                   self.ws_fwd, None, self.t_logits)
         if cfg.has_indexer and cfg.teacher != "none":
             grads = self.backward
             if grads:
@@ -150,7 +160,7 @@ class CsaLayer:
                        self.idx, qI, qs, inp["w"], kI, ks, cu_seqlens, self.cu_cmp,
                        self.grad_scale, self.kl, self.loss, self.dqI if grads else None,
                        self.dw if grads else None, self.dkI_cmp if grads else None, self.ws_kl,
-                       self.lse_cmp)
+                       self.lse_cmp, None, self.t_logits)
 
     def backward_step(self, inp, cu_seqlens):
         cfg, p = self.cfg, self.p

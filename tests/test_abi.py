@@ -23,14 +23,14 @@ def _params(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = B.header_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B._SIGS)
 
 
 def test_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 2
+    assert lib.csa_abi_version() == 3
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.csa_status_string(st)
     assert lib.csa_status_string(7) == b"unknown status"
@@ -110,16 +110,16 @@ def test_scores_and_topk_validation(lib):
 def test_attention_validation(lib):
     p = _params()
     f = lib.csa_sparse_attn_fwd
-    a = [FAKE] * 10
-    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, None, None, 0,
-             None) == B.CSA_ERR_NULL                                          # idx for sparse
+    a = [FAKE] * 10 + [None]
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, None, None,
+             None, 0, None) == B.CSA_ERR_NULL                                 # idx for sparse
     assert f(ctypes.byref(_params(window=0)), *a, None, 0, None) == B.CSA_ERR_ARG
     assert f(ctypes.byref(_params(scale=0.0)), *a, None, 0, None) == B.CSA_ERR_ARG
     assert f(ctypes.byref(_params(mode=3)), *a, None, 0, None) == B.CSA_ERR_ARG
     assert f(ctypes.byref(_params(head_dim=1024)), *a, None, 0, None) == B.CSA_ERR_UNSUPPORTED
     assert f(ctypes.byref(_params(dtype=B.CSA_FP8_E4M3)), *a, None, 0, None) == B.CSA_ERR_UNSUPPORTED
     assert f(ctypes.byref(_params(mode=B.CSA_DENSE)), FAKE, None, FAKE, None, None, FAKE, FAKE,
-             FAKE, FAKE, None, None, 0, None) == B.CSA_ERR_NULL              # kv_cmp for dense
+             FAKE, FAKE, None, None, None, 0, None) == B.CSA_ERR_NULL        # kv_cmp for dense
     b = lib.csa_sparse_attn_bwd
     args = [FAKE] * 14
     bf = _params(heads=64, head_dim=512, dtype=B.CSA_BF16)
@@ -133,9 +133,9 @@ def test_indexer_kl_validation(lib):
     p = _params()
     f = lib.csa_indexer_kl
 
-    def call(pp, idx=FAKE, grads=(FAKE, FAKE, FAKE), ld=64, gs=1.0):
-        return f(ctypes.byref(pp), FAKE, FAKE, FAKE, ld, idx, None, FAKE, None, FAKE, FAKE, None,
-                 FAKE, FAKE, gs, FAKE, FAKE, *grads, None, 0, None)
+    def call(pp, idx=FAKE, grads=(FAKE, FAKE, FAKE), ld=64, gs=1.0, cache=None):
+        return f(ctypes.byref(pp), FAKE, FAKE, FAKE, ld, idx, None, cache, FAKE, None, FAKE, FAKE,
+                 None, FAKE, FAKE, gs, FAKE, FAKE, *grads, None, 0, None)
 
     assert call(_params(teacher=B.CSA_TEACHER_NONE)) == B.CSA_ERR_ARG
     assert call(_params(teacher=B.CSA_TEACHER_SELECTED), idx=None) == B.CSA_ERR_NULL
@@ -144,3 +144,26 @@ def test_indexer_kl_validation(lib):
     assert call(p, gs=float("nan")) == B.CSA_ERR_ARG
     assert call(_params(heads=128)) == B.CSA_ERR_UNSUPPORTED
     assert call(_params(idx_dtype=B.CSA_FP8_E4M3)) == B.CSA_ERR_NULL
+
+
+def test_teacher_logits_cache_contract(lib):
+    stride = lib.csa_teacher_logits_stride
+    stride.argtypes = [ctypes.POINTER(B.CsaParams)]
+    stride.restype = ctypes.c_int64
+    assert stride(ctypes.byref(_params(topk_cap=128))) == 128                 # sparse: topk_cap
+    assert stride(ctypes.byref(_params(mode=B.CSA_DENSE, max_seqlen=260, ratio=4))) == 128
+    assert stride(ctypes.byref(_params(mode=B.CSA_WINDOW))) == 0
+    assert stride(ctypes.byref(_params(window=0))) == 0                      # invalid params
+    f = lib.csa_indexer_kl
+
+    def call(pp, cache):
+        return f(ctypes.byref(pp), FAKE, FAKE, FAKE, 1 << 16, FAKE, None, cache, FAKE, None, FAKE,
+                 FAKE, None, FAKE, FAKE, 1.0, FAKE, FAKE, None, None, None, None, 0, None)
+    # the cache only stands in for the teacher when the candidate sets agree
+    assert call(_params(teacher=B.CSA_TEACHER_SELECTED, mode=B.CSA_DENSE), FAKE) == B.CSA_ERR_ARG
+    assert call(_params(teacher=B.CSA_TEACHER_DENSE, mode=B.CSA_SPARSE), FAKE) == B.CSA_ERR_ARG
+    big = dict(heads=64, head_dim=512, idx_heads=64, idx_dim=128, dtype=B.CSA_BF16,
+               idx_dtype=B.CSA_BF16, teacher=B.CSA_TEACHER_SELECTED, topk_cap=1024, topk=1024,
+               total_tokens=65536, max_seqlen=16384)
+    n = B.csa_workspace_size(_params(**big), B.CSA_OP_INDEXER_KL_CACHED)
+    assert n >= 16384 * 1024 * 128 * 2                                       # bf16 staging

@@ -276,9 +276,12 @@ def test_attn_fwd(name):
     idx_d = torch.from_numpy(idx.astype(np.int32)).cuda() if w.mode == "sparse" else None
     sink = host.get("sink")
     lse_cmp = torch.empty_like(L.lse)
+    ld_t = B.csa_teacher_logits_stride(L.p)
+    t_logits = (torch.full((w.total_tokens, w.heads, ld_t), float("nan"), device="cuda")
+                if ld_t else None)
     B.csa_sparse_attn_fwd(L.p, host["q"].cuda(), kvc, host["kv"].cuda(), idx_d,
                           None if sink is None else sink.cuda(), cu, L.cu_cmp, L.out, L.lse,
-                          lse_cmp, ws=L.ws_fwd)
+                          lse_cmp, ws=L.ws_fwd, t_logits=t_logits)
     n = int(host["cu_seqlens"][-1])
     rows = np.arange(n)
     Oref, Lref = O.sparse_attn_fwd(h64["q"], kv_cmp_r, h64["kv"], _mode_idx(w, idx),
@@ -303,6 +306,16 @@ def test_attn_fwd(name):
         _, Lc = O.sparse_attn_fwd(h64["q"], kv_cmp_r, h64["kv"], mi, None, host["cu_seqlens"],
                                   w.ratio, 0, w.scale, rows=rc)
         G.check("LSE(compressed only)", got_c[has_c], Lc, w.dtype)
+    if t_logits is not None:
+        # cached compressed-candidate logits, slot order of the attention call
+        ref_l = O.compressed_logits(h64["q"], kv_cmp_r, None if _mode_idx(w, idx) is None
+                                    else idx[rows], host["cu_seqlens"], w.ratio, w.scale,
+                                    rows=rows)
+        tl = G.back(t_logits)
+        got_f = np.concatenate([tl[t, :, :r.shape[1]].ravel() for t, r in zip(rows, ref_l)])
+        ref_f = np.concatenate([r.ravel() for r in ref_l])
+        assert got_f.size > 0
+        G.check("teacher logits cache", got_f, ref_f, w.dtype)
     if n < w.total_tokens:
         assert torch.all(L.out[n:] == 0) and torch.all(L.lse[n:] == 0)
 
@@ -360,17 +373,20 @@ def _kl_variants():
     out = []
     for n in _kl_cases():
         w = configs.workload(CASES[n][0], **CASES[n][1])
-        out += [(n, True, False), (n, False, False)]
+        out += [(n, True, "none"), (n, False, "none")]
         if w.teacher == "selected":
-            out.append((n, True, True))
+            out += [(n, True, "lse"), (n, True, "cache"), (n, False, "cache")]
     return out
 
 
-@pytest.mark.parametrize("name,grads,fwd_lse", _kl_variants())
-def test_indexer_kl(name, grads, fwd_lse):
+@pytest.mark.parametrize("name,grads,from_fwd", _kl_variants())
+def test_indexer_kl(name, grads, from_fwd):
+    """from_fwd: "none" (teacher recomputed), "lse" (teacher normalizer from the GPU
+    forward), "cache" (normalizer and teacher logits from the GPU forward)."""
     from long_context_compressed_amd import binding as B
     w, host, h64 = _case(name)
-    _announce(name, f"indexer_kl grads={grads} fwd_lse={fwd_lse}")
+    _announce(name, f"indexer_kl grads={grads} from_fwd={from_fwd}")
+    fwd_lse = from_fwd != "none"
     L = _layer(w, host, backward=True)
     cu = _cu(host)
     L.metadata(cu)
@@ -380,19 +396,25 @@ def test_indexer_kl(name, grads, fwd_lse):
     sc = O.index_scores(qI64, h64["w"], kI64, host["cu_seqlens"], w.ratio, L.n_cap)
     s32 = np.where(np.isfinite(sc), sc, 0.0).astype(np.float32)
     gs = 0.5
-    teacher_lse = None
+    teacher_lse = t_logits = None
+    ws = L.ws_kl
     if fwd_lse:
-        # the selected-set teacher normalizer taken from the GPU forward on the same inputs
+        # the selected-set teacher normalizer (and logits) from the GPU forward on the same inputs
         teacher_lse = torch.empty_like(L.lse)
+        if from_fwd == "cache":
+            ld_t = B.csa_teacher_logits_stride(L.p)
+            t_logits = torch.full((w.total_tokens, w.heads, ld_t), float("nan"), device="cuda")
+            n_ws = B.csa_workspace_size(L.p, B.CSA_OP_INDEXER_KL_CACHED)
+            ws = torch.empty(n_ws, dtype=torch.uint8, device="cuda") if n_ws else None
         B.csa_sparse_attn_fwd(L.p, host["q"].cuda(), G.dev(kv_cmp_r, dt), host["kv"].cuda(),
                               torch.from_numpy(idx.astype(np.int32)).cuda(), None, cu, L.cu_cmp,
-                              L.out, L.lse, teacher_lse, ws=L.ws_fwd)
+                              L.out, L.lse, teacher_lse, ws=L.ws_fwd, t_logits=t_logits)
     L.dkI_cmp.zero_()
     B.csa_indexer_kl(L.p, host["q"].cuda(), G.dev(kv_cmp_r, dt), torch.from_numpy(s32).cuda(),
                      torch.from_numpy(idx.astype(np.int32)).cuda(), d["qI"], d["qI_scale"],
                      host["w"].cuda(), d["kI"], d["kI_scale"], cu, L.cu_cmp, gs, L.kl, L.loss,
                      L.dqI if grads else None, L.dw if grads else None,
-                     L.dkI_cmp if grads else None, L.ws_kl, teacher_lse)
+                     L.dkI_cmp if grads else None, ws, teacher_lse, teacher_logits=t_logits)
     n = int(host["cu_seqlens"][-1])
     rows = np.arange(n)
     kl, loss, dqI, dw, dkI = O.indexer_kl(h64["q"], kv_cmp_r, s32[:n], idx[:n], qI64, h64["w"],
