@@ -10,6 +10,9 @@
 #include "attn_common.h"
 #include "csa_launch.h"
 
+// M0 is named as clobbered by the LDS-DMA asm below; the compiler keeps no value in it here.
+#pragma clang diagnostic ignored "-Winline-asm"
+
 namespace csa {
 
 using namespace attn;
@@ -44,6 +47,18 @@ constexpr int kDW = 128;          // d per wave, kernel 2
 constexpr int kNB1 = 32;          // candidates per block, kernel 1
 constexpr int kKS = kD + 16;      // row stride (bf16) of LDS row tiles
 constexpr int kNB2 = 64;          // candidates per block, kernel 2
+constexpr int kPTS = 136;         // row stride (bf16) of the dS | P transpose tile
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// One 16-byte-per-lane global -> LDS load (global_load_lds_dwordx4): lane l's 16 bytes land
+// at LDS byte offset lds_row + 16 l.  Issued through asm so that the compiler does not order
+// LDS reads of the other tile buffer behind it; completion is awaited with wait_vmem().
+__device__ __forceinline__ void dma_row16(const void* src, const void* lds_row) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_row);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(src) : "memory", "m0");
+}
 constexpr int64_t kStageBudget = 24ll << 30;   // bytes of pds + staging per chunk
 
 struct BwdArgs {
@@ -106,8 +121,8 @@ __device__ __forceinline__ int cmp_row(const BwdArgs& b, int t, int row0, int nv
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_attn_bwd_dq_mfma(BwdArgs b) {
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][kNB1][kKS];
-  __shared__ int valid_s[2][kNB1];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][kNB1][kD];       // swizzled 1 KiB rows
+  __shared__ __attribute__((aligned(16))) uint16_t PT[2][kNB1][kPTS];     // [slot][dS | P]
   __shared__ int s_tmp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -115,18 +130,16 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
   if (tl >= b.nT) return;
   const int t = b.t0 + tl;
   TokenInfo ti;
-  if (!token_info(b.cu, b.B, t, ti)) {
+  if (!token_info_wave(b.cu, b.B, t, ti)) {
     uint4* o = reinterpret_cast<uint4*>(b.dq + (int64_t)t * kH * kD);
     for (int e = tid; e < kH * kD / 8; e += 256) o[e] = make_uint4(0, 0, 0, 0);
     if (tid == 0) b.nc[t] = 0;
     return;
   }
-  const CandSet cs = make_cands(b, t, ti, &s_tmp);
-  if (tid == 0) b.nc[t] = cs.n_c;
-  const int n_tot = cs.n_c + cs.n_w;
   const int h = 16 * wave + c16;  // this lane's head for S^T / dP^T (n index)
 
-  // B operands: Q[h][32ks + 8g ..] and dO[h][...]; Dt = dO . O for head h
+  // B operands: Q[h][32ks + 8g ..] and dO[h][...]; Dt = dO . O for head h (loads first, so
+  // they overlap the metadata loads)
   bf16x8 qb[16], gb[16];
   const int64_t rowq = ((int64_t)t * kH + h) * kD;
   float dt = 0.f;
@@ -140,6 +153,17 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) dt = fmaf(ov[i], gv[i], dt);
   }
+  const int32_t* idx_t = b.mode == 0 ? b.idx + (int64_t)t * b.k_cap : nullptr;
+  // raw idx entry of slot 32 blk + (lane & 31)
+  auto raw_of = [&](int blk) {
+    const int c = kNB1 * blk + (lane & 31);
+    return (b.mode == 0 && c < b.k_cap) ? idx_t[c] : 0;
+  };
+  int raw_cur = raw_of(0), raw_nxt = raw_of(1);
+  const CandSet cs = make_cands(b, t, ti, &s_tmp);
+  if (tid == 0) b.nc[t] = cs.n_c;
+  const int n_tot = cs.n_c + cs.n_w;
+  const int nblk = (n_tot + kNB1 - 1) / kNB1;
   dt += __shfl_xor(dt, 16, 64);
   dt += __shfl_xor(dt, 32, 64);
   const float lse_t = b.lse[(int64_t)t * kH + h];
@@ -149,88 +173,155 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
 #pragma unroll
   for (int nt = 0; nt < 32; ++nt) dq[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // row fetch split in two halves: issue (global -> registers) early, commit (-> LDS) late,
-  // so the loads of block c+1 are in flight while block c computes
-  uint4 pre[8];
-  int pre_ok = 0;
-  auto issue = [&](int c0) {
-    pre_ok = 0;
+  // row id of slot 32 blk + (lane & 31): >= 0 compressed row, <= -2 raw row -2 - id, -1 none
+  auto rid_of = [&](int blk, int raw) {
+    const int c = kNB1 * blk + (lane & 31);
+    if (blk >= nblk) return -1;
+    if (c < cs.n_c) {
+      const int gr = b.mode == 1 ? cs.row0 + c : raw;
+      return (gr >= cs.row0 && gr < cs.row0 + cs.nv) ? gr : -1;
+    }
+    if (c < n_tot) return -2 - (cs.win0 + (c - cs.n_c));
+    return -1;
+  };
+  // wave w gathers rows 8w .. 8w+7 of a block (one 1 KiB row per instruction, lane l fills
+  // physical chunk l); an absent slot loads the query's own raw row (finite, masked)
+  auto issue = [&](int rid, int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint16_t* src = cand_ptr(b, t, cs, c0 + 4 * i + wave);
-      pre[i] = src ? *reinterpret_cast<const uint4*>(src + 8 * lane) : make_uint4(0, 0, 0, 0);
-      pre_ok |= (src != nullptr) << i;
+    for (int j = 0; j < 8; ++j) {
+      const int r = 8 * wave + j;
+      const int id = __builtin_amdgcn_readlane(rid, r);
+      const uint16_t* src = id >= 0 ? b.kv_cmp + (int64_t)id * kD
+                                    : b.kv + (int64_t)(id == -1 ? t : -2 - id) * kD;
+      dma_row16(src + 8 * (lane ^ swz(r)), &Kt[buf][r][0]);
     }
   };
-  auto commit = [&](int buf) {
+  // per-lane LDS offsets (elements): S^T A operand rows 16mt + c16, logical chunk 4ks + g
+  int eq[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<uint4*>(&Kt[buf][4 * i + wave][8 * lane]) = pre[i];
-      if (lane == 0) valid_s[buf][4 * i + wave] = (pre_ok >> i) & 1;
+  for (int q = 0; q < 4; ++q) eq[q] = 8 * ((4 * q + g) ^ swz(c16));
+  // dq B operand (transposed): rows 4g + c16/4 (lo) and 16 + 4g + c16/4 (hi), both with
+  // swizzle s = swz(4g + c16/4); column 16nt + 4(c16 & 3) at 16nt ^ 8((c16 & 3)/2 ^ s) + 4(c16 & 1)
+  const int trr = 4 * g + (c16 >> 2);
+  const int trk = 8 * (((c16 & 3) >> 1) ^ swz(trr)), troff = 4 * (c16 & 1);
+
+  uint16_t* pds_t = b.pds + (int64_t)tl * b.n_slots * 128;
+  auto store_pds = [&](int blk) {   // slots of block blk from PT[blk & 1], 16-byte stores
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = tid + 256 * k, s = e >> 4, cc = e & 15;
+      *reinterpret_cast<uint4*>(pds_t + (int64_t)(kNB1 * blk + s) * 128 + 8 * cc) =
+          *reinterpret_cast<const uint4*>(&PT[blk & 1][s][8 * cc]);
     }
   };
 
-  uint16_t* pds_t = b.pds + (int64_t)tl * b.n_slots * 128;
-  const int jr = c16 >> 2, jc = 4 * (c16 & 3);
-  int buf = 0;
-  if (n_tot > 0) {
-    issue(0);
-    commit(0);
-  }
-  for (int c0 = 0; c0 < n_tot; c0 += kNB1, buf ^= 1) {
-    __syncthreads();
-    const bool more = c0 + kNB1 < n_tot;
-    if (more) issue(c0 + kNB1);
-    // S^T, dP^T for 32 candidates x this wave's 16 heads
+  int rid_cur = rid_of(0, raw_cur), rid_nxt = rid_of(1, raw_nxt);
+  if (nblk > 0) issue(rid_cur, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int buf = blk & 1;
+    const uint32_t valid = (uint32_t)__ballot(rid_cur != -1);
+    if (blk + 1 < nblk) issue(rid_nxt, buf ^ 1);
+    const int raw_nn = raw_of(blk + 2);
+    if (blk > 0) store_pds(blk - 1);
+    // ---- S^T, dP^T for 32 candidates x this wave's 16 heads (operands read 3 steps ahead)
     f32x4 st[2], gt[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      gt[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < 2; ++mt) st[mt] = gt[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      const uint16_t* rb = &Kt[buf][c16][0];
+      auto seg = [&](int ks, int mt) { return ld16(rb + 16 * mt * kD + 128 * (ks >> 2) + eq[ks & 3]); };
+      constexpr int kPre = 3;
+      bf16x8 av[kPre][2];
+#pragma unroll
+      for (int j = 0; j < kPre; ++j)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) av[j][mt] = seg(j, mt);
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) {
-        const bf16x8 av = ld16(&Kt[buf][16 * mt + c16][32 * ks + 8 * g]);
-        st[mt] = mfma16(av, qb[ks], st[mt]);
-        gt[mt] = mfma16(av, gb[ks], gt[mt]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          st[mt] = mfma16(av[ks % kPre][mt], qb[ks], st[mt]);
+          gt[mt] = mfma16(av[ks % kPre][mt], gb[ks], gt[mt]);
+        }
+        if (ks + kPre < 16) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) av[ks % kPre][mt] = seg(ks + kPre, mt);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // P, scale*dS for candidates c = c0 + 16mt + 4g + i, head h
+    // ---- P, scale*dS for slots 16mt + 4g + i, head h -> PT (bf16) and the dq A operand
     uint32_t dsw[4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) {
+      float pv[4], dv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int cl = 16 * mt + 4 * g + i;
-        float p = 0.f, ds = 0.f;
-        if (valid_s[buf][cl]) {
-          p = exp2f(st[mt][i] * b.scale_log2 - lse2);
-          ds = b.scale * p * (gt[mt][i] - dt);
-        }
-        const uint16_t pb = f32_to_bf16_bits(p), db = f32_to_bf16_bits(ds);
-        uint16_t* dst = pds_t + (int64_t)(c0 + cl) * 128;
-        dst[h] = db;
-        dst[64 + h] = pb;
-        const int k = 4 * mt + i;   // k-slot of the dq product
-        if (k & 1) dsw[k >> 1] |= (uint32_t)db << 16;
-        else dsw[k >> 1] = db;
+        const bool ok = (valid >> cl) & 1;
+        pv[i] = ok ? __builtin_amdgcn_exp2f(st[mt][i] * b.scale_log2 - lse2) : 0.f;
+        dv[i] = ok ? b.scale * pv[i] * (gt[mt][i] - dt) : 0.f;
       }
-    const bf16x8 dsa = __builtin_bit_cast(bf16x8, make_uint4(dsw[0], dsw[1], dsw[2], dsw[3]));
-    // dq[h'][d] += sum_c dS[h'][c] K[c][d]; B = rows {4g..4g+3, 16+4g..16+4g+3} of the tile
+      dsw[2 * mt] = pack_bf16x2(dv[0], dv[1]);
+      dsw[2 * mt + 1] = pack_bf16x2(dv[2], dv[3]);
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt) {
-      const v4i16 lo = ld_tr(&Kt[buf][4 * g + jr][16 * nt + jc]);
-      const v4i16 hi = ld_tr(&Kt[buf][16 + 4 * g + jr][16 * nt + jc]);
-      dq[nt] = mfma16(dsa, join8(lo, hi), dq[nt]);
+      for (int i = 0; i < 4; ++i) {
+        const int cl = 16 * mt + 4 * g + i;
+        const uint32_t wd = dsw[2 * mt + (i >> 1)], wp = pack_bf16x2(pv[i], 0.f);
+        PT[buf][cl][h] = (uint16_t)((i & 1) ? (wd >> 16) : (wd & 0xffffu));
+        PT[buf][cl][64 + h] = (uint16_t)(wp & 0xffffu);
+      }
     }
-    if (more) commit(buf ^ 1);
+    const bf16x8 dsa = __builtin_bit_cast(bf16x8, make_uint4(dsw[0], dsw[1], dsw[2], dsw[3]));
+    // ---- dq[h'][d] += sum_c dS[h'][c] K[c][d]; B = rows {4g..4g+3, 16+4g..16+4g+3}
+    {
+      const uint16_t* klo = &Kt[buf][trr][troff];
+      const uint16_t* khi = &Kt[buf][16 + trr][troff];
+      constexpr int kPre = 4;
+      v4i16 lo[kPre], hi[kPre];
+#pragma unroll
+      for (int j = 0; j < kPre; ++j) {
+        lo[j] = ld_tr(klo + ((16 * j) ^ trk));
+        hi[j] = ld_tr(khi + ((16 * j) ^ trk));
+      }
+#pragma unroll
+      for (int nt = 0; nt < 32; ++nt) {
+        __builtin_amdgcn_sched_barrier(0);
+        dq[nt] = mfma16(dsa, join8(lo[nt % kPre], hi[nt % kPre]), dq[nt]);
+        if (nt + kPre < 32) {
+          lo[nt % kPre] = ld_tr(klo + ((16 * (nt + kPre)) ^ trk));
+          hi[nt % kPre] = ld_tr(khi + ((16 * (nt + kPre)) ^ trk));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmem();
+    __syncthreads();
+    rid_cur = rid_nxt;
+    rid_nxt = rid_of(blk + 2, raw_nn);
   }
-  // dq rows h' = 16 wave + 4g + i, columns 16nt + c16
-  uint16_t* dqp = b.dq + (int64_t)t * kH * kD;
+  if (nblk > 0) store_pds(nblk - 1);
+  // ---- dq (bf16) through LDS as [head][d] (swizzled rows), then full-row stores
+  uint16_t* dqt = &Kt[0][0][0];   // 64 rows x 1 KiB = both tile buffers
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int hh = 16 * wave + 4 * g + i;
+    const int hr = 16 * wave + 4 * g + i;
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt) dqp[hh * kD + 16 * nt + c16] = f32_to_bf16_bits(dq[nt][i]);
+    for (int nt = 0; nt < 32; ++nt) {
+      const int d = 16 * nt + c16;
+      dqt[hr * kD + 8 * ((d >> 3) ^ swz(hr)) + (d & 7)] = (uint16_t)(pack_bf16x2(dq[nt][i], 0.f) & 0xffffu);
+    }
+  }
+  __syncthreads();
+  uint16_t* dqp = b.dq + (int64_t)t * kH * kD;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int e = tid + 256 * k, hr = e >> 6, cc = e & 63;
+    *reinterpret_cast<uint4*>(dqp + hr * kD + 8 * cc) =
+        *reinterpret_cast<const uint4*>(&dqt[hr * kD + 8 * (cc ^ swz(hr))]);
   }
   if (b.sink && b.dsink && g == 0)
     atomicAdd(b.dsink + h, -expf(b.sink[h] - lse_t) * dt);
@@ -238,15 +329,28 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_attn_bwd_dkv_mfma(BwdArgs b) {
-  __shared__ __attribute__((aligned(16))) uint16_t QO[2 * kH][kKS];
+  // Q and dO staging at the start, then two output tiles of 64 rows x 1 KiB (swizzled)
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kH * kKS];
+  uint16_t (*QO)[kKS] = reinterpret_cast<uint16_t (*)[kKS]>(lds);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int tl = token_of_block(blockIdx.x);
   if (tl >= b.nT) return;
   const int t = b.t0 + tl;
   TokenInfo ti;
-  if (!token_info(b.cu, b.B, t, ti)) return;
+  if (!token_info_wave(b.cu, b.B, t, ti)) return;
   const int n_tot = b.nc[t] + min(b.W, ti.p + 1);
+  const uint16_t* pds_t = b.pds + (int64_t)tl * b.n_slots * 128;
+  uint16_t* stg_t = b.stage + (int64_t)tl * b.n_slots * kD;
+  bf16x8 av[4][4], nx[4][4];
+  auto fetch = [&](int c0, bf16x8 (&dst)[4][4]) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        dst[mt][ks] = ld16(pds_t + (int64_t)(c0 + 16 * mt + c16) * 128 + 32 * ks + 8 * g);
+  };
+  if (n_tot > 0) fetch(0, av);
   // stage Q (rows 0..63) and dO (rows 64..127) of the token
   const uint16_t* qt = b.q + (int64_t)t * kH * kD;
   const uint16_t* gt = b.dout + (int64_t)t * kH * kD;
@@ -268,37 +372,33 @@ void k_attn_bwd_dkv_mfma(BwdArgs b) {
       const v4i16 hi = ld_tr(&QO[32 * ks + 8 * g + 4 + jr][dw + 16 * nt + jc]);
       bo[nt][ks] = join8(lo, hi);
     }
-  const uint16_t* pds_t = b.pds + (int64_t)tl * b.n_slots * 128;
-  uint16_t* stg_t = b.stage + (int64_t)tl * b.n_slots * kD;
-  bf16x8 av[4][4], nx[4][4];
-  auto fetch = [&](int c0, bf16x8 (&dst)[4][4]) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        dst[mt][ks] = ld16(pds_t + (int64_t)(c0 + 16 * mt + c16) * 128 + 32 * ks + 8 * g);
-  };
-  if (n_tot > 0) fetch(0, av);
-  for (int c0 = 0; c0 < n_tot; c0 += kNB2) {
+  __syncthreads();   // QO no longer read: its space becomes the output tiles
+  uint16_t (*OT)[kNB2][kD] = reinterpret_cast<uint16_t (*)[kNB2][kD]>(lds);
+  int ob = 0;
+  for (int c0 = 0; c0 < n_tot; c0 += kNB2, ob ^= 1) {
     const bool more = c0 + kNB2 < n_tot;
     if (more) fetch(c0 + kNB2, nx);
+    // row gradients of candidates c0 + 16mt + c16 -> OT[ob][16mt + c16][d], chunk-swizzled
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const int c = c0 + 16 * mt + c16;       // this lane's candidate (output column)
-      uint16_t* dst = stg_t + (int64_t)c * kD + dw + 4 * g;
+      const int row = 16 * mt + c16;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) x = mfma16(bo[nt][ks], av[mt][ks], x);
-        // lane holds d = dw + 16nt + 4g .. +3 of candidate c
-        if (c < n_tot) {
-          const uint32_t lo = (uint32_t)f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
-          const uint32_t hi = (uint32_t)f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
-          *reinterpret_cast<uint2*>(dst + 16 * nt) = make_uint2(lo, hi);
-        }
+        // lane holds d = dw + 16nt + 4g .. +3 (logical chunk (dw + 16nt)/8 + g/2)
+        const int ck = ((dw + 16 * nt) >> 3) + (g >> 1);
+        *reinterpret_cast<uint2*>(&OT[ob][row][8 * (ck ^ swz(row)) + 4 * (g & 1)]) =
+            make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
       }
     }
+    __syncthreads();
+    // full-row 16-byte stores: wave w writes rows w, w+4, ...
+    const int nrow = min(kNB2, n_tot - c0);
+    for (int r = wave; r < nrow; r += 4)
+      *reinterpret_cast<uint4*>(stg_t + (int64_t)(c0 + r) * kD + 8 * lane) =
+          *reinterpret_cast<const uint4*>(&OT[ob][r][8 * (lane ^ swz(r))]);
     if (more) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
