@@ -329,9 +329,13 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_attn_bwd_dkv_mfma(BwdArgs b) {
-  // Q and dO staging at the start, then two output tiles of 64 rows x 1 KiB (swizzled)
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kH * kKS];
+  // LDS: Q and dO staging at the start; then two output tiles of 64 rows x 1 KiB and two
+  // dS|P tiles of 64 rows x 256 bytes (all rows chunk-swizzled)
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kNB2 * kD + 2 * kNB2 * 128];
   uint16_t (*QO)[kKS] = reinterpret_cast<uint16_t (*)[kKS]>(lds);
+  uint16_t (*OT)[kNB2][kD] = reinterpret_cast<uint16_t (*)[kNB2][kD]>(lds);
+  uint16_t (*PS)[kNB2][128] = reinterpret_cast<uint16_t (*)[kNB2][128]>(lds + 2 * kNB2 * kD);
+  static_assert(2 * kH * kKS <= 2 * kNB2 * kD + 2 * kNB2 * 128, "Q/dO staging fits");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int tl = token_of_block(blockIdx.x);
@@ -340,25 +344,21 @@ void k_attn_bwd_dkv_mfma(BwdArgs b) {
   TokenInfo ti;
   if (!token_info_wave(b.cu, b.B, t, ti)) return;
   const int n_tot = b.nc[t] + min(b.W, ti.p + 1);
+  const int nblk = (n_tot + kNB2 - 1) / kNB2;
   const uint16_t* pds_t = b.pds + (int64_t)tl * b.n_slots * 128;
   uint16_t* stg_t = b.stage + (int64_t)tl * b.n_slots * kD;
-  bf16x8 av[4][4], nx[4][4];
-  auto fetch = [&](int c0, bf16x8 (&dst)[4][4]) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        dst[mt][ks] = ld16(pds_t + (int64_t)(c0 + 16 * mt + c16) * 128 + 32 * ks + 8 * g);
-  };
-  if (n_tot > 0) fetch(0, av);
-  // stage Q (rows 0..63) and dO (rows 64..127) of the token
-  const uint16_t* qt = b.q + (int64_t)t * kH * kD;
-  const uint16_t* gt = b.dout + (int64_t)t * kH * kD;
-  for (int e = tid; e < 2 * kH * (kD / 8); e += 256) {
-    const int row = e / (kD / 8), ch = e % (kD / 8);
-    const uint16_t* src = row < kH ? qt + row * kD : gt + (row - kH) * kD;
-    *reinterpret_cast<uint4*>(&QO[row][8 * ch]) = *reinterpret_cast<const uint4*>(src + 8 * ch);
+  // stage Q (rows 0..63) and dO (rows 64..127) of the token: wave w loads rows 32w .. 32w+31
+  {
+    const uint16_t* qt = b.q + (int64_t)t * kH * kD;
+    const uint16_t* gt = b.dout + (int64_t)t * kH * kD;
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) {
+      const int row = 32 * wave + j;
+      const uint16_t* src = row < kH ? qt + row * kD : gt + (row - kH) * kD;
+      dma_row16(src + 8 * lane, &QO[row][0]);
+    }
   }
+  wait_vmem();
   __syncthreads();
   const int dw = wave * kDW;
   const int jr = c16 >> 2, jc = 4 * (c16 & 3);
@@ -372,24 +372,45 @@ void k_attn_bwd_dkv_mfma(BwdArgs b) {
       const v4i16 hi = ld_tr(&QO[32 * ks + 8 * g + 4 + jr][dw + 16 * nt + jc]);
       bo[nt][ks] = join8(lo, hi);
     }
-  __syncthreads();   // QO no longer read: its space becomes the output tiles
-  uint16_t (*OT)[kNB2][kD] = reinterpret_cast<uint16_t (*)[kNB2][kD]>(lds);
-  int ob = 0;
-  for (int c0 = 0; c0 < n_tot; c0 += kNB2, ob ^= 1) {
-    const bool more = c0 + kNB2 < n_tot;
-    if (more) fetch(c0 + kNB2, nx);
-    // row gradients of candidates c0 + 16mt + c16 -> OT[ob][16mt + c16][d], chunk-swizzled
+  __syncthreads();   // QO no longer read: its space becomes the output and dS|P tiles
+  // dS|P rows of block blk into PS[buf]: 4 rows of 256 bytes per instruction, wave w rows
+  // 16w .. 16w+15, lane l fills physical chunk l % 16 of row 4i + l / 16
+  auto issue = [&](int blk, int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * wave + 4 * i + (lane >> 4);
+      dma_row16(pds_t + (int64_t)(kNB2 * blk + r) * 128 + 8 * ((lane & 15) ^ swz(r)),
+                &PS[buf][16 * wave + 4 * i][0]);
+    }
+  };
+  // B operand reads: row 16mt + c16, logical chunk 4ks + g
+  int eq[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) eq[q] = 8 * ((4 * q + g) ^ swz(c16));
+  if (nblk > 0) issue(0, 0);
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int buf = blk & 1, c0 = kNB2 * blk;
+    // this block's dS|P rows: after block 0 the only younger memory operations are the
+    // previous (full) block's 16 row stores, which may stay in flight
+    if (blk == 0) wait_vmem();
+    else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    __syncthreads();
+    if (blk + 1 < nblk) issue(blk + 1, buf ^ 1);
+    // row gradients of candidates c0 + 16mt + c16 -> OT[buf][16mt + c16][d], chunk-swizzled
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int row = 16 * mt + c16;
+      bf16x8 av[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) av[ks] = ld16(&PS[buf][row][eq[ks]]);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) x = mfma16(bo[nt][ks], av[mt][ks], x);
+        for (int ks = 0; ks < 4; ++ks) x = mfma16(bo[nt][ks], av[ks], x);
         // lane holds d = dw + 16nt + 4g .. +3 (logical chunk (dw + 16nt)/8 + g/2)
         const int ck = ((dw + 16 * nt) >> 3) + (g >> 1);
-        *reinterpret_cast<uint2*>(&OT[ob][row][8 * (ck ^ swz(row)) + 4 * (g & 1)]) =
+        *reinterpret_cast<uint2*>(&OT[buf][row][8 * (ck ^ swz(row)) + 4 * (g & 1)]) =
             make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
       }
     }
@@ -398,13 +419,7 @@ void k_attn_bwd_dkv_mfma(BwdArgs b) {
     const int nrow = min(kNB2, n_tot - c0);
     for (int r = wave; r < nrow; r += 4)
       *reinterpret_cast<uint4*>(stg_t + (int64_t)(c0 + r) * kD + 8 * lane) =
-          *reinterpret_cast<const uint4*>(&OT[ob][r][8 * (lane ^ swz(r))]);
-    if (more) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) av[mt][ks] = nx[mt][ks];
-    }
+          *reinterpret_cast<const uint4*>(&OT[buf][r][8 * (lane ^ swz(r))]);
   }
 }
 

@@ -487,33 +487,41 @@ __global__ __launch_bounds__(1024) void k_csr_scan(CsrArgs c) {
   }
 }
 
-// dst[j, :] += sum of the staged bf16 rows listed for j; one wave per row, 2 floats per lane,
-// four waves per workgroup
+// dst[j, :] += sum of the staged bf16 rows listed for j.  One workgroup per row; wave w takes
+// list entries w, w+4, ... in batches of 64 (one coalesced list read per batch, the entries
+// then broadcast from registers), lane l sums elements 2l, 2l+1 with many loads in flight.
 __global__ __launch_bounds__(256) void k_csr_reduce(CsrArgs c) {
-  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (j >= c.n_rows) return;
+  __shared__ float2 part[4][64];
+  const int j = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = c.cnt[j];
   if (n == 0) return;
   const int32_t* lst = c.list + c.off[j];
-  float s0 = 0.f, s1 = 0.f, u0 = 0.f, u1 = 0.f;
-  int e = 0;
-  for (; e + 1 < n; e += 2) {
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(c.stage + (int64_t)lst[e] * kDI + 2 * lane);
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(c.stage + (int64_t)lst[e + 1] * kDI + 2 * lane);
-    s0 += __uint_as_float(v << 16);
-    s1 += __uint_as_float(v & 0xffff0000u);
-    u0 += __uint_as_float(w << 16);
-    u1 += __uint_as_float(w & 0xffff0000u);
+  float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+  for (int base = 64 * wave; base < n; base += 256) {
+    const int my = base + lane < n ? lst[base + lane] : -1;
+    const int m = min(64, n - base);
+#pragma unroll 8
+    for (int k = 0; k < m; k += 2) {
+      const int e0 = __shfl(my, k, 64), e1 = __shfl(my, k + 1, 64);
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(c.stage + (int64_t)e0 * kDI + 2 * lane);
+      a0 += __uint_as_float(v << 16);
+      a1 += __uint_as_float(v & 0xffff0000u);
+      if (e1 >= 0) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(c.stage + (int64_t)e1 * kDI + 2 * lane);
+        b0 += __uint_as_float(w << 16);
+        b1 += __uint_as_float(w & 0xffff0000u);
+      }
+    }
   }
-  if (e < n) {
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(c.stage + (int64_t)lst[e] * kDI + 2 * lane);
-    s0 += __uint_as_float(v << 16);
-    s1 += __uint_as_float(v & 0xffff0000u);
+  part[wave][lane] = make_float2(a0 + b0, a1 + b1);
+  __syncthreads();
+  if (wave == 0) {
+    const float2 p0 = part[0][lane], p1 = part[1][lane], p2 = part[2][lane], p3 = part[3][lane];
+    float2* d = reinterpret_cast<float2*>(c.dst + (int64_t)j * kDI + 2 * lane);
+    const float2 o = *d;
+    *d = make_float2(o.x + ((p0.x + p1.x) + (p2.x + p3.x)), o.y + ((p0.y + p1.y) + (p2.y + p3.y)));
   }
-  float2* d = reinterpret_cast<float2*>(c.dst + (int64_t)j * kDI + 2 * lane);
-  const float2 o = *d;
-  *d = make_float2(o.x + (s0 + u0), o.y + (s1 + u1));
 }
 
 struct KlcPlan {
@@ -611,7 +619,7 @@ hipError_t launch_indexer_kl_cached(const Shape& sh, const KlIO& io, hipStream_t
       hipLaunchKernelGGL(k_csr_pairs<false>, dim3(c.nT), dim3(256), 0, s, c);
       hipLaunchKernelGGL(k_csr_scan, dim3(1), dim3(1024), 0, s, c);
       hipLaunchKernelGGL(k_csr_pairs<true>, dim3(c.nT), dim3(256), 0, s, c);
-      hipLaunchKernelGGL(k_csr_reduce, dim3((c.n_rows + 3) / 4), dim3(256), 0, s, c);
+      hipLaunchKernelGGL(k_csr_reduce, dim3(c.n_rows), dim3(256), 0, s, c);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
