@@ -47,7 +47,7 @@ constexpr int kDW = 128;          // d per wave, kernel 2
 constexpr int kNB1 = 32;          // candidates per block, kernel 1
 constexpr int kKS = kD + 16;      // row stride (bf16) of LDS row tiles
 constexpr int kNB2 = 64;          // candidates per block, kernel 2
-constexpr int kPTS = 136;         // row stride (bf16) of the dS | P transpose tile
+constexpr int kPTS = 144;         // row stride (bf16) of the dS | P tile (conflict-free reads)
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -169,9 +169,11 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
   const float lse_t = b.lse[(int64_t)t * kH + h];
   const float lse2 = lse_t * 1.44269504088896341f;
 
-  f32x4 dq[32];
+  f32x4 dq[4][8];   // heads 16mt + 4g + i, d = 128 wave + 16nt + c16
 #pragma unroll
-  for (int nt = 0; nt < 32; ++nt) dq[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) dq[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // row id of slot 32 blk + (lane & 31): >= 0 compressed row, <= -2 raw row -2 - id, -1 none
   auto rid_of = [&](int blk, int raw) {
@@ -186,24 +188,27 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
   };
   // wave w gathers rows 8w .. 8w+7 of a block (one 1 KiB row per instruction, lane l fills
   // physical chunk l); an absent slot loads the query's own raw row (finite, masked)
+  auto issue_row = [&](int rid, int buf, int j) {
+    const int r = 8 * wave + j;
+    const int id = __builtin_amdgcn_readlane(rid, r);
+    const uint16_t* src = id >= 0 ? b.kv_cmp + (int64_t)id * kD
+                                  : b.kv + (int64_t)(id == -1 ? t : -2 - id) * kD;
+    dma_row16(src + 8 * (lane ^ swz(r)), &Kt[buf][r][0]);
+  };
   auto issue = [&](int rid, int buf) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = 8 * wave + j;
-      const int id = __builtin_amdgcn_readlane(rid, r);
-      const uint16_t* src = id >= 0 ? b.kv_cmp + (int64_t)id * kD
-                                    : b.kv + (int64_t)(id == -1 ? t : -2 - id) * kD;
-      dma_row16(src + 8 * (lane ^ swz(r)), &Kt[buf][r][0]);
-    }
+    for (int j = 0; j < 8; ++j) issue_row(rid, buf, j);
   };
   // per-lane LDS offsets (elements): S^T A operand rows 16mt + c16, logical chunk 4ks + g
   int eq[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) eq[q] = 8 * ((4 * q + g) ^ swz(c16));
-  // dq B operand (transposed): rows 4g + c16/4 (lo) and 16 + 4g + c16/4 (hi), both with
-  // swizzle s = swz(4g + c16/4); column 16nt + 4(c16 & 3) at 16nt ^ 8((c16 & 3)/2 ^ s) + 4(c16 & 1)
-  const int trr = 4 * g + (c16 >> 2);
-  const int trk = 8 * (((c16 & 3) >> 1) ^ swz(trr)), troff = 4 * (c16 & 1);
+  // dq product, wave w = d slice 128w .. 128w+127 for all 64 heads, k = the block's 32 slots:
+  //  A = dS (transposed read of PT[slot][head]), rows 8g + c16/4 (lo) and +4 (hi);
+  //  B = row tile read transposed, the same rows, column 128w + 16nt + 4(c16 & 3) at
+  //      128w + (16nt ^ 8((c16 & 3)/2 ^ s)) + 4(c16 & 1) with s the row's swizzle
+  const int trr = 8 * g + (c16 >> 2), tre = (c16 & 3) >> 1, troff = 4 * (c16 & 1);
+  const int klo_s = 8 * (tre ^ swz(trr)), khi_s = 8 * (tre ^ swz(trr + 4));
 
   uint16_t* pds_t = b.pds + (int64_t)tl * b.n_slots * 128;
   auto store_pds = [&](int blk) {   // slots of block blk from PT[blk & 1], 16-byte stores
@@ -222,7 +227,7 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
   for (int blk = 0; blk < nblk; ++blk) {
     const int buf = blk & 1;
     const uint32_t valid = (uint32_t)__ballot(rid_cur != -1);
-    if (blk + 1 < nblk) issue(rid_nxt, buf ^ 1);
+    const bool more = blk + 1 < nblk;
     const int raw_nn = raw_of(blk + 2);
     if (blk > 0) store_pds(blk - 1);
     // ---- S^T, dP^T for 32 candidates x this wave's 16 heads (operands read 3 steps ahead)
@@ -250,10 +255,12 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt) av[ks % kPre][mt] = seg(ks + kPre, mt);
         }
+        // the next block's rows, one per two k-steps, between the MFMAs
+        if (more && (ks & 1)) issue_row(rid_nxt, buf ^ 1, ks >> 1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- P, scale*dS for slots 16mt + 4g + i, head h -> PT (bf16) and the dq A operand
+    // ---- P, scale*dS for slots 16mt + 4g + i, head h -> PT (bf16)
     uint32_t dsw[4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -275,28 +282,22 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
         PT[buf][cl][64 + h] = (uint16_t)(wp & 0xffffu);
       }
     }
-    const bf16x8 dsa = __builtin_bit_cast(bf16x8, make_uint4(dsw[0], dsw[1], dsw[2], dsw[3]));
-    // ---- dq[h'][d] += sum_c dS[h'][c] K[c][d]; B = rows {4g..4g+3, 16+4g..16+4g+3}
+    __syncthreads();   // dS of all heads in PT[buf]
+    // ---- dq[h][d] += sum_c dS[h][c] K[c][d] over this block's 32 slots
     {
-      const uint16_t* klo = &Kt[buf][trr][troff];
-      const uint16_t* khi = &Kt[buf][16 + trr][troff];
-      constexpr int kPre = 4;
-      v4i16 lo[kPre], hi[kPre];
+      bf16x8 da[4];
 #pragma unroll
-      for (int j = 0; j < kPre; ++j) {
-        lo[j] = ld_tr(klo + ((16 * j) ^ trk));
-        hi[j] = ld_tr(khi + ((16 * j) ^ trk));
-      }
+      for (int mt = 0; mt < 4; ++mt)
+        da[mt] = join8(ld_tr(&PT[buf][trr][16 * mt + 4 * (c16 & 3)]),
+                       ld_tr(&PT[buf][trr + 4][16 * mt + 4 * (c16 & 3)]));
+      const uint16_t* klo = &Kt[buf][trr][128 * wave + troff];
+      const uint16_t* khi = &Kt[buf][trr + 4][128 * wave + troff];
 #pragma unroll
-      for (int nt = 0; nt < 32; ++nt) {
-        __builtin_amdgcn_sched_barrier(0);
-        dq[nt] = mfma16(dsa, join8(lo[nt % kPre], hi[nt % kPre]), dq[nt]);
-        if (nt + kPre < 32) {
-          lo[nt % kPre] = ld_tr(klo + ((16 * (nt + kPre)) ^ trk));
-          hi[nt % kPre] = ld_tr(khi + ((16 * (nt + kPre)) ^ trk));
-        }
+      for (int nt = 0; nt < 8; ++nt) {
+        const bf16x8 kb = join8(ld_tr(klo + ((16 * nt) ^ klo_s)), ld_tr(khi + ((16 * nt) ^ khi_s)));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) dq[mt][nt] = mfma16(da[mt], kb, dq[mt][nt]);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
     wait_vmem();
     __syncthreads();
@@ -307,14 +308,17 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
   // ---- dq (bf16) through LDS as [head][d] (swizzled rows), then full-row stores
   uint16_t* dqt = &Kt[0][0][0];   // 64 rows x 1 KiB = both tile buffers
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int hr = 16 * wave + 4 * g + i;
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt) {
-      const int d = 16 * nt + c16;
-      dqt[hr * kD + 8 * ((d >> 3) ^ swz(hr)) + (d & 7)] = (uint16_t)(pack_bf16x2(dq[nt][i], 0.f) & 0xffffu);
+    for (int i = 0; i < 4; ++i) {
+      const int hr = 16 * mt + 4 * g + i;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const int d = 128 * wave + 16 * nt + c16;
+        dqt[hr * kD + 8 * ((d >> 3) ^ swz(hr)) + (d & 7)] =
+            (uint16_t)(pack_bf16x2(dq[mt][nt][i], 0.f) & 0xffffu);
+      }
     }
-  }
   __syncthreads();
   uint16_t* dqp = b.dq + (int64_t)t * kH * kD;
 #pragma unroll
