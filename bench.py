@@ -44,7 +44,78 @@ def parse():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run one plain device-to-device copy of this many bytes before "
                          "the timed steps (a known-traffic reference for HBM counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the per-call HBM traffic summary of two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE) of 'bench.py --steps 1 --warmup 0 "
+                         "--copy-bytes N' and exit")
     return ap.parse_args()
+
+
+# kernels of each multi-kernel ABI call, by the demangled name prefix rocprofv3 reports
+CALL_KERNELS = {
+    "attn_bwd": ("k_attn_bwd_dq_mfma", "k_attn_bwd_dkv_mfma", "k_bwd_fill_zero", "k_bwd_csr_pass",
+                 "k_bwd_csr_scan", "k_bwd_reduce_cmp", "k_bwd_reduce_win", "k_attn_bwd_generic"),
+    "attn_fwd": ("k_attn_fwd_mfma", "k_attn_fwd_generic"),
+    "indexer_kl": ("k_kl_cached", "k_fill_zero_i32", "k_csr_pairs", "k_csr_scan", "k_csr_reduce",
+                   "k_indexer_kl_mfma", "k_kl_generic", "k_sum"),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "thd64k_csa_bf16_traffic.md")
+
+
+def source_hash():
+    """Hash of the kernel sources: traffic counters taken on other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_compressed_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _pmc_rows(d):
+    import csv
+    path = os.path.join(d, "run_counter_collection.csv")
+    out = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+            name = name.split("(")[0].replace("void ", "")
+            name = name.split("::")[-1].split("<")[0]
+            out.append((int(r["Dispatch_Id"]), name, r["Counter_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def summarize_pmc(fetch_dir, write_dir, copy_bytes):
+    """Per-call HBM bytes of one step: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+    scaled by what the same counter reads for the plain copy of copy_bytes bytes."""
+    res = {}
+    for label, d, cname in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = [r for r in _pmc_rows(d) if r[2] == cname]
+        copies = [v for _, n, _, v in rows if "copyBuffer" in n]
+        factor = copy_bytes / (max(copies) * 1024.0)
+        per_call = {}
+        for _, n, _, v in rows:
+            for call, ks in CALL_KERNELS.items():
+                if n in ks:
+                    per_call[call] = per_call.get(call, 0.0) + v * 1024.0 * factor
+        res[label] = {"factor": factor, "copy_kib": max(copies), "per_call_bytes": per_call}
+    return res
+
+
+def load_traffic():
+    """Per-call HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        data = json.loads(blob)
+    except Exception:
+        return None
+    if data.get("source_hash") != source_hash():
+        return None
+    return data.get("per_call_bytes")
 
 
 class EventTimer:
@@ -168,6 +239,28 @@ def cpu_baseline(w, host, budget_s):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        res = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
+                            args.copy_bytes or (1 << 30))
+        calls = sorted(set(res["fetch"]["per_call_bytes"]) | set(res["write"]["per_call_bytes"]))
+        per_call = {c: res["fetch"]["per_call_bytes"].get(c, 0.0) +
+                    res["write"]["per_call_bytes"].get(c, 0.0) for c in calls}
+        print("| Call | HBM read (GB) | HBM write (GB) | total (GB) |")
+        print("| --- | --- | --- | --- |")
+        for c in calls:
+            print(f"| {c} | {res['fetch']['per_call_bytes'].get(c, 0) / 1e9:.3f} | "
+                  f"{res['write']['per_call_bytes'].get(c, 0) / 1e9:.3f} | {per_call[c] / 1e9:.3f} |")
+        print()
+        print(f"Copy calibration: FETCH_SIZE read {res['fetch']['copy_kib']:.0f} KiB and WRITE_SIZE "
+              f"{res['write']['copy_kib']:.0f} KiB for the plain copy of {args.copy_bytes or (1 << 30)} "
+              f"bytes; factors {res['fetch']['factor']:.4f} and {res['write']['factor']:.4f}.")
+        print()
+        print("```json")
+        print(json.dumps({"source_hash": source_hash(), "per_call_bytes": per_call,
+                          "fetch_factor": res["fetch"]["factor"],
+                          "write_factor": res["write"]["factor"]}))
+        print("```")
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (no collectives or "
@@ -235,7 +328,8 @@ def main():
         roof = {"bound": "mfma", "achieved": amount / tdom / 1e12, "peak": PEAK[bound] / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    traffic = load_traffic()
+    roof["traffic"] = traffic.get(dom) if traffic else None
     roof["kernel"] = dom
     roof["algorithmic_per_launch"] = amount
     tokens = c["tokens"]
