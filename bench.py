@@ -180,6 +180,10 @@ def roofline_table(w, c, T):
         "quantize_qI": ("hbm", c["tokens"] * HI * dI * (2 + 1) + c["tokens"] * HI * 4),
         "quantize_kI": ("hbm", c["tcmp"] * dI * (2 + 1) + c["tcmp"] * 4),
         "index_scores": ("fp8" if w.idx_dtype == "fp8" else mm, 2 * dI * HI * c["vis"]),
+        # fused scores + top-k: the score products dominate (every visible entry is scored
+        # when the loss reads scores; rows with n_vis <= k skip them otherwise)
+        "index_topk": ("fp8" if w.idx_dtype == "fp8" else mm,
+                       2 * dI * HI * (c["vis"] if w.teacher != "none" else c["vis_read"])),
         "topk_select": ("hbm", 4 * c["vis_read"] + 4 * T * max(w.topk_cap, 1)),
         "attn_fwd": (mm, 4 * D * H * c["cand"]),
         "indexer_kl": (mm, kl_flops),
@@ -189,6 +193,38 @@ def roofline_table(w, c, T):
     }
     _ = ei
     return tab
+
+
+def standalone_topk(layer, dev, cu, reps):
+    """Mean ms of csa_index_scores and csa_topk_select run as separate calls (HIP events on
+    the stream they run on) for the layer's current inputs."""
+    from long_context_compressed_amd import binding as B
+    p, cfg = layer.p, layer.cfg
+    if cfg.idx_dtype == "fp8":
+        qI, qs, kI, ks = layer.qI8, layer.qI_scale, layer.kI8, layer.kI_scale
+    else:
+        qI, qs, kI, ks = dev["qI"], None, layer.kI_cmp, None
+    scores = torch.empty_like(layer.scores)
+    idx = torch.empty_like(layer.idx)
+    timer = EventTimer()
+    for i in range(reps + 1):
+        tm = timer if i > 0 else None
+        for name, fn, args in (
+                ("index_scores", B.csa_index_scores,
+                 (p, qI, qs, dev["w"], kI, ks, cu, layer.cu_cmp, scores)),
+                ("topk_select", B.csa_topk_select, (p, scores, cu, layer.cu_cmp, idx))):
+            if tm:
+                tm.mark(name)
+            fn(*args)
+            if tm:
+                tm.done(name)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(idx, layer.idx))
+    print(f"[bench] stand-alone scores + top-k: same selection as the fused call: {same}",
+          file=sys.stderr, flush=True)
+    if not same:
+        raise RuntimeError("fused and stand-alone top-k selections differ")
+    return {f"{k}_standalone": v for k, v in timer.mean_ms().items()}
 
 
 def cpu_baseline(w, host, budget_s):
@@ -307,9 +343,13 @@ def main():
 
     c = work_counts(w, host["lengths"])
     tab = roofline_table(w, c, w.total_tokens)
+    if layer.fused_topk:
+        # the step selects with the fused call; the stand-alone top-k over a materialized
+        # score matrix is timed after the step loop, on the same inputs
+        per_call.update(standalone_topk(layer, dev, cu, reps=max(args.steps, 3)))
     breakdown = {}
     for name, t in per_call.items():
-        bound, amount = tab.get(name, ("", 0))
+        bound, amount = tab.get(name.replace("_standalone", ""), ("", 0))
         ent = {"ms": round(t, 4)}
         if bound == "hbm" and t > 0:
             ent["GB/s"] = round(amount / (t * 1e-3) / 1e9, 1)
@@ -318,7 +358,8 @@ def main():
             ent["TFLOP/s"] = round(amount / (t * 1e-3) / 1e12, 2)
             ent["frac_mfma"] = round(amount / (t * 1e-3) / PEAK[bound], 4)
         breakdown[name] = ent
-    dom = max(per_call, key=per_call.get)
+    in_step = {k: v for k, v in per_call.items() if not k.endswith("_standalone")}
+    dom = max(in_step, key=in_step.get)
     bound, amount = tab[dom]
     tdom = per_call[dom] * 1e-3
     if bound == "hbm":
@@ -347,7 +388,8 @@ def main():
                    "teacher": w.teacher, "pass": "fwd+bwd" if w.backward else "fwd"},
         "roofline": roof,
         "attention_tflops": attn_flops / max(attn_ms * 1e-3, 1e-12) / 1e12 if attn_ms else None,
-        "topk_gbps": breakdown.get("topk_select", {}).get("GB/s"),
+        "topk_gbps": (breakdown.get("topk_select") or
+                      breakdown.get("topk_select_standalone", {})).get("GB/s"),
         "breakdown": breakdown,
         "work": c,
     }

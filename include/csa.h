@@ -11,6 +11,7 @@
  *   csa_quantize_fp8     optional e4m3 operands of an FP8 indexer         (section 9)
  *   csa_index_scores     lightning-indexer logits over visible entries   (section 3)
  *   csa_topk_select      per-query top-k + lowering to global rows        (sections 3, 8.1, 8.2)
+ *   csa_index_topk       the two above fused: logits never leave the chip  (sections 3, 8.2)
  *   csa_sparse_attn_fwd  selected (or all) compressed rows + local window (sections 2, 8.2)
  *   csa_indexer_kl       KL auxiliary loss and its eager indexer backward (sections 3, 8.2)
  *   csa_sparse_attn_bwd  dq, dkv, dsink from saved O, LSE and dO          (section 8.2)
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 3
+#define CSA_ABI_VERSION 4
 
 typedef int32_t csa_status_t;
 enum {
@@ -164,6 +165,19 @@ csa_status_t csa_index_scores(const csa_params_t* p, const void* qI, const float
 csa_status_t csa_topk_select(const csa_params_t* p, const float* scores, int64_t ld_scores,
                              const int32_t* cu_seqlens, const int32_t* cu_cmp, int32_t* idx,
                              hipStream_t stream);
+
+/* Indexer scores and top-k selection in one pass (section 3 logits and selection; section
+ * 8.2 names score/top-k fusion as open work): the same idx as csa_index_scores followed by
+ * csa_topk_select on the same operands, without the full [T, ld_scores] score matrix
+ * making a round trip through HBM.  scores_mode: 0 = scores not written (scores may be
+ * NULL); 1 = scores[t, j] written for the selected j only (what a selected-set indexer loss
+ * reads); 2 = written for every visible j.  Other entries of scores are untouched.
+ * Supported for idx_heads = 64, idx_dim = 128 (bf16 or fp8 indexer) and max_seqlen / ratio
+ * <= 4096; else CSA_ERR_UNSUPPORTED (use the two calls).  idx: int32 [T, topk_cap]. */
+csa_status_t csa_index_topk(const csa_params_t* p, const void* qI, const float* qI_scale,
+                            const float* w, const void* kI_cmp, const float* kI_scale,
+                            const int32_t* cu_seqlens, const int32_t* cu_cmp, int32_t scores_mode,
+                            float* scores, int64_t ld_scores, int32_t* idx, hipStream_t stream);
 
 /* Sparse attention forward (sections 2 and 8.2).  Candidates of query t: the compressed
  * rows idx[t, 0 .. first -1) (CSA_SPARSE; entries outside the query's visible range are

@@ -56,6 +56,7 @@ _SIGS = {
     "csa_quantize_fp8": ([_P, _I32, _I64, _I32, _P, _P, _P], _I32),
     "csa_index_scores": ([_PP, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _P], _I32),
     "csa_topk_select": ([_PP, _P, _I64, _P, _P, _P, _P], _I32),
+    "csa_index_topk": ([_PP, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I64, _P, _P], _I32),
     "csa_sparse_attn_fwd": ([_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
     "csa_teacher_logits_stride": ([_PP], _I64),
     "csa_sparse_attn_bwd": ([_PP] + [_P] * 14 + [_P, _SZ, _P], _I32),
@@ -174,6 +175,15 @@ def csa_topk_select(p, scores, cu_seqlens, cu_cmp, idx, stream=None):
     _check("csa_topk_select", lib().csa_topk_select(
         ctypes.byref(p), _ptr(scores), scores.shape[-1], _ptr(cu_seqlens), _ptr(cu_cmp),
         _ptr(idx), _stream(stream)))
+
+
+def csa_index_topk(p, qI, qI_scale, w, kI_cmp, kI_scale, cu_seqlens, cu_cmp, idx,
+                   scores=None, scores_mode=0, stream=None):
+    """scores_mode 0: scores untouched; 1: the selected entries written; 2: every visible one."""
+    _check("csa_index_topk", lib().csa_index_topk(
+        ctypes.byref(p), _ptr(qI), _ptr(qI_scale), _ptr(w), _ptr(kI_cmp), _ptr(kI_scale),
+        _ptr(cu_seqlens), _ptr(cu_cmp), scores_mode, _ptr(scores),
+        scores.shape[-1] if scores is not None else 0, _ptr(idx), _stream(stream)))
 
 
 def csa_sparse_attn_fwd(p, q, kv_cmp, kv, idx, sink, cu_seqlens, cu_cmp, out, lse, lse_cmp=None,

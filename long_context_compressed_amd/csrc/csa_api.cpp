@@ -164,6 +164,32 @@ csa_status_t csa_topk_select(const csa_params_t* p, const float* scores, int64_t
                                    stream));
 }
 
+csa_status_t csa_index_topk(const csa_params_t* p, const void* qI, const float* qI_scale,
+                            const float* w, const void* kI_cmp, const float* kI_scale,
+                            const int32_t* cu_seqlens, const int32_t* cu_cmp, int32_t scores_mode,
+                            float* scores, int64_t ld_scores, int32_t* idx, hipStream_t stream) {
+  csa_status_t st = check_common(p);
+  if (st) return st;
+  if (!qI || !w || !kI_cmp || !cu_seqlens || !cu_cmp || !idx) return CSA_ERR_NULL;
+  if (scores_mode < 0 || scores_mode > 2) return CSA_ERR_ARG;
+  if (scores_mode != 0 && !scores) return CSA_ERR_NULL;
+  if (scores_mode != 0 && ld_scores < n_cap_of(p)) return CSA_ERR_ARG;
+  st = check_indexer(p);
+  if (st) return st;
+  const bool fp8 = p->idx_dtype == CSA_FP8_E4M3;
+  if (fp8 && (!qI_scale || !kI_scale)) return CSA_ERR_NULL;
+  if (p->topk < 1 || p->topk_cap < p->topk || p->topk_cap % 64 != 0) return CSA_ERR_ARG;
+  if (p->idx_heads != 64 || p->idx_dim != 128 || p->idx_dtype == CSA_F32 || n_cap_of(p) > 4096)
+    return CSA_ERR_UNSUPPORTED;
+  bool handled = false;
+  const hipError_t e = csa::launch_index_topk(make_shape(p, cu_seqlens, cu_cmp), qI,
+                                              fp8 ? qI_scale : nullptr, w, kI_cmp,
+                                              fp8 ? kI_scale : nullptr, scores_mode, scores,
+                                              ld_scores, idx, stream, &handled);
+  if (!handled) return CSA_ERR_UNSUPPORTED;
+  return launched(e);
+}
+
 csa_status_t csa_sparse_attn_fwd(const csa_params_t* p, const void* q, const void* kv_cmp,
                                  const void* kv, const int32_t* idx, const float* sink,
                                  const int32_t* cu_seqlens, const int32_t* cu_cmp, void* out,

@@ -42,6 +42,11 @@ hipError_t launch_index_scores(const Shape& sh, const void* qI, const float* qI_
                                float* scores, int64_t ld, hipStream_t s);
 hipError_t launch_topk(const Shape& sh, const float* scores, int64_t ld, int32_t* idx,
                        hipStream_t s);
+// fused scores + top-k; *handled = false when the shape has no fused kernel
+hipError_t launch_index_topk(const Shape& sh, const void* qI, const float* qI_scale,
+                             const float* w, const void* kI, const float* kI_scale,
+                             int scores_mode, float* scores, int64_t ld, int32_t* idx,
+                             hipStream_t s, bool* handled);
 
 struct AttnIO {
   const void* q;

@@ -12,13 +12,18 @@
 //   bf16: v_mfma_f32_16x16x32_bf16, 4 k-steps per tile.
 //   fp8 (OCP e4m3 codes): v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales, one
 //   instruction per tile; the per-row fp32 scales of qI and kI multiply the result.
-#include "csa_device.h"
+// The fused variant keeps each token's scores in a wave-private LDS row and runs the
+// wave-level radix top-k on it, so the score matrix need not round-trip through HBM
+// (section 8.2 lists fusing scores with top-k as open work).
+#include "attn_common.h"
 #include "csa_launch.h"
+#include "topk_wave.h"
 
 namespace csa {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+using attn::bf16x8;
+using attn::f32x4;
+using attn::token_info_wave;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 namespace {
@@ -39,16 +44,15 @@ struct ScArgs {
   int B, T, r, n_cap;
 };
 
-template <bool FP8>
-__device__ __forceinline__ void scores_token(const ScArgs& a, int t) {
+// Scores of one token's visible keys j < nv, 64 at a time: emit(j0, s) is called once per
+// block with lane l holding the score of j = j0 + l (keys past nv hold unspecified values).
+// The product for keys j0 + 16 nt + c16 finishes with the sum over the four lane groups in
+// every group alike, so the lane of group g keeps its value from tile nt = g.
+template <bool FP8, class Emit>
+__device__ __forceinline__ void score_blocks(const ScArgs& a, int t, int row0, int nv,
+                                             Emit&& emit) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, c16 = lane & 15;
-  TokenInfo ti;
-  if (!token_info(a.cu, a.B, t, ti)) return;
-  const int nv = min((ti.p + 1) / a.r, a.n_cap);
-  if (nv <= 0) return;
-  const int row0 = a.cu_cmp[ti.b];
-  float* out = a.scores + (int64_t)t * a.ld;
 
   // per-lane weights of the output rows h = 16mt + 4g + i (and fp8 query scales)
   float wv[4][4];
@@ -85,6 +89,7 @@ __device__ __forceinline__ void scores_token(const ScArgs& a, int t) {
           kb[nt][ks] = __builtin_bit_cast(bf16x8, v);
         }
       }
+      float mine = 0.f;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         float s = 0.f;
@@ -99,9 +104,9 @@ __device__ __forceinline__ void scores_token(const ScArgs& a, int t) {
         }
         s += __shfl_xor(s, 16, 64);
         s += __shfl_xor(s, 32, 64);
-        const int j = j0 + 16 * nt + c16;
-        if (g == 0 && j < nv) out[j] = s + 0.0f;
+        if (nt == g) mine = s;
       }
+      emit(j0, mine + 0.0f);
     }
   } else {
     const uint8_t* q = (const uint8_t*)a.qI + (int64_t)t * kHI * kDI;
@@ -132,6 +137,7 @@ __device__ __forceinline__ void scores_token(const ScArgs& a, int t) {
                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         ks_[nt] = sc;
       }
+      float mine = 0.f;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         float s = 0.f;
@@ -146,9 +152,9 @@ __device__ __forceinline__ void scores_token(const ScArgs& a, int t) {
         }
         s += __shfl_xor(s, 16, 64);
         s += __shfl_xor(s, 32, 64);
-        const int j = j0 + 16 * nt + c16;
-        if (g == 0 && j < nv) out[j] = s + 0.0f;
+        if (nt == g) mine = s;
       }
+      emit(j0, mine + 0.0f);
     }
   }
 }
@@ -157,7 +163,58 @@ template <bool FP8>
 __global__ __launch_bounds__(256) void k_index_scores_mfma(ScArgs a) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
-  scores_token<FP8>(a, t);
+  TokenInfo ti;
+  if (!token_info_wave(a.cu, a.B, t, ti)) return;
+  const int nv = min((ti.p + 1) / a.r, a.n_cap);
+  if (nv <= 0) return;
+  float* out = a.scores + (int64_t)t * a.ld;
+  const int lane = threadIdx.x & 63;
+  score_blocks<FP8>(a, t, a.cu_cmp[ti.b], nv, [&](int j0, float s) {
+    if (j0 + lane < nv) out[j0 + lane] = s;
+  });
+}
+
+// Fused scores + top-k for rows of up to 64 * KPL visible keys, one wave per token: the
+// scores go to a wave-private LDS row (plus HBM when mode 2 asks for all of them), then the
+// wave's radix top-k selects from LDS and, in mode 1, stores the selected scores only.
+// Rows with nv <= k select every visible key, and skip the scores unless they are wanted.
+template <bool FP8, int KPL>
+__global__ __launch_bounds__(256) void k_index_topk(ScArgs a, int k, int k_cap, int mode,
+                                                    int32_t* __restrict__ idx) {
+  __shared__ float rows[4][64 * KPL];
+  __shared__ uint32_t hist[4][4][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.T) return;
+  int32_t* out = idx + (int64_t)t * k_cap;
+  TokenInfo ti;
+  const bool real = token_info_wave(a.cu, a.B, t, ti);
+  const int nv = real ? min((ti.p + 1) / a.r, a.n_cap) : 0;
+  const int row0 = real ? a.cu_cmp[ti.b] : 0;
+  float* srow = a.scores ? a.scores + (int64_t)t * a.ld : nullptr;
+  if (nv <= k) {  // every visible row is selected (also covers padding rows: nv = 0)
+    if (mode != 0 && nv > 0)
+      score_blocks<FP8>(a, t, row0, nv, [&](int j0, float s) {
+        if (j0 + lane < nv) srow[j0 + lane] = s;
+      });
+    for (int c = lane; c < k_cap; c += 64) out[c] = c < nv ? row0 + c : -1;
+    return;
+  }
+  float* lrow = rows[wave];
+  score_blocks<FP8>(a, t, row0, nv, [&](int j0, float s) {
+    if (j0 + lane < nv) {
+      lrow[j0 + lane] = s;
+      if (mode == 2) srow[j0 + lane] = s;
+    }
+  });
+  __builtin_amdgcn_wave_barrier();
+  const int n_it = __builtin_amdgcn_readfirstlane((nv + 63) >> 6);
+  float* sel = mode == 1 ? srow : nullptr;
+  if (KPL >= 16 && n_it <= 16) topk_row_wave<16>(lrow, nv, n_it, k, row0, out, hist[wave], sel);
+  else if (KPL >= 32 && n_it <= 32) topk_row_wave<32>(lrow, nv, n_it, k, row0, out, hist[wave], sel);
+  else if (KPL >= 48 && n_it <= 48) topk_row_wave<48>(lrow, nv, n_it, k, row0, out, hist[wave], sel);
+  else topk_row_wave<(KPL > 48 ? 64 : KPL)>(lrow, nv, n_it, k, row0, out, hist[wave], sel);
+  for (int c = k + lane; c < k_cap; c += 64) out[c] = -1;
 }
 
 }  // namespace
@@ -187,6 +244,44 @@ hipError_t launch_index_scores_mfma(const Shape& sh, const void* qI, const float
     hipLaunchKernelGGL(k_index_scores_mfma<true>, dim3(grid), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(k_index_scores_mfma<false>, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_topk(const Shape& sh, const void* qI, const float* qI_scale,
+                             const float* w, const void* kI, const float* kI_scale,
+                             int scores_mode, float* scores, int64_t ld, int32_t* idx,
+                             hipStream_t s, bool* handled) {
+  *handled = false;
+  const int n_cap = sh.max_seqlen / sh.r;
+  if (sh.HI != kHI || sh.dI != kDI || sh.idx_dtype == 0 || n_cap > 64 * 64) return hipSuccess;
+  *handled = true;
+  if (sh.T == 0) return hipSuccess;
+  ScArgs a;
+  a.qI = qI;
+  a.qI_scale = qI_scale;
+  a.w = w;
+  a.kI = kI;
+  a.kI_scale = kI_scale;
+  a.cu = sh.cu;
+  a.cu_cmp = sh.cu_cmp;
+  a.scores = scores_mode != 0 ? scores : nullptr;
+  a.ld = ld;
+  a.B = sh.B;
+  a.T = sh.T;
+  a.r = sh.r;
+  a.n_cap = n_cap;
+  const dim3 grid((sh.T + 3) / 4), block(256);
+  const bool fp8 = sh.idx_dtype == 2;
+#define CSA_LAUNCH_FUSED(F, K)                                                                 \
+  hipLaunchKernelGGL((k_index_topk<F, K>), grid, block, 0, s, a, sh.k, sh.k_cap, scores_mode, idx)
+  if (n_cap <= 64 * 16) {
+    if (fp8) CSA_LAUNCH_FUSED(true, 16); else CSA_LAUNCH_FUSED(false, 16);
+  } else if (n_cap <= 64 * 32) {
+    if (fp8) CSA_LAUNCH_FUSED(true, 32); else CSA_LAUNCH_FUSED(false, 32);
+  } else {
+    if (fp8) CSA_LAUNCH_FUSED(true, 64); else CSA_LAUNCH_FUSED(false, 64);
+  }
+#undef CSA_LAUNCH_FUSED
   return hipGetLastError();
 }
 

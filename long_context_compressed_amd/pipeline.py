@@ -55,6 +55,7 @@ class CsaLayer:
                  device="cuda", backward: bool = True, grad_scale: float = 1.0):
         self.cfg = cfg
         self.timer = None          # optional object with mark(name) / done(name) around calls
+        self.fused_topk = None     # fused scores + top-k: None until the first forward tries it
         self.backward = backward
         self.grad_scale = grad_scale
         dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
@@ -144,10 +145,23 @@ class CsaLayer:
                 qI, qs, kI, ks = self.qI8, self.qI_scale, self.kI8, self.kI_scale
             else:
                 qI, qs, kI, ks = inp["qI"], None, self.kI_cmp, None
-            self._call("index_scores", B.csa_index_scores, p, qI, qs, inp["w"], kI, ks, cu_seqlens,
-                       self.cu_cmp, self.scores)
-            self._call("topk_select", B.csa_topk_select, p, self.scores, cu_seqlens, self.cu_cmp,
-                       self.idx)
+            if self.fused_topk is not False:
+                # one pass: the selection never materializes the full score matrix; the
+                # loss reads scores only where its teacher does
+                mode = {"none": 0, "selected": 1, "dense": 2}[cfg.teacher]
+                try:
+                    self._call("index_topk", B.csa_index_topk, p, qI, qs, inp["w"], kI, ks,
+                               cu_seqlens, self.cu_cmp, self.idx, self.scores, mode)
+                    self.fused_topk = True
+                except B.CsaError as e:
+                    if self.fused_topk or e.status != B.CSA_ERR_UNSUPPORTED:
+                        raise
+                    self.fused_topk = False      # no fused kernel for this shape
+            if not self.fused_topk:
+                self._call("index_scores", B.csa_index_scores, p, qI, qs, inp["w"], kI, ks,
+                           cu_seqlens, self.cu_cmp, self.scores)
+                self._call("topk_select", B.csa_topk_select, p, self.scores, cu_seqlens,
+                           self.cu_cmp, self.idx)
             idx = self.idx
         self._call("attn_fwd", B.csa_sparse_attn_fwd, p, inp["q"], self.kv_cmp, inp["kv"], idx,
                    inp.get("sink"), cu_seqlens, self.cu_cmp, self.out, self.lse, self.lse_cmp,

@@ -23,14 +23,14 @@ def _params(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = B.header_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B._SIGS)
 
 
 def test_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 3
+    assert lib.csa_abi_version() == 4
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.csa_status_string(st)
     assert lib.csa_status_string(7) == b"unknown status"
@@ -105,6 +105,29 @@ def test_scores_and_topk_validation(lib):
     assert t(ctypes.byref(p), FAKE, 10, FAKE, FAKE, FAKE, None) == B.CSA_ERR_ARG
     huge = _params(total_tokens=1 << 20, max_seqlen=1 << 20)
     assert t(ctypes.byref(huge), FAKE, 1 << 18, FAKE, FAKE, FAKE, None) == B.CSA_ERR_UNSUPPORTED
+
+
+def test_fused_index_topk_validation(lib):
+    f = lib.csa_index_topk
+    big = dict(idx_heads=64, idx_dim=128, idx_dtype=B.CSA_BF16)
+    p = _params(**big)
+    ops = [FAKE, None, FAKE, FAKE, None, FAKE, FAKE]         # qI .. cu_cmp
+
+    def call(pp, mode=0, scores=None, ld=0, idx=FAKE, ops=ops):
+        return f(ctypes.byref(pp), *ops, mode, scores, ld, idx, None)
+
+    assert call(p, idx=None) == B.CSA_ERR_NULL
+    assert call(p, mode=3) == B.CSA_ERR_ARG
+    assert call(p, mode=1) == B.CSA_ERR_NULL                   # scores wanted, none given
+    assert call(p, mode=2, scores=FAKE, ld=63) == B.CSA_ERR_ARG  # ld < n_cap = 64
+    assert call(_params(idx_dtype=B.CSA_FP8_E4M3, idx_heads=64, idx_dim=128)) == B.CSA_ERR_NULL
+    assert call(_params(topk_cap=48, **big)) == B.CSA_ERR_ARG
+    assert call(_params(topk=0, **big)) == B.CSA_ERR_ARG
+    # shapes without a fused kernel: the separate score and top-k calls serve them
+    assert call(_params()) == B.CSA_ERR_UNSUPPORTED                    # f32, 2 x 32 indexer
+    assert call(_params(idx_heads=32, idx_dim=128, idx_dtype=B.CSA_BF16)) == B.CSA_ERR_UNSUPPORTED
+    long_ = _params(total_tokens=1 << 16, max_seqlen=1 << 16, **big)  # 16384 visible > 4096
+    assert call(long_) == B.CSA_ERR_UNSUPPORTED
 
 
 def test_attention_validation(lib):

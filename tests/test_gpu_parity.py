@@ -242,6 +242,151 @@ def test_topk_ties_signed_zero_and_long_rows():
             assert np.all(got[i][n:] == -1)
 
 
+def _check_selection(got, ref_scores, row0, k, rel_tol, tag):
+    """`got` (one idx row) against fp64 oracle scores of the same query: the min(k, n_vis)
+    selected rows ascending, -1 after them, and the set equal to the oracle's top-k except
+    for swaps across the k-th score within rel_tol * max|score| (the device accumulates the
+    same products in fp32, so entries that close may order either way)."""
+    vis = np.isfinite(ref_scores)
+    nv = int(vis.sum())
+    m = min(k, nv)
+    sel = got[:m].astype(np.int64) - row0
+    assert np.all(got[m:] == -1), tag
+    assert np.all(np.diff(sel) > 0) and (m == 0 or (sel[0] >= 0 and sel[-1] < nv)), tag
+    if m == nv:
+        return 0
+    s = ref_scores[:nv]
+    order = np.lexsort((np.arange(nv), -s))        # descending score, ties to smaller j
+    ref = set(order[:m].tolist())
+    thr = s[order[m - 1]]
+    tol = rel_tol * float(np.abs(s).max())
+    extra = set(sel.tolist()) - ref
+    missing = ref - set(sel.tolist())
+    assert len(extra) == len(missing), tag
+    assert all(s[j] >= thr - tol for j in extra), (tag, "selected below the k-th score")
+    assert all(s[j] <= thr + tol for j in missing), (tag, "skipped above the k-th score")
+    return len(extra)
+
+
+@pytest.mark.parametrize("name", _idx_cases())
+def test_index_topk_fused(name):
+    """Fused scores + top-k: idx against the oracle's top-k of its fp64 scores (near-tie
+    swaps only), the score output of each mode, and agreement with the two separate calls."""
+    from long_context_compressed_amd import binding as B
+    w, host, h64 = _case(name)
+    _announce(name, "index_topk")
+    L = _layer(w, host, backward=False)
+    cu = _cu(host)
+    L.metadata(cu)
+    d, qI64, kI64 = _indexer_inputs(w, host, h64)
+    wd = host["w"].cuda()
+    args = (L.p, d["qI"], d["qI_scale"], wd, d["kI"], d["kI_scale"], cu, L.cu_cmp)
+    if w.idx_dtype == "f32" or w.idx_heads != 64 or w.idx_dim != 128:
+        with pytest.raises(B.CsaError):
+            B.csa_index_topk(*args, L.idx)
+        return
+    ref = O.index_scores(qI64, h64["w"], kI64, host["cu_seqlens"], w.ratio, L.n_cap)
+    vis = np.isfinite(ref)
+    out = {}
+    for mode in (0, 1, 2):
+        sc = torch.full_like(L.scores, 12345.0)
+        idx = torch.full_like(L.idx, -7)
+        B.csa_index_topk(*args, idx, scores=sc, scores_mode=mode)
+        torch.cuda.synchronize()
+        out[mode] = (G.back(sc), idx.cpu().numpy())
+    s2, i2 = out[2]
+    assert np.all(s2[~vis] == 12345.0), "non-visible score entries were written"
+    G.check("fused scores(visible)", s2[vis], ref[vis], "bf16")
+    assert np.array_equal(out[0][1], i2) and np.array_equal(out[1][1], i2)
+    assert np.all(out[0][0] == 12345.0), "mode 0 wrote scores"
+    s1 = out[1][0]
+    chosen = np.zeros_like(vis)
+    cu_cmp = O.cmp_seqlens(host["cu_seqlens"], w.ratio)
+    bb, _ = O.token_positions(host["cu_seqlens"], w.total_tokens)
+    swaps = 0
+    for t_ in range(w.total_tokens):
+        row0 = int(cu_cmp[bb[t_]]) if bb[t_] >= 0 else 0
+        sel = i2[t_][i2[t_] >= 0] - row0
+        chosen[t_, sel] = True
+        swaps += _check_selection(i2[t_], ref[t_], row0, w.topk, 1e-4, (name, t_))
+    assert np.array_equal(s1[chosen], s2[chosen]), "mode 1 selected scores differ from mode 2"
+    assert np.all(s1[~chosen] == 12345.0), "mode 1 wrote unselected scores"
+    print(f"[gpu] {name}: near-tie swaps {swaps}", flush=True)
+    # the separate calls on the same operands give the same selection
+    sc = torch.zeros_like(L.scores)
+    B.csa_index_scores(*args, sc)
+    idx = torch.empty_like(L.idx)
+    B.csa_topk_select(L.p, sc, cu, L.cu_cmp, idx)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), i2)
+    assert np.array_equal(G.back(sc)[vis], s2[vis])
+
+
+def _random_e4m3(rng, shape):
+    """Finite e4m3 codes with exponent fields 3..11 (magnitudes 2^-4 .. 2^4), random sign."""
+    e = rng.integers(3, 12, size=shape)
+    m = rng.integers(0, 8, size=shape)
+    s = rng.integers(0, 2, size=shape)
+    return ((s << 7) | (e << 3) | m).astype(np.uint8)
+
+
+@pytest.mark.parametrize("idx_dtype", ["bf16", "fp8"])
+def test_index_topk_fused_long_rows(idx_dtype):
+    """Rows of up to 4096 visible entries (the largest register footprint of the fused
+    kernel) in a two-sample batch, k not a multiple of 64; sampled rows against the oracle."""
+    from long_context_compressed_amd import binding as B
+    print(f"[gpu] case=index_topk_long dtype={idx_dtype}", flush=True)
+    rng = np.random.default_rng(11)
+    lengths = (16384, 2500)
+    T = sum(lengths)
+    cu = np.array([0, lengths[0], T], dtype=np.int64)
+    r, k, kcap = 4, 1000, 1024
+    n_cap = 16384 // r
+    cu_cmp = O.cmp_seqlens(cu, r)
+    n_c = int(cu_cmp[-1])
+    wts = (rng.standard_normal((T, 64)) / 8).astype(np.float32)
+    if idx_dtype == "bf16":
+        q = torch.from_numpy(rng.standard_normal((T, 64, 128), dtype=np.float32)).to(torch.bfloat16)
+        kk = torch.from_numpy(rng.standard_normal((n_c, 128), dtype=np.float32)
+                              / np.sqrt(128)).to(torch.bfloat16)
+        q64, k64 = q.double().numpy(), kk.double().numpy()
+        dq, dk, dqs, dks = q.cuda(), kk.cuda(), None, None
+        code = B.CSA_BF16
+    else:
+        qc, kc = _random_e4m3(rng, (T, 64, 128)), _random_e4m3(rng, (n_c, 128))
+        qs = rng.uniform(0.5, 2.0, (T, 64)).astype(np.float32)
+        ks = rng.uniform(0.01, 0.05, (n_c,)).astype(np.float32)
+        q64, k64 = O.dequantize_fp8(qc, qs), O.dequantize_fp8(kc, ks)
+        dq, dk = torch.from_numpy(qc).cuda(), torch.from_numpy(kc).cuda()
+        dqs, dks = torch.from_numpy(qs).cuda(), torch.from_numpy(ks).cuda()
+        code = B.CSA_FP8_E4M3
+    p = B.make_params(batch=2, total_tokens=T, max_seqlen=16384, ratio=r, window=128, topk=k,
+                      topk_cap=kcap, heads=64, head_dim=512, idx_heads=64, idx_dim=128,
+                      scale=1.0 / np.sqrt(512), mode=B.CSA_SPARSE, teacher=B.CSA_TEACHER_SELECTED,
+                      dtype=B.CSA_BF16, idx_dtype=code)
+    cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    cmp_d = torch.tensor(cu_cmp, dtype=torch.int32, device="cuda")
+    idx = torch.full((T, kcap), -7, dtype=torch.int32, device="cuda")
+    sc = torch.full((T, n_cap), 12345.0, dtype=torch.float32, device="cuda")
+    B.csa_index_topk(p, dq, dqs, torch.from_numpy(wts).cuda(), dk, dks, cu_d, cmp_d, idx,
+                     scores=sc, scores_mode=1)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(16384 - 8, 16384), [16383 - 4 * 1500, 4 * 1024 + 3,
+                           4 * 1000 + 7, 4 * 999 + 2, 4 * 700, 5000, 9999],
+                           16384 + np.array([0, 3, 4, 1500, 2499])])
+    ref = O.index_scores(q64, wts.astype(np.float64), k64, cu, r, n_cap, rows=rows)
+    got_i = idx.cpu().numpy()[rows]
+    got_s = sc.cpu().numpy().astype(np.float64)[rows]
+    for i, t_ in enumerate(rows):
+        row0 = int(cu_cmp[0 if t_ < 16384 else 1])
+        _check_selection(got_i[i], ref[i], row0, k, 1e-4, (idx_dtype, int(t_)))
+        sel = got_i[i][got_i[i] >= 0] - row0
+        G.check(f"selected scores t={t_}", got_s[i][sel], ref[i][sel], "bf16")
+        mask = np.ones(n_cap, bool)
+        mask[sel] = False
+        assert np.all(got_s[i][mask] == 12345.0), t_
+
+
 # ------------------------------------------------------------------------- attention
 def _attn_inputs(w, host, h64):
     cu = host["cu_seqlens"]
