@@ -181,8 +181,10 @@ __global__ __launch_bounds__(256) void k_index_scores_mfma(ScArgs a) {
 template <bool FP8, int KPL>
 __global__ __launch_bounds__(256) void k_index_topk(ScArgs a, int k, int k_cap, int mode,
                                                     int32_t* __restrict__ idx) {
-  __shared__ float rows[4][64 * KPL];
-  __shared__ uint32_t hist[4][4][256];
+  // each wave's score row, reused for its radix histograms once the keys are in registers
+  constexpr int kSub = 8;
+  constexpr int kRow = 64 * KPL > kSub * kHistStride ? 64 * KPL : kSub * kHistStride;
+  __shared__ __attribute__((aligned(16))) float rows[4][kRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= a.T) return;
@@ -210,10 +212,11 @@ __global__ __launch_bounds__(256) void k_index_topk(ScArgs a, int k, int k_cap, 
   __builtin_amdgcn_wave_barrier();
   const int n_it = __builtin_amdgcn_readfirstlane((nv + 63) >> 6);
   float* sel = mode == 1 ? srow : nullptr;
-  if (KPL >= 16 && n_it <= 16) topk_row_wave<16>(lrow, nv, n_it, k, row0, out, hist[wave], sel);
-  else if (KPL >= 32 && n_it <= 32) topk_row_wave<32>(lrow, nv, n_it, k, row0, out, hist[wave], sel);
-  else if (KPL >= 48 && n_it <= 48) topk_row_wave<48>(lrow, nv, n_it, k, row0, out, hist[wave], sel);
-  else topk_row_wave<(KPL > 48 ? 64 : KPL)>(lrow, nv, n_it, k, row0, out, hist[wave], sel);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(lrow);
+  if (KPL >= 16 && n_it <= 16) topk_row_wave<16, kSub>(lrow, nv, n_it, k, row0, out, hist, sel);
+  else if (KPL >= 32 && n_it <= 32) topk_row_wave<32, kSub>(lrow, nv, n_it, k, row0, out, hist, sel);
+  else if (KPL >= 48 && n_it <= 48) topk_row_wave<48, kSub>(lrow, nv, n_it, k, row0, out, hist, sel);
+  else topk_row_wave<(KPL > 48 ? 64 : KPL), kSub>(lrow, nv, n_it, k, row0, out, hist, sel);
   for (int c = k + lane; c < k_cap; c += 64) out[c] = -1;
 }
 

@@ -22,6 +22,7 @@ namespace csa {
 using attn::token_info_wave;
 
 constexpr int kTopkThreads = 512;
+constexpr int kTopkSub = 8;   // sub-histograms per wave
 
 template <int ITEMS>
 __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ scores,
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(256) void k_topk_wave(const float* __restrict__ sco
                                                    const int32_t* __restrict__ cu_cmp, int B,
                                                    int r, int n_cap, int k, int k_cap, int T,
                                                    int32_t* __restrict__ idx) {
-  __shared__ uint32_t hist_all[4][4][256];
+  __shared__ __attribute__((aligned(16))) uint32_t hist_all[4][kTopkSub * kHistStride];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
@@ -152,10 +153,10 @@ __global__ __launch_bounds__(256) void k_topk_wave(const float* __restrict__ sco
   }
   const int n_it = __builtin_amdgcn_readfirstlane((nv + 63) >> 6);
   const float* row = scores + (int64_t)t * ld;
-  if (KPL >= 16 && n_it <= 16) topk_row_wave<16>(row, nv, n_it, k, row0, out, hist_all[wave], nullptr);
-  else if (KPL >= 32 && n_it <= 32) topk_row_wave<32>(row, nv, n_it, k, row0, out, hist_all[wave], nullptr);
-  else if (KPL >= 48 && n_it <= 48) topk_row_wave<48>(row, nv, n_it, k, row0, out, hist_all[wave], nullptr);
-  else topk_row_wave<(KPL > 48 ? 64 : KPL)>(row, nv, n_it, k, row0, out, hist_all[wave], nullptr);
+  if (KPL >= 16 && n_it <= 16) topk_row_wave<16, kTopkSub>(row, nv, n_it, k, row0, out, hist_all[wave], nullptr);
+  else if (KPL >= 32 && n_it <= 32) topk_row_wave<32, kTopkSub>(row, nv, n_it, k, row0, out, hist_all[wave], nullptr);
+  else if (KPL >= 48 && n_it <= 48) topk_row_wave<48, kTopkSub>(row, nv, n_it, k, row0, out, hist_all[wave], nullptr);
+  else topk_row_wave<(KPL > 48 ? 64 : KPL), kTopkSub>(row, nv, n_it, k, row0, out, hist_all[wave], nullptr);
   for (int c = k + lane; c < k_cap; c += 64) out[c] = -1;
 }
 
