@@ -72,6 +72,12 @@ __device__ __forceinline__ void dma_row16(const void* src, const void* lds_row) 
                :: "s"(lds), "v"(src) : "memory", "m0");
 }
 
+// The same with the row address as a scalar base plus a per-lane byte offset (saddr form).
+__device__ __forceinline__ void dma_row16_s(uint64_t row, uint32_t lane_off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(lane_off), "s"(row) : "memory", "m0");
+}
+
 }  // namespace
 
 // NW waves per query: NW/2 candidate groups of CPW = 128/NW candidates for S^T, and d slices
@@ -181,6 +187,16 @@ void k_attn_fwd_mfma(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < RPW; ++j) issue_row(rid, buf, j);
   };
+  // the next block's rows are gathered one per S^T k-step, so the loads overlap the MFMAs
+  // instead of stalling the wave at the block start: lane l holds the source of slot l, row
+  // RPW wave + j is read with two lane reads; swz(row) depends on the row's low 4 bits only
+  static_assert(RPW == 16, "one row per S^T k-step");
+  const uint32_t lane16 = 16u * (uint32_t)lane;
+  const uint32_t tile_lds = (uint32_t)(uintptr_t)&tile[0][0][0];
+  auto row_addr = [&](int rid) {
+    return (uint64_t)(uintptr_t)(rid >= 0 ? a.kv_cmp + (int64_t)rid * kD
+                                          : a.kv + (int64_t)(rid == -1 ? t : -2 - rid) * kD);
+  };
 
   int rid_cur = rid_of(0, raw_cur);
   int rid_nxt = rid_of(1, raw_nxt);
@@ -191,7 +207,16 @@ void k_attn_fwd_mfma(FwdArgs a) {
   for (int b = 0; b < nblk; ++b) {
     const int buf = b & 1;
     const uint64_t valid = __ballot(rid_cur != -1);
-    if (b + 1 < nblk) issue(rid_nxt, buf ^ 1);
+    const bool more = b + 1 < nblk;
+    const uint64_t nsrc = row_addr(rid_nxt);
+    const uint32_t nlds = __builtin_amdgcn_readfirstlane(tile_lds + (buf ^ 1) * (kNB * kD * 2) +
+                                                         RPW * wave * (kD * 2));
+    auto gather = [&](int j) {   // row RPW wave + j of the next block
+      const int r = RPW * wave + j;
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)nsrc, r);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(nsrc >> 32), r);
+      dma_row16_s(((uint64_t)hi << 32) | lo, lane16 ^ (16u * swz(j)), nlds + j * (kD * 2));
+    };
     const int raw_nn = raw_of(b + 2);   // consumed after this block's final wait
 
     // ---- S^T: candidates CPW ch + 16 mq + 4g + i, heads 32hh + 16nt + c16
@@ -216,6 +241,7 @@ void k_attn_fwd_mfma(FwdArgs a) {
           st[mq][0] = mfma16(av[ks % kPre][mq], qb[0][ks], st[mq][0]);
           st[mq][1] = mfma16(av[ks % kPre][mq], qb[1][ks], st[mq][1]);
         }
+        if (more) gather(ks);
         if (ks + kPre < 16) {
 #pragma unroll
           for (int mq = 0; mq < MQ; ++mq) av[ks % kPre][mq] = seg(ks + kPre, mq);
@@ -330,6 +356,7 @@ void k_attn_fwd_mfma(FwdArgs a) {
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) pb[1][nt] = ld16(&Ps[16 * nt + c16][32 + 8 * g]);
         }
+
       }
       __builtin_amdgcn_sched_barrier(0);
     }
