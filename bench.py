@@ -58,6 +58,12 @@ CALL_KERNELS = {
     "attn_fwd": ("k_attn_fwd_mfma", "k_attn_fwd_generic"),
     "indexer_kl": ("k_kl_cached", "k_fill_zero_i32", "k_csr_pairs", "k_csr_scan", "k_csr_reduce",
                    "k_indexer_kl_mfma", "k_kl_generic", "k_sum"),
+    "index_topk": ("k_index_topk",),
+    "index_scores": ("k_index_scores_mfma", "k_index_scores_generic"),
+    "topk_select": ("k_topk_wave", "k_topk"),
+    "quantize": ("k_quantize_fp8",),
+    "compress (kv + kI)": ("k_compress",),
+    "compress_bwd (kv + kI)": ("k_compress_bwd",),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "thd64k_csa_bf16_traffic.md")
 
