@@ -7,13 +7,9 @@
 
 namespace csa {
 
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;                       // -0 and +0 are the same value
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // ascending float <=> ascending key
-}
-
-__device__ __forceinline__ float key_value(uint32_t key) {   // inverse of order_key
+// Keys: u = bits of (score + 0) (so -0 becomes +0), key = u ^ (sign ? 0xffffffff : 0x80000000),
+// ascending in the score; key_value inverts it.
+__device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
