@@ -262,8 +262,10 @@ __global__ __launch_bounds__(256) void k_sum(const float* __restrict__ x, int n,
 
 hipError_t launch_indexer_kl_mfma(const Shape& sh, const KlIO& io, hipStream_t s, bool* handled);
 hipError_t launch_indexer_kl_cached(const Shape& sh, const KlIO& io, hipStream_t s, bool* handled);
+hipError_t launch_indexer_kl_dense(const Shape& sh, const KlIO& io, hipStream_t s, bool* handled);
+size_t indexer_kl_dense_workspace(const Shape& sh);
 
-size_t indexer_kl_workspace(const Shape& sh) { (void)sh; return 0; }
+size_t indexer_kl_workspace(const Shape& sh) { return indexer_kl_dense_workspace(sh); }
 
 hipError_t launch_indexer_kl(const Shape& sh, const KlIO& io, hipStream_t s) {
   if (sh.T == 0) {
@@ -272,6 +274,7 @@ hipError_t launch_indexer_kl(const Shape& sh, const KlIO& io, hipStream_t s) {
   }
   bool handled = false;
   hipError_t e = launch_indexer_kl_cached(sh, io, s, &handled);
+  if (!handled && !io.t_logits) e = launch_indexer_kl_dense(sh, io, s, &handled);
   if (!handled) e = launch_indexer_kl_mfma(sh, io, s, &handled);
   if (!handled) {
     KlK a;

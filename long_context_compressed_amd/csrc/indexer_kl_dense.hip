@@ -1,0 +1,744 @@
+// Indexer KL loss with the dense (all visible compressed entries) teacher recomputed, for
+// bf16 main operands (H = 64, D = 512) and a 64 x 128 indexer in bf16 or fp8, on gfx950.
+//
+// "DeepSeek-V4 Attention Training Systems", section 3: in the dense-loss warm-up the KL
+// set C_t is the whole visible compressed history; the teacher is detached and the
+// gradients reach the indexer query, head weights and indexer keys only.  Section 8.2:
+// teacher scores are recomputed and the indexer backward runs eagerly, scaled by the
+// caller's loss scale.  Teacher reading: P_t = mean over heads of the per-head softmax.
+//
+// The dense teacher costs 2 D H FLOP per (query, visible entry) and pass, against 1 KiB
+// of key row: read per query, as the selected-set kernels do, it is bound by the row
+// gathers.  Here the work is split three ways so each shared operand is read once per
+// tile instead of once per (query, entry):
+//   k_kld_teacher  one workgroup per 4 consecutive queries of one sample, one query per
+//                  wave with its 64 x 512 Q resident; each 64-row key block is loaded once
+//                  into LDS (direct global->LDS loads, one row per S^T k-step, a block
+//                  ahead) and feeds all 4 queries.  Pass 1: per-head online log-sum-exp
+//                  of the teacher and the student log-sum-exp; pass 2: P (head mean), Q,
+//                  KL_t and g = grad_scale (Q - P), written to the workspace.
+//   k_kld_queries  the same 4-query groups, one query per wave with its qI resident; each
+//                  64-key block of kI is staged once into LDS for the 4 queries; z^T, E =
+//                  g w 1[z > 0] (kept in registers as the A operand), dw and dqI = E kI.
+//   k_kld_keys     one workgroup per (64-key block, query range): kI block in LDS, one
+//                  query per wave; z, E and dkI += E^T qI accumulate in registers over the
+//                  range, one fp32 atomic add per key element and wave at the end.
+// Queries are processed in chunks of kChunkRows (the workspace holds g for one chunk).
+#include <math.h>
+
+#include "attn_common.h"
+#include "csa_launch.h"
+
+// M0 is named as clobbered by the LDS-DMA asm below; the compiler keeps no value in it here.
+#pragma clang diagnostic ignored "-Winline-asm"
+
+namespace csa {
+
+using namespace attn;
+
+namespace {
+
+constexpr int kHI = 64, kDI = 128;
+constexpr int kKB = 64;            // key rows per block
+constexpr int kChunkRows = 8192;   // queries per chunk
+constexpr int kRange = 512;        // queries per key-gradient workgroup
+constexpr int kIS = kDI + 8;       // bf16 row stride of the indexer tiles
+constexpr int kI8S = kDI + 16;     // byte row stride of the fp8 code tiles
+constexpr float kLazy = 8.f;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+struct KldArgs {
+  const uint16_t* q;
+  const uint16_t* kv_cmp;
+  const float* scores;
+  int64_t ld;
+  const void* qI;
+  const float* qI_scale;
+  const uint16_t* qI16;   // bf16 indexer query rows from q16_t0 (the dequantized copy for fp8)
+  int q16_t0;
+  const float* w;
+  const void* kI;
+  const float* kI_scale;
+  const uint16_t* kI16;   // fp8: bf16 copy of the indexer keys
+  const int32_t* cu;
+  const int32_t* cu_cmp;
+  float* g;               // [kChunkRows, n_cap]: g of query t at row t - t_lo
+  float* kl;
+  float* dqI;
+  float* dw;
+  float* dkI;
+  float gs, scale_log2;
+  int B, T, r, n_cap, t_lo, t_hi, tc_blocks, fp8;
+};
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// One 16-byte-per-lane global -> LDS load: lane l's 16 bytes (scalar row base + per-lane
+// offset) land at LDS byte address lds + 16 l.  Completion is awaited with wait_vmem().
+__device__ __forceinline__ void dma_row16_s(uint64_t row, uint32_t lane_off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(lane_off), "s"(row) : "memory", "m0");
+}
+
+// The queries of workgroup bid of a chunk: regular groups are 4 consecutive queries from a
+// 4-aligned row t0, cut at the end of t0's sample; the first (unaligned) queries of sample
+// b = bid - kChunkRows / 4 form one more group.  Every query of the chunk falls in exactly
+// one group, and a group never spans two samples.
+__device__ __forceinline__ bool query_group(const KldArgs& a, int bid, int& t_first, int& n,
+                                            TokenInfo& ti) {
+  int t0, lim;
+  if (bid < kChunkRows / 4) {
+    t0 = a.t_lo + 4 * bid;
+    if (t0 >= a.t_hi || !token_info(a.cu, a.B, t0, ti)) return false;
+    lim = min(t0 + 4, ti.start + ti.len);
+  } else {
+    const int b = bid - kChunkRows / 4;
+    if (b >= a.B) return false;
+    const int s = a.cu[b], e = a.cu[b + 1];
+    if ((s & 3) == 0 || s == e || s < a.t_lo || s >= a.t_hi) return false;
+    t0 = s;
+    lim = min((s + 3) & ~3, e);
+    if (!token_info(a.cu, a.B, t0, ti)) return false;
+  }
+  t_first = t0;
+  n = min(lim, a.t_hi) - t0;
+  return n > 0;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------- teacher
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_kld_teacher(KldArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kKB][kD];
+  __shared__ float Is[4][kKB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  if ((int)blockIdx.x < kChunkRows / 4 && tid < 4) {   // capacity padding rows: kl = 0
+    const int u = a.t_lo + 4 * blockIdx.x + tid;
+    if (u < a.t_hi && u >= a.cu[a.B]) a.kl[u] = 0.f;
+  }
+  int t_first, n_tok;
+  TokenInfo ti;
+  if (!query_group(a, blockIdx.x, t_first, n_tok, ti)) return;
+  const bool active = wave < n_tok;
+  const int t = t_first + (active ? wave : 0);
+  const int row0 = __builtin_amdgcn_readfirstlane(a.cu_cmp[ti.b]);
+  const int nv_w = active ? min((ti.p + wave + 1) / a.r, a.n_cap) : 0;
+  const int nv_max = __builtin_amdgcn_readfirstlane(min((ti.p + n_tok) / a.r, a.n_cap));
+  if (nv_max == 0) {
+    if (active && lane == 0) a.kl[t] = 0.f;
+    return;
+  }
+  const int nblk = (nv_max + kKB - 1) / kKB;
+  const float* srow = a.scores + (int64_t)t * a.ld;
+  float* grow = a.g + (int64_t)(t - a.t_lo) * a.n_cap;
+
+  // Q^T as the B operand: qb[nt][ks] = Q[16 nt + c16][32 ks + 8 g .. +7] of this wave's query
+  bf16x8 qb[4][16];
+  {
+    const uint16_t* qt = a.q + ((int64_t)t * kH + c16) * kD + 8 * g;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) qb[nt][ks] = ld16(qt + 16 * nt * kD + 32 * ks);
+  }
+
+  // key rows of a block: row 16 wave + j of block jb is visible row 64 jb + 16 wave + j
+  // (row0 for slots past the last query's visible range: finite, masked below)
+  const uint32_t lane16 = 16u * (uint32_t)lane;
+  const uint32_t tile_lds = (uint32_t)(uintptr_t)&tile[0][0][0];
+  auto gather = [&](int jb, int buf, int j) {
+    const int key = kKB * jb + 16 * wave + j;
+    const int row = __builtin_amdgcn_readfirstlane(row0 + (key < nv_max ? key : 0));
+    const uint64_t src = (uint64_t)(uintptr_t)(a.kv_cmp + (int64_t)row * kD);
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(tile_lds + buf * (kKB * kD * 2) +
+                                                        (16 * wave + j) * (kD * 2));
+    dma_row16_s(src, lane16 ^ (16u * swz(j)), lds);
+  };
+  int eq[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) eq[q] = 8 * ((4 * q + g) ^ swz(c16));
+
+  // pass-1 state: per-head (m, l) of the 4 heads 16 nt + c16 over this lane's keys, and the
+  // student (m, l) over the whole row (the same in every lane)
+  float m_run[4], l_run[4], lse2[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) { m_run[nt] = -INFINITY; l_run[nt] = 0.f; lse2[nt] = 0.f; }
+  float ms = -INFINITY, lsum = 0.f, lseS = 0.f, kl_acc = 0.f;
+
+  for (int j = 0; j < 16; ++j) gather(0, 0, j);
+  wait_vmem();
+  __syncthreads();
+
+  const int n_items = 2 * nblk;
+  for (int it = 0; it < n_items; ++it) {
+    const int buf = it & 1;
+    const bool pass2 = it >= nblk;
+    const int jb = pass2 ? it - nblk : it;
+    const bool more = it + 1 < n_items;
+    const int jb_next = it + 1 == nblk ? 0 : jb + 1;
+
+    // scores of this block's keys (one per lane, coalesced), for the student
+    {
+      const int j = kKB * jb + lane;
+      Is[wave][lane] = j < nv_w ? srow[j] : -INFINITY;
+      __builtin_amdgcn_wave_barrier();
+    }
+
+    // ---- S^T[key 16 mt + 4 g + i][head 16 nt + c16] over the block
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      const uint16_t* rb = &tile[buf][c16][0];
+      auto seg = [&](int ks, int mt) { return ld16(rb + 16 * mt * kD + 128 * (ks >> 2) + eq[ks & 3]); };
+      bf16x8 av[2][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) av[0][mt] = seg(0, mt);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + 1 < 16) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) av[(ks + 1) & 1][mt] = seg(ks + 1, mt);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma16(av[ks & 1][mt], qb[nt][ks], acc[mt][nt]);
+        if (more) gather(jb_next, buf ^ 1, ks);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int kbase = kKB * jb + 4 * g;
+    if (!pass2) {
+      // ---- teacher: lazily rescaled online (max, sum) per head in log2 units
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        float s[16];
+        float bm = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = kbase + 16 * mt + i < nv_w ? acc[mt][nt][i] * a.scale_log2 : -INFINITY;
+            s[4 * mt + i] = v;
+            bm = fmaxf(bm, v);
+          }
+        if (bm > m_run[nt] + kLazy) {
+          l_run[nt] *= __builtin_amdgcn_exp2f(m_run[nt] - bm);
+          m_run[nt] = bm;
+        }
+        if (m_run[nt] != -INFINITY) {
+          float add = 0.f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) add += __builtin_amdgcn_exp2f(s[e] - m_run[nt]);
+          l_run[nt] += add;
+        }
+      }
+      // ---- student: online (max, sum) of the scores (natural log), lane = key
+      {
+        const float iv = Is[wave][lane];
+        const float bm = wave_max(iv);
+        if (bm > ms) {
+          lsum = ms == -INFINITY ? 0.f : lsum * expf(ms - bm);
+          ms = bm;
+        }
+        if (ms != -INFINITY) lsum += wave_sum(iv == -INFINITY ? 0.f : expf(iv - ms));
+      }
+      if (it == nblk - 1) {
+        // merge the 4 lane groups of each head; the student normalizer to every lane
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+          for (int o = 16; o <= 32; o <<= 1) {
+            const float mo = __shfl_xor(m_run[nt], o, 64), lo = __shfl_xor(l_run[nt], o, 64);
+            const float mn = fmaxf(m_run[nt], mo);
+            if (mn != -INFINITY) {
+              l_run[nt] = l_run[nt] * __builtin_amdgcn_exp2f(m_run[nt] - mn) +
+                          lo * __builtin_amdgcn_exp2f(mo - mn);
+              m_run[nt] = mn;
+            }
+          }
+          lse2[nt] = l_run[nt] > 0.f ? m_run[nt] + __log2f(l_run[nt]) : INFINITY;
+        }
+        lseS = lsum > 0.f ? ms + logf(lsum) : INFINITY;
+      }
+    } else {
+      // ---- P = mean over heads of exp2(s - lse2); Q, KL and g for this block's keys
+      float ps[16];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float p = 0.f;
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+            p += __builtin_amdgcn_exp2f(acc[mt][nt][i] * a.scale_log2 - lse2[nt]);
+          ps[4 * mt + i] = p;
+        }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) ps[e] += __shfl_xor(ps[e], o, 64);
+      }
+      if (c16 == 0) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kj = 16 * mt + 4 * g + i;   // key within the block
+            float gv = 0.f;
+            if (kKB * jb + kj < nv_w) {
+              const float P = ps[4 * mt + i] * (1.f / kH);
+              const float logQ = Is[wave][kj] - lseS;
+              const float Q = expf(logQ);
+              if (P > 0.f) kl_acc += P * (logf(P) - logQ);
+              gv = a.gs * (Q - P);
+            }
+            Is[wave][kj] = gv;   // this wave's slot, read back below as a row
+          }
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int j = kKB * jb + lane;
+      if (active && j < nv_w) grow[j] = Is[wave][lane];
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+  if (active) {
+    float v = kl_acc;
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    if (lane == 0) a.kl[t] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------- dkI
+// Workgroup (x, y): key block x (64 rows of one sample: regular blocks start at 64-aligned
+// rows and stop at the sample end; block tc_blocks + b holds the first unaligned rows of
+// sample b), queries y kRange .. of the chunk that see its first key.  One query per wave.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_kld_keys(KldArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t KIt[kKB][kIS];
+  __shared__ __attribute__((aligned(16))) uint8_t KI8[kKB][kI8S];
+  __shared__ float ksc_s[kKB];
+  __shared__ __attribute__((aligned(16))) uint16_t QIt[4][kHI][kIS];
+  __shared__ __attribute__((aligned(16))) uint8_t QI8[4][kHI][kI8S];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int Tc = a.cu_cmp[a.B];
+  int r_lo, r_hi, b;
+  if ((int)blockIdx.x < a.tc_blocks) {
+    r_lo = kKB * blockIdx.x;
+    if (r_lo >= Tc) return;
+    b = upper_bound_i32(a.cu_cmp, a.B + 1, r_lo) - 1;
+    r_hi = min(r_lo + kKB, a.cu_cmp[b + 1]);
+  } else {
+    b = blockIdx.x - a.tc_blocks;
+    if (b >= a.B) return;
+    r_lo = a.cu_cmp[b];
+    r_hi = min((r_lo + kKB - 1) & ~(kKB - 1), a.cu_cmp[b + 1]);
+    if ((r_lo & (kKB - 1)) == 0 || r_hi <= r_lo) return;
+  }
+  const int s_b = a.cu[b], e_b = a.cu[b + 1];
+  const int jl0 = r_lo - a.cu_cmp[b];                 // first key, local to the sample
+  const int t_min = s_b + a.r * (jl0 + 1) - 1;        // first query that sees it
+  const int q_lo = max(max(t_min, a.t_lo + kRange * (int)blockIdx.y), s_b);
+  const int q_hi = min(min(e_b, a.t_hi), a.t_lo + kRange * ((int)blockIdx.y + 1));
+  if (q_lo >= q_hi) return;
+  const int nk = r_hi - r_lo;
+
+  // key block: bf16 rows (or fp8 codes and scales), rows past nk zero
+  for (int e = tid; e < kKB * (kDI / 8); e += 256) {
+    const int row = e >> 4, ch = e & 15;
+    if (!a.fp8) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < nk) v = *reinterpret_cast<const uint4*>((const uint16_t*)a.kI + (int64_t)(r_lo + row) * kDI + 8 * ch);
+      *reinterpret_cast<uint4*>(&KIt[row][8 * ch]) = v;
+    } else {
+      uint2 v = make_uint2(0, 0);
+      if (row < nk) v = *reinterpret_cast<const uint2*>((const uint8_t*)a.kI + (int64_t)(r_lo + row) * kDI + 8 * ch);
+      *reinterpret_cast<uint2*>(&KI8[row][8 * ch]) = v;
+      if (ch == 0) ksc_s[row] = row < nk ? a.kI_scale[r_lo + row] : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // dkI^T partial sums: acc[nt][dt] = rows 16 nt + 4 g + i, columns 16 dt + c16
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int jr = c16 >> 2, jc = 4 * (c16 & 3);
+
+  for (int t0 = q_lo; t0 < q_hi; t0 += 4) {
+    const int t = t0 + wave;
+    const bool act = t < q_hi;
+    const int tq = act ? t : q_lo;
+    // this query's indexer query tile into the wave's LDS slot
+    for (int e = lane; e < kHI * (kDI / 8); e += 64) {
+      const int hh = e >> 4, ch = e & 15;
+      *reinterpret_cast<uint4*>(&QIt[wave][hh][8 * ch]) =
+          *reinterpret_cast<const uint4*>(a.qI16 + ((int64_t)(tq - a.q16_t0) * kHI + hh) * kDI + 8 * ch);
+      if (a.fp8)
+        *reinterpret_cast<uint2*>(&QI8[wave][hh][8 * ch]) =
+            *reinterpret_cast<const uint2*>((const uint8_t*)a.qI + ((int64_t)tq * kHI + hh) * kDI + 8 * ch);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    const int nv_t = act ? min((tq - s_b + 1) / a.r, a.n_cap) : 0;
+    const float* gr = a.g + (int64_t)(tq - a.t_lo) * a.n_cap + jl0;
+    float wv[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[mt][i] = a.w[(int64_t)tq * kHI + 16 * mt + 4 * g + i];
+    // z[head 16 mt + 4 g + i][key 16 nt + c16] (the ReLU mask needs only its sign, so fp8
+    // codes need no scales), then E = g w 1[z > 0] as bf16 A operands of the dkI product:
+    // k-step ks takes head tiles 2 ks (k-slots 8g..8g+3) and 2 ks + 1 (8g+4..8g+7); the qI
+    // rows are read transposed in the same order
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int kj = 16 * nt + c16;
+      const float gv = (act && kj < nk && jl0 + kj < nv_t) ? gr[kj] : 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        uint32_t e4[4];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int mt = 2 * ks + h2;
+          f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (!a.fp8) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+              z = mfma16(ld16(&QIt[wave][16 * mt + c16][32 * kk + 8 * g]),
+                         ld16(&KIt[16 * nt + c16][32 * kk + 8 * g]), z);
+          } else {
+            const uint4* qp = reinterpret_cast<const uint4*>(&QI8[wave][16 * mt + c16][32 * g]);
+            const uint4* kp = reinterpret_cast<const uint4*>(&KI8[16 * nt + c16][32 * g]);
+            const uint4 q0 = qp[0], q1 = qp[1], k0 = kp[0], k1 = kp[1];
+            z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                i32x8{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w},
+                i32x8{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w},
+                z, 0, 0, 0, 127, 0, 127);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const float e0 = z[i] > 0.f ? gv * wv[mt][i] : 0.f;
+            const float e1 = z[i + 1] > 0.f ? gv * wv[mt][i + 1] : 0.f;
+            e4[2 * h2 + (i >> 1)] = pack_bf16x2(e0, e1);
+          }
+        }
+        const bf16x8 ea = __builtin_bit_cast(bf16x8, make_uint4(e4[0], e4[1], e4[2], e4[3]));
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const v4i16 lo = ld_tr(&QIt[wave][32 * ks + 4 * g + jr][16 * dt + jc]);
+          const v4i16 hi = ld_tr(&QIt[wave][32 * ks + 16 + 4 * g + jr][16 * dt + jc]);
+          acc[nt][dt] = mfma16(ea, join8(lo, hi), acc[nt][dt]);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  // each wave adds its partial sums (rows past the block are zero and skipped)
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kj = 16 * nt + 4 * g + i;
+      if (kj < nk) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          atomicAdd(a.dkI + (int64_t)(r_lo + kj) * kDI + 16 * dt + c16, acc[nt][dt][i]);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------- dqI, dw
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_kld_queries(KldArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t KIt[2][kKB][kIS];
+  __shared__ __attribute__((aligned(16))) uint8_t KI8[2][kKB][kI8S];
+  __shared__ float ksc_s[2][kKB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  if ((int)blockIdx.x < kChunkRows / 4) {   // capacity padding rows: dqI = 0, dw = 0
+    const int u = a.t_lo + 4 * blockIdx.x + wave;
+    if (u < a.t_hi && u >= a.cu[a.B]) {
+      for (int e = lane; e < kHI * kDI; e += 64) a.dqI[(int64_t)u * kHI * kDI + e] = 0.f;
+      a.dw[(int64_t)u * kHI + lane] = 0.f;
+    }
+  }
+  int t_first, n_tok;
+  TokenInfo ti;
+  if (!query_group(a, blockIdx.x, t_first, n_tok, ti)) return;
+  const bool active = wave < n_tok;
+  const int t = t_first + (active ? wave : 0);
+  const int row0 = a.cu_cmp[ti.b];
+  const int nv_w = active ? min((ti.p + wave + 1) / a.r, a.n_cap) : 0;
+  const int nv_max = min((ti.p + n_tok) / a.r, a.n_cap);
+  const int nblk = (nv_max + kKB - 1) / kKB;
+  const float* grow = a.g + (int64_t)(t - a.t_lo) * a.n_cap;
+
+  // resident: qI^T as B operands (heads 16 nt + c16), head weights, fp8 row scales
+  bf16x8 qb[4][4];
+  i32x8 q8[4];
+  float wv[4], qsc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int h = 16 * nt + c16;
+    wv[nt] = a.w[(int64_t)t * kHI + h];
+    if (!a.fp8) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qb[nt][ks] = ld16((const uint16_t*)a.qI + ((int64_t)t * kHI + h) * kDI + 32 * ks + 8 * g);
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>((const uint8_t*)a.qI + ((int64_t)t * kHI + h) * kDI + 32 * g);
+      const uint4 lo = p[0], hi = p[1];
+      q8[nt] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      qsc[nt] = a.qI_scale[(int64_t)t * kHI + h];
+    }
+  }
+
+  // kI block jb: 64 rows of 16-byte chunks, 4 per thread (bf16 rows: the fp8 path reads the
+  // dequantized copy), fp8 codes 2 per thread and the row scales; rows past the last visible
+  // key repeat row0 (finite; their g is 0)
+  uint4 pre[4], pre8[2];
+  float pre_s = 0.f;
+  const uint16_t* kI16 = a.fp8 ? a.kI16 : (const uint16_t*)a.kI;
+  auto fetch = [&](int jb) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 256 * u, row = e >> 4, ch = e & 15;
+      const int key = kKB * jb + row;
+      pre[u] = *reinterpret_cast<const uint4*>(kI16 + (int64_t)(row0 + (key < nv_max ? key : 0)) * kDI + 8 * ch);
+    }
+    if (a.fp8) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = tid + 256 * u, row = e >> 3, ch = e & 7;
+        const int key = kKB * jb + row;
+        pre8[u] = *reinterpret_cast<const uint4*>((const uint8_t*)a.kI + (int64_t)(row0 + (key < nv_max ? key : 0)) * kDI + 16 * ch);
+      }
+      if (tid < kKB) {
+        const int key = kKB * jb + tid;
+        pre_s = a.kI_scale[row0 + (key < nv_max ? key : 0)];
+      }
+    }
+  };
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 256 * u, row = e >> 4, ch = e & 15;
+      *reinterpret_cast<uint4*>(&KIt[buf][row][8 * ch]) = pre[u];
+    }
+    if (a.fp8) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = tid + 256 * u, row = e >> 3, ch = e & 7;
+        *reinterpret_cast<uint4*>(&KI8[buf][row][16 * ch]) = pre8[u];
+      }
+      if (tid < kKB) ksc_s[buf][tid] = pre_s;
+    }
+  };
+
+  f32x4 acc[4][8];   // dqI: heads 16 nt + 4 g + i, d 16 dt + c16
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dwp[4] = {0.f, 0.f, 0.f, 0.f};
+  const int jr = c16 >> 2, jc = 4 * (c16 & 3);
+
+  if (nblk > 0) {
+    fetch(0);
+    commit(0);
+  }
+  for (int jb = 0; jb < nblk; ++jb) {
+    const int buf = jb & 1;
+    __syncthreads();
+    if (jb + 1 < nblk) fetch(jb + 1);
+    // g of keys 16 mt + 4 g + i of the block for this wave's query (0 past its visible range)
+    float gk[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = kKB * jb + 16 * mt + 4 * g + i;
+        gk[mt][i] = j < nv_w ? grow[j] : 0.f;
+      }
+    // z^T[key 16 mt + 4 g + i][head 16 nt + c16]; E as the A operand of dqI = E kI with
+    // k-step ks over key tiles 2 ks (k-slots 8g..8g+3) and 2 ks + 1 (8g+4..8g+7)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        uint32_t e4[4];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int mt = 2 * ks + h2;
+          f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (!a.fp8) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+              z = mfma16(ld16(&KIt[buf][16 * mt + c16][32 * kk + 8 * g]), qb[nt][kk], z);
+          } else {
+            const uint4* kp = reinterpret_cast<const uint4*>(&KI8[buf][16 * mt + c16][32 * g]);
+            const uint4 k0 = kp[0], k1 = kp[1];
+            z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                i32x8{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w},
+                q8[nt], z, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[i] = z[i] * ksc_s[buf][16 * mt + 4 * g + i] * qsc[nt];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            dwp[nt] = fmaf(gk[mt][i], fmaxf(z[i], 0.f), dwp[nt]);
+            dwp[nt] = fmaf(gk[mt][i + 1], fmaxf(z[i + 1], 0.f), dwp[nt]);
+            const float e0 = z[i] > 0.f ? gk[mt][i] * wv[nt] : 0.f;
+            const float e1 = z[i + 1] > 0.f ? gk[mt][i + 1] * wv[nt] : 0.f;
+            e4[2 * h2 + (i >> 1)] = pack_bf16x2(e0, e1);
+          }
+        }
+        const bf16x8 ea = __builtin_bit_cast(bf16x8, make_uint4(e4[0], e4[1], e4[2], e4[3]));
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const v4i16 lo = ld_tr(&KIt[buf][32 * ks + 4 * g + jr][16 * dt + jc]);
+          const v4i16 hi = ld_tr(&KIt[buf][32 * ks + 16 + 4 * g + jr][16 * dt + jc]);
+          acc[nt][dt] = mfma16(ea, join8(lo, hi), acc[nt][dt]);
+        }
+      }
+    }
+    if (jb + 1 < nblk) commit(buf ^ 1);
+  }
+  if (!active) return;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    float v = dwp[nt];
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    if (g == 0) a.dw[(int64_t)t * kHI + 16 * nt + c16] = v;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a.dqI[((int64_t)t * kHI + 16 * nt + 4 * g + i) * kDI + 16 * dt + c16] = acc[nt][dt][i];
+  }
+}
+
+// bf16 copy of fp8 rows of d_I codes (code * row scale, rounded once): rows row_lo ..
+// row_lo + n_rows - 1 (at most *n_max of them when n_max is given) to out[(row - row_lo) d_I]
+__global__ __launch_bounds__(256) void k_kld_dequant(const uint8_t* __restrict__ codes,
+                                                    const float* __restrict__ scale,
+                                                    int64_t row_lo, int64_t n_rows,
+                                                    const int32_t* __restrict__ n_max,
+                                                    uint16_t* __restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 8 elements each
+  const int64_t rows = n_max ? min(n_rows, (int64_t)*n_max - row_lo) : n_rows;
+  if (e >= rows * (kDI / 8)) return;
+  const int64_t src = row_lo * kDI + 8 * e;
+  const uint2 c = *reinterpret_cast<const uint2*>(codes + src);
+  const float s = scale[src / kDI];
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t wd = i < 2 ? c.x : c.y;
+    const uint32_t b0 = (wd >> (16 * (i & 1))) & 0xffu, b1 = (wd >> (16 * (i & 1) + 8)) & 0xffu;
+    o[i] = (uint32_t)f32_to_bf16_bits(e4m3_to_f32(b0) * s) |
+           ((uint32_t)f32_to_bf16_bits(e4m3_to_f32(b1) * s) << 16);
+  }
+  *reinterpret_cast<uint4*>(out + 8 * e) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+static bool kld_handles(const Shape& sh) {
+  return sh.teacher == 2 && sh.mode == 0 && sh.dtype == 1 && sh.H == kH && sh.D == kD &&
+         sh.HI == kHI && sh.dI == kDI && sh.idx_dtype != 0;
+}
+
+static int kld_rows(const Shape& sh) { return sh.T < kChunkRows ? sh.T : kChunkRows; }
+
+size_t indexer_kl_dense_workspace(const Shape& sh) {
+  if (!kld_handles(sh) || sh.T == 0) return 0;
+  const size_t rows = (size_t)kld_rows(sh);
+  size_t bytes = rows * (size_t)(sh.max_seqlen / sh.r) * sizeof(float);
+  bytes = (bytes + 255) & ~(size_t)255;
+  if (sh.idx_dtype == 2)
+    bytes += rows * kHI * kDI * sizeof(uint16_t) + (size_t)(sh.T / sh.r) * kDI * sizeof(uint16_t);
+  return bytes;
+}
+
+hipError_t launch_indexer_kl_dense(const Shape& sh, const KlIO& io, hipStream_t s,
+                                   bool* handled) {
+  *handled = false;
+  if (!kld_handles(sh)) return hipSuccess;
+  *handled = true;
+  const int n_cap = sh.max_seqlen / sh.r;
+  const int rows = kld_rows(sh);
+  KldArgs a;
+  a.q = (const uint16_t*)io.q;
+  a.kv_cmp = (const uint16_t*)io.kv_cmp;
+  a.scores = io.scores;
+  a.ld = io.ld;
+  a.qI = io.qI;
+  a.qI_scale = io.qI_scale;
+  a.w = io.w;
+  a.kI = io.kI;
+  a.kI_scale = io.kI_scale;
+  a.cu = sh.cu;
+  a.cu_cmp = sh.cu_cmp;
+  a.g = (float*)io.ws;
+  size_t g_bytes = (size_t)rows * n_cap * sizeof(float);
+  g_bytes = (g_bytes + 255) & ~(size_t)255;
+  uint16_t* q16 = sh.idx_dtype == 2 ? (uint16_t*)((char*)io.ws + g_bytes) : nullptr;
+  uint16_t* k16 = sh.idx_dtype == 2 ? q16 + (size_t)rows * kHI * kDI : nullptr;
+  a.kI16 = k16;
+  a.qI16 = sh.idx_dtype == 2 ? q16 : (const uint16_t*)io.qI;
+  a.q16_t0 = 0;
+  a.kl = io.kl;
+  a.dkI = io.dkI;
+  a.gs = io.grad_scale;
+  a.scale_log2 = sh.scale * 1.44269504088896341f;
+  a.B = sh.B;
+  a.T = sh.T;
+  a.r = sh.r;
+  a.n_cap = n_cap;
+  a.tc_blocks = (sh.T / sh.r + kKB - 1) / kKB;
+  a.fp8 = sh.idx_dtype == 2;
+  const bool grads = io.dqI != nullptr;
+  if (grads && a.fp8) {
+    const int64_t n = (int64_t)(sh.T / sh.r) * (kDI / 8);
+    hipLaunchKernelGGL(k_kld_dequant, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       (const uint8_t*)io.kI, io.kI_scale, (int64_t)0, (int64_t)(sh.T / sh.r),
+                       sh.cu_cmp + sh.B, k16);
+  }
+  for (int t_lo = 0; t_lo < sh.T; t_lo += rows) {
+    a.t_lo = t_lo;
+    a.t_hi = t_lo + rows < sh.T ? t_lo + rows : sh.T;
+    hipLaunchKernelGGL(k_kld_teacher, dim3(kChunkRows / 4 + sh.B), dim3(256), 0, s, a);
+    if (!grads) continue;
+    a.dqI = io.dqI;
+    a.dw = io.dw;
+    hipLaunchKernelGGL(k_kld_queries, dim3(kChunkRows / 4 + sh.B), dim3(256), 0, s, a);
+    if (a.fp8) {
+      const int64_t n = (int64_t)(a.t_hi - a.t_lo) * kHI * (kDI / 8);
+      hipLaunchKernelGGL(k_kld_dequant, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                         (const uint8_t*)io.qI, io.qI_scale, (int64_t)a.t_lo * kHI,
+                         (int64_t)(a.t_hi - a.t_lo) * kHI, (const int32_t*)nullptr, q16);
+      a.q16_t0 = a.t_lo;   // the copy holds rows t - t_lo
+    }
+    hipLaunchKernelGGL(k_kld_keys, dim3(a.tc_blocks + sh.B, kChunkRows / kRange), dim3(256), 0,
+                       s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace csa

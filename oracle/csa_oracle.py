@@ -365,7 +365,7 @@ def _teacher_set(t, bb, pp, cu_cmp, ratio, teacher, idx_row):
 
 
 def indexer_kl(q, kv_cmp, scores, idx, qI, w, kI_cmp, cu_seqlens, ratio, scale, teacher,
-               grad_scale=1.0, rows=None):
+               grad_scale=1.0, rows=None, relu_eps=None):
     """KL_t = sum_{j in C_t} P_t[j] (log P_t[j] - log Q_t[j]) with
       P_t = (1/H) sum_h softmax_{C_t}(scale q[t,h] . kv_cmp[j])   (detached teacher, R9)
       Q_t = softmax_{C_t}(I[t, j])                                 (student = indexer logits)
@@ -374,7 +374,12 @@ def indexer_kl(q, kv_cmp, scores, idx, qI, w, kI_cmp, cu_seqlens, ratio, scale, 
       dw[t,h] = sum_j g relu(z);  dqI[t,h] = sum_j g w[t,h] 1[z>0] kI[j];
       dkI_cmp[j] += sum_{t,h} g w[t,h] 1[z>0] qI[t,h].
     scores[i] is the score row of query rows[i]; idx[i] its selected global rows
-    (teacher "selected").  Returns kl [len(rows)], loss, dqI, dw, dkI_cmp [Tc, d_I]."""
+    (teacher "selected").  Returns kl [len(rows)], loss, dqI, dw, dkI_cmp [Tc, d_I].
+
+    The ReLU mask 1[z>0] is a floating-point decision: with relu_eps given, every z with
+    |z| <= relu_eps * sum_d |qI[t,h,d] kI[j,d]| counts as undecided, and a sixth value
+    (dqI, dw, dkI_cmp bounds) gives, per output element, the sum of |change| that flipping
+    the mask of all undecided z would cause."""
     q = np.asarray(q, dtype=np.float64)
     kv_cmp = np.asarray(kv_cmp, dtype=np.float64)
     qI = np.asarray(qI, dtype=np.float64)
@@ -389,6 +394,8 @@ def indexer_kl(q, kv_cmp, scores, idx, qI, w, kI_cmp, cu_seqlens, ratio, scale, 
     dqI = np.zeros((rows.size, HI, dI))
     dw = np.zeros((rows.size, HI))
     dkI = np.zeros_like(kI_cmp)
+    if relu_eps is not None:
+        b_dqI, b_dw, b_dkI = np.zeros_like(dqI), np.zeros_like(dw), np.zeros_like(dkI)
     for i, t in enumerate(rows):
         if bb[t] < 0:
             continue
@@ -414,6 +421,15 @@ def indexer_kl(q, kv_cmp, scores, idx, qI, w, kI_cmp, cu_seqlens, ratio, scale, 
         E = act * (w[t][:, None] * g[None, :])                # [H_I, |C|] = dI/dz * g
         dqI[i] = E @ K
         np.add.at(dkI, g_rows, E.T @ qI[t])
+        if relu_eps is not None:
+            open_ = np.abs(z) <= relu_eps * (np.abs(qI[t]) @ np.abs(K).T)
+            if open_.any():
+                flip = open_ * np.abs(w[t][:, None] * g[None, :])   # |E| a flip adds or removes
+                b_dqI[i] = flip @ np.abs(K)
+                b_dw[i] = (open_ * np.abs(z)) @ np.abs(g)
+                np.add.at(b_dkI, g_rows, flip.T @ np.abs(qI[t]))
+    if relu_eps is not None:
+        return kl, float(kl.sum()), dqI, dw, dkI, (b_dqI, b_dw, b_dkI)
     return kl, float(kl.sum()), dqI, dw, dkI
 
 

@@ -580,6 +580,69 @@ def test_indexer_kl(name, grads, from_fwd):
         G.check("dkI_cmp", G.back(L.dkI_cmp)[:Tc], dkI, kind)
 
 
+def _check_open(name, got, ref, bound):
+    """bf16 tolerance plus, per element, the oracle's bound for ReLU masks left undecided by
+    the fp32 accumulation (the device and the fp64 oracle may take either side)."""
+    got = np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values in the GPU result"
+    tol = G.TOL_BF16_REL * float(np.abs(ref).max())
+    excess = np.abs(got - ref) - tol - bound
+    n_open = int((bound > 0).sum())
+    print(f"[gpu] {name}: max|err| {np.abs(got - ref).max():.3e} tol {tol:.3e}, "
+          f"{n_open} elements with an open-mask bound", flush=True)
+    assert excess.max() <= 0, (name, float(excess.max()))
+
+
+@pytest.mark.parametrize("idx_dtype", ["bf16", "fp8"])
+def test_indexer_kl_dense_teacher_chunked(idx_dtype):
+    """Dense-teacher loss on the tiled path across more than one 8192-query chunk: three
+    samples starting at rows that are not multiples of 4, capacity padding, unit-variance
+    inputs (peaked teacher), with and without gradients, against the oracle."""
+    from long_context_compressed_amd import binding as B
+    w = configs.workload("csa128k_warmup_fp8", idx_dtype=idx_dtype, lengths=(4003, 2998, 2501),
+                         total_tokens=9560, topk=64, topk_cap=64)
+    host = synth_inputs.make_inputs(w, variant=0, strength=True)
+    h64 = {k: synth_inputs.to_f64(v) for k, v in host.items() if isinstance(v, torch.Tensor)}
+    h64["cu_seqlens"] = host["cu_seqlens"]
+    h64["max_seqlen"] = host["max_seqlen"]
+    name = f"dense_teacher_{idx_dtype}"
+    L = _layer(w, host, backward=True)
+    assert L.ws_kl is not None and B.csa_workspace_size(L.p, B.CSA_OP_INDEXER_KL) > 0
+    cu = _cu(host)
+    L.metadata(cu)
+    dt = G.torch_dtype(w.dtype)
+    kv_cmp_r, idx = _attn_inputs(w, host, h64)
+    d, qI64, kI64 = _indexer_inputs(w, host, h64)
+    sc = O.index_scores(qI64, h64["w"], kI64, host["cu_seqlens"], w.ratio, L.n_cap)
+    s32 = np.where(np.isfinite(sc), sc, 0.0).astype(np.float32)
+    gs = 0.25
+    n = int(host["cu_seqlens"][-1])
+    # fp32 accumulation of the exact products of the rounded operands: below 128 * 2^-24 of
+    # sum |products|; 2^-16 leaves a margin for any summation order
+    kl, loss, dqI, dw, dkI, open_bound = O.indexer_kl(
+        h64["q"], kv_cmp_r, s32[:n], idx[:n], qI64, h64["w"], kI64, host["cu_seqlens"],
+        w.ratio, w.scale, w.teacher, gs, rows=np.arange(n), relu_eps=2.0 ** -16)
+    for grads in (True, False):
+        _announce(name, f"indexer_kl grads={grads}")
+        L.kl.fill_(float("nan"))
+        L.dkI_cmp.zero_()
+        B.csa_indexer_kl(L.p, host["q"].cuda(), G.dev(kv_cmp_r, dt), torch.from_numpy(s32).cuda(),
+                         torch.from_numpy(idx.astype(np.int32)).cuda(), d["qI"], d["qI_scale"],
+                         host["w"].cuda(), d["kI"], d["kI_scale"], cu, L.cu_cmp, gs, L.kl,
+                         L.loss, L.dqI if grads else None, L.dw if grads else None,
+                         L.dkI_cmp if grads else None, L.ws_kl)
+        torch.cuda.synchronize()
+        got_loss = float(L.loss.item())
+        print(f"loss gpu={got_loss:.8e} ref={loss:.8e}", flush=True)
+        assert abs(got_loss - loss) <= G.TOL_LOSS_REL * abs(loss)
+        G.check("kl", G.back(L.kl)[:n], kl, "bf16")
+        assert torch.all(L.kl[n:] == 0)
+        if grads:
+            _check_open("dqI", G.back(L.dqI)[:n], dqI, open_bound[0])
+            _check_open("dw", G.back(L.dw)[:n], dw, open_bound[1])
+            _check_open("dkI_cmp", G.back(L.dkI_cmp)[:kI64.shape[0]], dkI, open_bound[2])
+
+
 # ------------------------------------------------------------------------- whole layer
 @pytest.mark.parametrize("name", list(CASES))
 def test_layer_end_to_end(name):

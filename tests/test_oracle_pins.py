@@ -527,6 +527,37 @@ def test_kl_grad_closed_form_and_finite_differences():
         assert abs(dw[t, 0] - float((Q - P) @ s1[t, :nv])) < 1e-12
 
 
+def test_kl_open_relu_bound_covers_mask_flips():
+    """The undecided-ReLU bound: zero when no logit is within relu_eps of zero; with every
+    mask open it dominates each gradient entry; and it covers the change that flipping one
+    mask actually makes (that logit nudged across zero through its key row)."""
+    lens = [15, 10]
+    cu, q, kc, qI, w, kI, sc, idx = _kl_case(lens, seed=29)
+    r, scale, gs = 2, 0.4, 0.75
+    for teacher in ("selected", "dense"):
+        base = O.indexer_kl(q, kc, sc, idx, qI, w, kI, cu, r, scale, teacher, gs)
+        out = O.indexer_kl(q, kc, sc, idx, qI, w, kI, cu, r, scale, teacher, gs, relu_eps=0.0)
+        for x, y in zip(base[2:5], out[2:5]):
+            assert np.array_equal(x, y)
+        assert all(not b.any() for b in out[5])
+        full = O.indexer_kl(q, kc, sc, idx, qI, w, kI, cu, r, scale, teacher, gs, relu_eps=1.0)
+        for grad, bound in zip(full[2:5], full[5]):
+            assert np.all(np.abs(grad) <= bound + 1e-12)
+    # one logit moved to +-tiny: both signs stay within the bound of either side
+    t, h = 12, 1
+    bb, pp = O.token_positions(cu, int(cu[-1]))
+    row = int(O.cmp_seqlens(cu, r)[bb[t]]) + 1
+    qI2 = qI.copy()
+    zt = qI2[t, h] @ kI[row]
+    qI2[t, h] -= (zt - 1e-12) * kI[row] / (kI[row] @ kI[row])
+    pos = O.indexer_kl(q, kc, sc, idx, qI2, w, kI, cu, r, scale, "dense", gs, relu_eps=1e-6)
+    qI2[t, h] -= 2e-12 * kI[row] / (kI[row] @ kI[row])
+    neg = O.indexer_kl(q, kc, sc, idx, qI2, w, kI, cu, r, scale, "dense", gs, relu_eps=1e-6)
+    for a_, b_, bound in zip(pos[2:5], neg[2:5], pos[5]):
+        assert np.any(a_ != b_)
+        assert np.all(np.abs(a_ - b_) <= bound + 1e-9)
+
+
 # --------------------------------------------------------------------------- fp8
 def test_e4m3_golden_codes():
     for ln in _gold_lines("e4m3_codes.txt"):
