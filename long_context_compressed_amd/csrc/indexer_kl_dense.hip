@@ -20,9 +20,10 @@
 //   k_kld_queries  the same 4-query groups, one query per wave with its qI resident; each
 //                  64-key block of kI is staged once into LDS for the 4 queries; z^T, E =
 //                  g w 1[z > 0] (kept in registers as the A operand), dw and dqI = E kI.
-//   k_kld_keys     one workgroup per (64-key block, query range): kI block in LDS, one
-//                  query per wave; z, E and dkI += E^T qI accumulate in registers over the
-//                  range, one fp32 atomic add per key element and wave at the end.
+//   k_kld_keys     one workgroup per (4 key blocks, query range), one block per wave; each
+//                  query's qI tile is staged once into LDS for the 4 blocks; z, E and
+//                  dkI += E^T qI accumulate in registers over the range, one fp32 atomic add
+//                  per key element at the end.
 // Queries are processed in chunks of kChunkRows (the workspace holds g for one chunk).
 #include <math.h>
 
@@ -41,7 +42,7 @@ namespace {
 constexpr int kHI = 64, kDI = 128;
 constexpr int kKB = 64;            // key rows per block
 constexpr int kChunkRows = 8192;   // queries per chunk
-constexpr int kRange = 512;        // queries per key-gradient workgroup
+constexpr int kRange = 256;        // queries per key-gradient workgroup
 constexpr int kIS = kDI + 8;       // bf16 row stride of the indexer tiles
 constexpr int kI8S = kDI + 16;     // byte row stride of the fp8 code tiles
 constexpr float kLazy = 8.f;
@@ -320,32 +321,34 @@ void k_kld_teacher(KldArgs a) {
 }
 
 // ---------------------------------------------------------------------------- dkI
-// Workgroup (x, y): key block x (64 rows of one sample: regular blocks start at 64-aligned
-// rows and stop at the sample end; block tc_blocks + b holds the first unaligned rows of
-// sample b), queries y kRange .. of the chunk that see its first key.  One query per wave.
+// Workgroup (x, y): 4 key blocks of 64 rows of one sample (regular groups start at
+// 256-aligned rows and stop at the sample end; group tc_groups + b holds the first
+// unaligned rows of sample b), wave w owning block w; queries y kRange .. of the chunk from
+// the first one that sees the group's first key.  Each query's indexer query tile is staged
+// once into LDS (double-buffered, fetched a query ahead) for the 4 blocks.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_kld_keys(KldArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t KIt[kKB][kIS];
-  __shared__ __attribute__((aligned(16))) uint8_t KI8[kKB][kI8S];
-  __shared__ float ksc_s[kKB];
-  __shared__ __attribute__((aligned(16))) uint16_t QIt[4][kHI][kIS];
-  __shared__ __attribute__((aligned(16))) uint8_t QI8[4][kHI][kI8S];
+  __shared__ __attribute__((aligned(16))) uint16_t QIt[2][kHI][kIS];
+  __shared__ __attribute__((aligned(16))) uint8_t QI8[2][kHI][kI8S];
+  __shared__ __attribute__((aligned(16))) uint16_t KIt[4][kKB][kIS];   // bf16 indexer only
+  __shared__ __attribute__((aligned(16))) uint8_t KI8[4][kKB][kI8S];   // fp8 codes only
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
+  constexpr int kGroup = 4 * kKB;
   const int Tc = a.cu_cmp[a.B];
   int r_lo, r_hi, b;
   if ((int)blockIdx.x < a.tc_blocks) {
-    r_lo = kKB * blockIdx.x;
+    r_lo = kGroup * blockIdx.x;
     if (r_lo >= Tc) return;
     b = upper_bound_i32(a.cu_cmp, a.B + 1, r_lo) - 1;
-    r_hi = min(r_lo + kKB, a.cu_cmp[b + 1]);
+    r_hi = min(r_lo + kGroup, a.cu_cmp[b + 1]);
   } else {
     b = blockIdx.x - a.tc_blocks;
     if (b >= a.B) return;
     r_lo = a.cu_cmp[b];
-    r_hi = min((r_lo + kKB - 1) & ~(kKB - 1), a.cu_cmp[b + 1]);
-    if ((r_lo & (kKB - 1)) == 0 || r_hi <= r_lo) return;
+    r_hi = min((r_lo + kGroup - 1) & ~(kGroup - 1), a.cu_cmp[b + 1]);
+    if ((r_lo & (kGroup - 1)) == 0 || r_hi <= r_lo) return;
   }
   const int s_b = a.cu[b], e_b = a.cu[b + 1];
   const int jl0 = r_lo - a.cu_cmp[b];                 // first key, local to the sample
@@ -353,25 +356,57 @@ void k_kld_keys(KldArgs a) {
   const int q_lo = max(max(t_min, a.t_lo + kRange * (int)blockIdx.y), s_b);
   const int q_hi = min(min(e_b, a.t_hi), a.t_lo + kRange * ((int)blockIdx.y + 1));
   if (q_lo >= q_hi) return;
-  const int nk = r_hi - r_lo;
+  // this wave's block: keys jw .. jw + nk - 1 (local), rows r_lo + 64 wave ..
+  const int jw = jl0 + kKB * wave;
+  const int nk = max(0, min(kKB, r_hi - (r_lo + kKB * wave)));
 
-  // key block: bf16 rows (or fp8 codes and scales), rows past nk zero
-  for (int e = tid; e < kKB * (kDI / 8); e += 256) {
+  // this wave's key block: bf16 rows (or fp8 codes), rows past nk zero
+  for (int e = lane; e < kKB * (kDI / 8); e += 64) {
     const int row = e >> 4, ch = e & 15;
+    const int64_t src = (int64_t)(r_lo + kKB * wave + row) * kDI;
     if (!a.fp8) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < nk) v = *reinterpret_cast<const uint4*>((const uint16_t*)a.kI + (int64_t)(r_lo + row) * kDI + 8 * ch);
-      *reinterpret_cast<uint4*>(&KIt[row][8 * ch]) = v;
-    } else {
-      uint2 v = make_uint2(0, 0);
-      if (row < nk) v = *reinterpret_cast<const uint2*>((const uint8_t*)a.kI + (int64_t)(r_lo + row) * kDI + 8 * ch);
-      *reinterpret_cast<uint2*>(&KI8[row][8 * ch]) = v;
-      if (ch == 0) ksc_s[row] = row < nk ? a.kI_scale[r_lo + row] : 0.f;
+      if (row < nk) v = *reinterpret_cast<const uint4*>((const uint16_t*)a.kI + src + 8 * ch);
+      *reinterpret_cast<uint4*>(&KIt[wave][row][8 * ch]) = v;
+    } else if (ch < 8) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < nk) v = *reinterpret_cast<const uint4*>((const uint8_t*)a.kI + src + 16 * ch);
+      *reinterpret_cast<uint4*>(&KI8[wave][row][16 * ch]) = v;
     }
   }
-  __syncthreads();
 
-  // dkI^T partial sums: acc[nt][dt] = rows 16 nt + 4 g + i, columns 16 dt + c16
+  // query tiles: 16 KiB of bf16 rows (4 chunks per thread) and 8 KiB of fp8 codes (2)
+  uint4 pq[4], pq8[2];
+  auto fetch = [&](int tq) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 256 * u, hh = e >> 4, ch = e & 15;
+      pq[u] = *reinterpret_cast<const uint4*>(a.qI16 + ((int64_t)(tq - a.q16_t0) * kHI + hh) * kDI + 8 * ch);
+    }
+    if (a.fp8) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = tid + 256 * u, hh = e >> 3, ch = e & 7;
+        pq8[u] = *reinterpret_cast<const uint4*>((const uint8_t*)a.qI + ((int64_t)tq * kHI + hh) * kDI + 16 * ch);
+      }
+    }
+  };
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 256 * u, hh = e >> 4, ch = e & 15;
+      *reinterpret_cast<uint4*>(&QIt[buf][hh][8 * ch]) = pq[u];
+    }
+    if (a.fp8) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = tid + 256 * u, hh = e >> 3, ch = e & 7;
+        *reinterpret_cast<uint4*>(&QI8[buf][hh][16 * ch]) = pq8[u];
+      }
+    }
+  };
+
+  // dkI partial sums: acc[nt][dt] = keys 16 nt + 4 g + i of the wave's block, d 16 dt + c16
   f32x4 acc[4][8];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
@@ -379,76 +414,69 @@ void k_kld_keys(KldArgs a) {
     for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int jr = c16 >> 2, jc = 4 * (c16 & 3);
 
-  for (int t0 = q_lo; t0 < q_hi; t0 += 4) {
-    const int t = t0 + wave;
-    const bool act = t < q_hi;
-    const int tq = act ? t : q_lo;
-    // this query's indexer query tile into the wave's LDS slot
-    for (int e = lane; e < kHI * (kDI / 8); e += 64) {
-      const int hh = e >> 4, ch = e & 15;
-      *reinterpret_cast<uint4*>(&QIt[wave][hh][8 * ch]) =
-          *reinterpret_cast<const uint4*>(a.qI16 + ((int64_t)(tq - a.q16_t0) * kHI + hh) * kDI + 8 * ch);
-      if (a.fp8)
-        *reinterpret_cast<uint2*>(&QI8[wave][hh][8 * ch]) =
-            *reinterpret_cast<const uint2*>((const uint8_t*)a.qI + ((int64_t)tq * kHI + hh) * kDI + 8 * ch);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    const int nv_t = act ? min((tq - s_b + 1) / a.r, a.n_cap) : 0;
-    const float* gr = a.g + (int64_t)(tq - a.t_lo) * a.n_cap + jl0;
-    float wv[4][4];
+  fetch(q_lo);
+  commit(0);
+  for (int tq = q_lo; tq < q_hi; ++tq) {
+    const int buf = (tq - q_lo) & 1;
+    __syncthreads();
+    if (tq + 1 < q_hi) fetch(tq + 1);
+    const int nv_t = min((tq - s_b + 1) / a.r, a.n_cap);
+    if (nk > 0 && nv_t > jw) {
+      const float* gr = a.g + (int64_t)(tq - a.t_lo) * a.n_cap + jw;
+      float wv[4][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wv[mt][i] = a.w[(int64_t)tq * kHI + 16 * mt + 4 * g + i];
-    // z[head 16 mt + 4 g + i][key 16 nt + c16] (the ReLU mask needs only its sign, so fp8
-    // codes need no scales), then E = g w 1[z > 0] as bf16 A operands of the dkI product:
-    // k-step ks takes head tiles 2 ks (k-slots 8g..8g+3) and 2 ks + 1 (8g+4..8g+7); the qI
-    // rows are read transposed in the same order
+        for (int i = 0; i < 4; ++i) wv[mt][i] = a.w[(int64_t)tq * kHI + 16 * mt + 4 * g + i];
+      // z[head 16 mt + 4 g + i][key 16 nt + c16] (the ReLU mask needs only its sign, so fp8
+      // codes need no scales), then E = g w 1[z > 0] as bf16 A operands of the dkI product:
+      // k-step ks takes head tiles 2 ks (k-slots 8g..8g+3) and 2 ks + 1 (8g+4..8g+7); the qI
+      // rows are read transposed in the same order
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int kj = 16 * nt + c16;
-      const float gv = (act && kj < nk && jl0 + kj < nv_t) ? gr[kj] : 0.f;
+      for (int nt = 0; nt < 4; ++nt) {
+        const int kj = 16 * nt + c16;
+        const float gv = (kj < nk && jw + kj < nv_t) ? gr[kj] : 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        uint32_t e4[4];
+        for (int ks = 0; ks < 2; ++ks) {
+          uint32_t e4[4];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int mt = 2 * ks + h2;
-          f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (!a.fp8) {
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int mt = 2 * ks + h2;
+            f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (!a.fp8) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-              z = mfma16(ld16(&QIt[wave][16 * mt + c16][32 * kk + 8 * g]),
-                         ld16(&KIt[16 * nt + c16][32 * kk + 8 * g]), z);
-          } else {
-            const uint4* qp = reinterpret_cast<const uint4*>(&QI8[wave][16 * mt + c16][32 * g]);
-            const uint4* kp = reinterpret_cast<const uint4*>(&KI8[16 * nt + c16][32 * g]);
-            const uint4 q0 = qp[0], q1 = qp[1], k0 = kp[0], k1 = kp[1];
-            z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                i32x8{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w},
-                i32x8{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w},
-                z, 0, 0, 0, 127, 0, 127);
+              for (int kk = 0; kk < 4; ++kk)
+                z = mfma16(ld16(&QIt[buf][16 * mt + c16][32 * kk + 8 * g]),
+                           ld16(&KIt[wave][16 * nt + c16][32 * kk + 8 * g]), z);
+            } else {
+              const uint4* qp = reinterpret_cast<const uint4*>(&QI8[buf][16 * mt + c16][32 * g]);
+              const uint4* kp = reinterpret_cast<const uint4*>(&KI8[wave][16 * nt + c16][32 * g]);
+              const uint4 q0 = qp[0], q1 = qp[1], k0 = kp[0], k1 = kp[1];
+              z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  i32x8{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w},
+                  i32x8{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w},
+                  z, 0, 0, 0, 127, 0, 127);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+              const float e0 = z[i] > 0.f ? gv * wv[mt][i] : 0.f;
+              const float e1 = z[i + 1] > 0.f ? gv * wv[mt][i + 1] : 0.f;
+              e4[2 * h2 + (i >> 1)] = pack_bf16x2(e0, e1);
+            }
           }
+          const bf16x8 ea = __builtin_bit_cast(bf16x8, make_uint4(e4[0], e4[1], e4[2], e4[3]));
 #pragma unroll
-          for (int i = 0; i < 4; i += 2) {
-            const float e0 = z[i] > 0.f ? gv * wv[mt][i] : 0.f;
-            const float e1 = z[i + 1] > 0.f ? gv * wv[mt][i + 1] : 0.f;
-            e4[2 * h2 + (i >> 1)] = pack_bf16x2(e0, e1);
+          for (int dt = 0; dt < 8; ++dt) {
+            const v4i16 lo = ld_tr(&QIt[buf][32 * ks + 4 * g + jr][16 * dt + jc]);
+            const v4i16 hi = ld_tr(&QIt[buf][32 * ks + 16 + 4 * g + jr][16 * dt + jc]);
+            acc[nt][dt] = mfma16(ea, join8(lo, hi), acc[nt][dt]);
           }
-        }
-        const bf16x8 ea = __builtin_bit_cast(bf16x8, make_uint4(e4[0], e4[1], e4[2], e4[3]));
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const v4i16 lo = ld_tr(&QIt[wave][32 * ks + 4 * g + jr][16 * dt + jc]);
-          const v4i16 hi = ld_tr(&QIt[wave][32 * ks + 16 + 4 * g + jr][16 * dt + jc]);
-          acc[nt][dt] = mfma16(ea, join8(lo, hi), acc[nt][dt]);
         }
       }
     }
-    __builtin_amdgcn_wave_barrier();
+    if (tq + 1 < q_hi) commit(buf ^ 1);
   }
-  // each wave adds its partial sums (rows past the block are zero and skipped)
+  // each wave adds its partial sums (rows past the block are skipped)
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -457,7 +485,7 @@ void k_kld_keys(KldArgs a) {
       if (kj < nk) {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
-          atomicAdd(a.dkI + (int64_t)(r_lo + kj) * kDI + 16 * dt + c16, acc[nt][dt][i]);
+          atomicAdd(a.dkI + (int64_t)(r_lo + kKB * wave + kj) * kDI + 16 * dt + c16, acc[nt][dt][i]);
       }
     }
 }
@@ -711,7 +739,7 @@ hipError_t launch_indexer_kl_dense(const Shape& sh, const KlIO& io, hipStream_t 
   a.T = sh.T;
   a.r = sh.r;
   a.n_cap = n_cap;
-  a.tc_blocks = (sh.T / sh.r + kKB - 1) / kKB;
+  a.tc_blocks = (sh.T / sh.r + 4 * kKB - 1) / (4 * kKB);   // 256-row key groups
   a.fp8 = sh.idx_dtype == 2;
   const bool grads = io.dqI != nullptr;
   if (grads && a.fp8) {
