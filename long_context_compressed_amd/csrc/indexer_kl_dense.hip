@@ -11,8 +11,8 @@
 // of key row: read per query, as the selected-set kernels do, it is bound by the row
 // gathers.  Here the work is split three ways so each shared operand is read once per
 // tile instead of once per (query, entry):
-//   k_kld_teacher  one workgroup per 4 consecutive queries of one sample, one query per
-//                  wave with its 64 x 512 Q resident; each 64-row key block is loaded once
+//   k_kld_teacher  one workgroup per 4 consecutive queries of one sample, two waves per
+//                  query (32 heads each) with Q resident; each 64-row key block is loaded once
 //                  into LDS (direct global->LDS loads, one row per S^T k-step, a block
 //                  ahead) and feeds all 4 queries.  Pass 1: per-head online log-sum-exp
 //                  of the teacher and the student log-sum-exp; pass 2: P (head mean), Q,
@@ -110,13 +110,17 @@ __device__ __forceinline__ bool query_group(const KldArgs& a, int bid, int& t_fi
 }  // namespace
 
 // ---------------------------------------------------------------------------- teacher
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// 8 waves: wave w serves query w / 2 of the group with heads 32 (w % 2) .. + 31, so two
+// waves share each SIMD and one's softmax arithmetic overlaps the other's MFMAs.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_kld_teacher(KldArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[2][kKB][kD];
   __shared__ float Is[4][kKB];
+  __shared__ float Ps[4][2][kKB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
+  const int tw = wave >> 1, hh = wave & 1;
   if ((int)blockIdx.x < kChunkRows / 4 && tid < 4) {   // capacity padding rows: kl = 0
     const int u = a.t_lo + 4 * blockIdx.x + tid;
     if (u < a.t_hi && u >= a.cu[a.B]) a.kl[u] = 0.f;
@@ -124,53 +128,53 @@ void k_kld_teacher(KldArgs a) {
   int t_first, n_tok;
   TokenInfo ti;
   if (!query_group(a, blockIdx.x, t_first, n_tok, ti)) return;
-  const bool active = wave < n_tok;
-  const int t = t_first + (active ? wave : 0);
+  const bool active = tw < n_tok;
+  const int t = t_first + (active ? tw : 0);
   const int row0 = __builtin_amdgcn_readfirstlane(a.cu_cmp[ti.b]);
-  const int nv_w = active ? min((ti.p + wave + 1) / a.r, a.n_cap) : 0;
+  const int nv_w = active ? min((ti.p + tw + 1) / a.r, a.n_cap) : 0;
   const int nv_max = __builtin_amdgcn_readfirstlane(min((ti.p + n_tok) / a.r, a.n_cap));
   if (nv_max == 0) {
-    if (active && lane == 0) a.kl[t] = 0.f;
+    if (active && hh == 0 && lane == 0) a.kl[t] = 0.f;
     return;
   }
   const int nblk = (nv_max + kKB - 1) / kKB;
   const float* srow = a.scores + (int64_t)t * a.ld;
   float* grow = a.g + (int64_t)(t - a.t_lo) * a.n_cap;
 
-  // Q^T as the B operand: qb[nt][ks] = Q[16 nt + c16][32 ks + 8 g .. +7] of this wave's query
-  bf16x8 qb[4][16];
+  // Q rows as the A operand: qb[ht][ks] = Q[32 hh + 16 ht + c16][32 ks + 8 g .. +7]
+  bf16x8 qb[2][16];
   {
-    const uint16_t* qt = a.q + ((int64_t)t * kH + c16) * kD + 8 * g;
+    const uint16_t* qt = a.q + ((int64_t)t * kH + 32 * hh + c16) * kD + 8 * g;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) qb[nt][ks] = ld16(qt + 16 * nt * kD + 32 * ks);
   }
 
-  // key rows of a block: row 16 wave + j of block jb is visible row 64 jb + 16 wave + j
+  // key rows of a block: row 8 wave + j of block jb is visible row 64 jb + 8 wave + j
   // (row0 for slots past the last query's visible range: finite, masked below)
   const uint32_t lane16 = 16u * (uint32_t)lane;
   const uint32_t tile_lds = (uint32_t)(uintptr_t)&tile[0][0][0];
   auto gather = [&](int jb, int buf, int j) {
-    const int key = kKB * jb + 16 * wave + j;
+    const int r = 8 * wave + j;
+    const int key = kKB * jb + r;
     const int row = __builtin_amdgcn_readfirstlane(row0 + (key < nv_max ? key : 0));
     const uint64_t src = (uint64_t)(uintptr_t)(a.kv_cmp + (int64_t)row * kD);
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(tile_lds + buf * (kKB * kD * 2) +
-                                                        (16 * wave + j) * (kD * 2));
-    dma_row16_s(src, lane16 ^ (16u * swz(j)), lds);
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(tile_lds + buf * (kKB * kD * 2) + r * (kD * 2));
+    dma_row16_s(src, lane16 ^ (16u * swz(r)), lds);
   };
   int eq[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) eq[q] = 8 * ((4 * q + g) ^ swz(c16));
 
-  // pass-1 state: per-head (m, l) of the 4 heads 16 nt + c16 over this lane's keys, and the
-  // student (m, l) over the whole row (the same in every lane)
-  float m_run[4], l_run[4], lse2[4];
+  // pass-1 state: per-head (m, l) of the lane's 8 heads 32 hh + 16 ht + 4 g + i over its
+  // keys, and the student (m, l) over the whole row (the same in every lane)
+  float m_run[8], l_run[8], lse2[8];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) { m_run[nt] = -INFINITY; l_run[nt] = 0.f; lse2[nt] = 0.f; }
+  for (int hx = 0; hx < 8; ++hx) { m_run[hx] = -INFINITY; l_run[hx] = 0.f; lse2[hx] = 0.f; }
   float ms = -INFINITY, lsum = 0.f, lseS = 0.f, kl_acc = 0.f;
 
-  for (int j = 0; j < 16; ++j) gather(0, 0, j);
+  for (int j = 0; j < 8; ++j) gather(0, 0, j);
   wait_vmem();
   __syncthreads();
 
@@ -183,68 +187,62 @@ void k_kld_teacher(KldArgs a) {
     const int jb_next = it + 1 == nblk ? 0 : jb + 1;
 
     // scores of this block's keys (one per lane, coalesced), for the student
+    float iv = -INFINITY;
     {
       const int j = kKB * jb + lane;
-      Is[wave][lane] = j < nv_w ? srow[j] : -INFINITY;
-      __builtin_amdgcn_wave_barrier();
+      if (j < nv_w) iv = srow[j];
     }
 
-    // ---- S^T[key 16 mt + 4 g + i][head 16 nt + c16] over the block
-    f32x4 acc[4][4];
+    // ---- S[head 32 hh + 16 ht + 4 g + i][key 16 kt + c16] over the block: Q rows are the
+    // A operand (registers), key row segments the B operand (LDS)
+    f32x4 acc[4][2];   // [kt][ht]
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ht = 0; ht < 2; ++ht) acc[kt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
       const uint16_t* rb = &tile[buf][c16][0];
-      auto seg = [&](int ks, int mt) { return ld16(rb + 16 * mt * kD + 128 * (ks >> 2) + eq[ks & 3]); };
-      bf16x8 av[2][4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) av[0][mt] = seg(0, mt);
+      auto seg = [&](int ks, int kt) { return ld16(rb + 16 * kt * kD + 128 * (ks >> 2) + eq[ks & 3]); };
+      // (the other wave on the SIMD covers the LDS read latency: no software prefetch)
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (ks + 1 < 16) {
+        bf16x8 kb[4];
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) av[(ks + 1) & 1][mt] = seg(ks + 1, mt);
-        }
+        for (int kt = 0; kt < 4; ++kt) kb[kt] = seg(ks, kt);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma16(av[ks & 1][mt], qb[nt][ks], acc[mt][nt]);
-        if (more) gather(jb_next, buf ^ 1, ks);
+          for (int ht = 0; ht < 2; ++ht) acc[kt][ht] = mfma16(qb[ht][ks], kb[kt], acc[kt][ht]);
+        if (more && (ks & 1) == 0) gather(jb_next, buf ^ 1, ks >> 1);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
-    const int kbase = kKB * jb + 4 * g;
+    const int kbase = kKB * jb + c16;   // key of tile kt: kbase + 16 kt
     if (!pass2) {
-      // ---- teacher: lazily rescaled online (max, sum) per head in log2 units
+      // ---- teacher: per lane, lazily rescaled online (max, sum) of its 8 heads over its keys
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        float s[16];
-        float bm = -INFINITY;
+      for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int i = 0; i < 4; ++i) {
+          const int hx = 4 * ht + i;
+          float bm = -INFINITY;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = kbase + 16 * mt + i < nv_w ? acc[mt][nt][i] * a.scale_log2 : -INFINITY;
-            s[4 * mt + i] = v;
-            bm = fmaxf(bm, v);
+          for (int kt = 0; kt < 4; ++kt)
+            if (kbase + 16 * kt < nv_w) bm = fmaxf(bm, acc[kt][ht][i] * a.scale_log2);
+          if (bm > m_run[hx] + kLazy) {
+            l_run[hx] *= __builtin_amdgcn_exp2f(m_run[hx] - bm);
+            m_run[hx] = bm;
           }
-        if (bm > m_run[nt] + kLazy) {
-          l_run[nt] *= __builtin_amdgcn_exp2f(m_run[nt] - bm);
-          m_run[nt] = bm;
-        }
-        if (m_run[nt] != -INFINITY) {
-          float add = 0.f;
+          if (m_run[hx] != -INFINITY) {
+            float add = 0.f;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) add += __builtin_amdgcn_exp2f(s[e] - m_run[nt]);
-          l_run[nt] += add;
+            for (int kt = 0; kt < 4; ++kt)
+              if (kbase + 16 * kt < nv_w)
+                add += __builtin_amdgcn_exp2f(acc[kt][ht][i] * a.scale_log2 - m_run[hx]);
+            l_run[hx] += add;
+          }
         }
-      }
       // ---- student: online (max, sum) of the scores (natural log), lane = key
       {
-        const float iv = Is[wave][lane];
         const float bm = wave_max(iv);
         if (bm > ms) {
           lsum = ms == -INFINITY ? 0.f : lsum * expf(ms - bm);
@@ -253,69 +251,58 @@ void k_kld_teacher(KldArgs a) {
         if (ms != -INFINITY) lsum += wave_sum(iv == -INFINITY ? 0.f : expf(iv - ms));
       }
       if (it == nblk - 1) {
-        // merge the 4 lane groups of each head; the student normalizer to every lane
+        // merge the 16 lanes (keys) of each head; the student normalizer to every lane
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int hx = 0; hx < 8; ++hx) {
 #pragma unroll
-          for (int o = 16; o <= 32; o <<= 1) {
-            const float mo = __shfl_xor(m_run[nt], o, 64), lo = __shfl_xor(l_run[nt], o, 64);
-            const float mn = fmaxf(m_run[nt], mo);
+          for (int o = 1; o < 16; o <<= 1) {
+            const float mo = __shfl_xor(m_run[hx], o, 64), lo = __shfl_xor(l_run[hx], o, 64);
+            const float mn = fmaxf(m_run[hx], mo);
             if (mn != -INFINITY) {
-              l_run[nt] = l_run[nt] * __builtin_amdgcn_exp2f(m_run[nt] - mn) +
+              l_run[hx] = l_run[hx] * __builtin_amdgcn_exp2f(m_run[hx] - mn) +
                           lo * __builtin_amdgcn_exp2f(mo - mn);
-              m_run[nt] = mn;
+              m_run[hx] = mn;
             }
           }
-          lse2[nt] = l_run[nt] > 0.f ? m_run[nt] + __log2f(l_run[nt]) : INFINITY;
+          lse2[hx] = l_run[hx] > 0.f ? m_run[hx] + __log2f(l_run[hx]) : INFINITY;
         }
         lseS = lsum > 0.f ? ms + logf(lsum) : INFINITY;
       }
     } else {
-      // ---- P = mean over heads of exp2(s - lse2); Q, KL and g for this block's keys
-      float ps[16];
+      // ---- P = mean over heads of exp2(s - lse2): the lane's 8 heads in registers, the 4
+      // lane groups by two exchanges, the two head halves through LDS
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int kt = 0; kt < 4; ++kt) {
+        float p = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float p = 0.f;
+        for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-            p += __builtin_amdgcn_exp2f(acc[mt][nt][i] * a.scale_log2 - lse2[nt]);
-          ps[4 * mt + i] = p;
+          for (int i = 0; i < 4; ++i)
+            p += __builtin_amdgcn_exp2f(acc[kt][ht][i] * a.scale_log2 - lse2[4 * ht + i]);
+        p += __shfl_xor(p, 16, 64);
+        p += __shfl_xor(p, 32, 64);
+        if (g == 0) Ps[tw][hh][16 * kt + c16] = p;
+      }
+      __syncthreads();
+      // one key per lane (wave hh = 0 of each query): P, Q, the KL term and g
+      if (hh == 0) {
+        float gv = 0.f;
+        if (kKB * jb + lane < nv_w) {
+          const float P = (Ps[tw][0][lane] + Ps[tw][1][lane]) * (1.f / kH);
+          const float logQ = iv - lseS;
+          const float Q = expf(logQ);
+          if (P > 0.f) kl_acc += P * (logf(P) - logQ);
+          gv = a.gs * (Q - P);
         }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) ps[e] += __shfl_xor(ps[e], o, 64);
+        const int j = kKB * jb + lane;
+        if (active && j < nv_w) grow[j] = gv;
       }
-      if (c16 == 0) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kj = 16 * mt + 4 * g + i;   // key within the block
-            float gv = 0.f;
-            if (kKB * jb + kj < nv_w) {
-              const float P = ps[4 * mt + i] * (1.f / kH);
-              const float logQ = Is[wave][kj] - lseS;
-              const float Q = expf(logQ);
-              if (P > 0.f) kl_acc += P * (logf(P) - logQ);
-              gv = a.gs * (Q - P);
-            }
-            Is[wave][kj] = gv;   // this wave's slot, read back below as a row
-          }
-      }
-      __builtin_amdgcn_wave_barrier();
-      const int j = kKB * jb + lane;
-      if (active && j < nv_w) grow[j] = Is[wave][lane];
     }
     wait_vmem();
     __syncthreads();
   }
-  if (active) {
-    float v = kl_acc;
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
+  if (active && hh == 0) {
+    const float v = wave_sum(kl_acc);
     if (lane == 0) a.kl[t] = v;
   }
 }
@@ -751,7 +738,7 @@ hipError_t launch_indexer_kl_dense(const Shape& sh, const KlIO& io, hipStream_t 
   for (int t_lo = 0; t_lo < sh.T; t_lo += rows) {
     a.t_lo = t_lo;
     a.t_hi = t_lo + rows < sh.T ? t_lo + rows : sh.T;
-    hipLaunchKernelGGL(k_kld_teacher, dim3(kChunkRows / 4 + sh.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_kld_teacher, dim3(kChunkRows / 4 + sh.B), dim3(512), 0, s, a);
     if (!grads) continue;
     a.dqI = io.dqI;
     a.dw = io.dw;
