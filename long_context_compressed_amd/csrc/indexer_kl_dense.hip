@@ -419,12 +419,23 @@ void k_kld_keys(KldArgs a) {
       // codes need no scales), then E = g w 1[z > 0] as bf16 A operands of the dkI product:
       // k-step ks takes head tiles 2 ks (k-slots 8g..8g+3) and 2 ks + 1 (8g+4..8g+7); the qI
       // rows are read transposed in the same order
+      float gvs[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const int kj = 16 * nt + c16;
-        const float gv = (kj < nk && jw + kj < nv_t) ? gr[kj] : 0.f;
+        gvs[nt] = (kj < nk && jw + kj < nv_t) ? gr[kj] : 0.f;
+      }
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < 2; ++ks) {
+        // qI^T B operands of this k-step, shared by the 4 key tiles
+        bf16x8 qbt[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          qbt[dt] = join8(ld_tr(&QIt[buf][32 * ks + 4 * g + jr][16 * dt + jc]),
+                          ld_tr(&QIt[buf][32 * ks + 16 + 4 * g + jr][16 * dt + jc]));
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const float gv = gvs[nt];
           uint32_t e4[4];
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
@@ -453,11 +464,7 @@ void k_kld_keys(KldArgs a) {
           }
           const bf16x8 ea = __builtin_bit_cast(bf16x8, make_uint4(e4[0], e4[1], e4[2], e4[3]));
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) {
-            const v4i16 lo = ld_tr(&QIt[buf][32 * ks + 4 * g + jr][16 * dt + jc]);
-            const v4i16 hi = ld_tr(&QIt[buf][32 * ks + 16 + 4 * g + jr][16 * dt + jc]);
-            acc[nt][dt] = mfma16(ea, join8(lo, hi), acc[nt][dt]);
-          }
+          for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = mfma16(ea, qbt[dt], acc[nt][dt]);
         }
       }
     }
@@ -595,6 +602,12 @@ void k_kld_queries(KldArgs a) {
     // k-step ks over key tiles 2 ks (k-slots 8g..8g+3) and 2 ks + 1 (8g+4..8g+7)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      // kI^T B operands of this k-step, shared by the 4 head tiles
+      bf16x8 kbt[8];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        kbt[dt] = join8(ld_tr(&KIt[buf][32 * ks + 4 * g + jr][16 * dt + jc]),
+                        ld_tr(&KIt[buf][32 * ks + 16 + 4 * g + jr][16 * dt + jc]));
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         uint32_t e4[4];
@@ -626,11 +639,7 @@ void k_kld_queries(KldArgs a) {
         }
         const bf16x8 ea = __builtin_bit_cast(bf16x8, make_uint4(e4[0], e4[1], e4[2], e4[3]));
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const v4i16 lo = ld_tr(&KIt[buf][32 * ks + 4 * g + jr][16 * dt + jc]);
-          const v4i16 hi = ld_tr(&KIt[buf][32 * ks + 16 + 4 * g + jr][16 * dt + jc]);
-          acc[nt][dt] = mfma16(ea, join8(lo, hi), acc[nt][dt]);
-        }
+        for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = mfma16(ea, kbt[dt], acc[nt][dt]);
       }
     }
     if (jb + 1 < nblk) commit(buf ^ 1);
