@@ -364,7 +364,19 @@ void k_kld_keys(KldArgs a) {
 
   // query tiles: 16 KiB of bf16 rows (4 chunks per thread) and 8 KiB of fp8 codes (2)
   uint4 pq[4], pq8[2];
+  float pg[4], pw[4][4];   // the fetched query's g of the wave's keys 16 nt + c16, its w
   auto fetch = [&](int tq) {
+    const int nvq = min((tq - s_b + 1) / a.r, a.n_cap);
+    const float* grq = a.g + (int64_t)(tq - a.t_lo) * a.n_cap + jw;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int kj = 16 * nt + c16;
+      pg[nt] = (kj < nk && jw + kj < nvq) ? grq[kj] : 0.f;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw[mt][i] = a.w[(int64_t)tq * kHI + 16 * mt + 4 * g + i];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = tid + 256 * u, hh = e >> 4, ch = e & 15;
@@ -406,25 +418,20 @@ void k_kld_keys(KldArgs a) {
   for (int tq = q_lo; tq < q_hi; ++tq) {
     const int buf = (tq - q_lo) & 1;
     __syncthreads();
+    float gvs[4], wv[4][4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) gvs[nt] = pg[nt];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[mt][i] = pw[mt][i];
     if (tq + 1 < q_hi) fetch(tq + 1);
     const int nv_t = min((tq - s_b + 1) / a.r, a.n_cap);
     if (nk > 0 && nv_t > jw) {
-      const float* gr = a.g + (int64_t)(tq - a.t_lo) * a.n_cap + jw;
-      float wv[4][4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wv[mt][i] = a.w[(int64_t)tq * kHI + 16 * mt + 4 * g + i];
       // z[head 16 mt + 4 g + i][key 16 nt + c16] (the ReLU mask needs only its sign, so fp8
       // codes need no scales), then E = g w 1[z > 0] as bf16 A operands of the dkI product:
       // k-step ks takes head tiles 2 ks (k-slots 8g..8g+3) and 2 ks + 1 (8g+4..8g+7); the qI
       // rows are read transposed in the same order
-      float gvs[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int kj = 16 * nt + c16;
-        gvs[nt] = (kj < nk && jw + kj < nv_t) ? gr[kj] : 0.f;
-      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         // qI^T B operands of this k-step, shared by the 4 key tiles
@@ -536,6 +543,7 @@ void k_kld_queries(KldArgs a) {
   // key repeat row0 (finite; their g is 0)
   uint4 pre[4], pre8[2];
   float pre_s = 0.f;
+  float pre_g[4][4];   // g of keys 16 mt + 4 g + i of the fetched block (0 past nv_w)
   const uint16_t* kI16 = a.fp8 ? a.kI16 : (const uint16_t*)a.kI;
   auto fetch = [&](int jb) {
 #pragma unroll
@@ -544,6 +552,13 @@ void k_kld_queries(KldArgs a) {
       const int key = kKB * jb + row;
       pre[u] = *reinterpret_cast<const uint4*>(kI16 + (int64_t)(row0 + (key < nv_max ? key : 0)) * kDI + 8 * ch);
     }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = kKB * jb + 16 * mt + 4 * g + i;
+        pre_g[mt][i] = j < nv_w ? grow[j] : 0.f;
+      }
     if (a.fp8) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -588,16 +603,14 @@ void k_kld_queries(KldArgs a) {
   for (int jb = 0; jb < nblk; ++jb) {
     const int buf = jb & 1;
     __syncthreads();
-    if (jb + 1 < nblk) fetch(jb + 1);
-    // g of keys 16 mt + 4 g + i of the block for this wave's query (0 past its visible range)
+    // g of keys 16 mt + 4 g + i of the block for this wave's query (0 past its visible range),
+    // fetched with the block
     float gk[4][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = kKB * jb + 16 * mt + 4 * g + i;
-        gk[mt][i] = j < nv_w ? grow[j] : 0.f;
-      }
+      for (int i = 0; i < 4; ++i) gk[mt][i] = pre_g[mt][i];
+    if (jb + 1 < nblk) fetch(jb + 1);
     // z^T[key 16 mt + 4 g + i][head 16 nt + c16]; E as the A operand of dqI = E kI with
     // k-step ks over key tiles 2 ks (k-slots 8g..8g+3) and 2 ks + 1 (8g+4..8g+7)
 #pragma unroll
