@@ -21,7 +21,7 @@ from tests import gpu_support as G
 pytestmark = pytest.mark.gpu
 
 NAMES = ["tiny_csa_f32_L256", "csa_sparse_fwd_bf16_L4096", "thd64k_csa_bf16", "thd64k_hca_bf16",
-         "csa128k_warmup_fp8"]
+         "thd64k_window_bf16", "csa128k_warmup_fp8"]
 
 
 # relative rounding of a compressed indexer key on the GPU chain: bf16 storage (2^-9, with

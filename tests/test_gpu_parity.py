@@ -37,6 +37,8 @@ CASES = {
                                                    topk=64, topk_cap=64, draw=None)),
     "hca_bf16_thd_small": ("thd64k_hca_bf16", dict(lengths=(1024, 700, 300),
                                                    total_tokens=2048)),
+    "window_bf16_thd_small": ("thd64k_window_bf16", dict(lengths=(301, 515, 1027),
+                                                         total_tokens=1856, draw=None)),
     "fp8_warmup_small": ("csa128k_warmup_fp8", dict(lengths=(1500,), total_tokens=1536,
                                                     topk=64, topk_cap=64)),
 }
