@@ -37,7 +37,11 @@ Readings taken where the page leaves a step open (each restated where used):
      main-attention logits (window and sink excluded);
   R11 loss = sum over real rows of KL_t, KL_t = 0 for an empty C_t;
   R13 fp8 = OCP e4m3 (max 448), one scale per row = max|row| / 448 computed in
-     float32, codes = round-to-nearest-even(x / scale) saturated to +-448.
+     float32, codes = round-to-nearest-even(x / scale) saturated to +-448;
+  R20 learned compressor = per channel, softmax over the group's source tokens of
+     (score row + positional parameter) weighting the value rows; ratio-4 groups
+     overlap their left neighbour (8 source tokens), ratio-128 groups do not; the
+     normalization is the softmax's own (no further learned scaling).
 """
 import numpy as np
 
@@ -118,6 +122,79 @@ def compress_bwd(d_cmp, cu_seqlens, ratio, total_tokens):
         for j in range(int(L) // ratio):
             dx[s + j * ratio: s + (j + 1) * ratio] += d_cmp[cu_cmp[b] + j] / ratio
     return dx
+
+
+# ---------------------------------------------------------------------------
+# learned-score compressor (reading R20)
+# ---------------------------------------------------------------------------
+def _learned_groups(cu_seqlens, ratio, overlap):
+    """(output row, source token rows, positions in the positional parameter) per group.
+
+    Group j of sample b owns tokens s_b + j r .. s_b + j r + r - 1 (complete groups only,
+    section 4).  Overlapping groups (ratio-4 CSA, section 5.1: 8 source tokens) also read
+    the left neighbour's r tokens, at positions 0 .. r-1, their own at r .. 2r-1; group 0
+    of a sample has no left neighbour (compression restarts at the sample boundary).
+    Non-overlapping groups (HCA) read their own tokens at positions 0 .. r-1."""
+    starts, lens = sample_table(cu_seqlens)
+    cu_cmp = cmp_seqlens(cu_seqlens, ratio)
+    out = []
+    for b, (s, L) in enumerate(zip(starts, lens)):
+        for j in range(int(L) // ratio):
+            own = np.arange(s + j * ratio, s + (j + 1) * ratio)
+            if overlap and j > 0:
+                toks = np.arange(s + (j - 1) * ratio, s + (j + 1) * ratio)
+                pos = np.arange(2 * ratio)
+            elif overlap:
+                toks, pos = own, np.arange(ratio, 2 * ratio)
+            else:
+                toks, pos = own, np.arange(ratio)
+            out.append((int(cu_cmp[b]) + j, toks, pos))
+    return out
+
+
+def compress_learned(x, score, bias, cu_seqlens, ratio, overlap):
+    """x_cmp[row, d] = sum_u w[u, d] x[t_u, d],  w[:, d] = softmax_u(score[t_u, d] + bias[p_u, d])
+    over the group's source tokens t_u at positions p_u (see _learned_groups): a per-channel
+    learned-score reduction with an fp32 positional parameter (sections 8.2 and 9), reset
+    per sample.  bias: [2r, dim] if overlap else [r, dim].  Returns [Tc, dim]."""
+    x = np.asarray(x, dtype=np.float64)
+    score = np.asarray(score, dtype=np.float64)
+    bias = np.asarray(bias, dtype=np.float64)
+    groups = _learned_groups(cu_seqlens, ratio, overlap)
+    Tc = int(cmp_seqlens(cu_seqlens, ratio)[-1])
+    out = np.zeros((Tc, x.shape[1]))
+    for row, toks, pos in groups:
+        z = score[toks] + bias[pos]
+        z = z - z.max(axis=0, keepdims=True)
+        w = np.exp(z)
+        w /= w.sum(axis=0, keepdims=True)
+        out[row] = (w * x[toks]).sum(axis=0)
+    return out
+
+
+def compress_learned_bwd(x, score, bias, d_cmp, cu_seqlens, ratio, overlap, total_tokens):
+    """Adjoint of compress_learned: with c = sum_u w_u x_u per channel,
+      dx[t_u] += w_u dc,  dscore[t_u] += w_u (x_u - c) dc,  dbias[p_u] += w_u (x_u - c) dc
+    summed over every group reading the token (two for overlapping groups).  Returns
+    (dx [T, dim], dscore [T, dim], dbias like bias)."""
+    x = np.asarray(x, dtype=np.float64)
+    score = np.asarray(score, dtype=np.float64)
+    bias = np.asarray(bias, dtype=np.float64)
+    d_cmp = np.asarray(d_cmp, dtype=np.float64)
+    dx = np.zeros((total_tokens, x.shape[1]))
+    ds = np.zeros((total_tokens, x.shape[1]))
+    db = np.zeros_like(bias)
+    for row, toks, pos in _learned_groups(cu_seqlens, ratio, overlap):
+        z = score[toks] + bias[pos]
+        z = z - z.max(axis=0, keepdims=True)
+        w = np.exp(z)
+        w /= w.sum(axis=0, keepdims=True)
+        c = (w * x[toks]).sum(axis=0)
+        dz = w * (x[toks] - c) * d_cmp[row]
+        dx[toks] += w * d_cmp[row]
+        ds[toks] += dz
+        db[pos] += dz
+    return dx, ds, db
 
 
 # ---------------------------------------------------------------------------

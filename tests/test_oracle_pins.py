@@ -558,6 +558,83 @@ def test_kl_open_relu_bound_covers_mask_flips():
         assert np.all(np.abs(a_ - b_) <= bound + 1e-9)
 
 
+# ------------------------------------------------------------------ learned compressor
+def _learned_case(lens, dim=5, r=4, seed=31):
+    rng = np.random.default_rng(seed)
+    cu = _cu(lens)
+    T = int(cu[-1])
+    return cu, rng.standard_normal((T, dim)), rng.standard_normal((T, dim)), rng
+
+
+def test_learned_compressor_reduces_to_mean_pool_and_window_mean():
+    """Zero scores and positional parameter: non-overlapping groups are the mean-pool
+    compressor; overlapping groups are the plain mean of their 8 (group 0: 4) tokens."""
+    lens = [13, 9, 4, 3]
+    cu, x, _, _ = _learned_case(lens)
+    T, dim, r = x.shape[0], x.shape[1], 4
+    z = np.zeros((T, dim))
+    got = O.compress_learned(x, z, np.zeros((r, dim)), cu, r, overlap=False)
+    assert np.allclose(got, O.compress(x, cu, r), rtol=0, atol=1e-14)
+    got = O.compress_learned(x, z, np.zeros((2 * r, dim)), cu, r, overlap=True)
+    rows = []
+    for s, L in zip(cu[:-1], np.diff(cu)):
+        for j in range(L // r):
+            lo = s + max(0, j - 1) * r
+            rows.append(x[lo: s + (j + 1) * r].mean(axis=0))
+    assert np.allclose(got, np.array(rows), rtol=0, atol=1e-14)
+
+
+def test_learned_compressor_limits_and_invariances():
+    lens = [12, 8]
+    cu, x, s, rng = _learned_case(lens, seed=37)
+    T, dim, r = x.shape[0], x.shape[1], 4
+    bias = rng.standard_normal((2 * r, dim))
+    base = O.compress_learned(x, s, bias, cu, r, overlap=True)
+    # a per-channel constant added to every score leaves every softmax unchanged
+    shift = O.compress_learned(x, s + rng.standard_normal(dim), bias, cu, r, overlap=True)
+    assert np.allclose(base, shift, rtol=0, atol=1e-12)
+    # one dominant token per channel: the row is that token's value
+    s2 = s.copy()
+    s2[9] += 200.0      # token 9: in sample 0's group 2 (own) and nowhere else
+    out = O.compress_learned(x, s2, bias, cu, r, overlap=True)
+    assert np.allclose(out[2], x[9], rtol=0, atol=1e-12)
+    # compression restarts per sample: sample 0's tokens do not reach sample 1's rows
+    x3 = x.copy()
+    x3[:12] = rng.standard_normal((12, dim))
+    out3 = O.compress_learned(x3, s, bias, cu, r, overlap=True)
+    n0 = 12 // r
+    assert np.array_equal(out3[n0:], base[n0:])
+    assert not np.allclose(out3[:n0], base[:n0])
+
+
+def test_learned_compressor_adjoint_finite_differences():
+    lens = [11, 9]
+    for overlap in (True, False):
+        cu, x, s, rng = _learned_case(lens, dim=3, seed=41)
+        T, dim, r = x.shape[0], x.shape[1], 4
+        bias = rng.standard_normal(((2 if overlap else 1) * r, dim))
+        Tc = int(O.cmp_seqlens(cu, r)[-1])
+        dc = rng.standard_normal((Tc, dim))
+        dx, ds, db = O.compress_learned_bwd(x, s, bias, dc, cu, r, overlap, T)
+
+        def f(x_, s_, b_):
+            return float((O.compress_learned(x_, s_, b_, cu, r, overlap) * dc).sum())
+
+        eps = 1e-6
+        for arr, grad in ((x, dx), (s, ds), (bias, db)):
+            flat = arr.reshape(-1)
+            for pos in range(flat.size):
+                old = flat[pos]
+                flat[pos] = old + eps
+                fp = f(x, s, bias)
+                flat[pos] = old - eps
+                fm = f(x, s, bias)
+                flat[pos] = old
+                assert abs((fp - fm) / (2 * eps) - grad.reshape(-1)[pos]) <= 1e-7, (overlap, pos)
+        # tail tokens of a sample feed no group: zero gradient there
+        assert not dx[8:11].any() and not ds[8:11].any()
+
+
 # --------------------------------------------------------------------------- fp8
 def test_e4m3_golden_codes():
     for ln in _gold_lines("e4m3_codes.txt"):
