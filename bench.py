@@ -57,10 +57,13 @@ CALL_KERNELS = {
                  "k_bwd_csr_scan", "k_bwd_reduce_cmp", "k_bwd_reduce_win", "k_attn_bwd_generic"),
     "attn_fwd": ("k_attn_fwd_mfma", "k_attn_fwd_generic"),
     "indexer_kl": ("k_kl_cached", "k_fill_zero_i32", "k_csr_pairs", "k_csr_scan", "k_csr_reduce",
-                   "k_indexer_kl_mfma", "k_kl_generic", "k_sum"),
+                   "k_indexer_kl_mfma", "k_kl_generic", "k_sum", "k_kld_teacher",
+                   "k_kld_queries", "k_kld_keys", "k_kld_dequant"),
     "index_topk": ("k_index_topk",),
     "index_scores": ("k_index_scores_mfma", "k_index_scores_generic"),
-    "topk_select": ("k_topk_wave", "k_topk"),
+    "topk_select": ("k_topk_wave", "k_topk_wg"),
+    "compress_learned (kv + kI)": ("k_compress_learned",),
+    "compress_learned_bwd (kv + kI)": ("k_compress_learned_bwd",),
     "quantize": ("k_quantize_fp8",),
     "compress (kv + kI)": ("k_compress",),
     "compress_bwd (kv + kI)": ("k_compress_bwd",),
@@ -196,6 +199,14 @@ def roofline_table(w, c, T):
         "attn_bwd": (mm, 10 * D * H * c["cand"]),
         "compress_bwd_kv": ("hbm", c["tcmp"] * D * 4 + 2 * c["tcmp"] * w.ratio * D * 4),
         "compress_bwd_kI": ("hbm", c["tcmp"] * dI * 4 + 2 * c["tcmp"] * w.ratio * dI * 4),
+        # learned-score compressor: value and score rows read once, compressed rows written;
+        # adjoint: value/score rows and d_x_cmp read, dx and dscore read-modify-written
+        "compress_learned_kv": ("hbm", 2 * c["tokens"] * D * e + c["tcmp"] * D * e),
+        "compress_learned_bwd_kv": ("hbm", 2 * c["tokens"] * D * e + c["tcmp"] * D * 4 +
+                                    4 * c["tcmp"] * w.ratio * D * 4),
+        "compress_learned_kI": ("hbm", 2 * c["tokens"] * dI * 2 + c["tcmp"] * dI * 2),
+        "compress_learned_bwd_kI": ("hbm", 2 * c["tokens"] * dI * 2 + c["tcmp"] * dI * 4 +
+                                    4 * c["tcmp"] * w.ratio * dI * 4),
     }
     _ = ei
     return tab
@@ -230,6 +241,44 @@ def standalone_topk(layer, dev, cu, reps):
           file=sys.stderr, flush=True)
     if not same:
         raise RuntimeError("fused and stand-alone top-k selections differ")
+    return {f"{k}_standalone": v for k, v in timer.mean_ms().items()}
+
+
+def standalone_learned_compressor(layer, dev, w, cu, reps):
+    """Mean ms of the learned-score compressor and its adjoint on the step's main KV rows
+    (and indexer key rows), with seeded synthetic score rows and positional parameter;
+    ratio-4 groups overlap their left neighbour, ratio-128 groups do not."""
+    from long_context_compressed_amd import binding as B
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(97)
+    overlap = w.ratio == 4
+    span = (2 if overlap else 1) * w.ratio
+    jobs = [("kv", dev["kv"])]
+    if layer.cfg.has_indexer:
+        jobs.append(("kI", dev["kI_tok"]))
+    timer = EventTimer()
+    for tag, x in jobs:
+        dim = x.shape[-1]
+        sc = torch.randn(x.shape, generator=gen, device="cuda").to(x.dtype)
+        bias = torch.randn((span, dim), generator=gen, device="cuda")
+        out = torch.empty((layer.tc_cap, dim), dtype=x.dtype, device="cuda")
+        dc = torch.randn((layer.tc_cap, dim), generator=gen, device="cuda")
+        dx = torch.zeros(x.shape, dtype=torch.float32, device="cuda")
+        ds = torch.zeros_like(dx)
+        db = torch.zeros_like(bias)
+        for i in range(reps + 1):
+            tm = timer if i > 0 else None
+            for name, fn, args in (
+                    (f"compress_learned_{tag}", B.csa_compress_learned,
+                     (layer.p, x, sc, bias, overlap, cu, layer.cu_cmp, out)),
+                    (f"compress_learned_bwd_{tag}", B.csa_compress_learned_bwd,
+                     (layer.p, x, sc, bias, dc, overlap, cu, layer.cu_cmp, dx, ds, db))):
+                if tm:
+                    tm.mark(name)
+                fn(*args)
+                if tm:
+                    tm.done(name)
+    torch.cuda.synchronize()
     return {f"{k}_standalone": v for k, v in timer.mean_ms().items()}
 
 
@@ -353,6 +402,9 @@ def main():
         # the step selects with the fused call; the stand-alone top-k over a materialized
         # score matrix is timed after the step loop, on the same inputs
         per_call.update(standalone_topk(layer, dev, cu, reps=max(args.steps, 3)))
+    if w.mode != "window":
+        # the learned-score compressor (the mean-pool one runs in the step)
+        per_call.update(standalone_learned_compressor(layer, dev, w, cu, reps=max(args.steps, 3)))
     breakdown = {}
     for name, t in per_call.items():
         bound, amount = tab.get(name.replace("_standalone", ""), ("", 0))

@@ -16,6 +16,8 @@
  *   csa_indexer_kl       KL auxiliary loss and its eager indexer backward (sections 3, 8.2)
  *   csa_sparse_attn_bwd  dq, dkv, dsink from saved O, LSE and dO          (section 8.2)
  *   csa_compress_bwd     adjoint of the compressor                        (section 3 ownership)
+ *   csa_compress_learned      learned-score compressor, overlapping groups (sections 4, 5.1, 8.2, 9)
+ *   csa_compress_learned_bwd  its adjoint
  *
  * Conventions shared by every call
  * --------------------------------
@@ -56,7 +58,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 4
+#define CSA_ABI_VERSION 5
 
 typedef int32_t csa_status_t;
 enum {
@@ -137,6 +139,33 @@ csa_status_t csa_compress(const csa_params_t* p, int32_t dtype, const void* x, i
 csa_status_t csa_compress_bwd(const csa_params_t* p, const float* d_x_cmp, int32_t dim,
                               const int32_t* cu_seqlens, const int32_t* cu_cmp, float* dx,
                               hipStream_t stream);
+
+/* Learned-score compressor (sections 4, 5.1, 8.2, 9).  For group j of sample b (complete
+ * groups only, as csa_compress), per channel d:
+ *   x_cmp[cu_cmp[b] + j, d] = sum_u w_u[d] x[t_u, d],  w[d] = softmax_u(score[t_u, d] + bias[p_u, d]),
+ * over the source tokens t_u: the group's own r tokens at positions r .. 2r-1 and, when
+ * overlap != 0 and j > 0, its left neighbour's r tokens at positions 0 .. r-1 (compression
+ * restarts at each sample, so group 0 has no left neighbour); overlap == 0: the own tokens at
+ * positions 0 .. r-1.  x, score: [total_tokens, dim] of dtype (CSA_F32 / CSA_BF16); bias:
+ * fp32 [(overlap ? 2 : 1) * ratio, dim]; x_cmp: [Tc, dim] of dtype, overwritten.  dim % 8 ==
+ * 0, dim <= 2048; overlap is 0 or 1 (CSA_ERR_ARG otherwise).  Reads p->batch,
+ * total_tokens, ratio. */
+csa_status_t csa_compress_learned(const csa_params_t* p, int32_t dtype, const void* x,
+                                  const void* score, const float* bias, int32_t dim,
+                                  int32_t overlap, const int32_t* cu_seqlens,
+                                  const int32_t* cu_cmp, void* x_cmp, hipStream_t stream);
+
+/* Adjoint of csa_compress_learned for d_x_cmp (fp32 [Tc, dim]): with c the compressed row,
+ *   dx[t_u] += w_u d,  dscore[t_u] += w_u (x[t_u] - c) d,  dbias[p_u] += w_u (x[t_u] - c) d
+ * (per channel, d = d_x_cmp of the group), summed over every group that reads the token.
+ * dx, dscore: fp32 [total_tokens, dim]; dbias: fp32 like bias; all ACCUMULATE (caller
+ * zeroes).  Tail and padding rows are untouched.  Same operands and limits as the forward. */
+csa_status_t csa_compress_learned_bwd(const csa_params_t* p, int32_t dtype, const void* x,
+                                      const void* score, const float* bias,
+                                      const float* d_x_cmp, int32_t dim, int32_t overlap,
+                                      const int32_t* cu_seqlens, const int32_t* cu_cmp,
+                                      float* dx, float* dscore, float* dbias,
+                                      hipStream_t stream);
 
 /* Per-row OCP e4m3 quantization (FP8 indexer, section 9): scale = max|row| / 448 in
  * fp32 (1 for an all-zero row); code = e4m3(x / scale), fp32 division, round to nearest

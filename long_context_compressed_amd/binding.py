@@ -54,6 +54,9 @@ _SIGS = {
     "csa_compress": ([_PP, _I32, _P, _I32, _P, _P, _P, _P], _I32),
     "csa_compress_bwd": ([_PP, _P, _I32, _P, _P, _P, _P], _I32),
     "csa_quantize_fp8": ([_P, _I32, _I64, _I32, _P, _P, _P], _I32),
+    "csa_compress_learned": ([_PP, _I32, _P, _P, _P, _I32, _I32, _P, _P, _P, _P], _I32),
+    "csa_compress_learned_bwd": ([_PP, _I32, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P],
+                                 _I32),
     "csa_index_scores": ([_PP, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _P], _I32),
     "csa_topk_select": ([_PP, _P, _I64, _P, _P, _P, _P], _I32),
     "csa_index_topk": ([_PP, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I64, _P, _P], _I32),
@@ -155,6 +158,20 @@ def csa_compress_bwd(p, d_x_cmp, cu_seqlens, cu_cmp, dx, stream=None):
     _check("csa_compress_bwd", lib().csa_compress_bwd(
         ctypes.byref(p), _ptr(d_x_cmp), d_x_cmp.shape[-1], _ptr(cu_seqlens), _ptr(cu_cmp),
         _ptr(dx), _stream(stream)))
+
+
+def csa_compress_learned(p, x, score, bias, overlap, cu_seqlens, cu_cmp, x_cmp, stream=None):
+    _check("csa_compress_learned", lib().csa_compress_learned(
+        ctypes.byref(p), dtype_code(x), _ptr(x), _ptr(score), _ptr(bias), x.shape[-1],
+        int(overlap), _ptr(cu_seqlens), _ptr(cu_cmp), _ptr(x_cmp), _stream(stream)))
+
+
+def csa_compress_learned_bwd(p, x, score, bias, d_x_cmp, overlap, cu_seqlens, cu_cmp, dx,
+                             dscore, dbias, stream=None):
+    _check("csa_compress_learned_bwd", lib().csa_compress_learned_bwd(
+        ctypes.byref(p), dtype_code(x), _ptr(x), _ptr(score), _ptr(bias), _ptr(d_x_cmp),
+        x.shape[-1], int(overlap), _ptr(cu_seqlens), _ptr(cu_cmp), _ptr(dx), _ptr(dscore),
+        _ptr(dbias), _stream(stream)))
 
 
 def csa_quantize_fp8(x, codes, row_scale, stream=None):

@@ -126,6 +126,44 @@ csa_status_t csa_compress_bwd(const csa_params_t* p, const float* d_x_cmp, int32
                                            stream));
 }
 
+static csa_status_t check_learned(const csa_params_t* p, int32_t dtype, int32_t dim,
+                                  int32_t overlap) {
+  if (dim < 8 || (overlap != 0 && overlap != 1)) return CSA_ERR_ARG;
+  if (!dtype_main_ok(dtype) || dim % 8 != 0 || dim > 2048) return CSA_ERR_UNSUPPORTED;
+  (void)p;
+  return CSA_OK;
+}
+
+csa_status_t csa_compress_learned(const csa_params_t* p, int32_t dtype, const void* x,
+                                  const void* score, const float* bias, int32_t dim,
+                                  int32_t overlap, const int32_t* cu_seqlens,
+                                  const int32_t* cu_cmp, void* x_cmp, hipStream_t stream) {
+  csa_status_t st = check_common(p);
+  if (st) return st;
+  if (!x || !score || !bias || !cu_seqlens || !cu_cmp || !x_cmp) return CSA_ERR_NULL;
+  st = check_learned(p, dtype, dim, overlap);
+  if (st) return st;
+  return launched(csa::launch_compress_learned(make_shape(p, cu_seqlens, cu_cmp), dtype, x, score,
+                                               bias, dim, overlap, x_cmp, stream));
+}
+
+csa_status_t csa_compress_learned_bwd(const csa_params_t* p, int32_t dtype, const void* x,
+                                      const void* score, const float* bias,
+                                      const float* d_x_cmp, int32_t dim, int32_t overlap,
+                                      const int32_t* cu_seqlens, const int32_t* cu_cmp,
+                                      float* dx, float* dscore, float* dbias,
+                                      hipStream_t stream) {
+  csa_status_t st = check_common(p);
+  if (st) return st;
+  if (!x || !score || !bias || !d_x_cmp || !cu_seqlens || !cu_cmp || !dx || !dscore || !dbias)
+    return CSA_ERR_NULL;
+  st = check_learned(p, dtype, dim, overlap);
+  if (st) return st;
+  return launched(csa::launch_compress_learned_bwd(make_shape(p, cu_seqlens, cu_cmp), dtype, x,
+                                                   score, bias, d_x_cmp, dim, overlap, dx, dscore,
+                                                   dbias, stream));
+}
+
 csa_status_t csa_quantize_fp8(const void* x, int32_t x_dtype, int64_t rows, int32_t row_len,
                               uint8_t* codes, float* row_scale, hipStream_t stream) {
   if (!x || !codes || !row_scale) return CSA_ERR_NULL;

@@ -35,6 +35,13 @@ hipError_t launch_compress(const Shape& sh, int dtype, const void* x, int dim, v
                            hipStream_t s);
 hipError_t launch_compress_bwd(const Shape& sh, const float* d_cmp, int dim, float* dx,
                                hipStream_t s);
+hipError_t launch_compress_learned(const Shape& sh, int dtype, const void* x, const void* score,
+                                   const float* bias, int dim, int overlap, void* x_cmp,
+                                   hipStream_t s);
+hipError_t launch_compress_learned_bwd(const Shape& sh, int dtype, const void* x,
+                                       const void* score, const float* bias,
+                                       const float* d_x_cmp, int dim, int overlap, float* dx,
+                                       float* dscore, float* dbias, hipStream_t s);
 hipError_t launch_quantize_fp8(const void* x, int dtype, int64_t rows, int row_len,
                                uint8_t* codes, float* scale, hipStream_t s);
 hipError_t launch_index_scores(const Shape& sh, const void* qI, const float* qI_scale,

@@ -23,14 +23,14 @@ def _params(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = B.header_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B._SIGS)
 
 
 def test_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 4
+    assert lib.csa_abi_version() == 5
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.csa_status_string(st)
     assert lib.csa_status_string(7) == b"unknown status"
@@ -69,6 +69,22 @@ def test_compress_validation(lib):
     g = lib.csa_compress_bwd
     assert g(ctypes.byref(p), FAKE, 64, FAKE, FAKE, None, None) == B.CSA_ERR_NULL
     assert g(ctypes.byref(p), FAKE, 12, FAKE, FAKE, FAKE, None) == B.CSA_ERR_UNSUPPORTED
+
+
+def test_learned_compressor_validation(lib):
+    p = _params()
+    f, g = lib.csa_compress_learned, lib.csa_compress_learned_bwd
+    ok = [FAKE, FAKE, FAKE]                       # x, score, bias
+    assert f(ctypes.byref(p), 0, FAKE, FAKE, None, 64, 1, FAKE, FAKE, FAKE, None) == B.CSA_ERR_NULL
+    assert f(ctypes.byref(p), 0, *ok, 64, 2, FAKE, FAKE, FAKE, None) == B.CSA_ERR_ARG
+    assert f(ctypes.byref(p), 0, *ok, 4, 1, FAKE, FAKE, FAKE, None) == B.CSA_ERR_ARG
+    assert f(ctypes.byref(p), 0, *ok, 60, 1, FAKE, FAKE, FAKE, None) == B.CSA_ERR_UNSUPPORTED
+    assert f(ctypes.byref(p), 2, *ok, 64, 1, FAKE, FAKE, FAKE, None) == B.CSA_ERR_UNSUPPORTED
+    assert f(None, 0, *ok, 64, 1, FAKE, FAKE, FAKE, None) == B.CSA_ERR_NULL
+    assert g(ctypes.byref(p), 0, *ok, FAKE, 64, 1, FAKE, FAKE, FAKE, FAKE, None,
+             None) == B.CSA_ERR_NULL                                          # dbias
+    assert g(ctypes.byref(p), 1, *ok, FAKE, 4096, 0, FAKE, FAKE, FAKE, FAKE, FAKE,
+             None) == B.CSA_ERR_UNSUPPORTED
 
 
 def test_cmp_seqlens_and_quantize_validation(lib):

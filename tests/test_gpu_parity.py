@@ -133,6 +133,67 @@ def test_compress_bwd(name):
     G.check("dx", G.back(dx), ref, "f32")
 
 
+LEARNED_CASES = {
+    # name: (lengths, capacity T, dim, ratio, overlap, dtype)
+    "f32_overlap_tails_pad": ((13, 9, 4, 3, 20), 56, 64, 4, True, "f32"),
+    "f32_nonoverlap": ((13, 9, 4, 3, 20), 56, 64, 4, False, "f32"),
+    "bf16_csa_thd_kv": ((301, 515, 1027), 1856, 512, 4, True, "bf16"),
+    "bf16_csa_thd_indexer_key": ((301, 515, 1027), 1856, 128, 4, True, "bf16"),
+    "bf16_hca": ((1024, 700, 300), 2048, 512, 128, False, "bf16"),
+    "bf16_csa_64k_full": (None, 65536, 512, 4, True, "bf16"),
+}
+
+
+@pytest.mark.parametrize("name", list(LEARNED_CASES))
+def test_compress_learned_fwd_bwd(name):
+    """Learned-score compressor and its adjoint against the oracle on every row; capacity
+    padding rows hold NaN (never read)."""
+    from long_context_compressed_amd import binding as B
+    lens, T, dim, r, overlap, dt_name = LEARNED_CASES[name]
+    _announce(name, "compress_learned")
+    if lens is None:   # the 64K THD batch's lengths
+        lens = tuple(synth_inputs.draw_lengths(configs.workload("thd64k_csa_bf16")))
+    rng = np.random.default_rng(53)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n = int(cu[-1])
+    dt = G.torch_dtype(dt_name)
+    x = G.rounded(rng.standard_normal((T, dim)), dt)
+    sc = G.rounded(rng.standard_normal((T, dim)) * 2.0, dt)
+    x[n:] = np.nan
+    sc[n:] = np.nan
+    span = (2 if overlap else 1) * r
+    bias = rng.standard_normal((span, dim)).astype(np.float32).astype(np.float64)
+    p = B.make_params(batch=len(lens), total_tokens=T, max_seqlen=max(lens), ratio=r, window=1,
+                      topk=1, topk_cap=64, heads=1, head_dim=8, idx_heads=0, idx_dim=0,
+                      scale=1.0, mode=B.CSA_DENSE, teacher=B.CSA_TEACHER_NONE,
+                      dtype=B.CSA_BF16 if dt_name == "bf16" else B.CSA_F32, idx_dtype=B.CSA_BF16)
+    cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    cmp_d = torch.empty(len(lens) + 1, dtype=torch.int32, device="cuda")
+    B.csa_cmp_seqlens(cu_d, len(lens), r, cmp_d)
+    xd, sd = G.dev(x, dt), G.dev(sc, dt)
+    bd = torch.from_numpy(bias.astype(np.float32)).cuda()
+    Tc = int(O.cmp_seqlens(cu, r)[-1])
+    out = torch.full((max(Tc, 1), dim), float("nan"), dtype=dt, device="cuda")
+    B.csa_compress_learned(p, xd, sd, bd, overlap, cu_d, cmp_d, out)
+    ref = O.compress_learned(x[:n], sc[:n], bias, cu, r, overlap)
+    torch.cuda.synchronize()
+    G.check("x_cmp", G.back(out)[:Tc], ref, dt_name)
+    # adjoint, accumulated onto nonzero starting values
+    dc = rng.standard_normal((max(Tc, 1), dim)).astype(np.float32)
+    dx0 = rng.standard_normal((T, dim)).astype(np.float32)
+    dx = torch.from_numpy(dx0).cuda()
+    ds = torch.from_numpy(dx0[::-1].copy()).cuda()
+    db = torch.ones((span, dim), dtype=torch.float32, device="cuda")
+    B.csa_compress_learned_bwd(p, xd, sd, bd, torch.from_numpy(dc).cuda(), overlap, cu_d, cmp_d,
+                               dx, ds, db)
+    rdx, rds, rdb = O.compress_learned_bwd(x[:n], sc[:n], bias, dc[:Tc], cu, r, overlap, n)
+    torch.cuda.synchronize()
+    G.check("dx", G.back(dx)[:n] - dx0[:n], rdx, dt_name)
+    G.check("dscore", G.back(ds)[:n] - dx0[::-1][:n], rds, dt_name)
+    G.check("dbias", G.back(db) - 1.0, rdb, dt_name)
+    assert np.array_equal(G.back(dx)[n:], dx0[n:].astype(np.float64)), "padding rows of dx written"
+
+
 def test_quantize_fp8_bit_exact():
     from long_context_compressed_amd import binding as B
     rng = np.random.default_rng(5)
