@@ -39,6 +39,9 @@ CASES = {
                                                    total_tokens=2048)),
     "window_bf16_thd_small": ("thd64k_window_bf16", dict(lengths=(301, 515, 1027),
                                                          total_tokens=1856, draw=None)),
+    "sink_bf16_thd_small": ("thd64k_csa_sink_bf16", dict(lengths=(301, 515, 1027),
+                                                         total_tokens=1856, topk=64,
+                                                         topk_cap=64, draw=None)),
     "fp8_warmup_small": ("csa128k_warmup_fp8", dict(lengths=(1500,), total_tokens=1536,
                                                     topk=64, topk_cap=64)),
 }
