@@ -41,7 +41,11 @@ Readings taken where the page leaves a step open (each restated where used):
   R20 learned compressor = per channel, softmax over the group's source tokens of
      (score row + positional parameter) weighting the value rows; ratio-4 groups
      overlap their left neighbour (8 source tokens), ratio-128 groups do not; the
-     normalization is the softmax's own (no further learned scaling).
+     normalization is the softmax's own (no further learned scaling);
+  R22 RoPE = rotation of the interleaved channel pairs of the last rope_dim channels by
+     position * theta^(-2i / rope_dim); positions restart per sample, token rows use the
+     local token position, compressed rows their index within the sample; the inverse
+     (on the attention output, at the query's position) rotates by the opposite angle.
 """
 import numpy as np
 
@@ -195,6 +199,45 @@ def compress_learned_bwd(x, score, bias, d_cmp, cu_seqlens, ratio, overlap, tota
         ds[toks] += dz
         db[pos] += dz
     return dx, ds, db
+
+
+# ---------------------------------------------------------------------------
+# rotary position embedding (reading R22)
+# ---------------------------------------------------------------------------
+def rope_positions(cu_seqlens, n_rows, ratio=None):
+    """Position of each row, restarting at every packed sample (section 4): the local token
+    position p for token rows (ratio None), or the compressed index j within the sample for
+    compressed rows (ratio given: the compressed coordinate system, section 12).  -1 marks
+    rows outside every sample."""
+    if ratio is None:
+        _, pp = token_positions(cu_seqlens, n_rows)
+        return np.where(pp >= 0, pp, -1)
+    cu_cmp = cmp_seqlens(cu_seqlens, ratio)
+    pos = np.full(n_rows, -1, dtype=np.int64)
+    for b in range(len(cu_cmp) - 1):
+        pos[cu_cmp[b]:cu_cmp[b + 1]] = np.arange(cu_cmp[b + 1] - cu_cmp[b])
+    return pos
+
+
+def rope(x, pos, rope_dim, theta, inverse=False):
+    """Rotate the interleaved channel pairs (2i, 2i+1) of the last rope_dim channels of each
+    row by pos * theta^(-2i / rope_dim) (by minus that for the inverse); rows with pos < 0
+    are returned unchanged.  x: [rows, ..., dim]; pos: [rows]."""
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    dim = x.shape[-1]
+    i = np.arange(rope_dim // 2)
+    inv_freq = float(theta) ** (-2.0 * i / rope_dim)
+    for r, p in enumerate(np.asarray(pos)):
+        if p < 0:
+            continue
+        ang = (-1.0 if inverse else 1.0) * p * inv_freq
+        c, s = np.cos(ang), np.sin(ang)
+        a = x[r, ..., dim - rope_dim::2]
+        b_ = x[r, ..., dim - rope_dim + 1::2]
+        out[r, ..., dim - rope_dim::2] = a * c - b_ * s
+        out[r, ..., dim - rope_dim + 1::2] = a * s + b_ * c
+    return out
 
 
 # ---------------------------------------------------------------------------

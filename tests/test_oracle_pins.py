@@ -635,6 +635,49 @@ def test_learned_compressor_adjoint_finite_differences():
         assert not dx[8:11].any() and not ds[8:11].any()
 
 
+# ------------------------------------------------------------------------------ RoPE
+def test_rope_rotation_properties():
+    """Inverse is the transpose, norms of every pair are kept, position 0 is the identity,
+    and dot products of the rope band depend only on the relative position (the defining
+    property of a rotary embedding); the nope channels are untouched."""
+    rng = np.random.default_rng(61)
+    dim, rd, theta = 24, 8, 10000.0
+    x = rng.standard_normal((6, dim))
+    pos = np.array([0, 1, 5, 37, 1000, 131071])
+    y = O.rope(x, pos, rd, theta)
+    assert np.allclose(O.rope(y, pos, rd, theta, inverse=True), x, rtol=0, atol=1e-12)
+    assert np.array_equal(y[:, :dim - rd], x[:, :dim - rd])
+    assert np.array_equal(y[0], x[0])
+    pair = lambda a: a[:, dim - rd:].reshape(len(a), rd // 2, 2)      # noqa: E731
+    assert np.allclose(np.linalg.norm(pair(y), axis=2), np.linalg.norm(pair(x), axis=2))
+    q, k = rng.standard_normal(dim), rng.standard_normal(dim)
+    dots = []
+    for m, n in ((7, 3), (104, 100), (4, 0)):
+        qm = O.rope(q[None], [m], rd, theta)[0, dim - rd:]
+        kn = O.rope(k[None], [n], rd, theta)[0, dim - rd:]
+        dots.append(qm @ kn)
+    assert np.allclose(dots, dots[0], rtol=0, atol=1e-12)
+    # closed form: pair 0 (frequency 1) at position 1 turns by one radian
+    z = np.zeros((1, dim))
+    z[0, dim - rd], z[0, dim - rd + 1] = 2.0, 3.0
+    r1 = O.rope(z, [1], rd, theta)[0, dim - rd: dim - rd + 2]
+    assert np.allclose(r1, [2 * np.cos(1.0) - 3 * np.sin(1.0), 2 * np.sin(1.0) + 3 * np.cos(1.0)])
+    # pair 1 turns at theta^(-2/8) = 0.1 rad per position: one radian at position 10, while
+    # pair 0 has turned 10 radians there
+    z[0, dim - rd + 2], z[0, dim - rd + 3] = -1.0, 0.5
+    r10 = O.rope(z, [10], rd, theta)[0, dim - rd:]
+    c1, s1, c10, s10 = np.cos(1.0), np.sin(1.0), np.cos(10.0), np.sin(10.0)
+    assert np.allclose(r10[:4], [2 * c10 - 3 * s10, 2 * s10 + 3 * c10, -c1 - 0.5 * s1, -s1 + 0.5 * c1])
+    assert np.array_equal(r10[4:], np.zeros(rd - 4))
+
+
+def test_rope_positions_restart_per_sample():
+    cu = _cu([5, 3, 6])
+    assert list(O.rope_positions(cu, 16)) == [0, 1, 2, 3, 4, 0, 1, 2, 0, 1, 2, 3, 4, 5, -1, -1]
+    assert list(O.rope_positions(cu, 6, ratio=2)) == [0, 1, 0, 0, 1, 2]   # 2 + 1 + 3 rows
+    assert list(O.rope_positions(cu, 7, ratio=2)) == [0, 1, 0, 0, 1, 2, -1]
+
+
 # --------------------------------------------------------------------------- fp8
 def test_e4m3_golden_codes():
     for ln in _gold_lines("e4m3_codes.txt"):
