@@ -559,26 +559,49 @@ def indexer_kl(q, kv_cmp, scores, idx, qI, w, kI_cmp, cu_seqlens, ratio, scale, 
 def layer_step(inp, cfg, rows=None, backward=None, grad_scale=1.0):
     """Chain the steps on host arrays.  inp holds float64 arrays q, kv, [qI, kI_tok, w],
     [dO], [sink], cu_seqlens; cfg supplies ratio, window, topk, topk_cap, scale, mode,
-    teacher, idx_dtype.  Per-query outputs are returned for `rows`; the shared-row
-    gradients (dkv, dkI_tok) are complete only when rows covers every query."""
+    teacher, idx_dtype and optionally rope_dim / rope_theta.  Per-query outputs are returned
+    for `rows`; the shared-row gradients (dkv, dkI_tok) are complete only when rows covers
+    every query.
+
+    With rope_dim > 0 (reading R22) the layer rotates q, qI and the window rows of kv at
+    their token positions and the compressed rows of kv and kI at their compressed
+    positions, all restarting per sample (section 4); O stays unrotated (it is what the
+    attention backward consumes) and O_rot, the inverse rotation of O at the query's
+    position, is the layer output, so dO is taken as the gradient of O_rot.  The gradients
+    returned are those of the unrotated inputs (a rotation's adjoint is its inverse)."""
     cu = inp["cu_seqlens"]
     q = inp["q"]
     T = q.shape[0]
     rows = np.arange(T) if rows is None else np.asarray(rows)
     backward = cfg.backward if backward is None else backward
     r = cfg.ratio
+    rd = int(getattr(cfg, "rope_dim", 0) or 0)
+    theta = float(getattr(cfg, "rope_theta", 0.0) or 0.0)
     res = {}
-    kv_cmp = compress(inp["kv"], cu, r)
+    kv = inp["kv"]
+    kv_cmp = compress(kv, cu, r)
     res["kv_cmp"] = kv_cmp
+    if rd:
+        tpos = rope_positions(cu, T)
+        cpos = rope_positions(cu, kv_cmp.shape[0], ratio=r)
+        rot = lambda x, pos: rope(x, pos, rd, theta)                        # noqa: E731
+        unrot = lambda x, pos: rope(x, pos, rd, theta, inverse=True)        # noqa: E731
+        q = rot(q, tpos)
+        kv = rot(kv, tpos)
+        kv_cmp = rot(kv_cmp, cpos)
     idx = None
     if cfg.mode == "window":          # ratio-0 layer: no compressed candidates at all
         idx = np.full((rows.size, 1), -1, dtype=np.int64)
     if cfg.has_indexer and cfg.mode == "sparse":
         kI_cmp = compress(inp["kI_tok"], cu, r)
         qI = inp["qI"]
+        if rd:
+            qI = rot(qI, tpos)
+            kI_cmp = rot(kI_cmp, cpos)
         if cfg.idx_dtype == "fp8":
+            qI_full = qI
             qI = np.zeros(qI.shape)          # untouched pages stay unallocated
-            qc, qs = quantize_fp8(inp["qI"][rows].astype(np.float32))
+            qc, qs = quantize_fp8(qI_full[rows].astype(np.float32))
             qI[rows] = dequantize_fp8(qc, qs)
             kc, ks = quantize_fp8(kI_cmp.astype(np.float32))
             kI_cmp = dequantize_fp8(kc, ks)
@@ -588,18 +611,30 @@ def layer_step(inp, cfg, rows=None, backward=None, grad_scale=1.0):
         res["scores"] = scores
         idx = topk_select(scores, cu, r, cfg.topk, cfg.topk_cap, T, rows=rows)
         res["idx"] = idx
-    O, LSE = sparse_attn_fwd(q, kv_cmp, inp["kv"], idx, inp.get("sink"), cu, r, cfg.window,
+    O, LSE = sparse_attn_fwd(q, kv_cmp, kv, idx, inp.get("sink"), cu, r, cfg.window,
                              cfg.scale, rows=rows)
     res["O"], res["LSE"] = O, LSE
+    if rd:
+        res["O_rot"] = unrot(O, tpos[rows])
     if cfg.has_indexer and cfg.mode == "sparse" and cfg.teacher != "none":
         kl, loss, dqI, dw, dkI = indexer_kl(q, kv_cmp, res["scores"], idx, qI, inp["w"], kI_cmp,
                                             cu, r, cfg.scale, cfg.teacher, grad_scale, rows=rows)
+        if rd:
+            dqI = unrot(dqI, tpos[rows])
+            dkI = unrot(dkI, cpos)
         res.update(kl=kl, loss=loss, dqI=dqI, dw=dw, dkI_cmp=dkI)
         res["dkI_tok"] = compress_bwd(dkI, cu, r, T)
     if backward:
+        dO = inp["dO"][rows]
+        if rd:
+            dO = rot(dO, tpos[rows])          # gradient of O from that of O_rot
         dq, dkv_cmp, dkv_win, dsink = sparse_attn_bwd(
-            q, kv_cmp, inp["kv"], idx, inp.get("sink"), cu, r, cfg.window, cfg.scale,
-            O, LSE, inp["dO"][rows], rows=rows)
+            q, kv_cmp, kv, idx, inp.get("sink"), cu, r, cfg.window, cfg.scale,
+            O, LSE, dO, rows=rows)
+        if rd:
+            dq = unrot(dq, tpos[rows])
+            dkv_cmp = unrot(dkv_cmp, cpos)
+            dkv_win = unrot(dkv_win, tpos)
         res.update(dq=dq, dkv_cmp=dkv_cmp, dkv_win=dkv_win, dsink=dsink)
         res["dkv"] = dkv_win + compress_bwd(dkv_cmp, cu, r, T)
     return res

@@ -33,6 +33,8 @@ class Workload:
     backward: bool                   # whether the layer step includes backward
     input_std: str                   # "unit" => N(0,1); "inv_sqrt_d" => N(0,1)/sqrt(last dim)
     sink: bool = False               # optional per-head attention sink logit
+    rope_dim: int = 0                # rotary band: last rope_dim channels of q/kv/qI/kI rows
+    rope_theta: float = 10000.0      # rotary base
     draw: Optional[dict] = field(default=None, compare=False)   # length-draw rule
 
     @property

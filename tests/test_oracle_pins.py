@@ -711,11 +711,13 @@ def test_quantize_rows_scale_and_roundtrip():
 
 
 # --------------------------------------------------------------------------- packing
-def test_packing_invariance_whole_layer():
-    """A packed run equals each sample run alone (THD vs single-sequence parity)."""
+@pytest.mark.parametrize("rope_dim", [0, 4])
+def test_packing_invariance_whole_layer(rope_dim):
+    """A packed run equals each sample run alone (THD vs single-sequence parity); with RoPE
+    this pins the per-sample restart of the token and compressed positions."""
     from synth import configs
     cfg = configs.workload("tiny_csa_f32_L256", heads=2, head_dim=8, idx_heads=2, idx_dim=4,
-                           window=5, topk=3, topk_cap=64)
+                           window=5, topk=3, topk_cap=64, rope_dim=rope_dim, rope_theta=50.0)
     lens = [23, 17, 9]
     rng = np.random.default_rng(29)
     cu = _cu(lens)
@@ -734,7 +736,7 @@ def test_packing_invariance_whole_layer():
         one["max_seqlen"] = max(lens)     # same n_cap
         alone = O.layer_step(one, cfg)
         c0, c1 = int(cu_cmp[b]), int(cu_cmp[b + 1])
-        for key in ("O", "LSE", "dq", "dqI", "dw", "kl"):
+        for key in ("O", "LSE", "dq", "dqI", "dw", "kl") + (("O_rot",) if rope_dim else ()):
             np.testing.assert_allclose(packed[key][s:s + L], alone[key], atol=1e-12)
         for key in ("dkv", "dkI_tok"):
             np.testing.assert_allclose(packed[key][s:s + L], alone[key], atol=1e-12)
@@ -743,6 +745,55 @@ def test_packing_invariance_whole_layer():
         sel_p = packed["idx"][s:s + L]
         sel_a = alone["idx"]
         np.testing.assert_array_equal(np.where(sel_p >= 0, sel_p - c0, -1), sel_a)
+
+
+def _rope_layer_case(seed=31):
+    from synth import configs
+    cfg = configs.workload("tiny_csa_f32_L256", heads=2, head_dim=8, idx_heads=2, idx_dim=6,
+                           window=4, topk=3, topk_cap=64, teacher="dense", rope_dim=4,
+                           rope_theta=30.0)
+    lens = [14, 11]
+    rng = np.random.default_rng(seed)
+    cu = _cu(lens)
+    T = int(cu[-1])
+    inp = dict(cu_seqlens=cu, max_seqlen=max(lens),
+               q=rng.standard_normal((T, 2, 8)), kv=rng.standard_normal((T, 8)),
+               qI=rng.standard_normal((T, 2, 6)), kI_tok=rng.standard_normal((T, 6)),
+               w=rng.standard_normal((T, 2)), dO=rng.standard_normal((T, 2, 8)))
+    return cfg, inp
+
+
+def test_rope_layer_gradients_finite_differences():
+    """The rotated layer's gradients are those of the unrotated inputs: dq, dkv of
+    sum(O_rot * dO) and dqI, dkI_tok of the loss match central differences (a rotation used
+    where its inverse belongs, or a position from the wrong coordinate system, fails)."""
+    cfg, inp = _rope_layer_case()
+    res = O.layer_step(inp, cfg)
+    assert not np.allclose(res["O_rot"], res["O"])
+    eps = 1e-6
+    pick = np.random.default_rng(5)
+
+    def objective(key):
+        out = O.layer_step(inp, cfg, backward=False)
+        return float((out["O_rot"] * inp["dO"]).sum()) if key in ("q", "kv") else out["loss"]
+
+    for key, gkey in (("q", "dq"), ("kv", "dkv"), ("qI", "dqI"), ("kI_tok", "dkI_tok")):
+        flat = inp[key].reshape(-1)
+        D = inp[key].shape[-1]
+        # mostly rope-band channels (the last 4 of each row), a few nope ones
+        band = [i for i in range(flat.size) if i % D >= D - 4]
+        cand = np.concatenate([pick.choice(band, 10, replace=False),
+                               pick.choice(flat.size, 4, replace=False)])
+        for pos in cand:
+            old = flat[pos]
+            flat[pos] = old + eps
+            fp = objective(key)
+            flat[pos] = old - eps
+            fm = objective(key)
+            flat[pos] = old
+            num = (fp - fm) / (2 * eps)
+            got = res[gkey].reshape(-1)[pos]
+            assert abs(num - got) <= 1e-6 * max(1.0, abs(num)), (key, pos, num, got)
 
 
 def test_compressed_logits_normalize_to_compressed_lse_and_feed_the_teacher():
