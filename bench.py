@@ -67,6 +67,7 @@ CALL_KERNELS = {
     "quantize": ("k_quantize_fp8",),
     "compress (kv + kI)": ("k_compress",),
     "compress_bwd (kv + kI)": ("k_compress_bwd",),
+    "rope (all operands)": ("k_rope",),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "thd64k_csa_bf16_traffic.md")
 
@@ -208,7 +209,19 @@ def roofline_table(w, c, T):
         "compress_learned_bwd_kI": ("hbm", 2 * c["tokens"] * dI * 2 + c["tcmp"] * dI * 4 +
                                     4 * c["tcmp"] * w.ratio * dI * 4),
     }
-    _ = ei
+    # rotary band: in place the band of each row is read and written; the window rows of kv
+    # are rotated into a buffer of their own (every channel read and written)
+    rd = getattr(w, "rope_dim", 0)
+    if rd:
+        n, m = c["tokens"], c["tcmp"]
+        ei = 4 if w.idx_dtype == "f32" else 2          # rotated before any fp8 quantization
+        tab.update({
+            "rope_q": ("hbm", 2 * n * H * rd * e), "rope_dO": ("hbm", 2 * n * H * rd * e),
+            "rope_dq": ("hbm", 2 * n * H * rd * e), "rope_kv": ("hbm", 2 * n * D * e),
+            "rope_kv_cmp": ("hbm", 2 * m * rd * e), "rope_qI": ("hbm", 2 * n * HI * rd * ei),
+            "rope_kI_cmp": ("hbm", 2 * m * rd * ei), "rope_dqI": ("hbm", 2 * n * HI * rd * 4),
+            "rope_dkv": ("hbm", 2 * n * rd * 4), "rope_dkv_cmp": ("hbm", 2 * m * rd * 4),
+            "rope_dkI_cmp": ("hbm", 2 * m * rd * 4)})
     return tab
 
 
@@ -443,7 +456,8 @@ def main():
                    "lengths": host["lengths"], "heads": w.heads, "head_dim": w.head_dim,
                    "ratio": w.ratio, "window": w.window, "topk": w.topk, "mode": w.mode,
                    "idx_heads": w.idx_heads, "idx_dim": w.idx_dim, "idx_dtype": w.idx_dtype,
-                   "teacher": w.teacher, "pass": "fwd+bwd" if w.backward else "fwd"},
+                   "teacher": w.teacher, "rope_dim": w.rope_dim,
+                   "pass": "fwd+bwd" if w.backward else "fwd"},
         "roofline": roof,
         "attention_tflops": attn_flops / max(attn_ms * 1e-3, 1e-12) / 1e12 if attn_ms else None,
         "topk_gbps": (breakdown.get("topk_select") or

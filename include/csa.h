@@ -18,6 +18,7 @@
  *   csa_compress_bwd     adjoint of the compressor                        (section 3 ownership)
  *   csa_compress_learned      learned-score compressor, overlapping groups (sections 4, 5.1, 8.2, 9)
  *   csa_compress_learned_bwd  its adjoint
+ *   csa_rope             rotary embedding / its inverse at per-sample positions (sections 4, 12)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -58,7 +59,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 5
+#define CSA_ABI_VERSION 6
 
 typedef int32_t csa_status_t;
 enum {
@@ -103,6 +104,9 @@ typedef struct csa_params {
   int32_t teacher;      /* csa_teacher_t                                              */
   int32_t dtype;        /* csa_dtype_t of q, kv, kv_cmp, out, dO, dq: F32 or BF16     */
   int32_t idx_dtype;    /* csa_dtype_t of qI and kI_cmp: F32, BF16 or FP8_E4M3        */
+  int32_t rope_dim;     /* rotary band of the output rotation (csa_sparse_attn_fwd      */
+                        /* out_rot): 0 none, else a multiple of 8 <= head_dim          */
+  float rope_theta;     /* rotary base (> 0) when rope_dim > 0                         */
 } csa_params_t;
 
 /* Workspace-using operations, for csa_workspace_size. */
@@ -225,12 +229,36 @@ csa_status_t csa_index_topk(const csa_params_t* p, const void* qI, const float* 
  * attention's (selected teacher with CSA_SPARSE, dense teacher with CSA_DENSE).
  * q, out: [T, H, D]; kv_cmp: [Tc, D]; kv: [T, D] (dtype); idx: int32 [T, topk_cap] or NULL
  * unless CSA_SPARSE; sink: fp32 [H] or NULL; lse, lse_cmp: fp32 [T, H] (natural log);
- * t_logits: fp32 [T, H, csa_teacher_logits_stride(p)].  lse_cmp and t_logits may be NULL. */
+ * t_logits: fp32 [T, H, csa_teacher_logits_stride(p)].  lse_cmp and t_logits may be NULL.
+ * out_rot: NULL, or [T, H, D] (dtype) receiving out inverse-rotated at the query's local
+ * position (csa_rope with inverse = 1 on out, p->rope_dim and p->rope_theta; zero rows for
+ * padding), written by the same pass where the kernel has a rotating epilogue.  out itself
+ * stays unrotated: it is the saved output the backward consumes (section 10, the
+ * inverse-rotation aliasing contract; section 12, invariant 5), so out_rot must not alias it
+ * (CSA_ERR_ARG, as is out_rot with rope_dim 0). */
 csa_status_t csa_sparse_attn_fwd(const csa_params_t* p, const void* q, const void* kv_cmp,
                                  const void* kv, const int32_t* idx, const float* sink,
                                  const int32_t* cu_seqlens, const int32_t* cu_cmp, void* out,
-                                 float* lse, float* lse_cmp, float* t_logits, void* ws,
-                                 size_t ws_bytes, hipStream_t stream);
+                                 void* out_rot, float* lse, float* lse_cmp, float* t_logits,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Rotary position embedding (section 4: positions restart at every packed sample, for the
+ * main and the indexer operands; section 12, invariant 2: the positional mode is per layer
+ * and per compressed coordinate system).  Row `row` of sample b, row_offsets[b] <= row <
+ * row_offsets[b+1], has position pos = row - row_offsets[b]: pass cu_seqlens for token rows
+ * (q, kv, qI, the output) and cu_cmp for compressed rows (kv_cmp, kI_cmp).  In every head
+ * the interleaved channel pairs (2i, 2i+1) of the last rope_dim channels are rotated by
+ * pos * theta^(-2i / rope_dim) radians (angle formed in fp64), by minus that when inverse = 1;
+ * rows at or beyond row_offsets[batch] are copied unchanged.  A rotation's adjoint is its
+ * inverse, so the same call maps gradients back (inverse = 1 on the gradient of a rotated
+ * operand; inverse = 0 on the gradient of an inverse-rotated output).
+ * x, y: [rows, heads, dim] of dtype F32 or BF16.  y == x rotates in place and touches only
+ * the rotary channels; otherwise y receives every channel and must not overlap x.
+ * dim and rope_dim: multiples of 8, 8 <= rope_dim <= dim; theta > 0; rows < 2^31 (x and y
+ * may be NULL when rows is 0). */
+csa_status_t csa_rope(int32_t dtype, const void* x, void* y, int64_t rows, int32_t heads,
+                      int32_t dim, int32_t rope_dim, float theta, int32_t inverse,
+                      int32_t batch, const int32_t* row_offsets, hipStream_t stream);
 
 /* Row stride (in elements) of the t_logits cache: the compressed-slot capacity (topk_cap
  * for CSA_SPARSE, max_seqlen / ratio for CSA_DENSE) rounded up to a multiple of 64; 0 for

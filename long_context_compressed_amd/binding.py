@@ -28,7 +28,8 @@ class CsaParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "total_tokens", "max_seqlen", "ratio", "window", "topk", "topk_cap",
         "heads", "head_dim", "idx_heads", "idx_dim")] + [("scale", ctypes.c_float)] + [
-        (n, ctypes.c_int32) for n in ("mode", "teacher", "dtype", "idx_dtype")]
+        (n, ctypes.c_int32) for n in ("mode", "teacher", "dtype", "idx_dtype", "rope_dim")] + [
+        ("rope_theta", ctypes.c_float)]
 
 
 class CsaError(RuntimeError):
@@ -60,7 +61,8 @@ _SIGS = {
     "csa_index_scores": ([_PP, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _P], _I32),
     "csa_topk_select": ([_PP, _P, _I64, _P, _P, _P, _P], _I32),
     "csa_index_topk": ([_PP, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I64, _P, _P], _I32),
-    "csa_sparse_attn_fwd": ([_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
+    "csa_sparse_attn_fwd": ([_PP] + [_P] * 13 + [_SZ, _P], _I32),
+    "csa_rope": ([_I32, _P, _P, _I64, _I32, _I32, _I32, _F, _I32, _I32, _P, _P], _I32),
     "csa_teacher_logits_stride": ([_PP], _I64),
     "csa_sparse_attn_bwd": ([_PP] + [_P] * 14 + [_P, _SZ, _P], _I32),
     "csa_indexer_kl": ([_PP, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F,
@@ -204,11 +206,22 @@ def csa_index_topk(p, qI, qI_scale, w, kI_cmp, kI_scale, cu_seqlens, cu_cmp, idx
 
 
 def csa_sparse_attn_fwd(p, q, kv_cmp, kv, idx, sink, cu_seqlens, cu_cmp, out, lse, lse_cmp=None,
-                        ws=None, stream=None, t_logits=None):
+                        ws=None, stream=None, t_logits=None, out_rot=None):
     _check("csa_sparse_attn_fwd", lib().csa_sparse_attn_fwd(
         ctypes.byref(p), _ptr(q), _ptr(kv_cmp), _ptr(kv), _ptr(idx), _ptr(sink), _ptr(cu_seqlens),
-        _ptr(cu_cmp), _ptr(out), _ptr(lse), _ptr(lse_cmp), _ptr(t_logits), _ptr(ws), _nbytes(ws),
-        _stream(stream)))
+        _ptr(cu_cmp), _ptr(out), _ptr(out_rot), _ptr(lse), _ptr(lse_cmp), _ptr(t_logits),
+        _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def csa_rope(x, y, rope_dim, theta, inverse, batch, row_offsets, stream=None):
+    """x, y: [rows, dim] or [rows, heads, dim] of one dtype; y may be x (in place)."""
+    if y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError("x and y must have the same shape and dtype")
+    rows, dim = (x.shape[0], x.shape[-1]) if x.dim() >= 2 else (0, 0)
+    heads = x.numel() // (rows * dim) if rows and dim else 1
+    _check("csa_rope", lib().csa_rope(dtype_code(x), _ptr(x), _ptr(y), rows, heads, dim,
+                                      int(rope_dim), float(theta), int(inverse), int(batch),
+                                      _ptr(row_offsets), _stream(stream)))
 
 
 def csa_teacher_logits_stride(p) -> int:

@@ -350,7 +350,12 @@ hipError_t launch_attn_fwd(const Shape& sh, const AttnIO& io, hipStream_t s) {
                      sizeof(int) * kNB;
   if (sh.dtype == 0) hipLaunchKernelGGL(k_attn_fwd_generic<float>, grid, dim3(256), lds, s, a);
   else hipLaunchKernelGGL(k_attn_fwd_generic<uint16_t>, grid, dim3(256), lds, s, a);
-  return hipGetLastError();
+  e = hipGetLastError();
+  // the generic kernel has no rotating epilogue: the inverse rotation reads the output back
+  if (e == hipSuccess && io.out_rot)
+    e = launch_rope(sh.dtype, io.out, io.out_rot, sh.T, sh.H, sh.D, sh.rope_dim, sh.rope_theta,
+                    1, sh.B, sh.cu, s);
+  return e;
 }
 
 hipError_t launch_attn_bwd(const Shape& sh, const AttnIO& io, hipStream_t s) {

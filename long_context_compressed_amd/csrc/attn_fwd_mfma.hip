@@ -39,8 +39,8 @@ namespace {
 
 constexpr int kNB = 64;        // candidates per block
 constexpr int kPS = 72;        // P tile row stride (bf16)
-constexpr float kLazy = 8.f;
-constexpr int kFwdWaves = 4;     // one wave per SIMD: each wave holds Q (32 heads) and 1/4 of O   // growth (log2 units) of the running max tolerated before rescaling
+constexpr float kLazy = 8.f;   // growth (log2 units) of the running max tolerated before rescaling
+constexpr int kFwdWaves = 4;   // one wave per SIMD: each wave holds Q (32 heads) and 1/4 of O
 
 struct FwdArgs {
   const uint16_t* q;
@@ -51,6 +51,7 @@ struct FwdArgs {
   const int32_t* cu;
   const int32_t* cu_cmp;
   uint16_t* out;
+  uint16_t* out_rot;  // optional: out inverse-rotated at the query position
   float* lse;
   float* lse_cmp;    // optional log-sum-exp over the compressed candidates only
   float* t_logits;   // optional compressed-candidate logits [T, H, ld_t]
@@ -58,6 +59,8 @@ struct FwdArgs {
   int B, T, r, n_cap, W, k_cap, mode;
   float scale;
   float scale_log2;  // softmax scale * log2(e)
+  int rope_dim;      // rotary band of out_rot
+  double rope_l2t;   // log2(theta)
 };
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -95,6 +98,7 @@ void k_attn_fwd_mfma(FwdArgs a) {
   __shared__ float mrun_s[kH], msnap_s[kH], fin_s[kH];
   __shared__ int resc_s[2];
   __shared__ int s_tmp;
+  __shared__ float2 rope_s[kD / 2];   // cos, sin of the output rotation's pairs
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -106,6 +110,10 @@ void k_attn_fwd_mfma(FwdArgs a) {
   if (!token_info_wave(a.cu, a.B, t, ti)) {
     uint4* o = reinterpret_cast<uint4*>(a.out + (int64_t)t * kH * kD);
     for (int e = tid; e < kH * kD / 8; e += NT) o[e] = make_uint4(0, 0, 0, 0);
+    if (a.out_rot) {
+      uint4* orot = reinterpret_cast<uint4*>(a.out_rot + (int64_t)t * kH * kD);
+      for (int e = tid; e < kH * kD / 8; e += NT) orot[e] = make_uint4(0, 0, 0, 0);
+    }
     if (tid < kH) a.lse[(int64_t)t * kH + tid] = 0.f;
     if (a.lse_cmp && tid < kH) a.lse_cmp[(int64_t)t * kH + tid] = -INFINITY;
     return;
@@ -128,6 +136,17 @@ void k_attn_fwd_mfma(FwdArgs a) {
   };
   int raw_cur = raw_of(0);
   int raw_nxt = raw_of(1);
+  if (a.out_rot) {
+    // angles of the output's inverse rotation at this query's position, formed while the
+    // Q loads are in flight: pair i on lane i / NW of wave i % NW (at most kD / 2 <= NT pairs)
+    static_assert(kD / 2 <= NT, "one pair per thread");
+    const int i = wave + NW * lane;
+    if (i < a.rope_dim / 2) {
+      float c, s;
+      rope_cs(ti.p, i, a.rope_dim, a.rope_l2t, true, c, s);
+      rope_s[i] = make_float2(c, s);
+    }
+  }
 
   CandSet cs;
   cs.row0 = a.cu_cmp[ti.b];
@@ -424,6 +443,34 @@ void k_attn_fwd_mfma(FwdArgs a) {
   }
   __syncthreads();
   uint16_t* op = a.out + (int64_t)t * kH * kD;
+  if (a.out_rot) {
+    // the inverse rotation at the query's position into storage of its own: chunks outside
+    // the rotary band are stored twice, then the band's chunks are rotated by every lane
+    // (a lane-divergent rotation inside the first loop would cost every wave the math)
+    uint16_t* orp = a.out_rot + (int64_t)t * kH * kD;
+    const int nb = a.rope_dim / 8, band0 = kD / 8 - nb;
+#pragma unroll
+    for (int k = 0; k < kH * kD / 8 / NT; ++k) {
+      const int e = tid + NT * k;
+      const int h = e >> 6, cc = e & 63;
+      const uint4 v = *reinterpret_cast<const uint4*>(&ot[h * kD + 8 * (cc ^ swz(h))]);
+      *reinterpret_cast<uint4*>(op + h * kD + 8 * cc) = v;
+      if (cc < band0) *reinterpret_cast<uint4*>(orp + h * kD + 8 * cc) = v;
+    }
+    for (int e = tid; e < kH * nb; e += NT) {
+      const int h = e / nb, c = e - h * nb, cc = band0 + c;
+      const uint4 v = *reinterpret_cast<const uint4*>(&ot[h * kD + 8 * (cc ^ swz(h))]);
+      float f[8];
+      load8(reinterpret_cast<const uint16_t*>(&v), f);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float2 r = rope_s[4 * c + j];
+        rotate_pair(f[2 * j], f[2 * j + 1], r.x, r.y);
+      }
+      store8(orp + h * kD + 8 * cc, f);
+    }
+    return;
+  }
 #pragma unroll
   for (int k = 0; k < kH * kD / 8 / NT; ++k) {
     const int e = tid + NT * k;        // 16-byte chunk of the 64 x 512 output
@@ -446,6 +493,9 @@ hipError_t launch_attn_fwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s
   a.cu = sh.cu;
   a.cu_cmp = sh.cu_cmp;
   a.out = (uint16_t*)io.out;
+  a.out_rot = (uint16_t*)io.out_rot;
+  a.rope_dim = sh.rope_dim;
+  a.rope_l2t = sh.rope_dim > 0 ? log2((double)sh.rope_theta) : 0.0;
   a.lse = io.lse;
   a.lse_cmp = io.lse_cmp;
   a.t_logits = io.t_logits;

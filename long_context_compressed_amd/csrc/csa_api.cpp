@@ -33,6 +33,8 @@ csa_status_t check_attn(const csa_params_t* p) {
   if (p->heads < 1 || p->head_dim < 8) return CSA_ERR_ARG;
   if (!dtype_main_ok(p->dtype)) return CSA_ERR_UNSUPPORTED;
   if (p->heads > 128 || p->head_dim > 512 || p->head_dim % 8 != 0) return CSA_ERR_UNSUPPORTED;
+  if (p->rope_dim < 0 || p->rope_dim > p->head_dim || p->rope_dim % 8 != 0) return CSA_ERR_ARG;
+  if (p->rope_dim > 0 && !(p->rope_theta > 0.f && isfinite(p->rope_theta))) return CSA_ERR_ARG;
   return CSA_OK;
 }
 
@@ -49,7 +51,7 @@ Shape make_shape(const csa_params_t* p, const int32_t* cu, const int32_t* cu_cmp
   s.W = p->window; s.k = p->topk; s.k_cap = p->topk_cap; s.H = p->heads; s.D = p->head_dim;
   s.HI = p->idx_heads; s.dI = p->idx_dim; s.scale = p->scale; s.mode = p->mode;
   s.teacher = p->teacher; s.dtype = p->dtype; s.idx_dtype = p->idx_dtype; s.cu = cu;
-  s.cu_cmp = cu_cmp;
+  s.cu_cmp = cu_cmp; s.rope_dim = p->rope_dim; s.rope_theta = p->rope_theta;
   return s;
 }
 
@@ -231,11 +233,12 @@ csa_status_t csa_index_topk(const csa_params_t* p, const void* qI, const float* 
 csa_status_t csa_sparse_attn_fwd(const csa_params_t* p, const void* q, const void* kv_cmp,
                                  const void* kv, const int32_t* idx, const float* sink,
                                  const int32_t* cu_seqlens, const int32_t* cu_cmp, void* out,
-                                 float* lse, float* lse_cmp, float* t_logits, void* ws,
-                                 size_t ws_bytes, hipStream_t stream) {
+                                 void* out_rot, float* lse, float* lse_cmp, float* t_logits,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
   csa_status_t st = check_attn(p);
   if (st) return st;
   if (!q || !kv || !cu_seqlens || !cu_cmp || !out || !lse) return CSA_ERR_NULL;
+  if (out_rot && (p->rope_dim == 0 || out_rot == out)) return CSA_ERR_ARG;
   if (p->mode != CSA_WINDOW && !kv_cmp) return CSA_ERR_NULL;
   if (p->mode == CSA_SPARSE && !idx) return CSA_ERR_NULL;
   const Shape sh = make_shape(p, cu_seqlens, cu_cmp);
@@ -243,9 +246,22 @@ csa_status_t csa_sparse_attn_fwd(const csa_params_t* p, const void* q, const voi
   if (need > 0 && (!ws || ws_bytes < need)) return CSA_ERR_WORKSPACE;
   csa::AttnIO io = {};
   io.q = q; io.kv_cmp = kv_cmp; io.kv = kv; io.idx = p->mode == CSA_SPARSE ? idx : nullptr;
-  io.sink = sink; io.out = out; io.lse = lse; io.lse_cmp = lse_cmp;
+  io.sink = sink; io.out = out; io.out_rot = out_rot; io.lse = lse; io.lse_cmp = lse_cmp;
   io.t_logits = p->mode == CSA_WINDOW ? nullptr : t_logits; io.ws = ws; io.ws_bytes = ws_bytes;
   return launched(csa::launch_attn_fwd(sh, io, stream));
+}
+
+csa_status_t csa_rope(int32_t dtype, const void* x, void* y, int64_t rows, int32_t heads,
+                      int32_t dim, int32_t rope_dim, float theta, int32_t inverse,
+                      int32_t batch, const int32_t* row_offsets, hipStream_t stream) {
+  if (!row_offsets || (rows > 0 && (!x || !y))) return CSA_ERR_NULL;
+  if (rows < 0 || rows > INT32_MAX || heads < 1 || dim < 8 || batch < 0) return CSA_ERR_ARG;
+  if (inverse != 0 && inverse != 1) return CSA_ERR_ARG;
+  if (dim % 8 != 0 || rope_dim < 8 || rope_dim > dim || rope_dim % 8 != 0) return CSA_ERR_ARG;
+  if (!(theta > 0.f) || !isfinite(theta)) return CSA_ERR_ARG;
+  if (dtype != CSA_F32 && dtype != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  return launched(csa::launch_rope(dtype, x, y, rows, heads, dim, rope_dim, theta, inverse, batch,
+                                   row_offsets, stream));
 }
 
 int64_t csa_teacher_logits_stride(const csa_params_t* p) {

@@ -52,11 +52,8 @@ __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
 }
 
 __device__ __forceinline__ void store8(uint16_t* p, const float (&v)[8]) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = (uint32_t)f32_to_bf16_bits(v[2 * i]) | ((uint32_t)f32_to_bf16_bits(v[2 * i + 1]) << 16);
-  *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                            pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
 }
 
 __device__ __forceinline__ float load1(const float* p) { return *p; }
@@ -70,6 +67,26 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   float mag = (e == 0) ? (float)m * 0.001953125f                      // m * 2^-9
                        : __uint_as_float(((e + 120u) << 23) | (m << 20));  // 2^(e-7) (1 + m/8)
   return (c & 0x80u) ? -mag : mag;
+}
+
+// ---------------------------------------------------------------- rotary embedding
+// cos and sin of pair i of the rotary band at position pos: angle pos * theta^(-2i / rope_dim)
+// (its opposite when inverse), formed and reduced in fp64 so that the positions of long
+// samples keep fp32 accuracy; l2t = log2(theta).
+__device__ __forceinline__ void rope_cs(int pos, int i, int rope_dim, double l2t, bool inverse,
+                                        float& c, float& s) {
+  const double ang = (double)pos * exp2(-(double)(2 * i) / (double)rope_dim * l2t);
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  c = (float)cd;
+  s = inverse ? -(float)sd : (float)sd;
+}
+
+// (a, b) -> (a c - b s, a s + b c), in one fixed operation order wherever it is applied.
+__device__ __forceinline__ void rotate_pair(float& a, float& b, float c, float s) {
+  const float x = a, y = b;
+  a = fmaf(x, c, -(y * s));
+  b = fmaf(x, s, y * c);
 }
 
 // ---------------------------------------------------------------- metadata

@@ -24,6 +24,8 @@ struct Shape {
   int teacher;    // csa_teacher_t
   int dtype;      // csa_dtype_t main operands
   int idx_dtype;  // csa_dtype_t indexer operands
+  int rope_dim;   // rotary band width (0: none)
+  float rope_theta;
   const int32_t* cu;      // cu_seqlens [B+1]
   const int32_t* cu_cmp;  // cu_cmp [B+1]
 };
@@ -42,6 +44,11 @@ hipError_t launch_compress_learned_bwd(const Shape& sh, int dtype, const void* x
                                        const void* score, const float* bias,
                                        const float* d_x_cmp, int dim, int overlap, float* dx,
                                        float* dscore, float* dbias, hipStream_t s);
+// Rotary embedding of rows [rows, heads, dim] at positions row - offs[b] (sample b);
+// y == x rotates in place (rotary channels only), else y receives every channel.
+hipError_t launch_rope(int dtype, const void* x, void* y, int64_t rows, int heads, int dim,
+                       int rope_dim, float theta, int inverse, int B, const int32_t* offs,
+                       hipStream_t s);
 hipError_t launch_quantize_fp8(const void* x, int dtype, int64_t rows, int row_len,
                                uint8_t* codes, float* scale, hipStream_t s);
 hipError_t launch_index_scores(const Shape& sh, const void* qI, const float* qI_scale,
@@ -62,6 +69,7 @@ struct AttnIO {
   const int32_t* idx;
   const float* sink;
   void* out;
+  void* out_rot;     // optional: out inverse-rotated at the query position (rope_dim > 0)
   float* lse;
   float* lse_cmp;    // optional: log-sum-exp over the compressed candidates only
   float* t_logits;   // optional: compressed-candidate logits [T, H, ld_t]

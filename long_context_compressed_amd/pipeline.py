@@ -6,6 +6,15 @@ accumulated gradients) on the current stream.  The order follows the fused train
 flow of "DeepSeek-V4 Attention Training Systems", section 8.2: compress, indexer score
 + top-k, selected-attention forward, teacher recompute with the eager indexer-loss
 backward, then the attention backward and the compressor adjoints.
+
+With a rotary band (rope_dim > 0) the step also applies the layer's positional rotations
+(same page, section 4: positions restart per packed sample; section 12: per compressed
+coordinate system, and the saved output survives the inverse rotation): the projected q,
+qI and the incoming dO are rotated IN PLACE (rotary channels only, as a fused
+norm/rotation producer would leave them), the window rows of kv into a buffer of the
+layer's own (the compressor reads the unrotated rows), the compressed rows in place after
+the compressor, the output inverse-rotated by the attention forward into `out_rot` while
+`out` stays the saved unrotated output, and every gradient is rotated back.
 """
 from dataclasses import dataclass
 from typing import Optional
@@ -35,13 +44,16 @@ class LayerConfig:
     mode: str
     teacher: str
     scale: float
+    rope_dim: int = 0
+    rope_theta: float = 10000.0
 
     @classmethod
     def of(cls, w):
         return cls(heads=w.heads, head_dim=w.head_dim, ratio=w.ratio, window=w.window,
                    topk=w.topk, topk_cap=w.topk_cap, idx_heads=w.idx_heads, idx_dim=w.idx_dim,
                    dtype=w.dtype, idx_dtype=w.idx_dtype, mode=w.mode, teacher=w.teacher,
-                   scale=w.scale)
+                   scale=w.scale, rope_dim=getattr(w, "rope_dim", 0),
+                   rope_theta=getattr(w, "rope_theta", 10000.0))
 
     @property
     def has_indexer(self):
@@ -68,11 +80,16 @@ class CsaLayer:
             topk=max(1, cfg.topk), topk_cap=cfg.topk_cap, heads=H, head_dim=D,
             idx_heads=cfg.idx_heads, idx_dim=cfg.idx_dim, scale=cfg.scale, mode=MODE[cfg.mode],
             teacher=TEACHER[cfg.teacher], dtype=DTYPE[cfg.dtype],
-            idx_dtype=DTYPE[cfg.idx_dtype] if cfg.idx_heads else B.CSA_BF16)
+            idx_dtype=DTYPE[cfg.idx_dtype] if cfg.idx_heads else B.CSA_BF16,
+            rope_dim=cfg.rope_dim, rope_theta=cfg.rope_theta)
         z = lambda *s, dtype=torch.float32: torch.empty(*s, dtype=dtype, device=device)  # noqa
         self.cu_cmp = z(batch + 1, dtype=torch.int32)
         self.kv_cmp = z(self.tc_cap, D, dtype=dt)
         self.out = z(T, H, D, dtype=dt)
+        self.rope = cfg.rope_dim > 0
+        if self.rope:
+            self.out_rot = z(T, H, D, dtype=dt)
+            self.kv_rot = z(T, D, dtype=dt)
         self.lse = z(T, H)
         # selected-set teacher: the forward also returns the compressed-only normalizer
         self.lse_cmp = z(T, H) if (cfg.has_indexer and cfg.teacher == "selected") else None
@@ -130,15 +147,28 @@ class CsaLayer:
         self._call("cmp_seqlens", B.csa_cmp_seqlens, cu_seqlens, self.B, self.cfg.ratio,
                    self.cu_cmp)
 
+    def _rope(self, name, x, offsets, inverse, out=None):
+        self._call(name, B.csa_rope, x, x if out is None else out, self.cfg.rope_dim,
+                   self.cfg.rope_theta, inverse, self.B, offsets)
+
     def forward(self, inp, cu_seqlens):
         """inp: dict of device tensors q, kv, [qI, kI_tok, w], [sink]."""
         cfg, p = self.cfg, self.p
         self._call("compress_kv", B.csa_compress, p, inp["kv"], cu_seqlens, self.cu_cmp,
                    self.kv_cmp)
+        kv = inp["kv"]
+        if self.rope:
+            self._rope("rope_kv_cmp", self.kv_cmp, self.cu_cmp, 0)
+            self._rope("rope_kv", inp["kv"], cu_seqlens, 0, out=self.kv_rot)
+            self._rope("rope_q", inp["q"], cu_seqlens, 0)
+            kv = self.kv_rot
         idx = None
         if cfg.has_indexer:
             self._call("compress_kI", B.csa_compress, p, inp["kI_tok"], cu_seqlens, self.cu_cmp,
                        self.kI_cmp)
+            if self.rope:
+                self._rope("rope_kI_cmp", self.kI_cmp, self.cu_cmp, 0)
+                self._rope("rope_qI", inp["qI"], cu_seqlens, 0)
             if cfg.idx_dtype == "fp8":
                 self._call("quantize_qI", B.csa_quantize_fp8, inp["qI"], self.qI8, self.qI_scale)
                 self._call("quantize_kI", B.csa_quantize_fp8, self.kI_cmp, self.kI8, self.kI_scale)
@@ -163,9 +193,9 @@ class CsaLayer:
                 self._call("topk_select", B.csa_topk_select, p, self.scores, cu_seqlens,
                            self.cu_cmp, self.idx)
             idx = self.idx
-        self._call("attn_fwd", B.csa_sparse_attn_fwd, p, inp["q"], self.kv_cmp, inp["kv"], idx,
+        self._call("attn_fwd", B.csa_sparse_attn_fwd, p, inp["q"], self.kv_cmp, kv, idx,
                    inp.get("sink"), cu_seqlens, self.cu_cmp, self.out, self.lse, self.lse_cmp,
-                   self.ws_fwd, None, self.t_logits)
+                   self.ws_fwd, None, self.t_logits, self.out_rot if self.rope else None)
         if cfg.has_indexer and cfg.teacher != "none":
             grads = self.backward
             if grads:
@@ -175,6 +205,8 @@ class CsaLayer:
                        self.grad_scale, self.kl, self.loss, self.dqI if grads else None,
                        self.dw if grads else None, self.dkI_cmp if grads else None, self.ws_kl,
                        self.lse_cmp, None, self.t_logits)
+            if grads and self.rope:
+                self._rope("rope_dqI", self.dqI, cu_seqlens, 1)
 
     def backward_step(self, inp, cu_seqlens):
         cfg, p = self.cfg, self.p
@@ -183,14 +215,24 @@ class CsaLayer:
         sink = inp.get("sink")
         if sink is not None:
             self.dsink.zero_()
-        self._call("attn_bwd", B.csa_sparse_attn_bwd, p, inp["q"], self.kv_cmp, inp["kv"],
+        if self.rope:
+            # the incoming gradient is that of out_rot: rotate it to the gradient of out
+            self._rope("rope_dO", inp["dO"], cu_seqlens, 0)
+        self._call("attn_bwd", B.csa_sparse_attn_bwd, p, inp["q"], self.kv_cmp,
+                   self.kv_rot if self.rope else inp["kv"],
                    self.idx if cfg.has_indexer else None, sink, cu_seqlens, self.cu_cmp, self.out,
                    self.lse, inp["dO"], self.dq, self.dkv_cmp, self.dkv,
                    self.dsink if sink is not None else None, self.ws_bwd)
+        if self.rope:
+            self._rope("rope_dq", self.dq, cu_seqlens, 1)
+            self._rope("rope_dkv", self.dkv, cu_seqlens, 1)
+            self._rope("rope_dkv_cmp", self.dkv_cmp, self.cu_cmp, 1)
         self._call("compress_bwd_kv", B.csa_compress_bwd, p, self.dkv_cmp, cu_seqlens,
                    self.cu_cmp, self.dkv)
         if cfg.has_indexer and cfg.teacher != "none":
             self.dkI_tok.zero_()
+            if self.rope:
+                self._rope("rope_dkI_cmp", self.dkI_cmp, self.cu_cmp, 1)
             self._call("compress_bwd_kI", B.csa_compress_bwd, p, self.dkI_cmp, cu_seqlens,
                        self.cu_cmp, self.dkI_tok)
 

@@ -74,6 +74,14 @@ WORKLOADS = {
         idx_heads=64, idx_dim=128, dtype="bf16", idx_dtype="bf16",
         mode="sparse", teacher="selected", backward=True, input_std="inv_sqrt_d", sink=True,
         draw={"n": 8, "lo": 1024, "hi": 16384, "total": 65536}),
+    # the same layer step with the positional rotations: a 64-channel rotary band of the
+    # 512-wide rows and of the 128-wide indexer rows, output inverse-rotated
+    "thd64k_csa_rope_bf16": Workload(
+        name="thd64k_csa_rope_bf16", cfg_id=3, lengths=None, total_tokens=65536,
+        heads=64, head_dim=512, ratio=4, window=128, topk=1024, topk_cap=1024,
+        idx_heads=64, idx_dim=128, dtype="bf16", idx_dtype="bf16",
+        mode="sparse", teacher="selected", backward=True, input_std="inv_sqrt_d",
+        rope_dim=64, draw={"n": 8, "lo": 1024, "hi": 16384, "total": 65536}),
     # window-only layer (no compressed history) on the same 64K THD batch as above
     "thd64k_window_bf16": Workload(
         name="thd64k_window_bf16", cfg_id=3, lengths=None, total_tokens=65536,

@@ -23,14 +23,14 @@ def _params(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = B.header_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B._SIGS)
 
 
 def test_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 5
+    assert lib.csa_abi_version() == 6
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.csa_status_string(st)
     assert lib.csa_status_string(7) == b"unknown status"
@@ -149,16 +149,26 @@ def test_fused_index_topk_validation(lib):
 def test_attention_validation(lib):
     p = _params()
     f = lib.csa_sparse_attn_fwd
-    a = [FAKE] * 10 + [None]
-    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, None, None,
-             None, 0, None) == B.CSA_ERR_NULL                                 # idx for sparse
+    a = [FAKE] * 8 + [None, FAKE, FAKE, None]         # q .. out, out_rot, lse, lse_cmp, t_logits
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, None,
+             None, None, 0, None) == B.CSA_ERR_NULL                           # idx for sparse
     assert f(ctypes.byref(_params(window=0)), *a, None, 0, None) == B.CSA_ERR_ARG
     assert f(ctypes.byref(_params(scale=0.0)), *a, None, 0, None) == B.CSA_ERR_ARG
     assert f(ctypes.byref(_params(mode=3)), *a, None, 0, None) == B.CSA_ERR_ARG
     assert f(ctypes.byref(_params(head_dim=1024)), *a, None, 0, None) == B.CSA_ERR_UNSUPPORTED
     assert f(ctypes.byref(_params(dtype=B.CSA_FP8_E4M3)), *a, None, 0, None) == B.CSA_ERR_UNSUPPORTED
     assert f(ctypes.byref(_params(mode=B.CSA_DENSE)), FAKE, None, FAKE, None, None, FAKE, FAKE,
-             FAKE, FAKE, None, None, None, 0, None) == B.CSA_ERR_NULL        # kv_cmp for dense
+             FAKE, None, FAKE, None, None, None, 0, None) == B.CSA_ERR_NULL  # kv_cmp for dense
+    # rotary band of the output rotation
+    OTHER = 2 * FAKE
+    rot = a[:8] + [OTHER] + a[9:]
+    assert f(ctypes.byref(p), *rot, None, 0, None) == B.CSA_ERR_ARG          # rope_dim 0
+    assert f(ctypes.byref(_params(rope_dim=8, rope_theta=1e4)), *a[:8], FAKE, *a[9:], None, 0,
+             None) == B.CSA_ERR_ARG                                          # out_rot aliases out
+    for bad in (dict(rope_dim=12, rope_theta=1e4), dict(rope_dim=72, rope_theta=1e4),
+                dict(rope_dim=-8, rope_theta=1e4), dict(rope_dim=8, rope_theta=0.0),
+                dict(rope_dim=8, rope_theta=float("inf"))):
+        assert f(ctypes.byref(_params(**bad)), *a, None, 0, None) == B.CSA_ERR_ARG, bad
     b = lib.csa_sparse_attn_bwd
     args = [FAKE] * 14
     bf = _params(heads=64, head_dim=512, dtype=B.CSA_BF16)
@@ -206,3 +216,21 @@ def test_teacher_logits_cache_contract(lib):
                total_tokens=65536, max_seqlen=16384)
     n = B.csa_workspace_size(_params(**big), B.CSA_OP_INDEXER_KL_CACHED)
     assert n >= 16384 * 1024 * 128 * 2                                       # bf16 staging
+
+
+def test_rope_validation(lib):
+    f = lib.csa_rope
+
+    def call(dtype=B.CSA_BF16, x=FAKE, y=FAKE, rows=16, heads=2, dim=64, rope_dim=16,
+             theta=1e4, inverse=0, batch=1, offs=FAKE):
+        return f(dtype, x, y, rows, heads, dim, rope_dim, theta, inverse, batch, offs, None)
+
+    assert call(x=None) == B.CSA_ERR_NULL
+    assert call(y=None) == B.CSA_ERR_NULL
+    assert call(offs=None) == B.CSA_ERR_NULL
+    assert call(x=None, y=None, rows=0, dtype=B.CSA_FP8_E4M3) == B.CSA_ERR_UNSUPPORTED  # no rows
+    assert call(dtype=B.CSA_FP8_E4M3) == B.CSA_ERR_UNSUPPORTED
+    for bad in (dict(rows=-1), dict(rows=1 << 31), dict(heads=0), dict(dim=4), dict(dim=60),
+                dict(rope_dim=0), dict(rope_dim=12), dict(rope_dim=72), dict(theta=0.0),
+                dict(theta=float("nan")), dict(inverse=2), dict(batch=-1)):
+        assert call(**bad) == B.CSA_ERR_ARG, bad

@@ -21,7 +21,7 @@ from tests import gpu_support as G
 pytestmark = pytest.mark.gpu
 
 NAMES = ["tiny_csa_f32_L256", "csa_sparse_fwd_bf16_L4096", "thd64k_csa_bf16", "thd64k_hca_bf16",
-         "thd64k_window_bf16", "csa128k_warmup_fp8"]
+         "thd64k_window_bf16", "csa128k_warmup_fp8", "thd64k_csa_rope_bf16"]
 
 
 # relative rounding of a compressed indexer key on the GPU chain: bf16 storage (2^-9, with
@@ -103,6 +103,9 @@ def test_fullsize_sampled(name):
     G.check("O(sampled)", G.back(layer.out[torch.as_tensor(rows).cuda()]), ref["O"],
             kind, rel_tol=3e-2 if kind != "f32" else None)
     G.check("LSE(sampled)", G.back(layer.lse[torch.as_tensor(rows).cuda()]), ref["LSE"], kind)
+    if "O_rot" in ref:
+        G.check("O_rot(sampled)", G.back(layer.out_rot[torch.as_tensor(rows).cuda()]),
+                ref["O_rot"], kind, rel_tol=3e-2 if kind != "f32" else None)
     if "kl" in ref:
         G.check("kl(sampled)", G.back(layer.kl[torch.as_tensor(rows).cuda()]), ref["kl"],
                 "f32" if kind == "f32" else "bf16", abs_tol=1e-4, rel_tol=5e-2)
@@ -111,11 +114,19 @@ def test_fullsize_sampled(name):
     G.check("dq(sampled)", G.back(layer.dq[torch.as_tensor(rows).cuda()]), ref["dq"], kind,
             rel_tol=3e-2 if kind != "f32" else None, abs_tol=1e-4 if kind == "f32" else None)
     if "dqI" in ref:
+        # the loss of a query is defined over its candidate set (the selected rows for a
+        # selected-set teacher): compare where the GPU selected the fp64 chain's set
         k2 = "f32" if (w.dtype == "f32" and w.idx_dtype == "f32") else "bf16"
-        G.check("dqI(sampled)", G.back(layer.dqI[torch.as_tensor(rows).cuda()]), ref["dqI"], k2,
-                abs_tol=1e-4, rel_tol=5e-2)
-        G.check("dw(sampled)", G.back(layer.dw[torch.as_tensor(rows).cuda()]), ref["dw"], k2,
-                abs_tol=1e-4, rel_tol=5e-2)
+        sel = np.arange(rows.size)
+        if w.teacher == "selected":
+            got = layer.idx[torch.as_tensor(rows).cuda()].cpu().numpy()
+            sel = np.array([i for i in range(rows.size) if set(got[i][got[i] >= 0].tolist()) ==
+                            set(ref["idx"][i][ref["idx"][i] >= 0].tolist())], dtype=np.int64)
+        rs = torch.as_tensor(rows[sel]).cuda()
+        G.check("dqI(sampled)", G.back(layer.dqI[rs]), ref["dqI"][sel], k2, abs_tol=1e-4,
+                rel_tol=5e-2)
+        G.check("dw(sampled)", G.back(layer.dw[rs]), ref["dw"][sel], k2, abs_tol=1e-4,
+                rel_tol=5e-2)
 
     # ---- shared-row gradients of the sampled queries only: dO is zero elsewhere, so every
     # other query contributes nothing (dS = P (dP - Dt) = 0 and P^T dO = 0)
@@ -129,11 +140,23 @@ def test_fullsize_sampled(name):
         same = [i for i in range(rows.size)
                 if set(got[i][got[i] >= 0].tolist()) == set(ref["idx"][i][ref["idx"][i] >= 0].tolist())]
         keep = rows[same]
+    rd = w.rope_dim
+    Tc = int(O.cmp_seqlens(cu, w.ratio)[-1])
+    kv_ref, kvc_ref, dO_ref = h64["kv"], ref["kv_cmp"], h64["dO"][keep]
+    if rd:
+        # the step left q and dO rotated in place (dO now the gradient of the unrotated
+        # output); the direct call below works in the rotated frame, and so does its oracle
+        tpos = O.rope_positions(cu, T)
+        h64["q"][rows] = O.rope(h64["q"][rows], tpos[rows], rd, w.rope_theta)
+        kv_ref = O.rope(h64["kv"], tpos, rd, w.rope_theta)
+        kvc_ref = O.rope(ref["kv_cmp"], O.rope_positions(cu, Tc, ratio=w.ratio), rd,
+                         w.rope_theta)
+        dO_ref = O.rope(dO_ref, tpos[keep], rd, w.rope_theta)
     dO_sub = torch.zeros_like(dev["dO"])
     dO_sub[torch.as_tensor(keep).cuda()] = dev["dO"][torch.as_tensor(keep).cuda()]
     layer.dkv_cmp.zero_()
     layer.dkv.zero_()
-    B.csa_sparse_attn_bwd(p, dev["q"], layer.kv_cmp, dev["kv"],
+    B.csa_sparse_attn_bwd(p, dev["q"], layer.kv_cmp, layer.kv_rot if rd else dev["kv"],
                           layer.idx if layer.cfg.has_indexer else None, sink, dev["cu_seqlens"],
                           layer.cu_cmp, layer.out, layer.lse, dO_sub, layer.dq, layer.dkv_cmp,
                           layer.dkv, layer.dsink if sink is not None else None, layer.ws_bwd)
@@ -143,10 +166,8 @@ def test_fullsize_sampled(name):
     if w.mode == "window":
         ref_idx = np.full((keep.size, 1), -1)
     Or, Lr = ref["O"][pos], ref["LSE"][pos]
-    _, dkc, dkw, _ = O.sparse_attn_bwd(h64["q"], ref["kv_cmp"], h64["kv"], ref_idx, None, cu,
-                                       w.ratio, w.window, w.scale, Or, Lr, h64["dO"][keep],
-                                       rows=keep)
-    Tc = int(O.cmp_seqlens(cu, w.ratio)[-1])
+    _, dkc, dkw, _ = O.sparse_attn_bwd(h64["q"], kvc_ref, kv_ref, ref_idx, None, cu,
+                                       w.ratio, w.window, w.scale, Or, Lr, dO_ref, rows=keep)
     G.check("dkv_cmp(sampled queries)", G.back(layer.dkv_cmp[:Tc]), dkc, kind,
             rel_tol=3e-2 if kind != "f32" else None, abs_tol=1e-4 if kind == "f32" else None)
     G.check("dkv window(sampled queries)", G.back(layer.dkv), dkw, kind,
@@ -162,13 +183,20 @@ def test_fullsize_sampled(name):
             qI_f = dev["qI"].float().cpu()
             kI_f = layer.kI_cmp[:Tc].float().cpu()
         del qI_dev
-        per_t = (layer.dqI[:n].cpu().double() * qI_f[:n].double()).sum(dim=(1, 2))
+        dqI_g, dkI_g = layer.dqI, layer.dkI_cmp
+        if rd:
+            # qI and kI_cmp hold the rotated operands; the gradients were rotated back
+            dqI_g, dkI_g = torch.empty_like(dqI_g), torch.empty_like(dkI_g)
+            B.csa_rope(layer.dqI, dqI_g, rd, w.rope_theta, 0, len(lens), dev["cu_seqlens"])
+            B.csa_rope(layer.dkI_cmp, dkI_g, rd, w.rope_theta, 0, len(lens), layer.cu_cmp)
+            torch.cuda.synchronize()
+        per_t = (dqI_g[:n].cpu().double() * qI_f[:n].double()).sum(dim=(1, 2))
         dww = (layer.dw[:n].cpu().double() * dev["w"][:n].cpu().double()).sum(dim=1)
         err = float((per_t - dww).abs().max())
         print(f"indexer identity per query: max |<dqI,qI> - <dw,w>| = {err:.3e} "
               f"(max {float(per_t.abs().max()):.3e})", flush=True)
         assert err <= 2e-2 * max(float(per_t.abs().max()), 1e-12)
         tot = float(per_t.sum())
-        kk = float((layer.dkI_cmp[:Tc].cpu().double() * kI_f.double()).sum())
+        kk = float((dkI_g[:Tc].cpu().double() * kI_f.double()).sum())
         print(f"indexer key identity: sum_t <dqI,qI> = {tot:.6e}  <dkI,kI> = {kk:.6e}", flush=True)
         assert abs(tot - kk) <= 2e-2 * max(float(per_t.abs().sum()), 1e-12)

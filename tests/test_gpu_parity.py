@@ -44,6 +44,14 @@ CASES = {
                                                          topk_cap=64, draw=None)),
     "fp8_warmup_small": ("csa128k_warmup_fp8", dict(lengths=(1500,), total_tokens=1536,
                                                     topk=64, topk_cap=64)),
+    "rope_bf16_thd_small": ("thd64k_csa_rope_bf16", dict(lengths=(301, 515, 1027),
+                                                         total_tokens=1856, topk=64,
+                                                         topk_cap=64, draw=None)),
+    "rope_f32_selected_pad": ("tiny_csa_f32_L256", dict(teacher="selected", lengths=(130, 90),
+                                                        total_tokens=224, rope_dim=16,
+                                                        rope_theta=500.0)),
+    "rope_fp8_warmup_small": ("csa128k_warmup_fp8", dict(lengths=(1500,), total_tokens=1536,
+                                                         topk=64, topk_cap=64, rope_dim=64)),
 }
 
 _CACHE = {}
@@ -732,6 +740,8 @@ def test_layer_end_to_end(name):
     if flips == 0:
         G.check("O", G.back(L.out)[:n], ref["O"], kind)
         G.check("LSE", G.back(L.lse)[:n], ref["LSE"], kind)
+        if "O_rot" in ref:
+            G.check("O_rot", G.back(L.out_rot)[:n], ref["O_rot"], kind)
         if "loss" in ref:
             print(f"loss gpu={L.loss.item():.8e} ref={ref['loss']:.8e}", flush=True)
             assert abs(L.loss.item() - ref["loss"]) <= G.TOL_LOSS_REL * abs(ref["loss"])
