@@ -295,6 +295,48 @@ def standalone_learned_compressor(layer, dev, w, cu, reps):
     return {f"{k}_standalone": v for k, v in timer.mean_ms().items()}
 
 
+def standalone_hbm(layer, dev, w, cu, reps):
+    """Kernel throughput of the HBM-bound compressor calls on the step's shapes: reps x n
+    back-to-back launches between two HIP events (on the stream they run on), cycling over
+    n copies of the operands that total at least 1 GiB, so that every launch reads HBM
+    rather than the 256 MB last-level cache and no per-call event or launch gap is timed."""
+    from long_context_compressed_amd import binding as B
+    p = layer.p
+    jobs = [("compress_kv", dev["kv"], layer.kv_cmp.shape[-1])]
+    if layer.cfg.has_indexer:
+        jobs.append(("compress_kI", dev["kI_tok"], layer.kI_cmp.shape[-1]))
+    out = {}
+    for tag, x, dim in jobs:
+        tc = layer.tc_cap
+        for kind in ("fwd", "bwd"):
+            if kind == "fwd":
+                one = x.numel() * x.element_size() + tc * dim * x.element_size()
+            else:
+                one = tc * dim * 4 + 2 * x.shape[0] * dim * 4
+            n = max(1, -(-(1 << 30) // one))
+            if kind == "fwd":
+                sets = [(x.clone(), torch.empty((tc, dim), dtype=x.dtype, device="cuda"))
+                        for _ in range(n)]
+                call = lambda s: B.csa_compress(p, s[0], cu, layer.cu_cmp, s[1])   # noqa: E731
+            else:
+                sets = [(torch.randn((tc, dim), device="cuda"),
+                         torch.zeros((x.shape[0], dim), device="cuda")) for _ in range(n)]
+                call = lambda s: B.csa_compress_bwd(p, s[0], cu, layer.cu_cmp, s[1])  # noqa: E731
+            for s in sets:
+                call(s)
+            torch.cuda.synchronize()
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record()
+            for i in range(reps * n):
+                call(sets[i % n])
+            end.record()
+            torch.cuda.synchronize()
+            name = tag if kind == "fwd" else tag.replace("compress", "compress_bwd")
+            out[f"{name}_standalone"] = start.elapsed_time(end) / (reps * n)
+            del sets
+    return out
+
+
 def cpu_baseline(w, host, budget_s):
     """The fp64 oracle, as it stands, on evenly spaced query rows of the same workload."""
     from oracle import csa_oracle as O
@@ -416,6 +458,7 @@ def main():
         # score matrix is timed after the step loop, on the same inputs
         per_call.update(standalone_topk(layer, dev, cu, reps=max(args.steps, 3)))
     if w.mode != "window":
+        per_call.update(standalone_hbm(layer, dev, w, cu, reps=max(args.steps, 3)))
         # the learned-score compressor (the mean-pool one runs in the step)
         per_call.update(standalone_learned_compressor(layer, dev, w, cu, reps=max(args.steps, 3)))
     breakdown = {}

@@ -46,7 +46,8 @@ namespace {
 constexpr int kDW = 128;          // d per wave, kernel 2
 constexpr int kNB1 = 32;          // candidates per block, kernel 1
 constexpr int kKS = kD + 16;      // row stride (bf16) of LDS row tiles
-constexpr int kNB2 = 64;          // candidates per block, kernel 2
+constexpr int kNB2 = 64;          // slot padding of the per-query staging rows
+constexpr int kNB3 = 32;          // candidates per block, kernel 2
 constexpr int kPTS = 144;         // row stride (bf16) of the dS | P tile (conflict-free reads)
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -331,15 +332,16 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
     atomicAdd(b.dsink + h, -expf(b.sink[h] - lse_t) * dt);
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_attn_bwd_dkv_mfma(BwdArgs b) {
-  // LDS: Q and dO staging at the start; then two output tiles of 64 rows x 1 KiB and two
-  // dS|P tiles of 64 rows x 256 bytes (all rows chunk-swizzled)
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kNB2 * kD + 2 * kNB2 * 128];
+  // LDS, sized for two workgroups per CU: Q, then dO, of the token staged in turn (64 rows
+  // each, read transposed into registers); then one output tile of 32 rows x 1 KiB and two
+  // dS|P tiles of 32 rows x 256 bytes (all rows chunk-swizzled)
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kH * kKS];
   uint16_t (*QO)[kKS] = reinterpret_cast<uint16_t (*)[kKS]>(lds);
-  uint16_t (*OT)[kNB2][kD] = reinterpret_cast<uint16_t (*)[kNB2][kD]>(lds);
-  uint16_t (*PS)[kNB2][128] = reinterpret_cast<uint16_t (*)[kNB2][128]>(lds + 2 * kNB2 * kD);
-  static_assert(2 * kH * kKS <= 2 * kNB2 * kD + 2 * kNB2 * 128, "Q/dO staging fits");
+  uint16_t (*OT)[kD] = reinterpret_cast<uint16_t (*)[kD]>(lds);
+  uint16_t (*PS)[kNB3][128] = reinterpret_cast<uint16_t (*)[kNB3][128]>(lds + kNB3 * kD);
+  static_assert(kNB3 * kD + 2 * kNB3 * 128 <= kH * kKS, "output and dS|P tiles fit");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int tl = token_of_block(blockIdx.x);
@@ -348,43 +350,43 @@ void k_attn_bwd_dkv_mfma(BwdArgs b) {
   TokenInfo ti;
   if (!token_info_wave(b.cu, b.B, t, ti)) return;
   const int n_tot = b.nc[t] + min(b.W, ti.p + 1);
-  const int nblk = (n_tot + kNB2 - 1) / kNB2;
+  const int nblk = (n_tot + kNB3 - 1) / kNB3;
   const uint16_t* pds_t = b.pds + (int64_t)tl * b.n_slots * 128;
   uint16_t* stg_t = b.stage + (int64_t)tl * b.n_slots * kD;
-  // stage Q (rows 0..63) and dO (rows 64..127) of the token: wave w loads rows 32w .. 32w+31
-  {
-    const uint16_t* qt = b.q + (int64_t)t * kH * kD;
-    const uint16_t* gt = b.dout + (int64_t)t * kH * kD;
-#pragma unroll 8
-    for (int j = 0; j < 32; ++j) {
-      const int row = 32 * wave + j;
-      const uint16_t* src = row < kH ? qt + row * kD : gt + (row - kH) * kD;
-      dma_row16(src + 8 * lane, &QO[row][0]);
-    }
-  }
-  wait_vmem();
-  __syncthreads();
   const int dw = wave * kDW;
   const int jr = c16 >> 2, jc = 4 * (c16 & 3);
-  // [Q; dO] read transposed: MFMA A operand with m = d, k = head slot
+  // [Q; dO] read transposed: MFMA A operand with m = d, k = head slot (Q heads in k-steps
+  // 0, 1; dO heads in k-steps 2, 3), staged 64 rows at a time
   bf16x8 bo[8][4];   // [tile of d][k-step over the 128 head slots]
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const v4i16 lo = ld_tr(&QO[32 * ks + 8 * g + jr][dw + 16 * nt + jc]);
-      const v4i16 hi = ld_tr(&QO[32 * ks + 8 * g + 4 + jr][dw + 16 * nt + jc]);
-      bo[nt][ks] = join8(lo, hi);
+  for (int half = 0; half < 2; ++half) {
+    const uint16_t* src = (half == 0 ? b.q : b.dout) + (int64_t)t * kH * kD;
+    if (half) __syncthreads();       // every wave has read the Q rows
+#pragma unroll 8
+    for (int j = 0; j < 16; ++j) {
+      const int row = 16 * wave + j;
+      dma_row16(src + row * kD + 8 * lane, &QO[row][0]);
     }
+    wait_vmem();
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const v4i16 lo = ld_tr(&QO[32 * k2 + 8 * g + jr][dw + 16 * nt + jc]);
+        const v4i16 hi = ld_tr(&QO[32 * k2 + 8 * g + 4 + jr][dw + 16 * nt + jc]);
+        bo[nt][2 * half + k2] = join8(lo, hi);
+      }
+  }
   __syncthreads();   // QO no longer read: its space becomes the output and dS|P tiles
   // dS|P rows of block blk into PS[buf]: 4 rows of 256 bytes per instruction, wave w rows
-  // 16w .. 16w+15, lane l fills physical chunk l % 16 of row 4i + l / 16
+  // 8w .. 8w+7, lane l fills physical chunk l % 16 of row 4i + l / 16
   auto issue = [&](int blk, int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * wave + 4 * i + (lane >> 4);
-      dma_row16(pds_t + (int64_t)(kNB2 * blk + r) * 128 + 8 * ((lane & 15) ^ swz(r)),
-                &PS[buf][16 * wave + 4 * i][0]);
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * wave + 4 * i + (lane >> 4);
+      dma_row16(pds_t + (int64_t)(kNB3 * blk + r) * 128 + 8 * ((lane & 15) ^ swz(r)),
+                &PS[buf][8 * wave + 4 * i][0]);
     }
   };
   // B operand reads: row 16mt + c16, logical chunk 4ks + g
@@ -393,16 +395,16 @@ void k_attn_bwd_dkv_mfma(BwdArgs b) {
   for (int q = 0; q < 4; ++q) eq[q] = 8 * ((4 * q + g) ^ swz(c16));
   if (nblk > 0) issue(0, 0);
   for (int blk = 0; blk < nblk; ++blk) {
-    const int buf = blk & 1, c0 = kNB2 * blk;
+    const int buf = blk & 1, c0 = kNB3 * blk;
     // this block's dS|P rows: after block 0 the only younger memory operations are the
-    // previous (full) block's 16 row stores, which may stay in flight
+    // previous (full) block's 8 row stores, which may stay in flight
     if (blk == 0) wait_vmem();
-    else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     __syncthreads();
     if (blk + 1 < nblk) issue(blk + 1, buf ^ 1);
-    // row gradients of candidates c0 + 16mt + c16 -> OT[buf][16mt + c16][d], chunk-swizzled
+    // row gradients of candidates c0 + 16mt + c16 -> OT[16mt + c16][d], chunk-swizzled
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < 2; ++mt) {
       const int row = 16 * mt + c16;
       bf16x8 av[4];
 #pragma unroll
@@ -414,16 +416,16 @@ void k_attn_bwd_dkv_mfma(BwdArgs b) {
         for (int ks = 0; ks < 4; ++ks) x = mfma16(bo[nt][ks], av[ks], x);
         // lane holds d = dw + 16nt + 4g .. +3 (logical chunk (dw + 16nt)/8 + g/2)
         const int ck = ((dw + 16 * nt) >> 3) + (g >> 1);
-        *reinterpret_cast<uint2*>(&OT[buf][row][8 * (ck ^ swz(row)) + 4 * (g & 1)]) =
+        *reinterpret_cast<uint2*>(&OT[row][8 * (ck ^ swz(row)) + 4 * (g & 1)]) =
             make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
       }
     }
     __syncthreads();
     // full-row 16-byte stores: wave w writes rows w, w+4, ...
-    const int nrow = min(kNB2, n_tot - c0);
+    const int nrow = min(kNB3, n_tot - c0);
     for (int r = wave; r < nrow; r += 4)
       *reinterpret_cast<uint4*>(stg_t + (int64_t)(c0 + r) * kD + 8 * lane) =
-          *reinterpret_cast<const uint4*>(&OT[buf][r][8 * (lane ^ swz(r))]);
+          *reinterpret_cast<const uint4*>(&OT[r][8 * (lane ^ swz(r))]);
   }
 }
 

@@ -48,17 +48,42 @@ hipError_t launch_validate_metadata(const int32_t* cu, int B, int T, int max_seq
   return hipGetLastError();
 }
 
+// Offsets of the packed samples copied to LDS once per workgroup (the per-row sample
+// lookups then cost LDS reads instead of a chain of dependent global loads); more samples
+// than kLdsSamples keep the lookups in global memory.
+constexpr int kLdsSamples = 255;
+
+struct SampleTables {
+  const int32_t* cu;
+  const int32_t* cu_cmp;
+};
+
+__device__ __forceinline__ SampleTables stage_samples(const int32_t* __restrict__ cu,
+                                                      const int32_t* __restrict__ cu_cmp, int B,
+                                                      int32_t* s_cu, int32_t* s_cmp) {
+  if (B > kLdsSamples) return {cu, cu_cmp};
+  for (int i = threadIdx.x; i <= B; i += blockDim.x) {
+    s_cu[i] = cu[i];
+    s_cmp[i] = cu_cmp[i];
+  }
+  __syncthreads();
+  return {s_cu, s_cmp};
+}
+
 // ------------------------------------------------------------------ compressor forward
 // A workgroup of 256 lanes covers `rows_per_wg` compressed rows; each row is split into
 // dim/8 chunks of 8 elements and the r source rows of a chunk into `rsplit` strided
-// parts whose fp32 partial sums are added in part order through LDS.
-template <typename T>
+// parts whose fp32 partial sums are added in part order through LDS.  RU > 0 fixes r = RU
+// (rsplit 1) so that all RU loads of a lane are issued before the first add.
+template <typename T, int RU>
 __global__ __launch_bounds__(256) void k_compress(const T* __restrict__ x, int dim,
                                                   const int32_t* __restrict__ cu,
                                                   const int32_t* __restrict__ cu_cmp, int B,
                                                   int r, T* __restrict__ out, int rows_per_wg,
                                                   int rsplit) {
   __shared__ float red[256 * 9];
+  __shared__ int32_t s_cu[kLdsSamples + 1], s_cmp[kLdsSamples + 1];
+  const SampleTables st = stage_samples(cu, cu_cmp, B, s_cu, s_cmp);
   const int chunks = dim >> 3;
   const int per_row = chunks * rsplit;
   const int tid = threadIdx.x;
@@ -67,20 +92,30 @@ __global__ __launch_bounds__(256) void k_compress(const T* __restrict__ x, int d
   const int part = rem / chunks;
   const int chunk = rem - part * chunks;
   const int64_t j = (int64_t)blockIdx.x * rows_per_wg + lrow;
-  const int Tc = cu_cmp[B];
+  const int Tc = st.cu_cmp[B];
   const bool active = lrow < rows_per_wg && j < Tc;
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   if (active) {
-    const int b = upper_bound_i32(cu_cmp, B + 1, (int)j) - 1;
-    const int64_t src = (int64_t)cu[b] + (j - cu_cmp[b]) * (int64_t)r;
+    const int b = upper_bound_i32(st.cu_cmp, B + 1, (int)j) - 1;
+    const int64_t src = (int64_t)st.cu[b] + (j - st.cu_cmp[b]) * (int64_t)r;
     const T* base = x + src * dim + chunk * 8;
-    for (int u = part; u < r; u += rsplit) {
-      float v[8];
-      load8(base + (int64_t)u * dim, v);
+    if constexpr (RU > 0) {
+      float v[RU][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+      for (int u = 0; u < RU; ++u) load8(base + (int64_t)u * dim, v[u]);
+#pragma unroll
+      for (int u = 0; u < RU; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[u][i];
+    } else {
+      for (int u = part; u < r; u += rsplit) {
+        float v[8];
+        load8(base + (int64_t)u * dim, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+      }
     }
   }
   if (rsplit > 1) {
@@ -115,14 +150,16 @@ hipError_t launch_compress(const Shape& sh, int dtype, const void* x, int dim, v
   const int64_t rows_cap = sh.r > 0 ? (int64_t)sh.T / sh.r : 0;
   const int64_t grid = (rows_cap + rows_per_wg - 1) / rows_per_wg;
   if (grid == 0) return hipSuccess;
-  if (dtype == 0)
-    hipLaunchKernelGGL(k_compress<float>, dim3((unsigned)grid), dim3(256), 0, s,
-                       (const float*)x, dim, sh.cu, sh.cu_cmp, sh.B, sh.r, (float*)x_cmp,
-                       rows_per_wg, rsplit);
-  else
-    hipLaunchKernelGGL(k_compress<uint16_t>, dim3((unsigned)grid), dim3(256), 0, s,
-                       (const uint16_t*)x, dim, sh.cu, sh.cu_cmp, sh.B, sh.r,
-                       (uint16_t*)x_cmp, rows_per_wg, rsplit);
+  const bool r4 = sh.r == 4 && rsplit == 1;
+  if (dtype == 0) {
+    auto k = r4 ? k_compress<float, 4> : k_compress<float, 0>;
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(256), 0, s, (const float*)x, dim, sh.cu,
+                       sh.cu_cmp, sh.B, sh.r, (float*)x_cmp, rows_per_wg, rsplit);
+  } else {
+    auto k = r4 ? k_compress<uint16_t, 4> : k_compress<uint16_t, 0>;
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(256), 0, s, (const uint16_t*)x, dim,
+                       sh.cu, sh.cu_cmp, sh.B, sh.r, (uint16_t*)x_cmp, rows_per_wg, rsplit);
+  }
   return hipGetLastError();
 }
 
@@ -134,17 +171,19 @@ __global__ __launch_bounds__(256) void k_compress_bwd(const float* __restrict__ 
                                                       const int32_t* __restrict__ cu_cmp,
                                                       int B, int r, float* __restrict__ dx,
                                                       int rows_per_wg) {
+  __shared__ int32_t s_cu[kLdsSamples + 1], s_cmp[kLdsSamples + 1];
+  const SampleTables st = stage_samples(cu, cu_cmp, B, s_cu, s_cmp);
   const int chunks = dim >> 3;
   const int lrow = threadIdx.x / chunks;
   const int chunk = threadIdx.x - lrow * chunks;
   const int64_t t = (int64_t)blockIdx.x * rows_per_wg + lrow;
   if (lrow >= rows_per_wg) return;
   TokenInfo ti;
-  if (!token_info(cu, B, (int)t, ti)) return;
+  if (!token_info(st.cu, B, (int)t, ti)) return;
   const int j = ti.p / r;
   if (j >= ti.len / r) return;
   float g[8], a[8];
-  load8(d_cmp + (int64_t)(cu_cmp[ti.b] + j) * dim + chunk * 8, g);
+  load8(d_cmp + (int64_t)(st.cu_cmp[ti.b] + j) * dim + chunk * 8, g);
   float* dst = dx + t * dim + chunk * 8;
   load8(dst, a);
   const float rf = (float)r;
