@@ -201,14 +201,17 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_wg(const float* __restric
 
 // One wave per query row for rows of up to 64 * KPL visible scores (no workgroup barriers):
 // keys live in registers lane-interleaved (j = lane + 64 i); each 8-bit radix pass counts
-// the keys matching the prefix into a wave-private LDS histogram split four ways by lane
+// the keys matching the prefix into a wave-private LDS histogram split eight ways by lane
 // (fewer same-address atomic collisions), the wave scans it from the top digit down and
 // picks the digit holding the k-th largest key.  The ordered output pass walks the keys in
 // j order 64 at a time: ballots give every lane its output position, so each step writes a
 // contiguous run of selected rows (ascending, ties to the smaller j).  Rows are dispatched
-// to a register footprint of 16, 32, 48 or 64 keys per lane by their visible count.
+// to a register footprint of 16, 32, 48 or 64 keys per lane by their visible count.  The
+// register budget is held to three waves per SIMD: a wave waits ~5 us for its row to
+// arrive from HBM, and three resident waves hide more of it than two (a few keys of the
+// 64-key footprint then live in scratch; measured 0.268 -> 0.222 ms at 64K THD).
 template <int KPL>
-__global__ __launch_bounds__(256) void k_topk_wave(const float* __restrict__ scores, int64_t ld,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_topk_wave(const float* __restrict__ scores, int64_t ld,
                                                    const int32_t* __restrict__ cu,
                                                    const int32_t* __restrict__ cu_cmp, int B,
                                                    int r, int n_cap, int k, int k_cap, int T,
