@@ -1,0 +1,110 @@
+"""GPU parity of whole layer steps on the degenerate packs of the method: no sample at all,
+empty samples between others, samples shorter than the ratio (no compressed row anywhere),
+one-token samples, samples of exactly one and two groups, the HCA boundary lengths
+r - 1, r, r + 1, and a window-only layer with one- and two-token samples, each followed by
+capacity padding.  Every step of the layer runs (the MFMA kernels for the 64 x 512 bf16
+shapes, the generic ones for the small fp32 shape) and is compared with the fp64 oracle's
+layer step; padding rows must come back zero (idx rows: -1).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa_oracle as O
+from synth import configs, inputs as synth_inputs
+from tests import gpu_support as G
+
+pytestmark = pytest.mark.gpu
+
+EDGE = {
+    "f32_no_samples": ("tiny_csa_f32_L256", dict(lengths=(), total_tokens=16,
+                                                 teacher="selected")),
+    "f32_all_shorter_than_ratio": ("tiny_csa_f32_L256", dict(lengths=(0, 3, 0, 2),
+                                                             total_tokens=8,
+                                                             teacher="selected")),
+    "f32_one_token_samples_dense_teacher": ("tiny_csa_f32_L256", dict(lengths=(1, 1, 4, 1, 8),
+                                                                      total_tokens=20)),
+    "bf16_csa_tiny_samples": ("thd64k_csa_bf16", dict(lengths=(3, 0, 5, 4, 8, 1),
+                                                      total_tokens=32, topk=64, topk_cap=64,
+                                                      draw=None)),
+    "bf16_csa_shorter_than_ratio": ("thd64k_csa_bf16", dict(lengths=(3, 2, 0, 1),
+                                                            total_tokens=12, topk=64,
+                                                            topk_cap=64, draw=None)),
+    "bf16_hca_ratio_boundaries": ("thd64k_hca_bf16", dict(lengths=(127, 128, 129, 0),
+                                                          total_tokens=400)),
+    "bf16_window_only_short": ("thd64k_window_bf16", dict(lengths=(1, 2, 130), total_tokens=140,
+                                                          draw=None)),
+    "bf16_rope_tiny_samples": ("thd64k_csa_rope_bf16", dict(lengths=(3, 0, 5, 4, 8, 1),
+                                                            total_tokens=32, topk=64,
+                                                            topk_cap=64, draw=None)),
+    "fp8_dense_teacher_tiny": ("csa128k_warmup_fp8", dict(lengths=(9, 0, 4, 2),
+                                                          total_tokens=20, topk=64,
+                                                          topk_cap=64)),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_degenerate_pack_layer(name):
+    from long_context_compressed_amd.pipeline import CsaLayer, LayerConfig, to_device
+    base, over = EDGE[name]
+    w = configs.workload(base, **over)
+    print(f"[gpu] edge case={name} lengths={over['lengths']}", flush=True)
+    host = synth_inputs.make_inputs(w)
+    h64 = {k: synth_inputs.to_f64(v) for k, v in host.items() if isinstance(v, torch.Tensor)}
+    h64["cu_seqlens"] = host["cu_seqlens"]
+    h64["max_seqlen"] = host["max_seqlen"]
+    L = CsaLayer(LayerConfig.of(w), len(host["lengths"]), w.total_tokens, host["max_seqlen"],
+                 backward=w.backward)
+    dev = to_device(host)
+    L.step(dev, dev["cu_seqlens"])
+    torch.cuda.synchronize()
+    n = int(host["cu_seqlens"][-1])
+    T = w.total_tokens
+    ref = O.layer_step(h64, w, rows=np.arange(n))
+    kind = w.dtype
+    Tc = int(O.cmp_seqlens(host["cu_seqlens"], w.ratio)[-1])
+    assert torch.equal(L.cu_cmp.cpu().to(torch.int64),
+                       torch.as_tensor(O.cmp_seqlens(host["cu_seqlens"], w.ratio)))
+    if Tc:
+        ref_kvc = ref["kv_cmp"]
+        if w.rope_dim:   # the layer rotates its compressed rows in place
+            ref_kvc = O.rope(ref_kvc, O.rope_positions(host["cu_seqlens"], Tc, ratio=w.ratio),
+                             w.rope_dim, w.rope_theta)
+        G.check("kv_cmp", G.back(L.kv_cmp)[:Tc], ref_kvc, kind)
+    if "idx" in ref:
+        got = L.idx.cpu().numpy()
+        assert G.idx_sets_equal(got[:n], ref["idx"]) == 0
+        assert np.all(got[n:] == -1)
+    if n:
+        G.check("O", G.back(L.out)[:n], ref["O"], kind)
+        G.check("LSE", G.back(L.lse)[:n], ref["LSE"], kind)
+        if "O_rot" in ref:
+            G.check("O_rot", G.back(L.out_rot)[:n], ref["O_rot"], kind)
+    assert torch.all(L.out[n:] == 0) and torch.all(L.lse[n:] == 0)
+    if "loss" in ref:
+        # the fp64 chain does not round the compressed keys to bf16 as the device does; with
+        # a loss made of a few one- and two-candidate rows that moves it by ~2^-9 relative
+        # per logit, so the bf16 chains are held to the bf16 tolerance, per row and in sum
+        got_loss = float(L.loss.item())
+        print(f"loss gpu={got_loss:.8e} ref={ref['loss']:.8e}", flush=True)
+        tol = G.TOL_LOSS_REL if kind == "f32" else G.TOL_BF16_REL
+        assert abs(got_loss - ref["loss"]) <= tol * abs(ref["loss"]) + 1e-12
+        if n:
+            G.check("kl", G.back(L.kl)[:n], ref["kl"], kind)
+        assert torch.all(L.kl[n:] == 0)
+    if w.backward:
+        if n:
+            G.check("dq", G.back(L.dq)[:n], ref["dq"], kind)
+        assert torch.all(L.dq[n:] == 0)
+        G.check("dkv", G.back(L.dkv), ref["dkv"], kind)
+        if "dkI_tok" in ref:
+            k2 = "f32" if (w.dtype == "f32" and w.idx_dtype == "f32") else "bf16"
+            # an fp8 chain quantizes the bf16-rounded keys, the fp64 chain the exact ones: a
+            # key element near a code boundary lands one e4m3 step (2^-3 relative) apart, and
+            # with a handful of keys one such element shows in the norm-relative error (the
+            # step-isolated fp8 tests hold the usual bf16 tolerance)
+            rt = 2.0 ** -3 if w.idx_dtype == "fp8" else None
+            G.check("dkI_tok", G.back(L.dkI_tok), ref["dkI_tok"], k2, rel_tol=rt)
+            if n:
+                G.check("dqI", G.back(L.dqI)[:n], ref["dqI"], k2, rel_tol=rt)
+    assert T >= n
