@@ -19,19 +19,18 @@ using namespace attn;
 
 // The backward is processed in chunks of query tokens (so the workspace stays bounded);
 // per chunk:
-// Kernel 1 (k_attn_bwd_dq_mfma): one workgroup per query token, wave w owns heads
-// 16w..16w+15 over the whole row.  Per block of 32 candidates the rows are staged once in
-// LDS (row-major; the next block's rows are fetched into registers while the current
-// block computes); each wave recomputes S^T and dP^T for its heads on MFMA (A = rows from
-// LDS, B = its Q / dO slice resident in registers), forms P = e^{S - LSE} and
-// dS = P (dP - Dt) in fp32, stores scale*dS and P (bf16) for kernel 2, and accumulates
-// dq += (scale dS) K with the row tile as a transposed B operand (ds_read_b64_tr_b16).
-// The S^T result layout (lane = head, 4 candidates per m-tile) is reused directly as the
-// A operand of the dq product by ordering the 32 candidates of a k-step as
-// {4g..4g+3, 16+4g..16+4g+3} for lane group g.
-// Kernel 2 (k_attn_bwd_dkv_mfma): one workgroup per query token, wave w owns d-slice
-// 128w..128w+127.  Q and dO of the token are staged once in LDS and read transposed into
-// registers; per block of 64 candidates the row gradients
+// Kernel 1 (k_attn_bwd_dq_mfma): one workgroup per query token.  Per block of 32
+// candidates the rows are gathered into swizzled LDS rows by direct global->LDS loads (the
+// next block's rows one per two k-steps of the current block's S^T loop); wave w recomputes
+// S^T and dP^T for heads 16w..16w+15 on MFMA (A = rows from LDS, B = its Q / dO slice
+// resident in registers), forms P = e^{S - LSE} and dS = P (dP - Dt) in fp32 and writes
+// scale*dS and P (bf16) to an LDS tile [slot][head]; after a barrier wave w accumulates
+// dq[:, 128w .. 128w+127] += (scale dS) K over all 64 heads, with dS read transposed from
+// the tile as the A operand and the row tile read transposed (ds_read_b64_tr_b16) as the B
+// operand; the tile is also stored as the dS|P rows kernel 2 reads.
+// Kernel 2 (k_attn_bwd_dkv_mfma): one workgroup per query token, two per CU, wave w owns
+// d-slice 128w..128w+127.  Q, then dO, of the token are staged in LDS and read transposed
+// into registers; per block of 32 candidates the row gradients
 // (d row)^T = [Q; dO]^T [scale dS | P]^T are formed on MFMA (lane = candidate, 4
 // consecutive d) and stored as bf16 to a staging buffer, one 1 KiB vector per
 // (query, candidate) pair, with plain stores.
