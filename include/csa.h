@@ -298,7 +298,8 @@ csa_status_t csa_sparse_attn_bwd(const csa_params_t* p, const void* q, const voi
  * from it instead of recomputed; results agree up to floating-point rounding.  With a
  * cache the workspace must be csa_workspace_size(p, CSA_OP_INDEXER_KL_CACHED) bytes.
  * kl: fp32 [T]; loss: fp32 [1]; dqI: fp32 [T, H_I, d_I]; dw: fp32 [T, H_I];
- * dkI_cmp: fp32 [Tc, d_I].  dqI, dw and dkI_cmp all NULL => loss only. */
+ * dkI_cmp: fp32 [Tc, d_I].  dqI, dw and dkI_cmp all NULL => loss only.
+ * Supported for heads <= 64 teacher heads (CSA_ERR_UNSUPPORTED beyond). */
 csa_status_t csa_indexer_kl(const csa_params_t* p, const void* q, const void* kv_cmp,
                             const float* scores, int64_t ld_scores, const int32_t* idx,
                             const float* teacher_lse, const float* teacher_logits,

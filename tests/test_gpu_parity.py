@@ -50,6 +50,16 @@ CASES = {
     "rope_f32_selected_pad": ("tiny_csa_f32_L256", dict(teacher="selected", lengths=(130, 90),
                                                         total_tokens=224, rope_dim=16,
                                                         rope_theta=500.0)),
+    # the generic (non-MFMA) kernels at the widest rows and the most heads the ABI accepts
+    "f32_wide_rows_generic": ("tiny_csa_f32_L256", dict(heads=64, head_dim=512, idx_heads=4,
+                                                        idx_dim=64, lengths=(40, 25),
+                                                        total_tokens=72, window=16, topk=8,
+                                                        teacher="selected")),
+    # (the indexer loss takes at most 64 teacher heads: selection only here)
+    "bf16_128_heads_generic": ("thd64k_csa_bf16", dict(heads=128, head_dim=256,
+                                                       lengths=(100, 77), total_tokens=192,
+                                                       topk=64, topk_cap=64, draw=None,
+                                                       teacher="none")),
     "rope_fp8_warmup_small": ("csa128k_warmup_fp8", dict(lengths=(1500,), total_tokens=1536,
                                                          topk=64, topk_cap=64, rope_dim=64)),
 }
