@@ -9,6 +9,7 @@
 
 #include "attn_common.h"
 #include "csa_launch.h"
+#include "csr_build.h"
 
 // M0 is named as clobbered by the LDS-DMA asm below; the compiler keeps no value in it here.
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -435,24 +436,11 @@ __global__ __launch_bounds__(256) void k_bwd_fill_zero(int32_t* __restrict__ p, 
 
 template <bool FILL>
 __global__ __launch_bounds__(256) void k_bwd_csr_pass(BwdArgs b) {
-  const int tl = blockIdx.x;
-  if (tl >= b.nT) return;
-  const int t = b.t0 + tl;
-  TokenInfo ti;
-  if (!token_info(b.cu, b.B, t, ti)) return;
-  const int row0 = b.cu_cmp[ti.b];
-  const int nv = min((ti.p + 1) / b.r, b.n_cap);
-  const int n_c = b.nc[t];
-  for (int c = threadIdx.x; c < n_c; c += 256) {
-    const int gr = cmp_row(b, t, row0, nv, c);
-    if (gr < 0) continue;
-    if (!FILL) {
-      atomicAdd(&b.cnt[gr], 1);
-    } else {
-      const int pos = atomicAdd(&b.cur[gr], 1);
-      b.list[pos] = tl * (int32_t)b.n_slots + c;
-    }
-  }
+  CsrBuild g;
+  g.idx = b.mode == 0 ? b.idx : nullptr; g.cu = b.cu; g.cu_cmp = b.cu_cmp; g.nc = b.nc;
+  g.cnt = b.cnt; g.cur = b.cur; g.list = b.list; g.slots = b.n_slots; g.t0 = b.t0;
+  g.nT = b.nT; g.B = b.B; g.r = b.r; g.n_cap = b.n_cap; g.k_cap = b.k_cap;
+  csr_group_pass<FILL>(g);
 }
 
 // exclusive scan of cnt[0 .. n) into off and cur (one workgroup of 1024 lanes)
@@ -627,9 +615,9 @@ hipError_t launch_attn_bwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s
     hipLaunchKernelGGL(k_attn_bwd_dkv_mfma, dim3((unsigned)grid), dim3(256), 0, s, b);
     if (sh.mode != 2) {
       hipLaunchKernelGGL(k_bwd_fill_zero, dim3(64), dim3(256), 0, s, b.cnt, b.Tc_cap);
-      hipLaunchKernelGGL(k_bwd_csr_pass<false>, dim3(b.nT), dim3(256), 0, s, b);
+      hipLaunchKernelGGL(k_bwd_csr_pass<false>, dim3(csr_grid(b.nT)), dim3(256), 0, s, b);
       hipLaunchKernelGGL(k_bwd_csr_scan, dim3(1), dim3(1024), 0, s, b, b.Tc_cap);
-      hipLaunchKernelGGL(k_bwd_csr_pass<true>, dim3(b.nT), dim3(256), 0, s, b);
+      hipLaunchKernelGGL(k_bwd_csr_pass<true>, dim3(csr_grid(b.nT)), dim3(256), 0, s, b);
       hipLaunchKernelGGL(k_bwd_reduce_cmp, dim3(b.Tc_cap), dim3(256), 0, s, b);
     }
     const int u_lo = b.t0 - sh.W + 1 > 0 ? b.t0 - sh.W + 1 : 0;

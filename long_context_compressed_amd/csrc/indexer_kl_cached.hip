@@ -26,6 +26,7 @@
 
 #include "attn_common.h"
 #include "csa_launch.h"
+#include "csr_build.h"
 
 #pragma clang diagnostic ignored "-Winline-asm"
 
@@ -439,24 +440,11 @@ struct CsrArgs {
 
 template <bool FILL>
 __global__ __launch_bounds__(256) void k_csr_pairs(CsrArgs c) {
-  const int tl = blockIdx.x;
-  const int t = c.t0 + tl;
-  const int n = c.nc[t];
-  if (n == 0) return;
-  TokenInfo ti;
-  if (!token_info_wave(c.cu, c.B, t, ti)) return;
-  const int row0 = c.cu_cmp[ti.b];
-  const int nv = min((ti.p + 1) / c.r, c.n_cap);
-  for (int s = threadIdx.x; s < n; s += 256) {
-    int gr = c.idx ? c.idx[(int64_t)t * c.k_cap + s] : row0 + s;
-    if (gr < row0 || gr >= row0 + nv) continue;
-    if (!FILL) {
-      atomicAdd(&c.cnt[gr], 1);
-    } else {
-      const int pos = atomicAdd(&c.cur[gr], 1);
-      c.list[pos] = tl * (int32_t)c.k_slots + s;
-    }
-  }
+  CsrBuild g;
+  g.idx = c.idx; g.cu = c.cu; g.cu_cmp = c.cu_cmp; g.nc = c.nc; g.cnt = c.cnt; g.cur = c.cur;
+  g.list = c.list; g.slots = c.k_slots; g.t0 = c.t0; g.nT = c.nT; g.B = c.B; g.r = c.r;
+  g.n_cap = c.n_cap; g.k_cap = c.k_cap;
+  csr_group_pass<FILL>(g);
 }
 
 __global__ __launch_bounds__(256) void k_fill_zero_i32(int32_t* __restrict__ p, int n) {
@@ -616,9 +604,9 @@ hipError_t launch_indexer_kl_cached(const Shape& sh, const KlIO& io, hipStream_t
     hipLaunchKernelGGL(k_kl_cached, dim3((unsigned)token_grid(a.nT)), dim3(256), 0, s, a);
     if (a.grads) {
       hipLaunchKernelGGL(k_fill_zero_i32, dim3(64), dim3(256), 0, s, c.cnt, c.n_rows);
-      hipLaunchKernelGGL(k_csr_pairs<false>, dim3(c.nT), dim3(256), 0, s, c);
+      hipLaunchKernelGGL(k_csr_pairs<false>, dim3(csr_grid(c.nT)), dim3(256), 0, s, c);
       hipLaunchKernelGGL(k_csr_scan, dim3(1), dim3(1024), 0, s, c);
-      hipLaunchKernelGGL(k_csr_pairs<true>, dim3(c.nT), dim3(256), 0, s, c);
+      hipLaunchKernelGGL(k_csr_pairs<true>, dim3(csr_grid(c.nT)), dim3(256), 0, s, c);
       hipLaunchKernelGGL(k_csr_reduce, dim3(c.n_rows), dim3(256), 0, s, c);
     }
     hipError_t e = hipGetLastError();
