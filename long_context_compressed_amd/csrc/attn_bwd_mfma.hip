@@ -499,12 +499,28 @@ __global__ __launch_bounds__(256) void k_bwd_reduce_cmp(BwdArgs b) {
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  int e = q;
-  for (; e + 4 < n; e += 8) {
-    add_staged(b.stage + (int64_t)lst[e] * kD + 8 * lane, acc);
-    add_staged(b.stage + (int64_t)lst[e + 4] * kD + 8 * lane, acc);
+  // wave q takes list entries 64q .. 64q + 63, then 64q + 256 .., each batch read with one
+  // coalesced load and broadcast from registers; 8 staged rows in flight per wave
+  for (int base = 64 * q; base < n; base += 256) {
+    const int my = base + lane < n ? lst[base + lane] : 0;
+    const int m = min(64, n - base);
+    for (int k = 0; k < m; k += 8) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = __shfl(my, k + u, 64);
+        v[u] = k + u < m ? *reinterpret_cast<const uint4*>(b.stage + (int64_t)e * kD + 8 * lane)
+                         : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        float f[8];
+        load8(reinterpret_cast<const uint16_t*>(&v[u]), f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += f[i];
+      }
+    }
   }
-  for (; e < n; e += 4) add_staged(b.stage + (int64_t)lst[e] * kD + 8 * lane, acc);
   finish_row(acc, b.dkv_cmp + (int64_t)j * kD, red);
 }
 

@@ -476,39 +476,63 @@ __global__ __launch_bounds__(1024) void k_csr_scan(CsrArgs c) {
 }
 
 // dst[j, :] += sum of the staged bf16 rows listed for j.  One workgroup per row; wave w takes
-// list entries w, w+4, ... in batches of 64 (one coalesced list read per batch, the entries
-// then broadcast from registers), lane l sums elements 2l, 2l+1 with many loads in flight.
+// list entries 64w .. 64w + 63, then 64w + 256 .., each batch read with one coalesced load
+// and broadcast from registers.  Sixteen lanes cover one 256-byte row (16 bytes each), so
+// one load instruction reads four rows and eight are kept in flight (32 rows per wave).
 __global__ __launch_bounds__(256) void k_csr_reduce(CsrArgs c) {
-  __shared__ float2 part[4][64];
+  __shared__ float part[4][kDI];
   const int j = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = c.cnt[j];
   if (n == 0) return;
   const int32_t* lst = c.list + c.off[j];
-  float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+  const int sub = lane >> 4, ch = lane & 15;   // row within a group of four, 16-byte chunk
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   for (int base = 64 * wave; base < n; base += 256) {
-    const int my = base + lane < n ? lst[base + lane] : -1;
+    const int my = base + lane < n ? lst[base + lane] : 0;
     const int m = min(64, n - base);
-#pragma unroll 8
-    for (int k = 0; k < m; k += 2) {
-      const int e0 = __shfl(my, k, 64), e1 = __shfl(my, k + 1, 64);
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(c.stage + (int64_t)e0 * kDI + 2 * lane);
-      a0 += __uint_as_float(v << 16);
-      a1 += __uint_as_float(v & 0xffff0000u);
-      if (e1 >= 0) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(c.stage + (int64_t)e1 * kDI + 2 * lane);
-        b0 += __uint_as_float(w << 16);
-        b1 += __uint_as_float(w & 0xffff0000u);
+    for (int k = 0; k < m; k += 32) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int x = k + 4 * u + sub;   // < 64
+        const int e = __shfl(my, x, 64);
+        v[u] = x < m ? *reinterpret_cast<const uint4*>(c.stage + (int64_t)e * kDI + 8 * ch)
+                     : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        float f[8];
+        load8(reinterpret_cast<const uint16_t*>(&v[u]), f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += f[i];
       }
     }
   }
-  part[wave][lane] = make_float2(a0 + b0, a1 + b1);
+  // lanes of the same chunk hold partial sums of the same eight elements
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc[i] += __shfl_xor(acc[i], 16, 64);
+    acc[i] += __shfl_xor(acc[i], 32, 64);
+  }
+  if (sub == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[wave][8 * ch + i] = acc[i];
+  }
   __syncthreads();
-  if (wave == 0) {
-    const float2 p0 = part[0][lane], p1 = part[1][lane], p2 = part[2][lane], p3 = part[3][lane];
-    float2* d = reinterpret_cast<float2*>(c.dst + (int64_t)j * kDI + 2 * lane);
-    const float2 o = *d;
-    *d = make_float2(o.x + ((p0.x + p1.x) + (p2.x + p3.x)), o.y + ((p0.y + p1.y) + (p2.y + p3.y)));
+  if (wave == 0 && lane < kDI / 4) {
+    float4* d = reinterpret_cast<float4*>(c.dst + (int64_t)j * kDI + 4 * lane);
+    float4 o = *d;
+    float s4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int x = 4 * lane + i;
+      s4[i] = (part[0][x] + part[1][x]) + (part[2][x] + part[3][x]);
+    }
+    o.x += s4[0]; o.y += s4[1]; o.z += s4[2]; o.w += s4[3];
+    *d = o;
   }
 }
 
