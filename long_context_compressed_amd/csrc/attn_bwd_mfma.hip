@@ -538,11 +538,27 @@ __global__ __launch_bounds__(256) void k_bwd_reduce_win(BwdArgs b, int u_lo) {
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int t = t_lo + q; t <= t_hi; t += 4) {
-    const int p = t - ti.start;
-    const int win0 = t - min(b.W, p + 1) + 1;
-    const int64_t slot = (int64_t)(t - b.t0) * b.n_slots + b.nc[t] + (u - win0);
-    add_staged(b.stage + slot * kD + 8 * lane, acc);
+  // wave q takes contributors t_lo + q, t_lo + q + 4, ..., eight staged rows in flight
+  for (int t0 = t_lo + q; t0 <= t_hi; t0 += 32) {
+    uint4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int t = t0 + 4 * k;
+      v[k] = make_uint4(0, 0, 0, 0);
+      if (t <= t_hi) {
+        const int p = t - ti.start;
+        const int win0 = t - min(b.W, p + 1) + 1;
+        const int64_t slot = (int64_t)(t - b.t0) * b.n_slots + b.nc[t] + (u - win0);
+        v[k] = *reinterpret_cast<const uint4*>(b.stage + slot * kD + 8 * lane);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float f[8];
+      load8(reinterpret_cast<const uint16_t*>(&v[k]), f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += f[i];
+    }
   }
   finish_row(acc, b.dkv + (int64_t)u * kD, red);
 }
