@@ -251,20 +251,32 @@ void k_kl_cached(KlcArgs a) {
   wait_vmem();
   __syncthreads();
 
+  // cached teacher logits of a block: thread = (heads 4 hq .. +3, slots 4 sq .. +3), read a
+  // block ahead (the logits come from HBM; reading them where they are used would expose
+  // that latency once per block)
+  const int hq = tid >> 4, sq = tid & 15;
+  auto load_logits = [&](int b, f32x4 (&v)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      v[k] = b < nblk ? *reinterpret_cast<const f32x4*>(tl_t + (int64_t)(4 * hq + k) * a.ld_t +
+                                                        kNB * b + 4 * sq)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  f32x4 lg_cur[4], lg_nxt[4];
+  load_logits(0, lg_cur);
+
   for (int b = 0; b < nblk; ++b) {
     const int buf = b & 1;
     const int rid_nn = row_of(b + 2);
     const float sc_nn = score_of(b + 2);
 
-    // ---- teacher probabilities: thread = (heads 4 hq .. +3, slots 4 sq .. +3)
+    // ---- teacher probabilities of this block's slots
     {
-      const int hq = tid >> 4, sq = tid & 15;
       float pj[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int h = 4 * hq + k;
-        const float l2 = lse2_s[h];
-        const f32x4 v = *reinterpret_cast<const f32x4*>(tl_t + (int64_t)h * a.ld_t + kNB * b + 4 * sq);
+        const float l2 = lse2_s[4 * hq + k];
+        const f32x4 v = lg_cur[k];
 #pragma unroll
         for (int i = 0; i < 4; ++i) pj[i] += __builtin_amdgcn_exp2f(v[i] * 1.44269504088896341f - l2);
       }
@@ -279,6 +291,7 @@ void k_kl_cached(KlcArgs a) {
     __syncthreads();
     // the other key buffer was last read before the previous block's second barrier
     if (b + 1 < nblk) issue(rid_nxt, buf ^ 1);
+    load_logits(b + 1, lg_nxt);
 
     // ---- per slot (lane l = slot 64 b + l): P, Q, KL and g; g w per wave in LDS
     float gl;
@@ -375,6 +388,8 @@ void k_kl_cached(KlcArgs a) {
     rid_nxt = rid_nn;
     sc_cur = sc_nxt;
     sc_nxt = sc_nn;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) lg_cur[k] = lg_nxt[k];
   }
 
   // ---- outputs: kl, dw, dqI (the two slot halves ch = 0, 1 summed through LDS)
