@@ -60,7 +60,7 @@ __device__ __forceinline__ void dma_row16(const void* src, const void* lds_row) 
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(lds), "v"(src) : "memory", "m0");
 }
-constexpr int64_t kStageBudget = 24ll << 30;   // bytes of pds + staging per chunk
+constexpr int64_t kStageBudget = 96ll << 30;   // bytes of pds + staging per chunk
 
 struct BwdArgs {
   const uint16_t* q;

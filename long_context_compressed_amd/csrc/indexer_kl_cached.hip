@@ -41,7 +41,7 @@ constexpr int kHI = 64;     // indexer heads
 constexpr int kDI = 128;    // indexer width
 constexpr int kNB = 64;     // slots per block
 constexpr int kES = 72;     // bf16 row stride of the E tile
-constexpr int64_t kStageBudget = 8ll << 30;   // bytes of staging per chunk
+constexpr int64_t kStageBudget = 16ll << 30;   // bytes of staging per chunk
 
 struct KlcArgs {
   const float* tl;          // cached teacher logits [T, 64, ld_t]
