@@ -42,6 +42,7 @@ constexpr int kDI = 128;    // indexer width
 constexpr int kNB = 64;     // slots per block
 constexpr int kES = 72;     // bf16 row stride of the E tile
 constexpr int64_t kStageBudget = 16ll << 30;   // bytes of staging per chunk
+constexpr int kIdxLds = 2048;                   // idx entries of a query staged in LDS
 
 struct KlcArgs {
   const float* tl;          // cached teacher logits [T, 64, ld_t]
@@ -67,6 +68,8 @@ struct KlcArgs {
 };
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// at most 8 vector memory operations outstanding (they complete in issue order)
+__device__ __forceinline__ void wait_vmem_8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
 
 __device__ __forceinline__ void dma_rows16(const void* src, const void* lds) {
   const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
@@ -90,8 +93,14 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 
 }  // namespace
 
+// IDX_LDS: the query's idx row (k_cap <= kIdxLds) is staged in LDS, so that the block loop's
+// only global loads are the cached logits, the index scores and the key rows, none of which
+// is needed in the block that issues it (a load consumed right away would make the wave wait
+// for every older memory operation, the previous block's staged stores included).
+template <bool IDX_LDS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_kl_cached(KlcArgs a) {
+  __shared__ int32_t idx_s[IDX_LDS ? kIdxLds : 1];
   __shared__ __attribute__((aligned(16))) uint16_t KIt[2][kNB][kDI];   // swizzled 256-byte rows
   __shared__ __attribute__((aligned(16))) uint16_t QIt[kHI][kDI];      // swizzled 256-byte rows
   __shared__ __attribute__((aligned(16))) uint16_t Es[kHI][kES];
@@ -115,7 +124,9 @@ void k_kl_cached(KlcArgs a) {
   if (real) {
     row0 = a.cu_cmp[ti.b];
     nv = min((ti.p + 1) / a.r, a.n_cap);
-    n_c = idx_t ? leading_valid(idx_t, a.k_cap, &s_tmp) : nv;
+    if (IDX_LDS && idx_t)
+      for (int c = tid; c < a.k_cap; c += 256) idx_s[c] = idx_t[c];
+    n_c = idx_t ? leading_valid(idx_t, a.k_cap, &s_tmp) : nv;   // its barriers publish idx_s
   }
   if (tid == 0) a.nc[t] = n_c;
   if (n_c == 0) {
@@ -132,7 +143,7 @@ void k_kl_cached(KlcArgs a) {
   auto slot_local = [&](int c) -> int {
     if (c >= n_c) return -1;
     if (!idx_t) return c;
-    const int gr = idx_t[c];
+    const int gr = IDX_LDS ? idx_s[c] : idx_t[c];
     return (gr >= row0 && gr < row0 + nv) ? gr - row0 : -1;
   };
 
@@ -264,11 +275,14 @@ void k_kl_cached(KlcArgs a) {
   };
   f32x4 lg_cur[4], lg_nxt[4];
   load_logits(0, lg_cur);
+  // block 0's logits complete before the loop, so that inside it the waits for the logits
+  // count only the previous block's younger loads and stores
+#pragma unroll
+  for (int k = 0; k < 4; ++k) asm volatile("" :: "v"(lg_cur[k]));
 
   for (int b = 0; b < nblk; ++b) {
     const int buf = b & 1;
     const int rid_nn = row_of(b + 2);
-    const float sc_nn = score_of(b + 2);
 
     // ---- teacher probabilities of this block's slots
     {
@@ -287,11 +301,16 @@ void k_kl_cached(KlcArgs a) {
       }
       if (g == 0) *reinterpret_cast<f32x4*>(&Pp[wave][4 * sq]) = f32x4{pj[0], pj[1], pj[2], pj[3]};
     }
-    wait_vmem();        // key rows of this block (issued during the previous block)
+    // key rows of this block, issued during the previous block; the only younger memory
+    // operations are that block's logit loads (already consumed above) and, if this wave
+    // staged any slot of it, its 8 dkI row stores, which may stay in flight
+    if (IDX_LDS && a.grads && b > 0 && kNB * (b - 1) + 16 * wave < n_c) wait_vmem_8();
+    else wait_vmem();
     __syncthreads();
     // the other key buffer was last read before the previous block's second barrier
     if (b + 1 < nblk) issue(rid_nxt, buf ^ 1);
     load_logits(b + 1, lg_nxt);
+    const float sc_nn = score_of(b + 2);   // used two blocks on
 
     // ---- per slot (lane l = slot 64 b + l): P, Q, KL and g; g w per wave in LDS
     float gl;
@@ -640,7 +659,10 @@ hipError_t launch_indexer_kl_cached(const Shape& sh, const KlIO& io, hipStream_t
   for (int64_t t0 = 0; t0 < sh.T; t0 += pl.chunk) {
     a.t0 = c.t0 = (int)t0;
     a.nT = c.nT = (int)(sh.T - t0 < pl.chunk ? sh.T - t0 : pl.chunk);
-    hipLaunchKernelGGL(k_kl_cached, dim3((unsigned)token_grid(a.nT)), dim3(256), 0, s, a);
+    if (sh.k_cap <= kIdxLds)
+      hipLaunchKernelGGL(k_kl_cached<true>, dim3((unsigned)token_grid(a.nT)), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_kl_cached<false>, dim3((unsigned)token_grid(a.nT)), dim3(256), 0, s, a);
     if (a.grads) {
       hipLaunchKernelGGL(k_fill_zero_i32, dim3(64), dim3(256), 0, s, c.cnt, c.n_rows);
       hipLaunchKernelGGL(k_csr_pairs<false>, dim3(csr_grid(c.nT)), dim3(256), 0, s, c);
