@@ -61,6 +61,7 @@ __device__ __forceinline__ void dma_row16(const void* src, const void* lds_row) 
                :: "s"(lds), "v"(src) : "memory", "m0");
 }
 constexpr int64_t kStageBudget = 96ll << 30;   // bytes of pds + staging per chunk
+constexpr int kIdxLds = 2048;                   // idx entries of a query staged in LDS (kernel 1)
 
 struct BwdArgs {
   const uint16_t* q;
@@ -90,15 +91,18 @@ struct BwdArgs {
   float scale, scale_log2;
 };
 
+// ti from token_info_wave with the compressed offsets; idx_lds: the query's idx row copied
+// into LDS by the calling block (published by the scan's first barrier), or null
 __device__ __forceinline__ CandSet make_cands(const BwdArgs& b, int t, const TokenInfo& ti,
-                                              int* s_tmp) {
+                                              int* s_tmp, const int32_t* idx_lds) {
   CandSet cs;
-  cs.row0 = b.cu_cmp[ti.b];
+  cs.row0 = ti.c0;
   cs.nv = min((ti.p + 1) / b.r, b.n_cap);
   cs.n_w = min(b.W, ti.p + 1);
   cs.win0 = t - cs.n_w + 1;
   if (b.mode == 1) cs.n_c = cs.nv;
   else if (b.mode == 2) cs.n_c = 0;
+  else if (idx_lds) cs.n_c = leading_valid_lds(idx_lds, b.k_cap, s_tmp);
   else cs.n_c = leading_valid(b.idx + (int64_t)t * b.k_cap, b.k_cap, s_tmp);
   cs.n_cs = cs.n_c;
   return cs;
@@ -120,10 +124,14 @@ __device__ __forceinline__ int cmp_row(const BwdArgs& b, int t, int row0, int nv
 
 }  // namespace
 
+// IDX_LDS: the query's idx row (k_cap <= kIdxLds) is staged in LDS once, so that the block
+// loop reads its next slots from LDS instead of issuing a global load per block.
+template <bool IDX_LDS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_attn_bwd_dq_mfma(BwdArgs b) {
   __shared__ __attribute__((aligned(16))) uint16_t Kt[2][kNB1][kD];       // swizzled 1 KiB rows
   __shared__ __attribute__((aligned(16))) uint16_t PT[2][kNB1][kPTS];     // [slot][dS | P]
+  __shared__ int32_t idx_s[IDX_LDS ? kIdxLds : 1];
   __shared__ int s_tmp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -131,7 +139,7 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
   if (tl >= b.nT) return;
   const int t = b.t0 + tl;
   TokenInfo ti;
-  if (!token_info_wave(b.cu, b.B, t, ti)) {
+  if (!token_info_wave(b.cu, b.B, t, ti, b.cu_cmp)) {
     uint4* o = reinterpret_cast<uint4*>(b.dq + (int64_t)t * kH * kD);
     for (int e = tid; e < kH * kD / 8; e += 256) o[e] = make_uint4(0, 0, 0, 0);
     if (tid == 0) b.nc[t] = 0;
@@ -143,6 +151,7 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
   // they overlap the metadata loads)
   bf16x8 qb[16], gb[16];
   const int64_t rowq = ((int64_t)t * kH + h) * kD;
+  const float lse_t = b.lse[(int64_t)t * kH + h];
   float dt = 0.f;
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
@@ -155,19 +164,21 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
     for (int i = 0; i < 8; ++i) dt = fmaf(ov[i], gv[i], dt);
   }
   const int32_t* idx_t = b.mode == 0 ? b.idx + (int64_t)t * b.k_cap : nullptr;
+  if (IDX_LDS && b.mode == 0)
+    for (int c = tid; c < b.k_cap; c += 256) idx_s[c] = idx_t[c];   // published by make_cands
   // raw idx entry of slot 32 blk + (lane & 31)
   auto raw_of = [&](int blk) {
     const int c = kNB1 * blk + (lane & 31);
-    return (b.mode == 0 && c < b.k_cap) ? idx_t[c] : 0;
+    if (b.mode != 0 || c >= b.k_cap) return 0;
+    return IDX_LDS ? idx_s[c] : idx_t[c];
   };
+  const CandSet cs = make_cands(b, t, ti, &s_tmp, IDX_LDS && b.mode == 0 ? idx_s : nullptr);
   int raw_cur = raw_of(0), raw_nxt = raw_of(1);
-  const CandSet cs = make_cands(b, t, ti, &s_tmp);
   if (tid == 0) b.nc[t] = cs.n_c;
   const int n_tot = cs.n_c + cs.n_w;
   const int nblk = (n_tot + kNB1 - 1) / kNB1;
   dt += __shfl_xor(dt, 16, 64);
   dt += __shfl_xor(dt, 32, 64);
-  const float lse_t = b.lse[(int64_t)t * kH + h];
   const float lse2 = lse_t * 1.44269504088896341f;
 
   f32x4 dq[4][8];   // heads 16mt + 4g + i, d = 128 wave + 16nt + c16
@@ -643,7 +654,10 @@ hipError_t launch_attn_bwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s
     b.t0 = (int)t0;
     b.nT = (int)(sh.T - t0 < pl.chunk ? sh.T - t0 : pl.chunk);
     const int64_t grid = token_grid(b.nT);
-    hipLaunchKernelGGL(k_attn_bwd_dq_mfma, dim3((unsigned)grid), dim3(256), 0, s, b);
+    if (sh.mode != 0 || sh.k_cap <= kIdxLds)
+      hipLaunchKernelGGL(k_attn_bwd_dq_mfma<true>, dim3((unsigned)grid), dim3(256), 0, s, b);
+    else
+      hipLaunchKernelGGL(k_attn_bwd_dq_mfma<false>, dim3((unsigned)grid), dim3(256), 0, s, b);
     hipLaunchKernelGGL(k_attn_bwd_dkv_mfma, dim3((unsigned)grid), dim3(256), 0, s, b);
     if (sh.mode != 2) {
       hipLaunchKernelGGL(k_bwd_fill_zero, dim3(64), dim3(256), 0, s, b.cnt, b.Tc_cap);

@@ -57,16 +57,33 @@ __device__ __forceinline__ int leading_valid(const int32_t* __restrict__ row, in
   return n;
 }
 
+// leading_valid of an idx row that the calling block has copied into LDS (row); the first
+// barrier publishes the copy, so the row is read from global memory once.
+__device__ __forceinline__ int leading_valid_lds(const int32_t* row, int k_cap, int* s_tmp) {
+  if (threadIdx.x == 0) *s_tmp = k_cap;
+  __syncthreads();
+  for (int c = threadIdx.x; c < k_cap; c += blockDim.x)
+    if (row[c] < 0) atomicMin(s_tmp, c);
+  __syncthreads();
+  const int n = *s_tmp;
+  __syncthreads();
+  return n;
+}
+
 // Sample of packed row t (false for capacity padding, t >= cu[B]).  The wave reads up to 64
 // entries of cu_seqlens at once and counts those <= t, so the lookup costs one load latency
-// per 64 samples instead of a chain of dependent loads.  Every lane of the wave must call it.
+// per 64 samples instead of a chain of dependent loads.  Given the compressed offsets
+// cu_cmp, the same pass also reads the sample's first compressed row into ti.c0.  Every
+// lane of the wave must call it.
 __device__ __forceinline__ bool token_info_wave(const int32_t* __restrict__ cu, int B, int t,
-                                                TokenInfo& ti) {
+                                                TokenInfo& ti,
+                                                const int32_t* __restrict__ cu_cmp = nullptr) {
   const int lane = threadIdx.x & 63;
-  int cnt = 0, lo = 0, hi = 0;   // cnt = #{i <= B : cu[i] <= t}
+  int cnt = 0, lo = 0, hi = 0, c0 = 0;   // cnt = #{i <= B : cu[i] <= t}
   for (int base = 0; base <= B; base += 64) {
     const int i = base + lane;
     const int v = i <= B ? cu[i] : 0x7fffffff;
+    const int vc = (cu_cmp && i <= B) ? cu_cmp[i] : 0;
     const uint64_t le = __ballot(v <= t);
     const int n = __popcll(le);
     if (n == 0) break;
@@ -74,6 +91,7 @@ __device__ __forceinline__ bool token_info_wave(const int32_t* __restrict__ cu, 
     // cu[cnt - 1] and cu[cnt] (if still within this group of 64)
     const int j = cnt - 1 - base;
     lo = __shfl(v, j, 64);
+    c0 = __shfl(vc, j, 64);
     hi = j + 1 < 64 ? __shfl(v, j + 1, 64) : 0x7fffffff;
     if (n < 64) break;
   }
@@ -83,6 +101,7 @@ __device__ __forceinline__ bool token_info_wave(const int32_t* __restrict__ cu, 
   ti.start = lo;
   ti.len = hi - lo;
   ti.p = t - lo;
+  ti.c0 = c0;
   return true;
 }
 

@@ -40,6 +40,7 @@ namespace {
 constexpr int kNB = 64;        // candidates per block
 constexpr int kPS = 72;        // P tile row stride (bf16)
 constexpr float kLazy = 8.f;   // growth (log2 units) of the running max tolerated before rescaling
+constexpr int kIdxLds = 2048;    // idx entries of a query staged in LDS
 constexpr int kFwdWaves = 4;   // one wave per SIMD: each wave holds Q (32 heads) and 1/4 of O
 
 struct FwdArgs {
@@ -85,7 +86,9 @@ __device__ __forceinline__ void dma_row16_s(uint64_t row, uint32_t lane_off, uin
 
 // NW waves per query: NW/2 candidate groups of CPW = 128/NW candidates for S^T, and d slices
 // of DPW = 512/NW columns for O^T.
-template <int NW>
+// IDX_LDS: the query's idx row (k_cap <= kIdxLds) is staged in LDS once, so that the block
+// loop reads its next slots from LDS instead of issuing a global load per block.
+template <int NW, bool IDX_LDS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void k_attn_fwd_mfma(FwdArgs a) {
   constexpr int NT = NW * 64, NCH = NW / 2, CPW = kNB / NCH, MQ = CPW / 16, DPW = kD / NW,
@@ -99,6 +102,7 @@ void k_attn_fwd_mfma(FwdArgs a) {
   __shared__ int resc_s[2];
   __shared__ int s_tmp;
   __shared__ float2 rope_s[kD / 2];   // cos, sin of the output rotation's pairs
+  __shared__ int32_t idx_s[IDX_LDS ? kIdxLds : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -107,7 +111,7 @@ void k_attn_fwd_mfma(FwdArgs a) {
   if (t >= a.T) return;
 
   TokenInfo ti;
-  if (!token_info_wave(a.cu, a.B, t, ti)) {
+  if (!token_info_wave(a.cu, a.B, t, ti, a.cu_cmp)) {
     uint4* o = reinterpret_cast<uint4*>(a.out + (int64_t)t * kH * kD);
     for (int e = tid; e < kH * kD / 8; e += NT) o[e] = make_uint4(0, 0, 0, 0);
     if (a.out_rot) {
@@ -129,13 +133,14 @@ void k_attn_fwd_mfma(FwdArgs a) {
       for (int ks = 0; ks < 16; ++ks) qb[nt][ks] = ld16(qt + 16 * nt * kD + 32 * ks);
   }
   const int32_t* idx_t = a.mode == 0 ? a.idx + (int64_t)t * a.k_cap : nullptr;
+  if (IDX_LDS && a.mode == 0)
+    for (int c = tid; c < a.k_cap; c += NT) idx_s[c] = idx_t[c];   // published by leading_valid_lds
   // raw idx entries of slot 64 b + lane; converted to row ids once the candidate counts are known
   auto raw_of = [&](int b) {
     const int c = kNB * b + lane;
-    return (a.mode == 0 && c < a.k_cap) ? idx_t[c] : 0;
+    if (a.mode != 0 || c >= a.k_cap) return 0;
+    return IDX_LDS ? idx_s[c] : idx_t[c];
   };
-  int raw_cur = raw_of(0);
-  int raw_nxt = raw_of(1);
   if (a.out_rot) {
     // angles of the output's inverse rotation at this query's position, formed while the
     // Q loads are in flight: pair i on lane i / NW of wave i % NW (at most kD / 2 <= NT pairs)
@@ -149,13 +154,16 @@ void k_attn_fwd_mfma(FwdArgs a) {
   }
 
   CandSet cs;
-  cs.row0 = a.cu_cmp[ti.b];
+  cs.row0 = ti.c0;
   cs.nv = min((ti.p + 1) / a.r, a.n_cap);
   cs.n_w = min(a.W, ti.p + 1);
   cs.win0 = t - cs.n_w + 1;
   if (a.mode == 1) cs.n_c = cs.nv;
   else if (a.mode == 2) cs.n_c = 0;
+  else if (IDX_LDS) cs.n_c = leading_valid_lds(idx_s, a.k_cap, &s_tmp);   // publishes idx_s
   else cs.n_c = leading_valid(idx_t, a.k_cap, &s_tmp);
+  int raw_cur = raw_of(0);
+  int raw_nxt = raw_of(1);
   // compressed slots padded to whole blocks, so a block never mixes compressed and window
   // rows and the compressed-only normalizer can be read off after the last compressed block
   cs.n_cs = ((cs.n_c + kNB - 1) / kNB) * kNB;
@@ -509,8 +517,12 @@ hipError_t launch_attn_fwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s
   a.k_cap = sh.k_cap;
   a.mode = sh.mode;
   a.scale_log2 = sh.scale * 1.44269504088896341f;
-  hipLaunchKernelGGL(k_attn_fwd_mfma<kFwdWaves>, dim3((unsigned)token_grid(sh.T)),
-                     dim3(kFwdWaves * 64), 0, s, a);
+  if (sh.mode != 0 || sh.k_cap <= kIdxLds)
+    hipLaunchKernelGGL((k_attn_fwd_mfma<kFwdWaves, true>), dim3((unsigned)token_grid(sh.T)),
+                       dim3(kFwdWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_attn_fwd_mfma<kFwdWaves, false>), dim3((unsigned)token_grid(sh.T)),
+                       dim3(kFwdWaves * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -106,6 +106,8 @@ struct TokenInfo {
   int start;   // first packed row of the sample
   int len;     // L_b
   int p;       // local position
+  int c0;      // first compressed row of the sample (set by attn::token_info_wave when it is
+               // given the compressed offsets)
 };
 
 // Sample of packed row t; returns false for capacity padding (t >= cu[B]).

@@ -118,15 +118,17 @@ void k_kl_cached(KlcArgs a) {
   const int t = a.t0 + tl;
 
   TokenInfo ti;
-  const bool real = token_info_wave(a.cu, a.B, t, ti);
+  const bool real = token_info_wave(a.cu, a.B, t, ti, a.cu_cmp);
   int row0 = 0, nv = 0, n_c = 0;
   const int32_t* idx_t = a.idx ? a.idx + (int64_t)t * a.k_cap : nullptr;
   if (real) {
-    row0 = a.cu_cmp[ti.b];
+    row0 = ti.c0;
     nv = min((ti.p + 1) / a.r, a.n_cap);
     if (IDX_LDS && idx_t)
       for (int c = tid; c < a.k_cap; c += 256) idx_s[c] = idx_t[c];
-    n_c = idx_t ? leading_valid(idx_t, a.k_cap, &s_tmp) : nv;   // its barriers publish idx_s
+    if (!idx_t) n_c = nv;
+    else if (IDX_LDS) n_c = leading_valid_lds(idx_s, a.k_cap, &s_tmp);   // publishes idx_s
+    else n_c = leading_valid(idx_t, a.k_cap, &s_tmp);
   }
   if (tid == 0) a.nc[t] = n_c;
   if (n_c == 0) {
