@@ -3,12 +3,17 @@
 // ("DeepSeek-V4 Attention Training Systems", section 3 indexer logits; section 9: the
 // indexer query is FP8-eligible).
 //
-// One wave per query token (4 tokens per workgroup, no LDS, no barriers).  The token's
-// 64 x 128 indexer query is resident in registers as the MFMA A operand; each step
-// multiplies it with 64 visible compressed keys (B operand, 16-byte row loads), so the
-// Z = qI kI^T tile [64 heads x 64 keys] lives in 16 accumulator tiles.  ReLU, the
-// per-(token, head) weight and the head sum are done in registers: 16 heads inside each
-// lane, then the 4 lane groups via cross-lane adds, in a fixed order (deterministic).
+// One wave per query token, 8 consecutive tokens per workgroup.  The token's 64 x 128
+// indexer query is resident in registers as the MFMA A operand; each step multiplies it
+// with 64 visible compressed keys (B operand), so the Z = qI kI^T tile [64 heads x 64 keys]
+// lives in 16 accumulator tiles.  When the 8 tokens lie in one sample (they then see the
+// same keys, up to one block), every 64-key block is gathered once into LDS for the whole
+// workgroup (direct global->LDS loads, a block ahead) and all 8 waves read their B operands
+// from there: the key bytes through the CU's load path drop 8-fold, which otherwise bound
+// the kernel at about the MFMA rate.  Groups that straddle a sample boundary load the keys
+// per wave (16-byte row loads).  ReLU, the per-(token, head) weight and the head sum are
+// done in registers: 16 heads inside each lane, then the 4 lane groups via cross-lane adds,
+// in a fixed order (deterministic; both paths sum alike).
 //   bf16: v_mfma_f32_16x16x32_bf16, 4 k-steps per tile.
 //   fp8 (OCP e4m3 codes): v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales, one
 //   instruction per tile; the per-row fp32 scales of qI and kI multiply the result.
@@ -19,10 +24,15 @@
 #include "csa_launch.h"
 #include "topk_wave.h"
 
+// M0 is named as clobbered by the LDS-DMA asm below; the compiler keeps no value in it here.
+#pragma clang diagnostic ignored "-Winline-asm"
+
 namespace csa {
 
 using attn::bf16x8;
 using attn::f32x4;
+using attn::ld16;
+using attn::swz;
 using attn::token_info_wave;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -30,6 +40,19 @@ namespace {
 
 constexpr int kHI = 64;
 constexpr int kDI = 128;
+constexpr int kSW = 8;    // tokens (waves) per workgroup
+constexpr int kKB = 64;   // keys per block
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Four 256-byte key rows per instruction (global_load_lds_dwordx4): lane l's 16 bytes land
+// at LDS byte offset lds + 16 l.  Issued through asm so that the compiler does not order LDS
+// reads of the other buffer behind it; completion is awaited with wait_vmem().
+__device__ __forceinline__ void dma_rows16(const void* src, const void* lds) {
+  const uint32_t d = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(d), "v"(src) : "memory", "m0");
+}
 
 struct ScArgs {
   const void* qI;
@@ -159,17 +182,117 @@ __device__ __forceinline__ void score_blocks(const ScArgs& a, int t, int row0, i
   }
 }
 
+// Whether the workgroup's kSW tokens t0 .. t0 + kSW - 1 are all real and in one sample
+// (then they share key blocks): gives that sample's first compressed row and the visible
+// count of its last token, the longest row of the group.  Wave-uniform, and the same in
+// every wave of the workgroup.
+__device__ __forceinline__ bool group_shares(const ScArgs& a, int t0, int& row0, int& nv_max) {
+  const int tl = t0 + kSW - 1;
+  if (tl >= a.T) return false;
+  TokenInfo f, l;
+  if (!token_info_wave(a.cu, a.B, t0, f, a.cu_cmp)) return false;
+  if (!token_info_wave(a.cu, a.B, tl, l)) return false;
+  if (f.b != l.b) return false;
+  row0 = f.c0;
+  nv_max = min((l.p + 1) / a.r, a.n_cap);
+  return true;
+}
+
+// bf16 scores of this wave's token (nv keys) with the workgroup's key blocks staged in LDS
+// (kbuf: two buffers of 64 swizzled 256-byte rows): every block of the group's longest row
+// (nv_max keys) is gathered once, a block ahead, and read by every wave as the B operand.
+// Every wave runs every block and its barrier; a wave with want = false, or whose row has
+// ended, only helps with the gathers.  emit as in score_blocks.
+template <class Emit>
+__device__ __forceinline__ void score_blocks_lds(const ScArgs& a, int t, int row0, int nv,
+                                                 bool want, int nv_max,
+                                                 uint16_t (*kbuf)[kKB][kDI], Emit&& emit) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  float wv[4][4];
+  bf16x8 qa[4][4];
+  if (want) {
+    const uint16_t* q = (const uint16_t*)a.qI + (int64_t)t * kHI * kDI;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[mt][i] = a.w[(int64_t)t * kHI + 16 * mt + 4 * g + i];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qa[mt][ks] = ld16(q + (16 * mt + c16) * kDI + 32 * ks + 8 * g);
+    }
+  }
+  const uint16_t* k = (const uint16_t*)a.kI;
+  const int nb = (nv_max + kKB - 1) / kKB;
+  // wave w gathers rows 8w .. 8w+7 of a block, four per instruction (lane l fills physical
+  // chunk l % 16 of row 4i + l / 16); rows past the group's longest row repeat its last key
+  // (finite, never emitted)
+  auto issue = [&](int b, int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * wave + 4 * i + (lane >> 4);
+      const int j = min(kKB * b + r, nv_max - 1);
+      dma_rows16(k + (int64_t)(row0 + j) * kDI + 8 * ((lane & 15) ^ swz(r)),
+                 &kbuf[buf][8 * wave + 4 * i][0]);
+    }
+  };
+  if (nb > 0) issue(0, 0);
+  for (int b = 0; b < nb; ++b) {
+    const int buf = b & 1;
+    wait_vmem();       // this wave's rows of block b
+    __syncthreads();   // every wave's rows of block b; block b - 1's buffer is free
+    if (b + 1 < nb) issue(b + 1, buf ^ 1);
+    if (!want || kKB * b >= nv) continue;
+    // B operand: key 16 nt + c16 (row bits 0-3 = c16), logical chunk 4 ks + g
+    const uint16_t* kr = &kbuf[buf][c16][0];
+    float mine = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      bf16x8 kb[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kb[ks] = ld16(kr + 16 * nt * kDI + 8 * ((4 * ks + g) ^ swz(c16)));
+      float s = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kb[ks], z, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s = fmaf(wv[mt][i], fmaxf(z[i], 0.f), s);
+      }
+      s += __shfl_xor(s, 16, 64);
+      s += __shfl_xor(s, 32, 64);
+      if (nt == g) mine = s;
+    }
+    emit(kKB * b, mine + 0.0f);
+  }
+}
+
 template <bool FP8>
-__global__ __launch_bounds__(256) void k_index_scores_mfma(ScArgs a) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+__global__ __launch_bounds__(kSW * 64) void k_index_scores_mfma(ScArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf[FP8 ? 1 : 2][FP8 ? 1 : kKB][kDI];
+  const int lane = threadIdx.x & 63;
+  const int t0 = blockIdx.x * kSW, t = t0 + (threadIdx.x >> 6);
+  if constexpr (!FP8) {
+    int row0 = 0, nv_max = 0;
+    if (group_shares(a, t0, row0, nv_max)) {
+      TokenInfo ti;
+      token_info_wave(a.cu, a.B, t, ti);   // inside the group's sample
+      const int nv = min((ti.p + 1) / a.r, a.n_cap);
+      float* out = a.scores + (int64_t)t * a.ld;
+      score_blocks_lds(a, t, row0, nv, nv > 0, nv_max, kbuf, [&](int j0, float s) {
+        if (j0 + lane < nv) out[j0 + lane] = s;
+      });
+      return;
+    }
+  }
   if (t >= a.T) return;
   TokenInfo ti;
-  if (!token_info_wave(a.cu, a.B, t, ti)) return;
+  if (!token_info_wave(a.cu, a.B, t, ti, a.cu_cmp)) return;
   const int nv = min((ti.p + 1) / a.r, a.n_cap);
   if (nv <= 0) return;
   float* out = a.scores + (int64_t)t * a.ld;
-  const int lane = threadIdx.x & 63;
-  score_blocks<FP8>(a, t, a.cu_cmp[ti.b], nv, [&](int j0, float s) {
+  score_blocks<FP8>(a, t, ti.c0, nv, [&](int j0, float s) {
     if (j0 + lane < nv) out[j0 + lane] = s;
   });
 }
@@ -179,36 +302,55 @@ __global__ __launch_bounds__(256) void k_index_scores_mfma(ScArgs a) {
 // wave's radix top-k selects from LDS and, in mode 1, stores the selected scores only.
 // Rows with nv <= k select every visible key, and skip the scores unless they are wanted.
 template <bool FP8, int KPL>
-__global__ __launch_bounds__(256) void k_index_topk(ScArgs a, int k, int k_cap, int mode,
-                                                    int32_t* __restrict__ idx) {
+__global__ __launch_bounds__(kSW * 64) void k_index_topk(ScArgs a, int k, int k_cap, int mode,
+                                                         int32_t* __restrict__ idx) {
   // each wave's score row, reused for its radix histograms once the keys are in registers
   constexpr int kSub = 8;
   constexpr int kRow = 64 * KPL > kSub * kHistStride ? 64 * KPL : kSub * kHistStride;
-  __shared__ __attribute__((aligned(16))) float rows[4][kRow];
+  __shared__ __attribute__((aligned(16))) float rows[kSW][kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf[FP8 ? 1 : 2][FP8 ? 1 : kKB][kDI];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= a.T) return;
+  const int t0 = blockIdx.x * kSW, t = t0 + wave;
+  int row0g = 0, nv_max = 0;
+  const bool shared = !FP8 && group_shares(a, t0, row0g, nv_max);
+  if (!shared && t >= a.T) return;
   int32_t* out = idx + (int64_t)t * k_cap;
   TokenInfo ti;
-  const bool real = token_info_wave(a.cu, a.B, t, ti);
+  const bool real = token_info_wave(a.cu, a.B, t, ti, a.cu_cmp);
   const int nv = real ? min((ti.p + 1) / a.r, a.n_cap) : 0;
-  const int row0 = real ? a.cu_cmp[ti.b] : 0;
+  const int row0 = real ? ti.c0 : 0;
   float* srow = a.scores ? a.scores + (int64_t)t * a.ld : nullptr;
+  float* lrow = rows[wave];
+  if constexpr (!FP8) {
+    if (shared) {
+      // rows with nv <= k need their scores only when the loss reads them (mode != 0)
+      score_blocks_lds(a, t, row0, nv, nv > k || mode != 0, nv_max, kbuf, [&](int j0, float s) {
+        if (j0 + lane < nv) {
+          if (nv > k) {
+            lrow[j0 + lane] = s;
+            if (mode == 2) srow[j0 + lane] = s;
+          } else {
+            srow[j0 + lane] = s;
+          }
+        }
+      });
+    }
+  }
   if (nv <= k) {  // every visible row is selected (also covers padding rows: nv = 0)
-    if (mode != 0 && nv > 0)
+    if (!shared && mode != 0 && nv > 0)
       score_blocks<FP8>(a, t, row0, nv, [&](int j0, float s) {
         if (j0 + lane < nv) srow[j0 + lane] = s;
       });
     for (int c = lane; c < k_cap; c += 64) out[c] = c < nv ? row0 + c : -1;
     return;
   }
-  float* lrow = rows[wave];
-  score_blocks<FP8>(a, t, row0, nv, [&](int j0, float s) {
-    if (j0 + lane < nv) {
-      lrow[j0 + lane] = s;
-      if (mode == 2) srow[j0 + lane] = s;
-    }
-  });
+  if (!shared)
+    score_blocks<FP8>(a, t, row0, nv, [&](int j0, float s) {
+      if (j0 + lane < nv) {
+        lrow[j0 + lane] = s;
+        if (mode == 2) srow[j0 + lane] = s;
+      }
+    });
   __builtin_amdgcn_wave_barrier();
   const int n_it = __builtin_amdgcn_readfirstlane((nv + 63) >> 6);
   float* sel = mode == 1 ? srow : nullptr;
@@ -242,11 +384,11 @@ hipError_t launch_index_scores_mfma(const Shape& sh, const void* qI, const float
   a.T = sh.T;
   a.r = sh.r;
   a.n_cap = sh.max_seqlen / sh.r;
-  const unsigned grid = (unsigned)((sh.T + 3) / 4);
+  const unsigned grid = (unsigned)((sh.T + kSW - 1) / kSW);
   if (sh.idx_dtype == 2)
-    hipLaunchKernelGGL(k_index_scores_mfma<true>, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_index_scores_mfma<true>, dim3(grid), dim3(kSW * 64), 0, s, a);
   else
-    hipLaunchKernelGGL(k_index_scores_mfma<false>, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_index_scores_mfma<false>, dim3(grid), dim3(kSW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -273,7 +415,7 @@ hipError_t launch_index_topk(const Shape& sh, const void* qI, const float* qI_sc
   a.T = sh.T;
   a.r = sh.r;
   a.n_cap = n_cap;
-  const dim3 grid((sh.T + 3) / 4), block(256);
+  const dim3 grid((sh.T + kSW - 1) / kSW), block(kSW * 64);
   const bool fp8 = sh.idx_dtype == 2;
 #define CSA_LAUNCH_FUSED(F, K)                                                                 \
   hipLaunchKernelGGL((k_index_topk<F, K>), grid, block, 0, s, a, sh.k, sh.k_cap, scores_mode, idx)
