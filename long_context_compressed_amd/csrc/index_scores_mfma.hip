@@ -198,41 +198,95 @@ __device__ __forceinline__ bool group_shares(const ScArgs& a, int t0, int& row0,
   return true;
 }
 
-// bf16 scores of this wave's token (nv keys) with the workgroup's key blocks staged in LDS
-// (kbuf: two buffers of 64 swizzled 256-byte rows): every block of the group's longest row
-// (nv_max keys) is gathered once, a block ahead, and read by every wave as the B operand.
+// LDS of the shared key blocks: two buffers of 64 rows (256-byte bf16 rows, or 128-byte
+// fp8 code rows and the rows' 64 fp32 scales).
+template <bool FP8>
+struct KeyTiles {
+  uint8_t rows[2][kKB * kDI * 2];
+};
+template <>
+struct KeyTiles<true> {
+  uint8_t rows[2][kKB * kDI];
+  float scale[2][kKB];
+};
+
+// 16-byte chunk swizzle of the fp8 128-byte rows: physical chunk = logical ^ swz8(row).  The
+// sixteen rows of one MFMA column tile read at one logical chunk then fall in sixteen
+// distinct 16-byte bank groups (row parity picks the half of the 64 banks).
+__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
+
+// 64 fp32 key scales of a block (global_load_lds_dword): lane l's 4 bytes land at lds + 4 l.
+__device__ __forceinline__ void dma_dword(const void* src, const void* lds) {
+  const uint32_t d = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(d), "v"(src) : "memory", "m0");
+}
+
+// Scores of this wave's token (nv keys) with the workgroup's key blocks staged in LDS: every
+// block of the group's longest row (nv_max keys) is gathered once, a block ahead, into
+// swizzled rows, and read by every wave as the B operand (fp8: with the keys' scales).
 // Every wave runs every block and its barrier; a wave with want = false, or whose row has
-// ended, only helps with the gathers.  emit as in score_blocks.
-template <class Emit>
+// ended, only helps with the gathers.  emit as in score_blocks, and the products, weights
+// and head sums are formed in the same order as there.
+template <bool FP8, class Emit>
 __device__ __forceinline__ void score_blocks_lds(const ScArgs& a, int t, int row0, int nv,
-                                                 bool want, int nv_max,
-                                                 uint16_t (*kbuf)[kKB][kDI], Emit&& emit) {
+                                                 bool want, int nv_max, KeyTiles<FP8>& kt,
+                                                 Emit&& emit) {
+  constexpr int kRowB = FP8 ? kDI : 2 * kDI;   // bytes per key row
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   float wv[4][4];
-  bf16x8 qa[4][4];
+  bf16x8 qa[4][4];   // bf16: [mt][ks]
+  i32x8 q8[4];       // fp8: [mt]
   if (want) {
-    const uint16_t* q = (const uint16_t*)a.qI + (int64_t)t * kHI * kDI;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wv[mt][i] = a.w[(int64_t)t * kHI + 16 * mt + 4 * g + i];
+      for (int i = 0; i < 4; ++i) {
+        const int h = 16 * mt + 4 * g + i;
+        float x = a.w[(int64_t)t * kHI + h];
+        if (FP8) x *= a.qI_scale[(int64_t)t * kHI + h];
+        wv[mt][i] = x;
+      }
+    if constexpr (FP8) {
+      const uint8_t* q = (const uint8_t*)a.qI + (int64_t)t * kHI * kDI;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qa[mt][ks] = ld16(q + (16 * mt + c16) * kDI + 32 * ks + 8 * g);
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint4* p = reinterpret_cast<const uint4*>(q + (16 * mt + c16) * kDI + 32 * g);
+        const uint4 lo = p[0], hi = p[1];
+        q8[mt] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    } else {
+      const uint16_t* q = (const uint16_t*)a.qI + (int64_t)t * kHI * kDI;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qa[mt][ks] = ld16(q + (16 * mt + c16) * kDI + 32 * ks + 8 * g);
     }
   }
-  const uint16_t* k = (const uint16_t*)a.kI;
+  const uint8_t* kg = (const uint8_t*)a.kI;
   const int nb = (nv_max + kKB - 1) / kKB;
-  // wave w gathers rows 8w .. 8w+7 of a block, four per instruction (lane l fills physical
-  // chunk l % 16 of row 4i + l / 16); rows past the group's longest row repeat its last key
-  // (finite, never emitted)
+  // bf16: wave w gathers rows 8w .. 8w+7, four per instruction (lane l fills physical chunk
+  // l % 16 of row 4i + l / 16); fp8: eight rows in one instruction (chunk l % 8 of row
+  // l / 8) and wave 0 also the 64 scales.  Rows past the group's longest row repeat its
+  // last key (finite, never emitted).
   auto issue = [&](int b, int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 8 * wave + 4 * i + (lane >> 4);
+    if constexpr (FP8) {
+      const int r = 8 * wave + (lane >> 3);
       const int j = min(kKB * b + r, nv_max - 1);
-      dma_rows16(k + (int64_t)(row0 + j) * kDI + 8 * ((lane & 15) ^ swz(r)),
-                 &kbuf[buf][8 * wave + 4 * i][0]);
+      dma_rows16(kg + (int64_t)(row0 + j) * kDI + 16 * ((lane & 7) ^ swz8(r)),
+                 &kt.rows[buf][8 * wave * kRowB]);
+      if (wave == 0)
+        dma_dword(a.kI_scale + row0 + min(kKB * b + lane, nv_max - 1), &kt.scale[buf][0]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 8 * wave + 4 * i + (lane >> 4);
+        const int j = min(kKB * b + r, nv_max - 1);
+        dma_rows16(kg + (int64_t)(row0 + j) * kRowB + 16 * ((lane & 15) ^ swz(r)),
+                   &kt.rows[buf][(8 * wave + 4 * i) * kRowB]);
+      }
     }
   };
   if (nb > 0) issue(0, 0);
@@ -242,27 +296,53 @@ __device__ __forceinline__ void score_blocks_lds(const ScArgs& a, int t, int row
     __syncthreads();   // every wave's rows of block b; block b - 1's buffer is free
     if (b + 1 < nb) issue(b + 1, buf ^ 1);
     if (!want || kKB * b >= nv) continue;
-    // B operand: key 16 nt + c16 (row bits 0-3 = c16), logical chunk 4 ks + g
-    const uint16_t* kr = &kbuf[buf][c16][0];
     float mine = 0.f;
+    if constexpr (FP8) {
+      // B operand: key 16 nt + c16 (swz8 depends on c16 only), logical chunks 2g, 2g + 1
+      const uint8_t* kr = &kt.rows[buf][c16 * kRowB];
+      const int s8 = swz8(c16);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      bf16x8 kb[4];
+      for (int nt = 0; nt < 4; ++nt) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(kr + 16 * nt * kRowB + 16 * ((2 * g) ^ s8));
+        const uint4 hi = *reinterpret_cast<const uint4*>(kr + 16 * nt * kRowB + 16 * ((2 * g + 1) ^ s8));
+        const i32x8 kb = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                               (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const float ksc = kt.scale[buf][16 * nt + c16];
+        float s = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kb[ks] = ld16(kr + 16 * nt * kDI + 8 * ((4 * ks + g) ^ swz(c16)));
-      float s = 0.f;
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+          // unit block scales (E8M0 127 = 2^0), A and B in fp8 e4m3 (format 0)
+          z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q8[mt], kb, z, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kb[ks], z, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s = fmaf(wv[mt][i], fmaxf(z[i], 0.f), s);
+          for (int i = 0; i < 4; ++i) s = fmaf(wv[mt][i], fmaxf(z[i] * ksc, 0.f), s);
+        }
+        s += __shfl_xor(s, 16, 64);
+        s += __shfl_xor(s, 32, 64);
+        if (nt == g) mine = s;
       }
-      s += __shfl_xor(s, 16, 64);
-      s += __shfl_xor(s, 32, 64);
-      if (nt == g) mine = s;
+    } else {
+      // B operand: key 16 nt + c16 (swz depends on the row's low 4 bits), logical chunk 4 ks + g
+      const uint16_t* kr = reinterpret_cast<const uint16_t*>(&kt.rows[buf][c16 * kRowB]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        bf16x8 kb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kb[ks] = ld16(kr + 16 * nt * kDI + 8 * ((4 * ks + g) ^ swz(c16)));
+        float s = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kb[ks], z, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s = fmaf(wv[mt][i], fmaxf(z[i], 0.f), s);
+        }
+        s += __shfl_xor(s, 16, 64);
+        s += __shfl_xor(s, 32, 64);
+        if (nt == g) mine = s;
+      }
     }
     emit(kKB * b, mine + 0.0f);
   }
@@ -270,21 +350,19 @@ __device__ __forceinline__ void score_blocks_lds(const ScArgs& a, int t, int row
 
 template <bool FP8>
 __global__ __launch_bounds__(kSW * 64) void k_index_scores_mfma(ScArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t kbuf[FP8 ? 1 : 2][FP8 ? 1 : kKB][kDI];
+  __shared__ __attribute__((aligned(16))) KeyTiles<FP8> kt;
   const int lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * kSW, t = t0 + (threadIdx.x >> 6);
-  if constexpr (!FP8) {
-    int row0 = 0, nv_max = 0;
-    if (group_shares(a, t0, row0, nv_max)) {
-      TokenInfo ti;
-      token_info_wave(a.cu, a.B, t, ti);   // inside the group's sample
-      const int nv = min((ti.p + 1) / a.r, a.n_cap);
-      float* out = a.scores + (int64_t)t * a.ld;
-      score_blocks_lds(a, t, row0, nv, nv > 0, nv_max, kbuf, [&](int j0, float s) {
-        if (j0 + lane < nv) out[j0 + lane] = s;
-      });
-      return;
-    }
+  int row0 = 0, nv_max = 0;
+  if (group_shares(a, t0, row0, nv_max)) {
+    TokenInfo ti;
+    token_info_wave(a.cu, a.B, t, ti);   // inside the group's sample
+    const int nv = min((ti.p + 1) / a.r, a.n_cap);
+    float* out = a.scores + (int64_t)t * a.ld;
+    score_blocks_lds<FP8>(a, t, row0, nv, nv > 0, nv_max, kt, [&](int j0, float s) {
+      if (j0 + lane < nv) out[j0 + lane] = s;
+    });
+    return;
   }
   if (t >= a.T) return;
   TokenInfo ti;
@@ -308,11 +386,11 @@ __global__ __launch_bounds__(kSW * 64) void k_index_topk(ScArgs a, int k, int k_
   constexpr int kSub = 8;
   constexpr int kRow = 64 * KPL > kSub * kHistStride ? 64 * KPL : kSub * kHistStride;
   __shared__ __attribute__((aligned(16))) float rows[kSW][kRow];
-  __shared__ __attribute__((aligned(16))) uint16_t kbuf[FP8 ? 1 : 2][FP8 ? 1 : kKB][kDI];
+  __shared__ __attribute__((aligned(16))) KeyTiles<FP8> kt;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kSW, t = t0 + wave;
   int row0g = 0, nv_max = 0;
-  const bool shared = !FP8 && group_shares(a, t0, row0g, nv_max);
+  const bool shared = group_shares(a, t0, row0g, nv_max);
   if (!shared && t >= a.T) return;
   int32_t* out = idx + (int64_t)t * k_cap;
   TokenInfo ti;
@@ -321,20 +399,18 @@ __global__ __launch_bounds__(kSW * 64) void k_index_topk(ScArgs a, int k, int k_
   const int row0 = real ? ti.c0 : 0;
   float* srow = a.scores ? a.scores + (int64_t)t * a.ld : nullptr;
   float* lrow = rows[wave];
-  if constexpr (!FP8) {
-    if (shared) {
-      // rows with nv <= k need their scores only when the loss reads them (mode != 0)
-      score_blocks_lds(a, t, row0, nv, nv > k || mode != 0, nv_max, kbuf, [&](int j0, float s) {
-        if (j0 + lane < nv) {
-          if (nv > k) {
-            lrow[j0 + lane] = s;
-            if (mode == 2) srow[j0 + lane] = s;
-          } else {
-            srow[j0 + lane] = s;
-          }
+  if (shared) {
+    // rows with nv <= k need their scores only when the loss reads them (mode != 0)
+    score_blocks_lds<FP8>(a, t, row0, nv, nv > k || mode != 0, nv_max, kt, [&](int j0, float s) {
+      if (j0 + lane < nv) {
+        if (nv > k) {
+          lrow[j0 + lane] = s;
+          if (mode == 2) srow[j0 + lane] = s;
+        } else {
+          srow[j0 + lane] = s;
         }
-      });
-    }
+      }
+    });
   }
   if (nv <= k) {  // every visible row is selected (also covers padding rows: nv = 0)
     if (!shared && mode != 0 && nv > 0)
