@@ -226,32 +226,36 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return sign | code;
 }
 
-// One wave per row; a row of up to 1024 elements is held as 8-element chunks.
-template <typename T>
+// A group of G lanes per row (G: the power of two, 8 .. 64, that covers the row's 8-element
+// chunks, so a wave quantizes 64 / G rows; rows of up to 1024 elements, two chunks per lane
+// at G = 64).  The row maximum is reduced within the group, then every lane encodes its
+// chunks and stores them as 8 bytes.
+template <typename T, int G>
 __global__ __launch_bounds__(256) void k_quantize_fp8(const T* __restrict__ x, int64_t rows,
                                                       int row_len, uint8_t* __restrict__ codes,
                                                       float* __restrict__ scale) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  const int lane = threadIdx.x & 63, li = lane & (G - 1);
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / G) + lane / G;
+  const bool ok = row < rows;   // no early exit: the group maximum is formed with shuffles
   const T* src = x + row * row_len;
   float v[2][8];
   float amax = 0.f;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    const int off = (lane + c * 64) * 8;
-    if (off < row_len) {
+    const int off = (li + c * G) * 8;
+    if (ok && off < row_len) {
       load8(src + off, v[c]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
     }
   }
-  amax = wave_max(amax);
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
   const float sc = amax > 0.f ? amax / 448.f : 1.f;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    const int off = (lane + c * 64) * 8;
-    if (off < row_len) {
+    const int off = (li + c * G) * 8;
+    if (ok && off < row_len) {
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(v[c][i] / sc) << (8 * i);
@@ -260,19 +264,29 @@ __global__ __launch_bounds__(256) void k_quantize_fp8(const T* __restrict__ x, i
       *reinterpret_cast<uint2*>(codes + row * row_len + off) = make_uint2(lo, hi);
     }
   }
-  if (lane == 0) scale[row] = sc;
+  if (ok && li == 0) scale[row] = sc;
+}
+
+template <typename T>
+static void launch_quantize_rows(const T* x, int64_t rows, int row_len, uint8_t* codes,
+                                 float* scale, hipStream_t s) {
+  const int chunks = row_len / 8;
+  const int g = chunks <= 8 ? 8 : chunks <= 16 ? 16 : chunks <= 32 ? 32 : 64;
+  const int64_t rows_per_wg = 4 * (64 / g);
+  const dim3 grid((unsigned)((rows + rows_per_wg - 1) / rows_per_wg)), block(256);
+  if (g == 8) hipLaunchKernelGGL((k_quantize_fp8<T, 8>), grid, block, 0, s, x, rows, row_len, codes, scale);
+  else if (g == 16) hipLaunchKernelGGL((k_quantize_fp8<T, 16>), grid, block, 0, s, x, rows, row_len, codes, scale);
+  else if (g == 32) hipLaunchKernelGGL((k_quantize_fp8<T, 32>), grid, block, 0, s, x, rows, row_len, codes, scale);
+  else hipLaunchKernelGGL((k_quantize_fp8<T, 64>), grid, block, 0, s, x, rows, row_len, codes, scale);
 }
 
 hipError_t launch_quantize_fp8(const void* x, int dtype, int64_t rows, int row_len,
                                uint8_t* codes, float* scale, hipStream_t s) {
-  const int64_t grid = (rows + 3) / 4;
-  if (grid == 0) return hipSuccess;
+  if (rows == 0) return hipSuccess;
   if (dtype == 0)
-    hipLaunchKernelGGL(k_quantize_fp8<float>, dim3((unsigned)grid), dim3(256), 0, s,
-                       (const float*)x, rows, row_len, codes, scale);
+    launch_quantize_rows((const float*)x, rows, row_len, codes, scale, s);
   else
-    hipLaunchKernelGGL(k_quantize_fp8<uint16_t>, dim3((unsigned)grid), dim3(256), 0, s,
-                       (const uint16_t*)x, rows, row_len, codes, scale);
+    launch_quantize_rows((const uint16_t*)x, rows, row_len, codes, scale, s);
   return hipGetLastError();
 }
 

@@ -215,15 +215,20 @@ def test_compress_learned_fwd_bwd(name):
     assert np.array_equal(G.back(dx)[n:], dx0[n:].astype(np.float64)), "padding rows of dx written"
 
 
-def test_quantize_fp8_bit_exact():
+@pytest.mark.parametrize("row_len,dtype", [(128, torch.bfloat16), (8, torch.bfloat16),
+                                           (64, torch.float32), (200, torch.bfloat16),
+                                           (512, torch.float32), (1024, torch.bfloat16)])
+def test_quantize_fp8_bit_exact(row_len, dtype):
+    # row lengths span every lane-group width of the kernel (8 .. 64 lanes per row, one or
+    # two 8-element chunks per lane); 777 rows leave a ragged last workgroup
     from long_context_compressed_amd import binding as B
     rng = np.random.default_rng(5)
-    x = rng.standard_normal((777, 128)) * np.logspace(-4, 3, 777)[:, None]
+    x = rng.standard_normal((777, row_len)) * np.logspace(-4, 3, 777)[:, None]
     x[3] = 0.0
     x[4, :5] = [1e-30, -0.0, 0.0, 448.0, -1e-9]
-    xb = torch.tensor(x).to(torch.bfloat16)
-    print("[gpu] case=quantize step=fp8", flush=True)
-    codes = torch.empty(777, 128, dtype=torch.uint8, device="cuda")
+    xb = torch.tensor(x).to(dtype)
+    print(f"[gpu] case=quantize step=fp8 row_len={row_len} dtype={dtype}", flush=True)
+    codes = torch.empty(777, row_len, dtype=torch.uint8, device="cuda")
     scale = torch.empty(777, dtype=torch.float32, device="cuda")
     B.csa_quantize_fp8(xb.cuda(), codes, scale)
     ref_codes, ref_scale = O.quantize_fp8(xb.to(torch.float32).numpy())
