@@ -101,6 +101,7 @@ template <bool IDX_LDS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_kl_cached(KlcArgs a) {
   __shared__ int32_t idx_s[IDX_LDS ? kIdxLds : 1];
+  __shared__ float sc_s[IDX_LDS ? kIdxLds : 1];   // student scores of the slots
   __shared__ __attribute__((aligned(16))) uint16_t KIt[2][kNB][kDI];   // swizzled 256-byte rows
   __shared__ __attribute__((aligned(16))) uint16_t QIt[kHI][kDI];      // swizzled 256-byte rows
   __shared__ __attribute__((aligned(16))) uint16_t Es[kHI][kES];
@@ -149,17 +150,65 @@ void k_kl_cached(KlcArgs a) {
     return (gr >= row0 && gr < row0 + nv) ? gr - row0 : -1;
   };
 
-  // ---- student log-sum-exp over C_t
-  float mx = -INFINITY;
-  for (int c = tid; c < n_c; c += 256) {
-    const int j = slot_local(c);
-    if (j >= 0) mx = fmaxf(mx, srow[j]);
+  // ---- loads of the query's resident operands, issued before the student scores so that
+  // their latencies overlap: qI^T B operand of z, the qI tile for dkI (into LDS), weights,
+  // teacher lse
+  bf16x8 qib[2][4];   // heads 32hh + 16nt + c16, d = 32ks + 8g .. +7
+  float wv[2];
+  if (a.grads) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const uint16_t* src = a.qI + ((int64_t)t * kHI + 32 * hh + 16 * nt + c16) * kDI + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qib[nt][ks] = ld16(src + 32 * ks);
+      wv[nt] = a.w[(int64_t)t * kHI + 32 * hh + 16 * nt + c16];
+    }
+    // QIt[h][chunk ^ swz(h)] (16-byte chunks of 256-byte rows) by direct loads: wave w
+    // fills rows 16w .. 16w+15, four per instruction (lane l: physical chunk l % 16 of row
+    // 4i + l / 16); complete at the wait before the block loop
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 16 * wave + 4 * i + (lane >> 4);
+      dma_rows16(a.qI + ((int64_t)t * kHI + h) * kDI + 8 * ((lane & 15) ^ swz(h)),
+                 &QIt[16 * wave + 4 * i][0]);
+    }
   }
-  const float mS = block_reduce(mx, red, true);
+  const float tlse_v = (a.tlse && tid < kHT) ? a.tlse[(int64_t)t * kHT + tid] : 0.f;
+
+  // ---- student log-sum-exp over C_t.  With up to kIdxLds slots the scores are read once,
+  // all loads in flight together, and kept in LDS for the block loop (-inf marks a slot
+  // outside C_t or the visible range); longer rows read them where they are used.
+  const bool sc_lds = IDX_LDS && n_c <= kIdxLds;
+  float mx = -INFINITY;
+  if (sc_lds) {
+    constexpr int kPT = (IDX_LDS ? kIdxLds : 256) / 256;
+    float sv[kPT];
+#pragma unroll
+    for (int i = 0; i < kPT; ++i) {
+      const int j = slot_local(tid + 256 * i);
+      sv[i] = j >= 0 ? srow[j] : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < kPT; ++i) {
+      if (tid + 256 * i < n_c) sc_s[tid + 256 * i] = sv[i];
+      mx = fmaxf(mx, sv[i]);
+    }
+  } else {
+    for (int c = tid; c < n_c; c += 256) {
+      const int j = slot_local(c);
+      if (j >= 0) mx = fmaxf(mx, srow[j]);
+    }
+  }
+  const float mS = block_reduce(mx, red, true);   // its barriers publish sc_s
   float sm = 0.f;
   for (int c = tid; c < n_c; c += 256) {
-    const int j = slot_local(c);
-    if (j >= 0) sm += expf(srow[j] - mS);
+    if (sc_lds) {
+      const float v = sc_s[c];
+      if (v > -INFINITY) sm += expf(v - mS);
+    } else {
+      const int j = slot_local(c);
+      if (j >= 0) sm += expf(srow[j] - mS);
+    }
   }
   const float sS = block_reduce(sm, red, false);
   // all slots out of the visible range (an invalid idx row): Q_t = 0 instead of NaN
@@ -168,10 +217,7 @@ void k_kl_cached(KlcArgs a) {
   // ---- teacher log-normalizer per head (log2 domain), from the forward or the cache
   const float* tl_t = a.tl + (int64_t)t * kHT * a.ld_t;
   if (a.tlse) {
-    if (tid < kHT) {
-      const float v = a.tlse[(int64_t)t * kHT + tid];
-      lse2_s[tid] = v > -INFINITY ? v * 1.44269504088896341f : INFINITY;
-    }
+    if (tid < kHT) lse2_s[tid] = tlse_v > -INFINITY ? tlse_v * 1.44269504088896341f : INFINITY;
   } else {
     // wave w: heads 16w..16w+15, one head at a time over all slots
     for (int hq = 0; hq < 16; ++hq) {
@@ -192,24 +238,6 @@ void k_kl_cached(KlcArgs a) {
     }
   }
 
-  // ---- resident indexer operands: qI^T B operand of z, qI tile for dkI
-  bf16x8 qib[2][4];   // heads 32hh + 16nt + c16, d = 32ks + 8g .. +7
-  float wv[2];
-  if (a.grads) {
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const uint16_t* src = a.qI + ((int64_t)t * kHI + 32 * hh + 16 * nt + c16) * kDI + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qib[nt][ks] = ld16(src + 32 * ks);
-      wv[nt] = a.w[(int64_t)t * kHI + 32 * hh + 16 * nt + c16];
-    }
-    // QIt[h][chunk ^ swz(h)] (16-byte chunks of 256-byte rows)
-    for (int e = tid; e < kHI * 16; e += 256) {
-      const int h = e >> 4, cc = e & 15;
-      *reinterpret_cast<uint4*>(&QIt[h][8 * (cc ^ swz(h))]) =
-          *reinterpret_cast<const uint4*>(a.qI + ((int64_t)t * kHI + h) * kDI + 8 * cc);
-    }
-  }
 
   // key-row ids of a block: lane l <-> slot 64 b + l (global compressed row or -1)
   const int nblk = (n_c + kNB - 1) / kNB;
@@ -219,7 +247,8 @@ void k_kl_cached(KlcArgs a) {
   };
   auto score_of = [&](int b) {
     const int j = b < nblk ? slot_local(kNB * b + lane) : -1;
-    return j >= 0 ? srow[j] : 0.f;
+    if (j < 0) return 0.f;
+    return sc_lds ? sc_s[kNB * b + lane] : srow[j];
   };
   // wave w gathers rows 16w .. 16w+15 (4 rows of 256 bytes per instruction, lane l fills
   // physical chunk l % 16 of row 4i + l / 16); an absent slot's row is zero-filled
