@@ -68,8 +68,8 @@ struct KlcArgs {
 };
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// at most 8 vector memory operations outstanding (they complete in issue order)
-__device__ __forceinline__ void wait_vmem_8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
+// at most 4 vector memory operations outstanding (they complete in issue order)
+__device__ __forceinline__ void wait_vmem_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 
 __device__ __forceinline__ void dma_rows16(const void* src, const void* lds) {
   const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
@@ -334,8 +334,8 @@ void k_kl_cached(KlcArgs a) {
     }
     // key rows of this block, issued during the previous block; the only younger memory
     // operations are that block's logit loads (already consumed above) and, if this wave
-    // staged any slot of it, its 8 dkI row stores, which may stay in flight
-    if (IDX_LDS && a.grads && b > 0 && kNB * (b - 1) + 16 * wave < n_c) wait_vmem_8();
+    // staged any slot of it, its 4 dkI row stores, which may stay in flight
+    if (IDX_LDS && a.grads && b > 0 && kNB * (b - 1) + 16 * wave < n_c) wait_vmem_4();
     else wait_vmem();
     __syncthreads();
     // the other key buffer was last read before the previous block's second barrier
@@ -424,14 +424,26 @@ void k_kl_cached(KlcArgs a) {
           dk[md] = mfma16(qa, eb, dk[md]);
         }
       }
-      // lane: slot 16 wave + c16, d = 16 md + 4g .. +3 -> bf16 staging row of (t, slot)
+      // lane: slot 16 wave + c16, d = 16 md + 4g .. +3 -> bf16 staging row of (t, slot).
+      // Lanes g and g ^ 1 (same slot) swap half of each md pair, so that every lane stores
+      // 8 consecutive d (16 bytes): even g keeps d 32m + 4g .. +3 of md = 2m and takes its
+      // neighbour's next four; odd g keeps d 32m + 16 + 4g .. +3 of md = 2m + 1 and takes the
+      // four before them.
       const int slot = kNB * b + 16 * wave + c16;
-      if (slot < n_c) {
-        uint16_t* dst = a.stage + ((int64_t)tl * a.k_slots + slot) * kDI + 4 * g;
+      const bool odd = g & 1;
+      uint16_t* dst = a.stage + ((int64_t)tl * a.k_slots + slot) * kDI;
 #pragma unroll
-        for (int md = 0; md < 8; ++md)
-          *reinterpret_cast<uint2*>(dst + 16 * md) =
-              make_uint2(pack_bf16x2(dk[md][0], dk[md][1]), pack_bf16x2(dk[md][2], dk[md][3]));
+      for (int m = 0; m < 4; ++m) {
+        const uint2 e = make_uint2(pack_bf16x2(dk[2 * m][0], dk[2 * m][1]),
+                                   pack_bf16x2(dk[2 * m][2], dk[2 * m][3]));
+        const uint2 o = make_uint2(pack_bf16x2(dk[2 * m + 1][0], dk[2 * m + 1][1]),
+                                   pack_bf16x2(dk[2 * m + 1][2], dk[2 * m + 1][3]));
+        const uint2 give = odd ? e : o;
+        const uint2 got = make_uint2((uint32_t)__shfl_xor((int)give.x, 16, 64),
+                                     (uint32_t)__shfl_xor((int)give.y, 16, 64));
+        const uint4 v = odd ? make_uint4(got.x, got.y, o.x, o.y) : make_uint4(e.x, e.y, got.x, got.y);
+        const int d0 = odd ? 32 * m + 16 + 4 * (g - 1) : 32 * m + 4 * g;
+        if (slot < n_c) *reinterpret_cast<uint4*>(dst + d0) = v;
       }
     }
     rid_cur = rid_nxt;
