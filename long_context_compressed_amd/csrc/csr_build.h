@@ -88,13 +88,33 @@ __device__ __forceinline__ void csr_group_pass(const CsrBuild& c) {
       }
     return;
   }
+  // every valid pair (q, s, row) of the group, f(q, s, row); the slots of kQB queries x kSI
+  // slots per lane are loaded together, so a lane waits for one load latency per batch
+  // instead of one per slot
+  int n_max = 0;
+  for (int q = 0; q < kCsrGroup; ++q) n_max = max(n_max, q_n[q]);
+  auto for_pairs = [&](auto&& f) {
+    constexpr int kQB = 4, kSI = 4;
+    for (int q0 = 0; q0 < kCsrGroup; q0 += kQB)
+      for (int sb = 0; sb < n_max; sb += 256 * kSI) {
+        int gr[kQB][kSI];
+#pragma unroll
+        for (int j = 0; j < kQB; ++j)
+#pragma unroll
+          for (int i = 0; i < kSI; ++i) {
+            const int s = sb + tid + 256 * i;
+            gr[j][i] = s < q_n[q0 + j] ? row_of(q0 + j, s) : -1;
+          }
+#pragma unroll
+        for (int j = 0; j < kQB; ++j)
+#pragma unroll
+          for (int i = 0; i < kSI; ++i)
+            if (gr[j][i] >= 0) f(q0 + j, sb + tid + 256 * i, gr[j][i]);
+      }
+  };
   for (int i = tid; i < span; i += 256) hist[i] = 0;
   __syncthreads();
-  for (int q = 0; q < kCsrGroup; ++q)
-    for (int s = tid; s < q_n[q]; s += 256) {
-      const int gr = row_of(q, s);
-      if (gr >= 0) atomicAdd(&hist[gr - lo], 1);
-    }
+  for_pairs([&](int, int, int gr) { atomicAdd(&hist[gr - lo], 1); });
   __syncthreads();
   if (!FILL) {
     for (int i = tid; i < span; i += 256) {
@@ -109,13 +129,10 @@ __device__ __forceinline__ void csr_group_pass(const CsrBuild& c) {
     hist[i] = 0;
   }
   __syncthreads();
-  for (int q = 0; q < kCsrGroup; ++q)
-    for (int s = tid; s < q_n[q]; s += 256) {
-      const int gr = row_of(q, s);
-      if (gr < 0) continue;
-      const int pos = base[gr - lo] + atomicAdd(&hist[gr - lo], 1);
-      c.list[pos] = (g0 + q) * (int32_t)c.slots + s;
-    }
+  for_pairs([&](int q, int s, int gr) {
+    const int pos = base[gr - lo] + atomicAdd(&hist[gr - lo], 1);
+    c.list[pos] = (g0 + q) * (int32_t)c.slots + s;
+  });
 }
 
 }  // namespace csa
