@@ -9,9 +9,10 @@
 // Design: one workgroup of 4 waves per query token (one per SIMD, 512 registers each);
 // candidates are processed in blocks of 64 rows, double-buffered in LDS.
 //   * Rows are gathered with direct global->LDS loads (global_load_lds_dwordx4, one 1 KiB
-//     row per wave instruction) one block ahead, so they land while the current block
-//     computes; the idx entries of a block are loaded a block before that.  LDS rows are 1 KiB with a 16-byte chunk swizzle, so both the row-segment
-//     reads of S = Q K^T and the transposed reads of P V are bank-conflict free.
+//     row per wave instruction) one block ahead, spread over the S^T k-steps so that they
+//     land while the current block computes; the query's idx row is staged in LDS once.
+//     LDS rows are 1 KiB with a 16-byte chunk swizzle, so both the row-segment reads of
+//     S = Q K^T and the transposed reads of P V are bank-conflict free.
 //   * S^T: wave (hh, ch) computes heads 32hh..32hh+31 against candidates 32ch..32ch+31 of
 //     the block on v_mfma_f32_16x16x32_bf16 (A = row segments from LDS, B = the query's Q
 //     resident in registers); every row segment read from LDS feeds two MFMAs.

@@ -93,9 +93,9 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 
 }  // namespace
 
-// IDX_LDS: the query's idx row (k_cap <= kIdxLds) is staged in LDS, so that the block loop's
-// only global loads are the cached logits, the index scores and the key rows, none of which
-// is needed in the block that issues it (a load consumed right away would make the wave wait
+// IDX_LDS: the query's idx row and its student scores (k_cap <= kIdxLds) are staged in LDS,
+// so that the block loop's only global loads are the cached logits and the key rows, neither
+// needed in the block that issues it (a load consumed right away would make the wave wait
 // for every older memory operation, the previous block's staged stores included).
 template <bool IDX_LDS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
