@@ -147,8 +147,11 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
   }
   const int h = 16 * wave + c16;  // this lane's head for S^T / dP^T (n index)
 
-  // B operands: Q[h][32ks + 8g ..] and dO[h][...]; Dt = dO . O for head h (loads first, so
-  // they overlap the metadata loads)
+  // the idx row first (into registers; to LDS once the operands are in flight), then the B
+  // operands Q[h][32ks + 8g ..] and dO[h][...] and Dt = dO . O for head h
+  const int32_t* idx_t = b.mode == 0 ? b.idx + (int64_t)t * b.k_cap : nullptr;
+  int iv[IDX_LDS ? kIdxLds / 256 : 1];
+  if (IDX_LDS && b.mode == 0) load_idx_regs(idx_t, b.k_cap, iv);
   bf16x8 qb[16], gb[16];
   const int64_t rowq = ((int64_t)t * kH + h) * kD;
   const float lse_t = b.lse[(int64_t)t * kH + h];
@@ -163,9 +166,7 @@ void k_attn_bwd_dq_mfma(BwdArgs b) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) dt = fmaf(ov[i], gv[i], dt);
   }
-  const int32_t* idx_t = b.mode == 0 ? b.idx + (int64_t)t * b.k_cap : nullptr;
-  if (IDX_LDS && b.mode == 0)
-    for (int c = tid; c < b.k_cap; c += 256) idx_s[c] = idx_t[c];   // published by make_cands
+  if (IDX_LDS && b.mode == 0) store_idx_lds(idx_s, b.k_cap, iv);   // published by make_cands
   // raw idx entry of slot 32 blk + (lane & 31)
   auto raw_of = [&](int blk) {
     const int c = kNB1 * blk + (lane & 31);

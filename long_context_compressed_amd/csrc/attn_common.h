@@ -57,6 +57,27 @@ __device__ __forceinline__ int leading_valid(const int32_t* __restrict__ row, in
   return n;
 }
 
+// An idx row of up to NPT * blockDim.x entries read into registers with every load in
+// flight at once (a copy loop that stores each entry before loading the next waits one
+// load latency per pass); store_idx_lds then writes it to LDS.  Entries past k_cap are 0.
+template <int NPT>
+__device__ __forceinline__ void load_idx_regs(const int32_t* __restrict__ row, int k_cap,
+                                              int (&v)[NPT]) {
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int c = threadIdx.x + blockDim.x * i;
+    v[i] = c < k_cap ? row[c] : 0;
+  }
+}
+template <int NPT>
+__device__ __forceinline__ void store_idx_lds(int32_t* dst, int k_cap, const int (&v)[NPT]) {
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int c = threadIdx.x + blockDim.x * i;
+    if (c < k_cap) dst[c] = v[i];
+  }
+}
+
 // leading_valid of an idx row that the calling block has copied into LDS (row); the first
 // barrier publishes the copy, so the row is read from global memory once.
 __device__ __forceinline__ int leading_valid_lds(const int32_t* row, int k_cap, int* s_tmp) {

@@ -123,8 +123,12 @@ void k_attn_fwd_mfma(FwdArgs a) {
     if (a.lse_cmp && tid < kH) a.lse_cmp[(int64_t)t * kH + tid] = -INFINITY;
     return;
   }
-  // Q^T as the B operand: qb[nt][ks] = Q[32hh + 16nt + c16][32ks + 8g .. +7] (loads issued
-  // first so they overlap the metadata loads below)
+  // the idx row first (into registers; to LDS once Q is in flight), so the first block's
+  // gather waits for the idx loads alone, then Q^T as the B operand:
+  // qb[nt][ks] = Q[32hh + 16nt + c16][32ks + 8g .. +7]
+  const int32_t* idx_t = a.mode == 0 ? a.idx + (int64_t)t * a.k_cap : nullptr;
+  int iv[IDX_LDS ? kIdxLds / NT : 1];
+  if (IDX_LDS && a.mode == 0) load_idx_regs(idx_t, a.k_cap, iv);
   bf16x8 qb[2][16];
   {
     const uint16_t* qt = a.q + ((int64_t)t * kH + 32 * hh + c16) * kD + 8 * g;
@@ -133,9 +137,7 @@ void k_attn_fwd_mfma(FwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) qb[nt][ks] = ld16(qt + 16 * nt * kD + 32 * ks);
   }
-  const int32_t* idx_t = a.mode == 0 ? a.idx + (int64_t)t * a.k_cap : nullptr;
-  if (IDX_LDS && a.mode == 0)
-    for (int c = tid; c < a.k_cap; c += NT) idx_s[c] = idx_t[c];   // published by leading_valid_lds
+  if (IDX_LDS && a.mode == 0) store_idx_lds(idx_s, a.k_cap, iv);   // published by leading_valid_lds
   // raw idx entries of slot 64 b + lane; converted to row ids once the candidate counts are known
   auto raw_of = [&](int b) {
     const int c = kNB * b + lane;

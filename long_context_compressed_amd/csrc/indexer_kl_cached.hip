@@ -125,8 +125,11 @@ void k_kl_cached(KlcArgs a) {
   if (real) {
     row0 = ti.c0;
     nv = min((ti.p + 1) / a.r, a.n_cap);
-    if (IDX_LDS && idx_t)
-      for (int c = tid; c < a.k_cap; c += 256) idx_s[c] = idx_t[c];
+    if (IDX_LDS && idx_t) {
+      int iv[IDX_LDS ? kIdxLds / 256 : 1];
+      load_idx_regs(idx_t, a.k_cap, iv);
+      store_idx_lds(idx_s, a.k_cap, iv);
+    }
     if (!idx_t) n_c = nv;
     else if (IDX_LDS) n_c = leading_valid_lds(idx_s, a.k_cap, &s_tmp);   // publishes idx_s
     else n_c = leading_valid(idx_t, a.k_cap, &s_tmp);
