@@ -347,18 +347,27 @@ void k_kld_keys(KldArgs a) {
   const int jw = jl0 + kKB * wave;
   const int nk = max(0, min(kKB, r_hi - (r_lo + kKB * wave)));
 
-  // this wave's key block: bf16 rows (or fp8 codes), rows past nk zero
-  for (int e = lane; e < kKB * (kDI / 8); e += 64) {
-    const int row = e >> 4, ch = e & 15;
-    const int64_t src = (int64_t)(r_lo + kKB * wave + row) * kDI;
-    if (!a.fp8) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < nk) v = *reinterpret_cast<const uint4*>((const uint16_t*)a.kI + src + 8 * ch);
-      *reinterpret_cast<uint4*>(&KIt[wave][row][8 * ch]) = v;
-    } else if (ch < 8) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < nk) v = *reinterpret_cast<const uint4*>((const uint8_t*)a.kI + src + 16 * ch);
-      *reinterpret_cast<uint4*>(&KI8[wave][row][16 * ch]) = v;
+  // this wave's key block: bf16 rows (or fp8 codes), rows past nk zero; every load of a
+  // lane is issued before its first store (a loop storing each chunk before loading the
+  // next waits one load latency per chunk)
+  {
+    constexpr int kPL = kKB * (kDI / 8) / 64;   // 16-byte chunks per lane
+    uint4 kv[kPL];
+#pragma unroll
+    for (int u = 0; u < kPL; ++u) {
+      const int e = lane + 64 * u, row = e >> 4, ch = e & 15;
+      const int64_t src = (int64_t)(r_lo + kKB * wave + row) * kDI;
+      kv[u] = make_uint4(0, 0, 0, 0);
+      if (row < nk) {
+        if (!a.fp8) kv[u] = *reinterpret_cast<const uint4*>((const uint16_t*)a.kI + src + 8 * ch);
+        else if (ch < 8) kv[u] = *reinterpret_cast<const uint4*>((const uint8_t*)a.kI + src + 16 * ch);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPL; ++u) {
+      const int e = lane + 64 * u, row = e >> 4, ch = e & 15;
+      if (!a.fp8) *reinterpret_cast<uint4*>(&KIt[wave][row][8 * ch]) = kv[u];
+      else if (ch < 8) *reinterpret_cast<uint4*>(&KI8[wave][row][16 * ch]) = kv[u];
     }
   }
 
