@@ -245,12 +245,22 @@ __global__ __launch_bounds__(256) void k_kl_generic(KlK a) {
   }
 }
 
-// Deterministic sum of the per-query KL values: fixed strided partial sums, fixed tree.
+// Deterministic sum of the per-query KL values: fixed strided partial sums, fixed tree.  The
+// strided loads are issued 16 at a time and added in the same order as one by one.
 __global__ __launch_bounds__(256) void k_sum(const float* __restrict__ x, int n,
                                              float* __restrict__ out) {
   __shared__ float red[256];
+  constexpr int kU = 16;
   float s = 0.f;
-  for (int i = threadIdx.x; i < n; i += 256) s += x[i];
+  int i = threadIdx.x;
+  for (; i + 256 * (kU - 1) < n; i += 256 * kU) {
+    float v[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) v[j] = x[i + 256 * j];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) s += v[j];
+  }
+  for (; i < n; i += 256) s += x[i];
   red[threadIdx.x] = s;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
