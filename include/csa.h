@@ -45,7 +45,9 @@
  *   and returns a negative csa_status_t with nothing launched.  Device metadata
  *   (cu_seqlens non-decreasing, cu_seqlens[B] <= total_tokens, every L_b <=
  *   max_seqlen) is the caller's contract, checkable on request with
- *   csa_validate_metadata.  A failed launch returns CSA_ERR_LAUNCH.
+ *   csa_validate_metadata; cu_cmp, wherever a call takes it, must hold what
+ *   csa_cmp_seqlens wrote for the same cu_seqlens (its values index the
+ *   compressed buffers unchecked).  A failed launch returns CSA_ERR_LAUNCH.
  * - Calls that share an output buffer must not overlap in time.
  */
 #ifndef CSA_H_

@@ -152,8 +152,10 @@ class CsaLayer:
                    self.cfg.rope_theta, inverse, self.B, offsets)
 
     def forward(self, inp, cu_seqlens):
-        """inp: dict of device tensors q, kv, [qI, kI_tok, w], [sink]."""
+        """inp: dict of device tensors q, kv, [qI, kI_tok, w], [sink].  Forms the compressed
+        offsets of cu_seqlens first: every later call indexes rows through them."""
         cfg, p = self.cfg, self.p
+        self.metadata(cu_seqlens)
         self._call("compress_kv", B.csa_compress, p, inp["kv"], cu_seqlens, self.cu_cmp,
                    self.kv_cmp)
         kv = inp["kv"]
@@ -237,7 +239,6 @@ class CsaLayer:
                        self.cu_cmp, self.dkI_tok)
 
     def step(self, inp, cu_seqlens):
-        self.metadata(cu_seqlens)
         self.forward(inp, cu_seqlens)
         if self.backward:
             self.backward_step(inp, cu_seqlens)
