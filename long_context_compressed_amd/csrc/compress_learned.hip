@@ -51,12 +51,46 @@ __device__ __forceinline__ bool group_span(const int32_t* __restrict__ cu,
   return true;
 }
 
+// group_softmax for a span of exactly N tokens (the ratio-4 spans: 4 or 8): the loops are
+// unrolled, so every token's loads are in flight together instead of one token at a time.
+template <int N, typename T>
+__device__ __forceinline__ void group_softmax_n(const T* __restrict__ x, const T* __restrict__ sc,
+                                                const float* __restrict__ bias, int dim, int c8,
+                                                const Span& sp, float (&m)[8], float (&l)[8],
+                                                float (&c)[8]) {
+  float s[N][8], bb[N][8], v[N][8];
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    load8(sc + (int64_t)(sp.t0 + u) * dim + c8, s[u]);
+    load8(bias + (int64_t)(sp.p0 + u) * dim + c8, bb[u]);
+    load8(x + (int64_t)(sp.t0 + u) * dim + c8, v[u]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { m[i] = -INFINITY; l[i] = 0.f; c[i] = 0.f; }
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], s[u][i] + bb[u][i]);
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float e = __expf(s[u][i] + bb[u][i] - m[i]);
+      l[i] += e;
+      c[i] = fmaf(e, v[u][i], c[i]);
+    }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] /= l[i];
+}
+
 // Per-channel max of the logits over the span, then the normalizer and the reduction.
 template <typename T>
 __device__ __forceinline__ void group_softmax(const T* __restrict__ x, const T* __restrict__ sc,
                                               const float* __restrict__ bias, int dim, int c8,
                                               const Span& sp, float (&m)[8], float (&l)[8],
                                               float (&c)[8]) {
+  if (sp.n == 8) return group_softmax_n<8>(x, sc, bias, dim, c8, sp, m, l, c);
+  if (sp.n == 4) return group_softmax_n<4>(x, sc, bias, dim, c8, sp, m, l, c);
 #pragma unroll
   for (int i = 0; i < 8; ++i) { m[i] = -INFINITY; l[i] = 0.f; c[i] = 0.f; }
   for (int u = 0; u < sp.n; ++u) {
@@ -132,6 +166,38 @@ __global__ __launch_bounds__(256) void k_compress_learned_bwd(
       float m[8], l[8], c[8], g[8];
       group_softmax(x, sc, bias, dim, c8, sp, m, l, c);
       load8(dc + (int64_t)(row_lo + k) * dim + c8, g);
+      if (u_hi - u_lo == 4) {
+        // the ratio-4 parts: the four tokens' loads are all in flight before the first use
+        constexpr int N = 4;
+        float s[N][8], bb[N][8], v[N][8], ox[N][8], os[N][8];
+#pragma unroll
+        for (int q = 0; q < N; ++q) {
+          const int u = u_lo + q;
+          const int64_t off = (int64_t)(sp.t0 + u) * dim + c8;
+          load8(sc + off, s[q]);
+          load8(bias + (int64_t)(sp.p0 + u) * dim + c8, bb[q]);
+          load8(x + off, v[q]);
+          load8(dx + off, ox[q]);
+          load8(ds + off, os[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < N; ++q) {
+          const int u = u_lo + q;
+          const int64_t off = (int64_t)(sp.t0 + u) * dim + c8;
+          float* db = &dbs[(sp.p0 + u) * cw + 8 * lc];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float w = __expf(s[q][i] + bb[q][i] - m[i]) / l[i];
+            ox[q][i] = fmaf(w, g[i], ox[q][i]);
+            const float dz = w * (v[q][i] - c[i]) * g[i];
+            os[q][i] += dz;
+            atomicAdd(db + i, dz);
+          }
+          store8(dx + off, ox[q]);
+          store8(ds + off, os[q]);
+        }
+        continue;
+      }
       for (int u = u_lo; u < u_hi; ++u) {
         const int64_t off = (int64_t)(sp.t0 + u) * dim + c8;
         float s[8], bb[8], v[8], ox[8], os[8];
