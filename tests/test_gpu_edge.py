@@ -108,3 +108,28 @@ def test_degenerate_pack_layer(name):
             if n:
                 G.check("dqI", G.back(L.dqI)[:n], ref["dqI"], k2, rel_tol=rt)
     assert T >= n
+
+
+def test_layer_forward_forms_compressed_offsets():
+    """A layer forward called without a separate metadata call forms the compressed offsets
+    itself (a forward that read a stale offsets buffer indexed rows through it); the offsets
+    buffer starts zeroed here, so a forward that skipped them would give wrong outputs."""
+    from long_context_compressed_amd.pipeline import CsaLayer, LayerConfig, to_device
+    w = configs.workload("thd64k_csa_bf16", lengths=(37, 0, 90, 5), total_tokens=160, topk=64,
+                         topk_cap=64, draw=None, backward=False)
+    print("[gpu] case=forward_forms_offsets", flush=True)
+    host = synth_inputs.make_inputs(w)
+    h64 = {k: synth_inputs.to_f64(v) for k, v in host.items() if isinstance(v, torch.Tensor)}
+    h64["cu_seqlens"] = host["cu_seqlens"]
+    h64["max_seqlen"] = host["max_seqlen"]
+    L = CsaLayer(LayerConfig.of(w), len(host["lengths"]), w.total_tokens, host["max_seqlen"],
+                 backward=False)
+    L.cu_cmp.zero_()
+    dev = to_device(host)
+    L.forward(dev, dev["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert torch.equal(L.cu_cmp.cpu().to(torch.int64),
+                       torch.as_tensor(O.cmp_seqlens(host["cu_seqlens"], w.ratio)))
+    n = int(host["cu_seqlens"][-1])
+    ref = O.layer_step(h64, w, rows=np.arange(n))
+    G.check("O", G.back(L.out)[:n], ref["O"], w.dtype)
