@@ -41,6 +41,21 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd-workspace-gib", type=float, default=None,
+                    help="cap the attention backward's workspace (more query chunks)")
+    ap.add_argument("--no-measured-peaks", action="store_true",
+                    help="skip the matrix-core loop and copy that measure the device's peaks")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="print the per-kernel summary of a 'rocprofv3 --kernel-trace' run of "
+                         "bench.py (files run_kernel_trace.csv) and exit: dispatches before the "
+                         "trace marker are the layer steps, after it the stand-alone timings")
+    ap.add_argument("--summarize-counters", metavar="PMC_DIR",
+                    help="print per-kernel matrix-core and LDS counters of a 'rocprofv3 --pmc "
+                         "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+                         "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_BUSY_CYCLES GRBM_GUI_ACTIVE' "
+                         "run of bench.py and exit")
+    ap.add_argument("--traced-steps", type=int, default=0,
+                    help="steps (warm-up + timed) in the traced run, for per-step figures")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run one plain device-to-device copy of this many bytes before "
                          "the timed steps (a known-traffic reference for HBM counters)")
@@ -96,6 +111,41 @@ def _pmc_rows(d):
     return out
 
 
+def summarize_counters(d, steps):
+    """Per kernel (dispatches of the traced steps summed).  GRBM_GUI_ACTIVE sums the cycle
+    counters of the 8 XCDs (8x the kernel's duration in cycles), SQ_VALU_MFMA_BUSY_CYCLES the
+    1024 SIMDs' busy cycles and SQ_LDS_* the 256 CUs' cycles, so: matrix-core busy =
+    MFMA_BUSY / (GUI / 8 x 1024); bf16 matrix FLOP issued = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512;
+    LDS bank-conflict share of the kernel's cycles = BANK_CONFLICT / 256 / (GUI / 8), and of the
+    LDS-active cycles = BANK_CONFLICT / LDS_IDX_ACTIVE."""
+    rows = _pmc_rows(d)
+    per = {}
+    for disp, name, cname, v in rows:
+        per.setdefault(name, {}).setdefault(cname, {})[disp] = v
+    print("| Kernel | Dispatches | MFMA busy | bf16 MFMA TFLOP per step | LDS bank conflicts, of kernel cycles | of LDS-active cycles |")
+    print("| --- | --- | --- | --- | --- | --- |")
+    out = []
+    for name, cs in per.items():
+        disp = set().union(*[set(x) for x in cs.values()])
+        tot = {c: sum(x.values()) for c, x in cs.items()}
+        gui = tot.get("GRBM_GUI_ACTIVE", 0.0)
+        busy = tot.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        mops = tot.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        lds = tot.get("SQ_LDS_IDX_ACTIVE", 0.0)
+        conf = tot.get("SQ_LDS_BANK_CONFLICT", 0.0)
+        cyc = gui / 8.0
+        out.append((gui, name, len(disp), busy / (cyc * 1024) if gui else 0.0,
+                    mops * 512 / max(steps, 1) / 1e12, conf / 256 / cyc if gui else 0.0,
+                    conf / lds if lds else 0.0))
+    for gui, name, nd, util, tf, lk, lc in sorted(out, reverse=True):
+        if name.startswith("k_mfma_") or name.startswith("k_trace_marker") or gui == 0:
+            continue
+        if not name.startswith("k_"):
+            continue
+        print(f"| {name} | {nd} | {100 * util:.1f} % | {tf:.3f} | {100 * lk:.1f} % | "
+              f"{100 * lc:.1f} % |")
+
+
 def summarize_pmc(fetch_dir, write_dir, copy_bytes):
     """Per-call HBM bytes of one step: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
     scaled by what the same counter reads for the plain copy of copy_bytes bytes."""
@@ -113,6 +163,47 @@ def summarize_pmc(fetch_dir, write_dir, copy_bytes):
     return res
 
 
+def _kernel_short(name):
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    base = name.split("(")[0]
+    short = base.split("::")[-1] if "<" not in base else base.split("<")[0].split("::")[-1] + \
+        "<" + base.split("<", 1)[1]
+    return short.replace("csa::", "")
+
+
+def summarize_trace(d, steps):
+    """Per-kernel calls, mean duration and per-step time of a kernel trace of bench.py; the
+    dispatches after the k_trace_marker kernel (the stand-alone timings) are listed apart."""
+    import csv
+    rows = []
+    with open(os.path.join(d, "run_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                         _kernel_short(r["Kernel_Name"])))
+    rows.sort()
+    cut = next((i for i, r in enumerate(rows) if r[2].startswith("k_trace_marker")), len(rows))
+    first_step = next((i for i, r in enumerate(rows) if r[2].startswith("k_cmp_seqlens")), 0)
+    parts = [("", rows[first_step:cut]), (" (stand-alone, after the steps)", rows[cut + 1:])]
+    step_total = sum(e - b for b, e, _ in parts[0][1])
+    print("| Kernel | Calls | Average (us) | Per step (ms) | Share |")
+    print("| --- | --- | --- | --- | --- |")
+    for tag, rs in parts:
+        agg = {}
+        for b, e, n in rs:
+            c, t = agg.get(n, (0, 0))
+            agg[n] = (c + 1, t + (e - b))
+        for n, (c, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+            if n.startswith("k_mfma_") or n.startswith("k_trace_marker"):
+                continue
+            per_step = f"{t / max(steps, 1) / 1e6:.2f}" if not tag and steps else "—"
+            share = f"{100.0 * t / step_total:.2f} %" if not tag and step_total else "—"
+            print(f"| {n}{tag} | {c} | {t / c / 1e3:.1f} | {per_step} | {share} |")
+    if steps:
+        print()
+        print(f"Sum of the step kernels: {step_total / max(steps, 1) / 1e6:.2f} ms per step "
+              f"({steps} steps traced).")
+
+
 def load_traffic():
     """Per-call HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel sources; else None."""
@@ -126,6 +217,54 @@ def load_traffic():
     if data.get("source_hash") != source_hash():
         return None
     return data.get("per_call_bytes")
+
+
+def measured_peaks():
+    """Peaks measured on this device: a loop of independent matrix-core operations on every
+    SIMD (bf16 16x16x32 and fp8 16x16x128, 8 accumulation chains per wave, 4 waves per SIMD)
+    and a device-to-device copy of 4 GiB (bytes read + written over its time)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_compressed_amd", "libcsa_probe.so"))
+    lib.csa_probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_void_p]
+    lib.csa_probe_mfma_loop.restype = ctypes.c_int
+    blocks, iters = 1024, 1000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for name, fp8, flop in (("bf16", 0, 16384), ("fp8", 1, 65536)):
+        def run():
+            rc = lib.csa_probe_mfma_loop(fp8, out.data_ptr(), blocks, iters, stream)
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed ({rc})")
+        run()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            run()
+            b.record()
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b) * 1e-3)
+        res[f"{name}_tflops"] = round(blocks * 4 * iters * 8 * flop / best / 1e12, 1)
+    n = 1 << 30                        # 4 GiB of fp32
+    src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b) * 1e-3)
+    res["hbm_gbps"] = round(2 * 4 * n / best / 1e9, 1)
+    del src, dst, out
+    torch.cuda.empty_cache()
+    return res
 
 
 class EventTimer:
@@ -176,14 +315,23 @@ def work_counts(w, lengths):
                 tokens=int(sum(lengths)))
 
 
-def roofline_table(w, c, T):
-    """(bound, algorithmic amount per launch, unit, peak) per ABI call."""
+def roofline_table(w, c, T, kl_cached=False):
+    """(bound, algorithmic amount per launch, unit, peak) per ABI call.
+
+    The indexer loss reading the forward's cached teacher logits computes no teacher
+    logits: it is priced against HBM on the bytes it cannot avoid (each (query, candidate)
+    pair's 64 cached logits and its score once, qI read and dqI / dw written once per query,
+    the indexer keys read and their gradient written once)."""
     H, D, HI, dI = w.heads, w.head_dim, w.idx_heads, w.idx_dim
     e = 4 if w.dtype == "f32" else 2
     ei = 1 if w.idx_dtype == "fp8" else (4 if w.idx_dtype == "f32" else 2)
     mm = "bf16" if w.dtype == "bf16" else "f32"
     teach = c["vis"] if w.teacher == "dense" else c["sel"]
     kl_flops = 2 * D * H * teach * (2 if w.teacher == "dense" else 1) + 4 * dI * HI * teach
+    kl_entry = (mm, kl_flops)
+    if kl_cached:
+        kl_entry = ("hbm", teach * (4 * H + 4) + c["tokens"] * (HI * dI * (ei + 4) + HI * 8 + H * 4)
+                    + c["tcmp"] * dI * (ei + 4))
     tab = {
         "compress_kv": ("hbm", c["tokens"] * D * e + c["tcmp"] * D * e),
         "compress_kI": ("hbm", c["tokens"] * dI * 2 + c["tcmp"] * dI * 2),
@@ -196,7 +344,7 @@ def roofline_table(w, c, T):
                        2 * dI * HI * (c["vis"] if w.teacher != "none" else c["vis_read"])),
         "topk_select": ("hbm", 4 * c["vis_read"] + 4 * T * max(w.topk_cap, 1)),
         "attn_fwd": (mm, 4 * D * H * c["cand"]),
-        "indexer_kl": (mm, kl_flops),
+        "indexer_kl": kl_entry,
         "attn_bwd": (mm, 10 * D * H * c["cand"]),
         "compress_bwd_kv": ("hbm", c["tcmp"] * D * 4 + 2 * c["tcmp"] * w.ratio * D * 4),
         "compress_bwd_kI": ("hbm", c["tcmp"] * dI * 4 + 2 * c["tcmp"] * w.ratio * dI * 4),
@@ -234,7 +382,7 @@ def standalone_topk(layer, dev, cu, reps):
         qI, qs, kI, ks = layer.qI8, layer.qI_scale, layer.kI8, layer.kI_scale
     else:
         qI, qs, kI, ks = dev["qI"], None, layer.kI_cmp, None
-    scores = torch.empty_like(layer.scores)
+    scores = torch.empty((layer.T, max(1, layer.n_cap)), dtype=torch.float32, device="cuda")
     idx = torch.empty_like(layer.idx)
     timer = EventTimer()
     for i in range(reps + 1):
@@ -407,6 +555,12 @@ def main():
                           "write_factor": res["write"]["factor"]}))
         print("```")
         return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.traced_steps)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.traced_steps)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (no collectives or "
@@ -416,13 +570,19 @@ def main():
     from long_context_compressed_amd.pipeline import CsaLayer, LayerConfig, to_device
     binding.lib()
     w = configs.workload(args.workload)
+    peaks = None
+    if not args.no_measured_peaks:
+        peaks = measured_peaks()
+        print(f"[bench] measured peaks {peaks}", file=sys.stderr, flush=True)
+    torch.cuda.reset_peak_memory_stats()
     t0 = time.time()
     host = inputs.make_inputs(w)
     dev = to_device(host)
     print(f"[bench] inputs ready in {time.time() - t0:.1f}s workload={w.name} "
           f"lengths={host['lengths']}", file=sys.stderr, flush=True)
+    ws_cap = None if args.bwd_workspace_gib is None else int(args.bwd_workspace_gib * 2**30)
     layer = CsaLayer(LayerConfig.of(w), len(host["lengths"]), w.total_tokens,
-                     host["max_seqlen"], backward=w.backward)
+                     host["max_seqlen"], backward=w.backward, bwd_ws_bytes=ws_cap)
     cu = dev["cu_seqlens"]
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -449,10 +609,22 @@ def main():
     total_ms = start.elapsed_time(end)
     ms = total_ms / max(args.steps, 1)
     per_call = timer.mean_ms()
+    mem = {"peak_allocated_gib": round(torch.cuda.max_memory_allocated() / 2**30, 2),
+           "attn_bwd_workspace_gib": round(layer.ws_bwd.numel() / 2**30, 2)
+           if getattr(layer, "ws_bwd", None) is not None else 0.0,
+           "indexer_kl_workspace_gib": round(layer.ws_kl.numel() / 2**30, 2)
+           if getattr(layer, "ws_kl", None) is not None else 0.0,
+           "teacher_logit_cache_gib": round(layer.t_logits.numel() * 4 / 2**30, 2)
+           if layer.t_logits is not None else 0.0}
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
+    # a marker dispatch: in a kernel trace, what follows are the stand-alone timings
+    import ctypes
+    _probe = ctypes.CDLL(os.path.join(ROOT, "long_context_compressed_amd", "libcsa_probe.so"))
+    _probe.csa_probe_marker.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    _probe.csa_probe_marker(None, torch.cuda.current_stream().cuda_stream)
     c = work_counts(w, host["lengths"])
-    tab = roofline_table(w, c, w.total_tokens)
+    tab = roofline_table(w, c, w.total_tokens, kl_cached=layer.t_logits is not None)
     if layer.fused_topk:
         # the step selects with the fused call; the stand-alone top-k over a materialized
         # score matrix is timed after the step loop, on the same inputs
@@ -483,6 +655,10 @@ def main():
         roof = {"bound": "mfma", "achieved": amount / tdom / 1e12, "peak": PEAK[bound] / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    if peaks:
+        mp = peaks["hbm_gbps"] if bound == "hbm" else peaks[f"{bound}_tflops"]
+        roof["measured_peak"] = mp
+        roof["frac_measured"] = roof["achieved"] / mp
     traffic = load_traffic()
     roof["traffic"] = traffic.get(dom) if traffic else None
     roof["kernel"] = dom
@@ -500,6 +676,7 @@ def main():
                    "ratio": w.ratio, "window": w.window, "topk": w.topk, "mode": w.mode,
                    "idx_heads": w.idx_heads, "idx_dim": w.idx_dim, "idx_dtype": w.idx_dtype,
                    "teacher": w.teacher, "rope_dim": w.rope_dim,
+                   "bwd_workspace_cap_gib": args.bwd_workspace_gib,
                    "pass": "fwd+bwd" if w.backward else "fwd"},
         "roofline": roof,
         "attention_tflops": attn_flops / max(attn_ms * 1e-3, 1e-12) / 1e12 if attn_ms else None,
@@ -507,6 +684,8 @@ def main():
                       breakdown.get("topk_select_standalone", {})).get("GB/s"),
         "breakdown": breakdown,
         "work": c,
+        "device_memory": mem,
+        "measured_peaks": peaks,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 6
+#define CSA_ABI_VERSION 7
 
 typedef int32_t csa_status_t;
 enum {
@@ -118,8 +118,15 @@ enum { CSA_OP_ATTN_FWD = 1, CSA_OP_ATTN_BWD = 2, CSA_OP_INDEXER_KL = 3,
 int csa_abi_version(void);
 const char* csa_status_string(csa_status_t status);
 
-/* Bytes of device workspace `op` needs for these params (0 is possible). */
+/* Bytes of device workspace `op` needs for these params (0 is possible).  For
+ * CSA_OP_ATTN_BWD this is the preferred size; the call also accepts any smaller
+ * workspace down to csa_workspace_size_min (it then processes the queries in more chunks:
+ * the same results up to the order of floating-point sums, more launches). */
 csa_status_t csa_workspace_size(const csa_params_t* p, int32_t op, size_t* bytes);
+
+/* The smallest workspace `op` accepts for these params (equal to csa_workspace_size for
+ * every op but CSA_OP_ATTN_BWD). */
+csa_status_t csa_workspace_size_min(const csa_params_t* p, int32_t op, size_t* bytes);
 
 /* cu_cmp[0] = 0, cu_cmp[b+1] = cu_cmp[b] + floor((cu_seqlens[b+1]-cu_seqlens[b]) / ratio).
  * (section 4, the n_b^cmp equation).  cu_seqlens, cu_cmp: int32 [batch+1]. */
@@ -208,7 +215,8 @@ csa_status_t csa_topk_select(const csa_params_t* p, const float* scores, int64_t
  * NULL); 1 = scores[t, j] written for the selected j only (what a selected-set indexer loss
  * reads); 2 = written for every visible j.  Other entries of scores are untouched.
  * Supported for idx_heads = 64, idx_dim = 128 (bf16 or fp8 indexer) and max_seqlen / ratio
- * <= 4096; else CSA_ERR_UNSUPPORTED (use the two calls).  idx: int32 [T, topk_cap]. */
+ * <= 32768 (the row limit of csa_topk_select); else CSA_ERR_UNSUPPORTED (use the two calls).
+ * idx: int32 [T, topk_cap]. */
 csa_status_t csa_index_topk(const csa_params_t* p, const void* qI, const float* qI_scale,
                             const float* w, const void* kI_cmp, const float* kI_scale,
                             const int32_t* cu_seqlens, const int32_t* cu_cmp, int32_t scores_mode,
@@ -273,7 +281,8 @@ int64_t csa_teacher_logits_stride(const csa_params_t* p);
  *   d row_x += scale dS q[t,h] + P dO[t,h]               (dkv_cmp / dkv, fp32, +=)
  *   dsink[h] += -e^{sink_h - lse[t,h]} Dt                (fp32, +=; NULL if no sink)
  * Same candidate sets and layouts as the forward; dkv receives window-row gradients only
- * (add the compressor's share with csa_compress_bwd).  ws: csa_workspace_size bytes. */
+ * (add the compressor's share with csa_compress_bwd).  ws: ws_bytes bytes, at least
+ * csa_workspace_size_min and best csa_workspace_size (CSA_ERR_WORKSPACE below the minimum). */
 csa_status_t csa_sparse_attn_bwd(const csa_params_t* p, const void* q, const void* kv_cmp,
                                  const void* kv, const int32_t* idx, const float* sink,
                                  const int32_t* cu_seqlens, const int32_t* cu_cmp,
@@ -299,6 +308,11 @@ csa_status_t csa_sparse_attn_bwd(const csa_params_t* p, const void* q, const voi
  * CSA_TEACHER_DENSE with CSA_DENSE; else CSA_ERR_ARG).  Teacher logits may then be read
  * from it instead of recomputed; results agree up to floating-point rounding.  With a
  * cache the workspace must be csa_workspace_size(p, CSA_OP_INDEXER_KL_CACHED) bytes.
+ * scores: fp32 [T, ld_scores] as csa_index_scores writes them (only the entries of C_t are
+ * read), or NULL for CSA_TEACHER_DENSE with a bf16 main path (H = 64, D = 512) and a 64 x 128
+ * bf16 / fp8 indexer: the student scores are then formed inside the call, a chunk of queries
+ * at a time, in the workspace (the same values csa_index_scores would write), so no
+ * [T, max_seqlen / ratio] score matrix need exist (CSA_ERR_NULL for other shapes).
  * kl: fp32 [T]; loss: fp32 [1]; dqI: fp32 [T, H_I, d_I]; dw: fp32 [T, H_I];
  * dkI_cmp: fp32 [Tc, d_I].  dqI, dw and dkI_cmp all NULL => loss only.
  * Supported for heads <= 64 teacher heads (CSA_ERR_UNSUPPORTED beyond). */

@@ -50,6 +50,7 @@ _SIGS = {
     "csa_abi_version": ([], ctypes.c_int),
     "csa_status_string": ([_I32], ctypes.c_char_p),
     "csa_workspace_size": ([_PP, _I32, ctypes.POINTER(_SZ)], _I32),
+    "csa_workspace_size_min": ([_PP, _I32, ctypes.POINTER(_SZ)], _I32),
     "csa_cmp_seqlens": ([_P, _I32, _I32, _P, _P], _I32),
     "csa_validate_metadata": ([_PP, _P, _P, _P], _I32),
     "csa_compress": ([_PP, _I32, _P, _I32, _P, _P, _P, _P], _I32),
@@ -137,6 +138,13 @@ def csa_abi_version() -> int:
 def csa_workspace_size(p: CsaParams, op: int) -> int:
     n = _SZ(0)
     _check("csa_workspace_size", lib().csa_workspace_size(ctypes.byref(p), op, ctypes.byref(n)))
+    return n.value
+
+
+def csa_workspace_size_min(p: CsaParams, op: int) -> int:
+    n = _SZ(0)
+    _check("csa_workspace_size_min",
+           lib().csa_workspace_size_min(ctypes.byref(p), op, ctypes.byref(n)))
     return n.value
 
 
@@ -240,7 +248,8 @@ def csa_indexer_kl(p, q, kv_cmp, scores, idx, qI, qI_scale, w, kI_cmp, kI_scale,
                    cu_cmp, grad_scale, kl, loss, dqI=None, dw=None, dkI_cmp=None, ws=None,
                    teacher_lse=None, stream=None, teacher_logits=None):
     _check("csa_indexer_kl", lib().csa_indexer_kl(
-        ctypes.byref(p), _ptr(q), _ptr(kv_cmp), _ptr(scores), scores.shape[-1], _ptr(idx),
+        ctypes.byref(p), _ptr(q), _ptr(kv_cmp), _ptr(scores),
+        scores.shape[-1] if scores is not None else 0, _ptr(idx),
         _ptr(teacher_lse), _ptr(teacher_logits), _ptr(qI), _ptr(qI_scale), _ptr(w), _ptr(kI_cmp), _ptr(kI_scale), _ptr(cu_seqlens),
         _ptr(cu_cmp), float(grad_scale), _ptr(kl), _ptr(loss), _ptr(dqI), _ptr(dw), _ptr(dkI_cmp),
         _ptr(ws), _nbytes(ws), _stream(stream)))

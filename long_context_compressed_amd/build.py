@@ -15,6 +15,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
+# peak-rate probes used only by the benchmark's measured roofline denominators
+PROBE_SRC = os.path.join(PKG, "probe", "peaks.hip")
+PROBE_LIB = os.path.join(PKG, "libcsa_probe.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
@@ -62,6 +65,9 @@ def build(verbose=False, jobs=None):
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    _run([HIPCC] + HIP_FLAGS + ["-shared", PROBE_SRC, "-o", tmp], verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

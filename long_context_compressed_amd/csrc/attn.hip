@@ -337,7 +337,9 @@ static AttnK make_k(const Shape& sh, const AttnIO& io) {
 
 size_t attn_fwd_workspace(const Shape& sh) { (void)sh; return 0; }
 size_t attn_bwd_workspace_mfma(const Shape& sh);
+size_t attn_bwd_workspace_min_mfma(const Shape& sh);
 size_t attn_bwd_workspace(const Shape& sh) { return attn_bwd_workspace_mfma(sh); }
+size_t attn_bwd_workspace_min(const Shape& sh) { return attn_bwd_workspace_min_mfma(sh); }
 
 hipError_t launch_attn_fwd(const Shape& sh, const AttnIO& io, hipStream_t s) {
   if (sh.T == 0) return hipSuccess;

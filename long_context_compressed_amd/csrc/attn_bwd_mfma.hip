@@ -582,15 +582,12 @@ struct BwdPlan {
   size_t off_pds, off_stage, off_nc, off_cnt, off_off, off_cur, off_list, total;
 };
 
-BwdPlan bwd_plan(const Shape& sh) {
+// Workspace layout for chunks of `chunk` query tokens.
+BwdPlan bwd_layout(const Shape& sh, int64_t chunk) {
   BwdPlan p;
   p.n_c_max = sh.mode == 0 ? sh.k_cap : (sh.mode == 1 ? sh.max_seqlen / sh.r : 0);
   p.n_slots = ((p.n_c_max + sh.W + kNB2 - 1) / kNB2) * kNB2;
-  const int64_t per_tok = p.n_slots * (128 + kD) * 2;
-  int64_t ch = kStageBudget / per_tok;
-  ch = (ch / (8 * kChunk)) * (8 * kChunk);
-  if (ch < 8 * kChunk) ch = 8 * kChunk;
-  p.chunk = ch < sh.T ? ch : sh.T;
+  p.chunk = chunk;
   p.Tc_cap = sh.r > 0 ? sh.T / sh.r + 1 : 1;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t o = 0;
@@ -605,18 +602,56 @@ BwdPlan bwd_plan(const Shape& sh) {
   return p;
 }
 
+// The largest chunk whose layout fits in `budget` bytes: whole multiples of the XCD token
+// mapping (8 * kChunk tokens) while that fits, else multiples of the CSR group, at least one
+// group (its total then exceeds a budget below the minimum; the caller checks).
+BwdPlan bwd_plan(const Shape& sh, size_t budget) {
+  const int64_t T = sh.T > 0 ? sh.T : 1;
+  const BwdPlan one = bwd_layout(sh, 1);
+  const int64_t per_tok = (int64_t)(bwd_layout(sh, 2).total - one.total) > 0
+                              ? (int64_t)(bwd_layout(sh, 2).total - one.total) : 1;
+  int64_t ch = budget > one.total ? (int64_t)((budget - one.total) / per_tok) + 1 : 1;
+  if (ch >= T) ch = T;
+  else if (ch >= 8 * kChunk) ch = (ch / (8 * kChunk)) * (8 * kChunk);
+  else ch = (ch / kCsrGroup) * kCsrGroup;
+  if (ch < kCsrGroup) ch = kCsrGroup < T ? kCsrGroup : T;
+  BwdPlan p = bwd_layout(sh, ch);
+  while (p.total > budget && ch > kCsrGroup) {   // alignment slack of the layout
+    ch -= kCsrGroup;
+    p = bwd_layout(sh, ch);
+  }
+  return p;
+}
+
+// Preferred workspace: chunks of up to kStageBudget bytes of staging (one chunk for a 64K
+// batch: one launch tail and one CSR per kernel per step).
+size_t bwd_preferred(const Shape& sh) {
+  const int64_t per_tok = bwd_layout(sh, 1).n_slots * (128 + kD) * 2;
+  int64_t ch = kStageBudget / per_tok;
+  ch = (ch / (8 * kChunk)) * (8 * kChunk);
+  if (ch < 8 * kChunk) ch = 8 * kChunk;
+  return bwd_layout(sh, ch < sh.T ? ch : (sh.T > 0 ? sh.T : 1)).total;
+}
+
 }  // namespace
 
 size_t attn_bwd_workspace_mfma(const Shape& sh) {
   if (sh.dtype != 1 || sh.H != kH || sh.D != kD) return 0;
-  return bwd_plan(sh).total;
+  return bwd_preferred(sh);
+}
+
+size_t attn_bwd_workspace_min_mfma(const Shape& sh) {
+  if (sh.dtype != 1 || sh.H != kH || sh.D != kD) return 0;
+  return bwd_layout(sh, sh.T < kCsrGroup ? (sh.T > 0 ? sh.T : 1) : kCsrGroup).total;
 }
 
 hipError_t launch_attn_bwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s, bool* handled) {
   *handled = false;
   if (sh.dtype != 1 || sh.H != kH || sh.D != kD) return hipSuccess;
   *handled = true;
-  const BwdPlan pl = bwd_plan(sh);
+  const size_t pref = bwd_preferred(sh);
+  const BwdPlan pl = bwd_plan(sh, io.ws_bytes < pref ? io.ws_bytes : pref);
+  if (pl.total > io.ws_bytes) return hipErrorInvalidValue;   // below the minimum: host-checked
   char* ws = (char*)io.ws;
   BwdArgs b;
   b.q = (const uint16_t*)io.q;

@@ -89,6 +89,17 @@ csa_status_t csa_workspace_size(const csa_params_t* p, int32_t op, size_t* bytes
   }
 }
 
+csa_status_t csa_workspace_size_min(const csa_params_t* p, int32_t op, size_t* bytes) {
+  if (!p || !bytes) return CSA_ERR_NULL;
+  if (op == CSA_OP_ATTN_BWD) {
+    csa_status_t st = check_common(p);
+    if (st) return st;
+    *bytes = csa::attn_bwd_workspace_min(make_shape(p, nullptr, nullptr));
+    return CSA_OK;
+  }
+  return csa_workspace_size(p, op, bytes);
+}
+
 csa_status_t csa_cmp_seqlens(const int32_t* cu_seqlens, int32_t batch, int32_t ratio,
                              int32_t* cu_cmp, hipStream_t stream) {
   if (!cu_seqlens || !cu_cmp) return CSA_ERR_NULL;
@@ -219,7 +230,7 @@ csa_status_t csa_index_topk(const csa_params_t* p, const void* qI, const float* 
   const bool fp8 = p->idx_dtype == CSA_FP8_E4M3;
   if (fp8 && (!qI_scale || !kI_scale)) return CSA_ERR_NULL;
   if (p->topk < 1 || p->topk_cap < p->topk || p->topk_cap % 64 != 0) return CSA_ERR_ARG;
-  if (p->idx_heads != 64 || p->idx_dim != 128 || p->idx_dtype == CSA_F32 || n_cap_of(p) > 4096)
+  if (p->idx_heads != 64 || p->idx_dim != 128 || p->idx_dtype == CSA_F32 || n_cap_of(p) > 64 * 512)
     return CSA_ERR_UNSUPPORTED;
   bool handled = false;
   const hipError_t e = csa::launch_index_topk(make_shape(p, cu_seqlens, cu_cmp), qI,
@@ -282,7 +293,7 @@ csa_status_t csa_sparse_attn_bwd(const csa_params_t* p, const void* q, const voi
   if (p->mode != CSA_WINDOW && (!kv_cmp || !dkv_cmp)) return CSA_ERR_NULL;
   if (p->mode == CSA_SPARSE && !idx) return CSA_ERR_NULL;
   const Shape sh = make_shape(p, cu_seqlens, cu_cmp);
-  const size_t need = csa::attn_bwd_workspace(sh);
+  const size_t need = csa::attn_bwd_workspace_min(sh);
   if (need > 0 && (!ws || ws_bytes < need)) return CSA_ERR_WORKSPACE;
   csa::AttnIO io = {};
   io.q = q; io.kv_cmp = kv_cmp; io.kv = kv; io.idx = p->mode == CSA_SPARSE ? idx : nullptr;
@@ -302,7 +313,7 @@ csa_status_t csa_indexer_kl(const csa_params_t* p, const void* q, const void* kv
                             void* ws, size_t ws_bytes, hipStream_t stream) {
   csa_status_t st = check_common(p);
   if (st) return st;
-  if (!q || !kv_cmp || !scores || !qI || !w || !kI_cmp || !cu_seqlens || !cu_cmp || !kl || !loss)
+  if (!q || !kv_cmp || !qI || !w || !kI_cmp || !cu_seqlens || !cu_cmp || !kl || !loss)
     return CSA_ERR_NULL;
   if (p->teacher != CSA_TEACHER_SELECTED && p->teacher != CSA_TEACHER_DENSE) return CSA_ERR_ARG;
   if (p->teacher == CSA_TEACHER_SELECTED) {
@@ -319,7 +330,10 @@ csa_status_t csa_indexer_kl(const csa_params_t* p, const void* q, const void* kv
   if (st) return st;
   const bool fp8 = p->idx_dtype == CSA_FP8_E4M3;
   if (fp8 && (!qI_scale || !kI_scale)) return CSA_ERR_NULL;
-  if (ld_scores < n_cap_of(p)) return CSA_ERR_ARG;
+  if (scores && ld_scores < n_cap_of(p)) return CSA_ERR_ARG;
+  if (!scores && (teacher_logits ||
+                  !csa::indexer_kl_recomputes_scores(make_shape(p, cu_seqlens, cu_cmp))))
+    return CSA_ERR_NULL;
   if (teacher_logits) {
     const bool same_set = (p->teacher == CSA_TEACHER_SELECTED && p->mode == CSA_SPARSE) ||
                           (p->teacher == CSA_TEACHER_DENSE && p->mode == CSA_DENSE);

@@ -85,7 +85,8 @@ struct AttnIO {
 };
 
 size_t attn_fwd_workspace(const Shape& sh);
-size_t attn_bwd_workspace(const Shape& sh);
+size_t attn_bwd_workspace(const Shape& sh);       // preferred size
+size_t attn_bwd_workspace_min(const Shape& sh);   // smallest size the call accepts
 hipError_t launch_attn_fwd(const Shape& sh, const AttnIO& io, hipStream_t s);
 hipError_t launch_attn_bwd(const Shape& sh, const AttnIO& io, hipStream_t s);
 
@@ -112,6 +113,14 @@ struct KlIO {
   size_t ws_bytes;
 };
 
+// Matrix-core scores of tokens t_lo .. t_hi - 1 (t_hi < 0: through T) into rows t - t_lo of
+// scores; handled = false for shapes without a matrix-core kernel.
+hipError_t launch_index_scores_mfma(const Shape& sh, const void* qI, const float* qI_scale,
+                                    const float* w, const void* kI, const float* kI_scale,
+                                    float* scores, int64_t ld, hipStream_t s, bool* handled,
+                                    int t_lo = 0, int t_hi = -1);
+// Whether csa_indexer_kl can form the student scores itself (scores == NULL).
+bool indexer_kl_recomputes_scores(const Shape& sh);
 size_t indexer_kl_workspace(const Shape& sh);
 size_t indexer_kl_cached_workspace(const Shape& sh);
 

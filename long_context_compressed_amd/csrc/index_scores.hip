@@ -80,9 +80,6 @@ __global__ __launch_bounds__(256) void k_index_scores_generic(
   }
 }
 
-hipError_t launch_index_scores_mfma(const Shape& sh, const void* qI, const float* qI_scale,
-                                    const float* w, const void* kI, const float* kI_scale,
-                                    float* scores, int64_t ld, hipStream_t s, bool* handled);
 
 hipError_t launch_index_scores(const Shape& sh, const void* qI, const float* qI_scale,
                                const float* w, const void* kI, const float* kI_scale,

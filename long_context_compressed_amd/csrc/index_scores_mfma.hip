@@ -65,15 +65,17 @@ struct ScArgs {
   float* scores;
   int64_t ld;
   int B, T, r, n_cap;
+  int t_lo;   // first token of the stand-alone score kernel (its row t - t_lo of scores)
 };
 
 // Scores of one token's visible keys j < nv, 64 at a time: emit(j0, s) is called once per
 // block with lane l holding the score of j = j0 + l (keys past nv hold unspecified values).
 // The product for keys j0 + 16 nt + c16 finishes with the sum over the four lane groups in
-// every group alike, so the lane of group g keeps its value from tile nt = g.
+// every group alike, so the lane of group g keeps its value from tile nt = g.  The wave
+// takes blocks b0, b0 + bstride, ... (several waves may share one token's blocks).
 template <bool FP8, class Emit>
 __device__ __forceinline__ void score_blocks(const ScArgs& a, int t, int row0, int nv,
-                                             Emit&& emit) {
+                                             Emit&& emit, int b0 = 0, int bstride = 1) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, c16 = lane & 15;
 
@@ -99,7 +101,7 @@ __device__ __forceinline__ void score_blocks(const ScArgs& a, int t, int row0, i
       for (int ks = 0; ks < 4; ++ks)
         qa[mt][ks] = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const uint4*>(q + (16 * mt + c16) * kDI + 32 * ks + 8 * g));
-    for (int j0 = 0; j0 < nv; j0 += 64) {
+    for (int j0 = kKB * b0; j0 < nv; j0 += kKB * bstride) {
       bf16x8 kb[4][4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
@@ -142,7 +144,7 @@ __device__ __forceinline__ void score_blocks(const ScArgs& a, int t, int row0, i
       qa[mt] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
-    for (int j0 = 0; j0 < nv; j0 += 64) {
+    for (int j0 = kKB * b0; j0 < nv; j0 += kKB * bstride) {
       i32x8 kb[4];
       float ks_[4];
 #pragma unroll
@@ -348,17 +350,18 @@ __device__ __forceinline__ void score_blocks_lds(const ScArgs& a, int t, int row
   }
 }
 
+// Tokens t_lo .. T - 1 (T: the end of the range), score row t - t_lo.
 template <bool FP8>
 __global__ __launch_bounds__(kSW * 64) void k_index_scores_mfma(ScArgs a) {
   __shared__ __attribute__((aligned(16))) KeyTiles<FP8> kt;
   const int lane = threadIdx.x & 63;
-  const int t0 = blockIdx.x * kSW, t = t0 + (threadIdx.x >> 6);
+  const int t0 = a.t_lo + blockIdx.x * kSW, t = t0 + (threadIdx.x >> 6);
   int row0 = 0, nv_max = 0;
   if (group_shares(a, t0, row0, nv_max)) {
     TokenInfo ti;
     token_info_wave(a.cu, a.B, t, ti);   // inside the group's sample
     const int nv = min((ti.p + 1) / a.r, a.n_cap);
-    float* out = a.scores + (int64_t)t * a.ld;
+    float* out = a.scores + (int64_t)(t - a.t_lo) * a.ld;
     score_blocks_lds<FP8>(a, t, row0, nv, nv > 0, nv_max, kt, [&](int j0, float s) {
       if (j0 + lane < nv) out[j0 + lane] = s;
     });
@@ -369,7 +372,7 @@ __global__ __launch_bounds__(kSW * 64) void k_index_scores_mfma(ScArgs a) {
   if (!token_info_wave(a.cu, a.B, t, ti, a.cu_cmp)) return;
   const int nv = min((ti.p + 1) / a.r, a.n_cap);
   if (nv <= 0) return;
-  float* out = a.scores + (int64_t)t * a.ld;
+  float* out = a.scores + (int64_t)(t - a.t_lo) * a.ld;
   score_blocks<FP8>(a, t, ti.c0, nv, [&](int j0, float s) {
     if (j0 + lane < nv) out[j0 + lane] = s;
   });
@@ -438,14 +441,59 @@ __global__ __launch_bounds__(kSW * 64) void k_index_topk(ScArgs a, int k, int k_
   for (int c = k + lane; c < k_cap; c += 64) out[c] = -1;
 }
 
+// Fused scores + top-k for rows beyond 4096 visible keys (up to kTopkThreads * KPL), one
+// workgroup of 8 waves per token: the waves score the token's 64-key blocks round robin
+// (wave w takes blocks w, w + 8, ...; keys read per wave from L2, the same products as the
+// other score kernels) into the workgroup's LDS row, and the workgroup radix top-k selects
+// from it, so the row never leaves the chip.  Scores reach HBM only as mode asks (1: the
+// selected ones, 2: every visible one).  Rows with nv <= k select every visible key and
+// compute their scores only when the loss reads them.
+template <bool FP8, int KPL>
+__global__ __launch_bounds__(kTopkThreads) void k_index_topk_wg(ScArgs a, int k, int k_cap,
+                                                                int mode,
+                                                                int32_t* __restrict__ idx) {
+  __shared__ __attribute__((aligned(16))) float lrow[kTopkThreads * KPL];
+  __shared__ TopkWgLds<KPL> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NW = kTopkThreads / 64;
+  const int t = blockIdx.x;
+  int32_t* out = idx + (int64_t)t * k_cap;
+  TokenInfo ti;
+  const bool real = token_info_wave(a.cu, a.B, t, ti, a.cu_cmp);
+  const int nv = real ? min((ti.p + 1) / a.r, a.n_cap) : 0;
+  const int row0 = real ? ti.c0 : 0;
+  float* srow = a.scores ? a.scores + (int64_t)t * a.ld : nullptr;
+  if (nv <= k) {  // every visible row is selected (also covers padding rows: nv = 0)
+    if (mode != 0 && nv > 0)
+      score_blocks<FP8>(a, t, row0, nv, [&](int j0, float s) {
+        if (j0 + lane < nv) srow[j0 + lane] = s;
+      }, wave, NW);
+    for (int c = tid; c < k_cap; c += kTopkThreads) out[c] = c < nv ? row0 + c : -1;
+    return;
+  }
+  score_blocks<FP8>(a, t, row0, nv, [&](int j0, float s) {
+    if (j0 + lane < nv) {
+      lrow[j0 + lane] = s;
+      if (mode == 2) srow[j0 + lane] = s;
+    }
+  }, wave, NW);
+  __syncthreads();
+  const int n_it = (nv + kTopkThreads - 1) / kTopkThreads;
+  topk_row_wg<KPL>(lrow, nv, n_it, k, row0, out, sm, mode == 1 ? srow : nullptr);
+  for (int c = k + tid; c < k_cap; c += kTopkThreads) out[c] = -1;
+}
+
 }  // namespace
 
 hipError_t launch_index_scores_mfma(const Shape& sh, const void* qI, const float* qI_scale,
                                     const float* w, const void* kI, const float* kI_scale,
-                                    float* scores, int64_t ld, hipStream_t s, bool* handled) {
+                                    float* scores, int64_t ld, hipStream_t s, bool* handled,
+                                    int t_lo, int t_hi) {
   *handled = false;
   if (sh.HI != kHI || sh.dI != kDI || sh.idx_dtype == 0) return hipSuccess;
   *handled = true;
+  if (t_hi < 0) t_hi = sh.T;
+  if (t_hi <= t_lo) return hipSuccess;
   ScArgs a;
   a.qI = qI;
   a.qI_scale = qI_scale;
@@ -457,10 +505,11 @@ hipError_t launch_index_scores_mfma(const Shape& sh, const void* qI, const float
   a.scores = scores;
   a.ld = ld;
   a.B = sh.B;
-  a.T = sh.T;
+  a.T = t_hi;
   a.r = sh.r;
   a.n_cap = sh.max_seqlen / sh.r;
-  const unsigned grid = (unsigned)((sh.T + kSW - 1) / kSW);
+  a.t_lo = t_lo;
+  const unsigned grid = (unsigned)((t_hi - t_lo + kSW - 1) / kSW);
   if (sh.idx_dtype == 2)
     hipLaunchKernelGGL(k_index_scores_mfma<true>, dim3(grid), dim3(kSW * 64), 0, s, a);
   else
@@ -474,7 +523,8 @@ hipError_t launch_index_topk(const Shape& sh, const void* qI, const float* qI_sc
                              hipStream_t s, bool* handled) {
   *handled = false;
   const int n_cap = sh.max_seqlen / sh.r;
-  if (sh.HI != kHI || sh.dI != kDI || sh.idx_dtype == 0 || n_cap > 64 * 64) return hipSuccess;
+  if (sh.HI != kHI || sh.dI != kDI || sh.idx_dtype == 0 || n_cap > kTopkThreads * 64)
+    return hipSuccess;
   *handled = true;
   if (sh.T == 0) return hipSuccess;
   ScArgs a;
@@ -491,8 +541,24 @@ hipError_t launch_index_topk(const Shape& sh, const void* qI, const float* qI_sc
   a.T = sh.T;
   a.r = sh.r;
   a.n_cap = n_cap;
-  const dim3 grid((sh.T + kSW - 1) / kSW), block(kSW * 64);
+  a.t_lo = 0;
   const bool fp8 = sh.idx_dtype == 2;
+  if (n_cap > 64 * 64) {   // rows beyond a wave's 4096 keys: a workgroup per token
+    const dim3 grid_w(sh.T), block_w(kTopkThreads);
+#define CSA_LAUNCH_FUSED_WG(F, K)                                                              \
+  hipLaunchKernelGGL((k_index_topk_wg<F, K>), grid_w, block_w, 0, s, a, sh.k, sh.k_cap,       \
+                     scores_mode, idx)
+    if (n_cap <= kTopkThreads * 16) {
+      if (fp8) CSA_LAUNCH_FUSED_WG(true, 16); else CSA_LAUNCH_FUSED_WG(false, 16);
+    } else if (n_cap <= kTopkThreads * 32) {
+      if (fp8) CSA_LAUNCH_FUSED_WG(true, 32); else CSA_LAUNCH_FUSED_WG(false, 32);
+    } else {
+      if (fp8) CSA_LAUNCH_FUSED_WG(true, 64); else CSA_LAUNCH_FUSED_WG(false, 64);
+    }
+#undef CSA_LAUNCH_FUSED_WG
+    return hipGetLastError();
+  }
+  const dim3 grid((sh.T + kSW - 1) / kSW), block(kSW * 64);
 #define CSA_LAUNCH_FUSED(F, K)                                                                 \
   hipLaunchKernelGGL((k_index_topk<F, K>), grid, block, 0, s, a, sh.k, sh.k_cap, scores_mode, idx)
   if (n_cap <= 64 * 16) {

@@ -73,6 +73,7 @@ __global__ __launch_bounds__(256) void k_kl_generic(KlK a) {
   int* rowid = (int*)(klp + kKB);       // [kKB]
   __shared__ int s_n;
   __shared__ float s_mS, s_lS;
+  __shared__ float Pc[64];       // teacher probabilities of the block's candidates
 
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
@@ -96,7 +97,11 @@ __global__ __launch_bounds__(256) void k_kl_generic(KlK a) {
   float dq_acc[kMaxQ];
 #pragma unroll
   for (int i = 0; i < kMaxQ; ++i) dq_acc[i] = 0.f;
-  float dw_acc = 0.f, kl_acc = 0.f;
+  // KL terms and the teacher's mass Z = sum_j P_j in fp64: the loss is A / Z - log Z with
+  // A = sum_j P_j (log P_j - log Q_j), the KL of P / Z, unbiased by the fp32 rounding of the
+  // normalizers when P and Q are near-uniform
+  float dw_acc = 0.f;
+  double kl_acc = 0.0, z_acc = 0.0;
 
   if (n_c > 0) {
     const T* qt = (const T*)a.q + (int64_t)t * H * D;
@@ -169,22 +174,31 @@ __global__ __launch_bounds__(256) void k_kl_generic(KlK a) {
         }
         // pass 1: teacher / student probabilities, KL and logit gradient
         if (tid < kKB) {
-          float g = 0.f, klv = 0.f;
+          float g = 0.f, klv = 0.f, pv = 0.f;
           if (rowid[tid] >= 0) {
             float P = 0.f;
             for (int h = 0; h < H; ++h) P += expf(lg[h * kKB + tid] - (mT[h] + logf(lT[h])));
             P /= (float)H;
             const float logQ = Ic[tid] - (s_mS + logf(s_lS));
             const float Q = expf(logQ);
-            if (P > 0.f) klv = P * (logf(P) - logQ);
+            // log P - log Q = log(P * l_S) - (I - m_S): no cancellation of two logs of
+            // the candidate count when both distributions are close to uniform
+            if (P > 0.f) {
+              klv = P * (logf(P * s_lS) - (Ic[tid] - s_mS));
+              pv = P;
+            }
             g = a.gs * (Q - P);
           }
           gc[tid] = g;
           klp[tid] = klv;
+          Pc[tid] = pv;
         }
         __syncthreads();
         if (tid == 0) {
-          for (int cc = 0; cc < kKB; ++cc) kl_acc += klp[cc];
+          for (int cc = 0; cc < kKB; ++cc) {
+            kl_acc += (double)klp[cc];
+            z_acc += (double)Pc[cc];
+          }
         }
         if (a.grads) {
           for (int e = tid; e < kKB * dI; e += 256) {
@@ -234,7 +248,7 @@ __global__ __launch_bounds__(256) void k_kl_generic(KlK a) {
       }
     }
   }
-  if (tid == 0) a.kl[t] = kl_acc;
+  if (tid == 0) a.kl[t] = z_acc > 0.0 ? (float)(kl_acc / z_acc - log1p(z_acc - 1.0)) : 0.f;
   if (a.grads) {
     if (tid < HI) a.dw[(int64_t)t * HI + tid] = dw_acc;
 #pragma unroll

@@ -77,6 +77,19 @@ __device__ __forceinline__ void dma_rows16(const void* src, const void* lds) {
                :: "s"(a), "v"(src) : "memory", "m0");
 }
 
+// Sum over the workgroup's 4 waves in fp64 (the normalizers of the loss: an fp32 sum of a
+// thousand terms of similar size carries a relative error of ~1e-7, as large as the KL of two
+// near-uniform distributions is small).
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const double r = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return r;
+}
+
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -108,6 +121,8 @@ void k_kl_cached(KlcArgs a) {
   __shared__ float Pp[4][kNB];
   __shared__ float gw_s[4][kNB];
   __shared__ float lse2_s[kHT];
+  __shared__ double red_d[4];
+  __shared__ float z_s;           // teacher mass over the blocks so far (wave 0)
   __shared__ float red[4];
   __shared__ int s_tmp;
 
@@ -203,17 +218,17 @@ void k_kl_cached(KlcArgs a) {
     }
   }
   const float mS = block_reduce(mx, red, true);   // its barriers publish sc_s
-  float sm = 0.f;
+  double sm = 0.0;
   for (int c = tid; c < n_c; c += 256) {
     if (sc_lds) {
       const float v = sc_s[c];
-      if (v > -INFINITY) sm += expf(v - mS);
+      if (v > -INFINITY) sm += (double)expf(v - mS);
     } else {
       const int j = slot_local(c);
-      if (j >= 0) sm += expf(srow[j] - mS);
+      if (j >= 0) sm += (double)expf(srow[j] - mS);
     }
   }
-  const float sS = block_reduce(sm, red, false);
+  const float sS = (float)block_sum_f64(sm, red_d);
   // all slots out of the visible range (an invalid idx row): Q_t = 0 instead of NaN
   const float lseS = sS > 0.f ? mS + logf(sS) : INFINITY;
 
@@ -275,7 +290,13 @@ void k_kl_cached(KlcArgs a) {
 #pragma unroll
     for (int nd = 0; nd < 8; ++nd) dq[nt][nd] = f32x4{0.f, 0.f, 0.f, 0.f};
   float dw_acc[2] = {0.f, 0.f};
+  // KL terms and the teacher's total mass Z = sum_j P_j (per block over the lanes, then over
+  // the blocks in LDS): the loss is A / Z - log Z with A = sum_j P_j (log P_j - log Q_j),
+  // i.e. the KL of P / Z, so the fp32 rounding of the per-head normalizers (which leaves
+  // sum_j P_j = 1 + O(1e-7)) does not bias it (for near-uniform P and Q the KL itself is of
+  // that order times the candidate count)
   float kl_acc = 0.f;
+  if (tid == 0) z_s = 0.f;   // first read after the block loop's barriers
 
   // per-lane LDS offsets (elements) of the swizzled 256-byte key rows
   //  z^T A operand: row 32ch + 16mt + c16, logical chunk 4ks + g
@@ -353,7 +374,13 @@ void k_kl_cached(KlcArgs a) {
       const float P = ((Pp[0][lane] + Pp[1][lane]) + (Pp[2][lane] + Pp[3][lane])) * (1.f / kHT);
       const float logQ = sc_cur - lseS;
       const float Q = in ? expf(logQ) : 0.f;
-      if (in && P > 0.f && wave == 0) kl_acc += P * (logf(P) - logQ);
+      // log P - log Q = log(P * s_S) - (s - m_S): no cancellation of two logs of the
+      // candidate count when both distributions are close to uniform
+      if (wave == 0) {
+        if (in && P > 0.f) kl_acc += P * (logf(P * sS) - (sc_cur - mS));
+        const float zb = wave_sum(in && P > 0.f ? P : 0.f);
+        if (lane == 0) z_s += zb;
+      }
       gl = in ? a.gs * (Q - P) : 0.f;
       gw_s[wave][lane] = gl;
     }
@@ -459,10 +486,8 @@ void k_kl_cached(KlcArgs a) {
 
   // ---- outputs: kl, dw, dqI (the two slot halves ch = 0, 1 summed through LDS)
   if (wave == 0) {
-    float v = kl_acc;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    if (lane == 0) a.kl[t] = v;
+    const double v = wave_sum_f64((double)kl_acc), z = (double)z_s;
+    if (lane == 0) a.kl[t] = z > 0.0 ? (float)(v / z - log1p(z - 1.0)) : 0.f;
   }
   if (!a.grads) return;
   __syncthreads();

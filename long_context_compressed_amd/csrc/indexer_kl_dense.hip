@@ -46,14 +46,16 @@ constexpr int kRange = 256;        // queries per key-gradient workgroup
 constexpr int kIS = kDI + 8;       // bf16 row stride of the indexer tiles
 constexpr int kI8S = kDI + 16;     // byte row stride of the fp8 code tiles
 constexpr float kLazy = 8.f;
+constexpr int kMaxBlocks = 512;    // key blocks of a row: n_cap <= 32768
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 struct KldArgs {
   const uint16_t* q;
   const uint16_t* kv_cmp;
-  const float* scores;
+  const float* scores;      // student scores, row t - s_t0
   int64_t ld;
+  int s_t0;
   const void* qI;
   const float* qI_scale;
   const uint16_t* qI16;   // bf16 indexer query rows from q16_t0 (the dequantized copy for fp8)
@@ -117,6 +119,7 @@ void k_kld_teacher(KldArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[2][kKB][kD];
   __shared__ float Is[4][kKB];
   __shared__ float Ps[4][2][kKB];
+  __shared__ float2 stu_s[4][kMaxBlocks];   // per query and key block: (max, sum of exp(I - max))
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -138,7 +141,7 @@ void k_kld_teacher(KldArgs a) {
     return;
   }
   const int nblk = (nv_max + kKB - 1) / kKB;
-  const float* srow = a.scores + (int64_t)t * a.ld;
+  const float* srow = a.scores + (int64_t)(t - a.s_t0) * a.ld;
   float* grow = a.g + (int64_t)(t - a.t_lo) * a.n_cap;
 
   // Q rows as the A operand: qb[ht][ks] = Q[32 hh + 16 ht + c16][32 ks + 8 g .. +7]
@@ -172,7 +175,11 @@ void k_kld_teacher(KldArgs a) {
   float m_run[8], l_run[8], lse2[8];
 #pragma unroll
   for (int hx = 0; hx < 8; ++hx) { m_run[hx] = -INFINITY; l_run[hx] = 0.f; lse2[hx] = 0.f; }
-  float ms = -INFINITY, lsum = 0.f, lseS = 0.f, kl_acc = 0.f;
+  // the student normalizer, the KL terms and the teacher's total mass Z = sum_j P_j are
+  // accumulated in fp64: the loss is A / Z - log Z with A = sum_j P_j (log P_j - log Q_j),
+  // the KL of P / Z, so neither the fp32 rounding of the per-head normalizers (sum_j P_j =
+  // 1 + O(1e-7)) nor that of a long fp32 sum biases a KL of near-uniform distributions
+  float ms = -INFINITY, lseS = 0.f, lsum_f = 0.f, kl_acc = 0.f, z_acc = 0.f;
 
   for (int j = 0; j < 8; ++j) gather(0, 0, j);
   wait_vmem();
@@ -243,12 +250,11 @@ void k_kld_teacher(KldArgs a) {
         }
       // ---- student: online (max, sum) of the scores (natural log), lane = key
       {
+        // each block's (max, sum) is recorded and the blocks are combined in fp64 once pass
+        // 1 ends (an fp32 running sum over hundreds of blocks would drift)
         const float bm = wave_max(iv);
-        if (bm > ms) {
-          lsum = ms == -INFINITY ? 0.f : lsum * expf(ms - bm);
-          ms = bm;
-        }
-        if (ms != -INFINITY) lsum += wave_sum(iv == -INFINITY ? 0.f : expf(iv - ms));
+        const float bs = bm == -INFINITY ? 0.f : wave_sum(iv == -INFINITY ? 0.f : expf(iv - bm));
+        if (hh == 0 && lane == 0) stu_s[tw][jb] = make_float2(bm, bs);
       }
       if (it == nblk - 1) {
         // merge the 16 lanes (keys) of each head; the student normalizer to every lane
@@ -266,7 +272,21 @@ void k_kld_teacher(KldArgs a) {
           }
           lse2[hx] = l_run[hx] > 0.f ? m_run[hx] + __log2f(l_run[hx]) : INFINITY;
         }
-        lseS = lsum > 0.f ? ms + logf(lsum) : INFINITY;
+        __syncthreads();   // every query's block records
+        {
+          float m = -INFINITY;
+          for (int b = lane; b < nblk; b += 64) m = fmaxf(m, stu_s[tw][b].x);
+          ms = wave_max(m);
+          double l = 0.0;
+          if (ms != -INFINITY)
+            for (int b = lane; b < nblk; b += 64) {
+              const float2 v = stu_s[tw][b];
+              if (v.x != -INFINITY) l += (double)(v.y * expf(v.x - ms));
+            }
+          l = wave_sum_f64(l);
+          lsum_f = (float)l;
+          lseS = l > 0.0 ? ms + logf(lsum_f) : INFINITY;
+        }
       }
     } else {
       // ---- P = mean over heads of exp2(s - lse2): the lane's 8 heads in registers, the 4
@@ -291,7 +311,12 @@ void k_kld_teacher(KldArgs a) {
           const float P = (Ps[tw][0][lane] + Ps[tw][1][lane]) * (1.f / kH);
           const float logQ = iv - lseS;
           const float Q = expf(logQ);
-          if (P > 0.f) kl_acc += P * (logf(P) - logQ);
+          // log P - log Q = log(P * l_S) - (I - m_S): no cancellation of two logs of the
+          // candidate count when both distributions are close to uniform
+          if (P > 0.f) {
+            kl_acc += P * (logf(P * lsum_f) - (iv - ms));
+            z_acc += P;
+          }
           gv = a.gs * (Q - P);
         }
         const int j = kKB * jb + lane;
@@ -302,8 +327,8 @@ void k_kld_teacher(KldArgs a) {
     __syncthreads();
   }
   if (active && hh == 0) {
-    const float v = wave_sum(kl_acc);
-    if (lane == 0) a.kl[t] = v;
+    const double v = wave_sum_f64((double)kl_acc), z = wave_sum_f64((double)z_acc);
+    if (lane == 0) a.kl[t] = z > 0.0 ? (float)(v / z - log1p(z - 1.0)) : 0.f;
   }
 }
 
@@ -707,10 +732,13 @@ __global__ __launch_bounds__(256) void k_kld_dequant(const uint8_t* __restrict__
 
 static bool kld_handles(const Shape& sh) {
   return sh.teacher == 2 && sh.mode == 0 && sh.dtype == 1 && sh.H == kH && sh.D == kD &&
-         sh.HI == kHI && sh.dI == kDI && sh.idx_dtype != 0;
+         sh.HI == kHI && sh.dI == kDI && sh.idx_dtype != 0 &&
+         sh.max_seqlen / sh.r <= kKB * kMaxBlocks;
 }
 
 static int kld_rows(const Shape& sh) { return sh.T < kChunkRows ? sh.T : kChunkRows; }
+
+bool indexer_kl_recomputes_scores(const Shape& sh) { return kld_handles(sh); }
 
 size_t indexer_kl_dense_workspace(const Shape& sh) {
   if (!kld_handles(sh) || sh.T == 0) return 0;
@@ -734,6 +762,7 @@ hipError_t launch_indexer_kl_dense(const Shape& sh, const KlIO& io, hipStream_t 
   a.kv_cmp = (const uint16_t*)io.kv_cmp;
   a.scores = io.scores;
   a.ld = io.ld;
+  a.s_t0 = 0;
   a.qI = io.qI;
   a.qI_scale = io.qI_scale;
   a.w = io.w;
@@ -769,6 +798,18 @@ hipError_t launch_indexer_kl_dense(const Shape& sh, const KlIO& io, hipStream_t 
   for (int t_lo = 0; t_lo < sh.T; t_lo += rows) {
     a.t_lo = t_lo;
     a.t_hi = t_lo + rows < sh.T ? t_lo + rows : sh.T;
+    if (!io.scores) {
+      // no score matrix given: the chunk's student scores are formed into its rows of the
+      // workspace (row t - t_lo), which the teacher pass then overwrites with g in place
+      bool sc_handled = false;
+      hipError_t e = launch_index_scores_mfma(sh, io.qI, io.qI_scale, io.w, io.kI, io.kI_scale,
+                                              a.g, n_cap, s, &sc_handled, a.t_lo, a.t_hi);
+      if (e != hipSuccess) return e;
+      if (!sc_handled) return hipErrorInvalidValue;
+      a.scores = a.g;
+      a.ld = n_cap;
+      a.s_t0 = a.t_lo;
+    }
     hipLaunchKernelGGL(k_kld_teacher, dim3(kChunkRows / 4 + sh.B), dim3(512), 0, s, a);
     if (!grads) continue;
     a.dqI = io.dqI;

@@ -117,6 +117,7 @@ void k_indexer_kl_mfma(KlArgs a) {
   __shared__ float I_s[2][kNB];
   __shared__ int rowid_s[2][kNB];
   __shared__ float red[4];
+  __shared__ double red_d[4];
   __shared__ int s_n;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -165,12 +166,19 @@ void k_indexer_kl_mfma(KlArgs a) {
     if (j >= 0) mx = fmaxf(mx, srow[j]);
   }
   const float mS = block_max(mx, red);
-  float sm = 0.f;
+  // the student normalizer, the KL terms and the teacher's mass Z = sum_j P_j in fp64: the
+  // loss is A / Z - log Z with A = sum_j P_j (log P_j - log Q_j) (the KL of P / Z), unbiased by
+  // the fp32 rounding of the normalizers when P and Q are both near-uniform
+  double sm = 0.0;
   for (int c = tid; c < n_c; c += 256) {
     const int j = slot_local(c);
-    if (j >= 0) sm += expf(srow[j] - mS);
+    if (j >= 0) sm += (double)expf(srow[j] - mS);
   }
-  const float sS = block_sum(sm, red);
+  double smw = wave_sum_f64(sm);
+  if ((tid & 63) == 0) red_d[tid >> 6] = smw;
+  __syncthreads();
+  const float sS = (float)((red_d[0] + red_d[1]) + (red_d[2] + red_d[3]));
+  __syncthreads();
   // all slots out of the visible range (an invalid idx row): Q_t = 0 instead of NaN
   const float lseS = sS > 0.f ? mS + logf(sS) : INFINITY;
 
@@ -336,7 +344,7 @@ void k_indexer_kl_mfma(KlArgs a) {
     sq_h = a.qI_scale[(int64_t)t * kHI + h];
   }
   f32x4 dqa[8];
-  float dw_acc = 0.f, kl_acc = 0.f;
+  float dw_acc = 0.f, kl_acc = 0.f, z_acc = 0.f;
   const float wh = a.w[(int64_t)t * kHI + h];
   __syncthreads();   // QIt staged; pass-1 tiles no longer read
   if (a.grads) {
@@ -381,7 +389,12 @@ void k_indexer_kl_mfma(KlArgs a) {
         const float P = ((Pp[0][tid] + Pp[1][tid]) + (Pp[2][tid] + Pp[3][tid])) * (1.f / kH);
         const float logQ = I_s[buf][tid] - lseS;
         const float Q = expf(logQ);
-        if (P > 0.f) kl_acc += P * (logf(P) - logQ);
+        // log P - log Q = log(P * s_S) - (I - m_S): no cancellation of two logs of the
+        // candidate count when both distributions are close to uniform
+        if (P > 0.f) {
+          kl_acc += P * (logf(P * sS) - (I_s[buf][tid] - mS));
+          z_acc += P;
+        }
         gv = a.gs * (Q - P);
       }
       g_s[tid] = gv;
@@ -467,9 +480,9 @@ void k_indexer_kl_mfma(KlArgs a) {
   }
   // kl: lanes 0..31 of wave 0 hold partial sums
   if (wave == 0) {
-    float v = lane < kNB ? kl_acc : 0.f;
-    v = wave_sum(v);
-    if (lane == 0) a.kl[t] = v;
+    const double v = wave_sum_f64(lane < kNB ? (double)kl_acc : 0.0);
+    const double z = wave_sum_f64(lane < kNB ? (double)z_acc : 0.0);
+    if (lane == 0) a.kl[t] = z > 0.0 ? (float)(v / z - log1p(z - 1.0)) : 0.f;
   }
 }
 

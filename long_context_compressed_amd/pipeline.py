@@ -64,7 +64,10 @@ class CsaLayer:
     """Buffers and calls of one layer step for a fixed capacity (T rows, max_seqlen)."""
 
     def __init__(self, cfg: LayerConfig, batch: int, total_tokens: int, max_seqlen: int,
-                 device="cuda", backward: bool = True, grad_scale: float = 1.0):
+                 device="cuda", backward: bool = True, grad_scale: float = 1.0,
+                 bwd_ws_bytes: Optional[int] = None):
+        """bwd_ws_bytes: cap on the attention backward's workspace (it then processes the
+        queries in more chunks; never below the library's minimum)."""
         self.cfg = cfg
         self.timer = None          # optional object with mark(name) / done(name) around calls
         self.fused_topk = None     # fused scores + top-k: None until the first forward tries it
@@ -104,8 +107,13 @@ class CsaLayer:
                 self.qI_scale = z(T, HI)
                 self.kI8 = z(self.tc_cap, dI, dtype=torch.uint8)
                 self.kI_scale = z(self.tc_cap)
-            self.scores = z(T, max(1, self.n_cap))
+            self._scores = None      # [T, n_cap] fp32, allocated only where a call needs it
+            self._device = device
             self.idx = z(T, cfg.topk_cap, dtype=torch.int32)
+            # the dense-teacher loss can form the student scores itself: with the fused
+            # selection the step then needs no [T, n_cap] score matrix at all
+            self.kl_recompute = (cfg.teacher == "dense" and
+                                 B.csa_workspace_size(self.p, B.CSA_OP_INDEXER_KL) > 0)
             if cfg.teacher != "none":
                 self.kl = z(T)
                 self.loss = z(1)
@@ -129,10 +137,19 @@ class CsaLayer:
             self.dkv_cmp = z(self.tc_cap, D)
             self.dkv = z(T, D)
             self.dsink = z(H)
-            self.ws_bwd = self._ws(B.CSA_OP_ATTN_BWD, device)
+            self.ws_bwd = self._ws(B.CSA_OP_ATTN_BWD, device, cap=bwd_ws_bytes)
 
-    def _ws(self, op, device):
+    @property
+    def scores(self):
+        if self._scores is None:
+            self._scores = torch.empty(self.T, max(1, self.n_cap), dtype=torch.float32,
+                                       device=self._device)
+        return self._scores
+
+    def _ws(self, op, device, cap=None):
         n = B.csa_workspace_size(self.p, op)
+        if n and cap is not None:
+            n = max(min(n, int(cap)), B.csa_workspace_size_min(self.p, op))
         return torch.empty(max(n, 1), dtype=torch.uint8, device=device) if n else None
 
     # ------------------------------------------------------------------ steps
@@ -179,11 +196,14 @@ class CsaLayer:
                 qI, qs, kI, ks = inp["qI"], None, self.kI_cmp, None
             if self.fused_topk is not False:
                 # one pass: the selection never materializes the full score matrix; the
-                # loss reads scores only where its teacher does
-                mode = {"none": 0, "selected": 1, "dense": 2}[cfg.teacher]
+                # loss reads scores only where its teacher does (a dense teacher that forms
+                # them itself needs none)
+                mode = {"none": 0, "selected": 1,
+                        "dense": 0 if self.kl_recompute else 2}[cfg.teacher]
                 try:
                     self._call("index_topk", B.csa_index_topk, p, qI, qs, inp["w"], kI, ks,
-                               cu_seqlens, self.cu_cmp, self.idx, self.scores, mode)
+                               cu_seqlens, self.cu_cmp, self.idx,
+                               self.scores if mode else None, mode)
                     self.fused_topk = True
                 except B.CsaError as e:
                     if self.fused_topk or e.status != B.CSA_ERR_UNSUPPORTED:
@@ -202,7 +222,9 @@ class CsaLayer:
             grads = self.backward
             if grads:
                 self.dkI_cmp.zero_()
-            self._call("indexer_kl", B.csa_indexer_kl, p, inp["q"], self.kv_cmp, self.scores,
+            scores = self._scores if (cfg.teacher != "dense" or not self.kl_recompute or
+                                      not self.fused_topk) else None
+            self._call("indexer_kl", B.csa_indexer_kl, p, inp["q"], self.kv_cmp, scores,
                        self.idx, qI, qs, inp["w"], kI, ks, cu_seqlens, self.cu_cmp,
                        self.grad_scale, self.kl, self.loss, self.dqI if grads else None,
                        self.dw if grads else None, self.dkI_cmp if grads else None, self.ws_kl,

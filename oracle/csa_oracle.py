@@ -45,11 +45,43 @@ Readings taken where the page leaves a step open (each restated where used):
   R22 RoPE = rotation of the interleaved channel pairs of the last rope_dim channels by
      position * theta^(-2i / rope_dim); positions restart per sample, token rows use the
      local token position, compressed rows their index within the sample; the inverse
-     (on the attention output, at the query's position) rotates by the opposite angle.
+     (on the attention output, at the query's position) rotates by the opposite angle;
+  R23 a layer chain "with storage rounding" holds every intermediate a step hands to the
+     next in the precision it is stored in: compressed main and indexer rows and rotated
+     operands in the layer's main / indexer dtype (the section 5.5 storage estimate counts
+     the compressed state in BF16), index scores and the log-sum-exp in FP32 (section 9:
+     score, softmax and KL math in FP32), the saved output in the main dtype; each step
+     itself is still evaluated in float64 on those rounded values.
 """
 import numpy as np
 
 F8_MAX = 448.0
+
+
+# ---------------------------------------------------------------------------
+# storage precision of intermediates (reading R23)
+# ---------------------------------------------------------------------------
+def round_bf16(x):
+    """x rounded to bfloat16 (float32 first, then round-to-nearest-even on the upper 16
+    bits of the float32 encoding), returned as float64.  Inputs are finite."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def store(x, dtype):
+    """x as a buffer of `dtype` holds it: "f32" -> float32, "bf16" -> bfloat16; the fp8
+    indexer path keeps its unquantized rows in bfloat16.  Infinities pass through."""
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if dtype in ("bf16", "fp8"):
+        fin = np.isfinite(x)
+        out = x.copy()
+        out[fin] = round_bf16(x[fin])
+        return out
+    raise ValueError(dtype)
 
 
 # ---------------------------------------------------------------------------
@@ -556,7 +588,7 @@ def indexer_kl(q, kv_cmp, scores, idx, qI, w, kI_cmp, cu_seqlens, ratio, scale, 
 # ---------------------------------------------------------------------------
 # one whole layer step (all steps chained, as the HIP path chains them)
 # ---------------------------------------------------------------------------
-def layer_step(inp, cfg, rows=None, backward=None, grad_scale=1.0):
+def layer_step(inp, cfg, rows=None, backward=None, grad_scale=1.0, stored=False):
     """Chain the steps on host arrays.  inp holds float64 arrays q, kv, [qI, kI_tok, w],
     [dO], [sink], cu_seqlens; cfg supplies ratio, window, topk, topk_cap, scale, mode,
     teacher, idx_dtype and optionally rope_dim / rope_theta.  Per-query outputs are returned
@@ -568,7 +600,12 @@ def layer_step(inp, cfg, rows=None, backward=None, grad_scale=1.0):
     positions, all restarting per sample (section 4); O stays unrotated (it is what the
     attention backward consumes) and O_rot, the inverse rotation of O at the query's
     position, is the layer output, so dO is taken as the gradient of O_rot.  The gradients
-    returned are those of the unrotated inputs (a rotation's adjoint is its inverse)."""
+    returned are those of the unrotated inputs (a rotation's adjoint is its inverse).
+
+    stored=True (reading R23) rounds every intermediate handed from one step to the next
+    to the precision it is stored in: compressed and rotated rows to the main / indexer
+    dtype, scores and LSE to float32, the output saved for the backward to the main dtype.
+    stored=False is the all-float64 chain."""
     cu = inp["cu_seqlens"]
     q = inp["q"]
     T = q.shape[0]
@@ -578,26 +615,34 @@ def layer_step(inp, cfg, rows=None, backward=None, grad_scale=1.0):
     rd = int(getattr(cfg, "rope_dim", 0) or 0)
     theta = float(getattr(cfg, "rope_theta", 0.0) or 0.0)
     res = {}
+    ident = lambda x: x                                                      # noqa: E731
+    st_main = (lambda x: store(x, cfg.dtype)) if stored else ident          # noqa: E731
+    st_idx = (lambda x: store(x, cfg.idx_dtype)) if stored else ident       # noqa: E731
+    st_f32 = (lambda x: store(x, "f32")) if stored else ident               # noqa: E731
     kv = inp["kv"]
-    kv_cmp = compress(kv, cu, r)
+    kv_cmp = st_main(compress(kv, cu, r))
     res["kv_cmp"] = kv_cmp
     if rd:
         tpos = rope_positions(cu, T)
         cpos = rope_positions(cu, kv_cmp.shape[0], ratio=r)
         rot = lambda x, pos: rope(x, pos, rd, theta)                        # noqa: E731
         unrot = lambda x, pos: rope(x, pos, rd, theta, inverse=True)        # noqa: E731
-        q = rot(q, tpos)
-        kv = rot(kv, tpos)
-        kv_cmp = rot(kv_cmp, cpos)
+        q_in = q
+        q = np.zeros(q_in.shape)             # untouched pages stay unallocated
+        q[rows] = st_main(rot(q_in[rows], tpos[rows]))
+        kv = st_main(rot(kv, tpos))
+        kv_cmp = st_main(rot(kv_cmp, cpos))
     idx = None
     if cfg.mode == "window":          # ratio-0 layer: no compressed candidates at all
         idx = np.full((rows.size, 1), -1, dtype=np.int64)
     if cfg.has_indexer and cfg.mode == "sparse":
-        kI_cmp = compress(inp["kI_tok"], cu, r)
+        kI_cmp = st_idx(compress(inp["kI_tok"], cu, r))
         qI = inp["qI"]
         if rd:
-            qI = rot(qI, tpos)
-            kI_cmp = rot(kI_cmp, cpos)
+            qI_in = qI
+            qI = np.zeros(qI_in.shape)
+            qI[rows] = st_idx(rot(qI_in[rows], tpos[rows]))
+            kI_cmp = st_idx(rot(kI_cmp, cpos))
         if cfg.idx_dtype == "fp8":
             qI_full = qI
             qI = np.zeros(qI.shape)          # untouched pages stay unallocated
@@ -607,7 +652,7 @@ def layer_step(inp, cfg, rows=None, backward=None, grad_scale=1.0):
             kI_cmp = dequantize_fp8(kc, ks)
         res["kI_cmp"] = kI_cmp
         n_cap = int(inp["max_seqlen"]) // r
-        scores = index_scores(qI, inp["w"], kI_cmp, cu, r, n_cap, rows=rows)
+        scores = st_f32(index_scores(qI, inp["w"], kI_cmp, cu, r, n_cap, rows=rows))
         res["scores"] = scores
         idx = topk_select(scores, cu, r, cfg.topk, cfg.topk_cap, T, rows=rows)
         res["idx"] = idx
@@ -627,10 +672,10 @@ def layer_step(inp, cfg, rows=None, backward=None, grad_scale=1.0):
     if backward:
         dO = inp["dO"][rows]
         if rd:
-            dO = rot(dO, tpos[rows])          # gradient of O from that of O_rot
+            dO = st_main(rot(dO, tpos[rows]))   # gradient of O from that of O_rot
         dq, dkv_cmp, dkv_win, dsink = sparse_attn_bwd(
             q, kv_cmp, kv, idx, inp.get("sink"), cu, r, cfg.window, cfg.scale,
-            O, LSE, dO, rows=rows)
+            st_main(O), st_f32(LSE), dO, rows=rows)
         if rd:
             dq = unrot(dq, tpos[rows])
             dkv_cmp = unrot(dkv_cmp, cpos)

@@ -89,6 +89,14 @@ WORKLOADS = {
         idx_heads=0, idx_dim=0, dtype="bf16", idx_dtype="bf16",
         mode="window", teacher="none", backward=True, input_std="inv_sqrt_d",
         draw={"n": 8, "lo": 1024, "hi": 16384, "total": 65536}),
+    # dense mode at ratio 4 on the same 64K THD batch: every visible compressed entry plus
+    # the window, no indexer (the dense phase of the curriculum, section 2)
+    "thd64k_dense_bf16": Workload(
+        name="thd64k_dense_bf16", cfg_id=3, lengths=None, total_tokens=65536,
+        heads=64, head_dim=512, ratio=4, window=128, topk=0, topk_cap=0,
+        idx_heads=0, idx_dim=0, dtype="bf16", idx_dtype="bf16",
+        mode="dense", teacher="none", backward=True, input_std="inv_sqrt_d",
+        draw={"n": 8, "lo": 1024, "hi": 16384, "total": 65536}),
     # HCA: ratio 128, no indexer, every completed entry + window, 4 x 16384
     "thd64k_hca_bf16": Workload(
         name="thd64k_hca_bf16", cfg_id=4, lengths=(16384,) * 4, total_tokens=65536,

@@ -23,14 +23,14 @@ def _params(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = B.header_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B._SIGS)
 
 
 def test_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 6
+    assert lib.csa_abi_version() == 7
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.csa_status_string(st)
     assert lib.csa_status_string(7) == b"unknown status"
@@ -46,6 +46,11 @@ def test_workspace_sizes(lib):
                   window=128, total_tokens=1000, max_seqlen=1000)
     n = B.csa_workspace_size(big, B.CSA_OP_ATTN_BWD)
     assert 1000 * 1152 * (128 + 512) * 2 <= n <= 1000 * 1152 * (128 + 512) * 2 + 8 * 2**20
+    # the backward also takes any workspace down to one chunk of 16 queries
+    m = B.csa_workspace_size_min(big, B.CSA_OP_ATTN_BWD)
+    assert 16 * 1152 * (128 + 512) * 2 <= m <= 16 * 1152 * (128 + 512) * 2 + 2**20
+    assert B.csa_workspace_size_min(p, B.CSA_OP_INDEXER_KL) == \
+        B.csa_workspace_size(p, B.CSA_OP_INDEXER_KL)
     n = ctypes.c_size_t(0)
     assert lib.csa_workspace_size(ctypes.byref(p), 99, ctypes.byref(n)) == B.CSA_ERR_ARG
     assert lib.csa_workspace_size(None, 1, ctypes.byref(n)) == B.CSA_ERR_NULL
@@ -142,7 +147,7 @@ def test_fused_index_topk_validation(lib):
     # shapes without a fused kernel: the separate score and top-k calls serve them
     assert call(_params()) == B.CSA_ERR_UNSUPPORTED                    # f32, 2 x 32 indexer
     assert call(_params(idx_heads=32, idx_dim=128, idx_dtype=B.CSA_BF16)) == B.CSA_ERR_UNSUPPORTED
-    long_ = _params(total_tokens=1 << 16, max_seqlen=1 << 16, **big)  # 16384 visible > 4096
+    long_ = _params(total_tokens=1 << 18, max_seqlen=1 << 18, **big)  # 65536 visible > 32768
     assert call(long_) == B.CSA_ERR_UNSUPPORTED
 
 

@@ -62,22 +62,85 @@ CASES = {
                                                        teacher="none")),
     "rope_fp8_warmup_small": ("csa128k_warmup_fp8", dict(lengths=(1500,), total_tokens=1536,
                                                          topk=64, topk_cap=64, rope_dim=64)),
+    # dense mode at ratio 4 (every visible compressed row + the window, no indexer) on the
+    # matrix-core kernels
+    "dense_bf16_thd_small": ("thd64k_csa_bf16", dict(mode="dense", teacher="none", idx_heads=0,
+                                                     lengths=(301, 515, 1027),
+                                                     total_tokens=1856, draw=None)),
 }
 
+# Sharp-softmax variants of the matrix-core cases: every tensor at unit variance (logits of
+# order 1 instead of 1e-3, so P depends on the logits), and "rescale" cases whose raw kv rows
+# in the second half of each sample are scaled by 8 (exact in bf16): a query there meets
+# logits in a later candidate block that exceed the first block's maximum by far more than
+# 2^8, so the lazily moved running maximum of the attention forward and of the dense teacher
+# normalizer is moved after the first block (checked below from the oracle's logits).
+SHARP = {
+    "csa_bf16_thd_unit": ("csa_bf16_thd_small", dict(strength=True)),
+    "csa_bf16_thd_rescale": ("csa_bf16_thd_small", dict(strength=True, kv_boost=8.0)),
+    "sink_bf16_thd_unit": ("sink_bf16_thd_small", dict(strength=True)),
+    "hca_bf16_thd_rescale": ("hca_bf16_thd_small", dict(strength=True, kv_boost=8.0)),
+    "window_bf16_thd_rescale": ("window_bf16_thd_small", dict(strength=True, kv_boost=8.0)),
+    "dense_bf16_thd_rescale": ("dense_bf16_thd_small", dict(strength=True, kv_boost=8.0)),
+    "fp8_warmup_unit": ("fp8_warmup_small", dict(strength=True)),
+    "fp8_warmup_rescale": ("fp8_warmup_small", dict(strength=True, kv_boost=8.0)),
+}
+for _n, (_b, _x) in SHARP.items():
+    CASES[_n] = CASES[_b] + (_x,)
+
+# the one fp32 case held to the summed-terms bound (64 heads x 512-wide rows)
+F32_SUM = {"f32_wide_rows_generic"}
+
 _CACHE = {}
+
+
+def _kind(name, kind):
+    return "f32_sum" if (kind == "f32" and name in F32_SUM) else kind
+
+
+def _boost_kv(host, factor):
+    """Scale the raw kv rows of the second half of every sample by `factor` (in place)."""
+    cu = host["cu_seqlens"]
+    for b in range(len(cu) - 1):
+        s, e = int(cu[b]), int(cu[b + 1])
+        host["kv"][s + (e - s) // 2:e] *= factor
 
 
 def _case(name):
     if name in _CACHE:
         return _CACHE[name]
-    base, over = CASES[name]
+    base, over = CASES[name][:2]
+    extra = CASES[name][2] if len(CASES[name]) > 2 else {}
     w = configs.workload(base, **over)
-    host = synth_inputs.make_inputs(w, variant=0)
+    host = synth_inputs.make_inputs(w, variant=0, strength=extra.get("strength", False))
+    if extra.get("kv_boost"):
+        _boost_kv(host, extra["kv_boost"])
     h64 = {k: synth_inputs.to_f64(v) for k, v in host.items() if isinstance(v, torch.Tensor)}
     h64["cu_seqlens"] = host["cu_seqlens"]
     h64["max_seqlen"] = host["max_seqlen"]
     _CACHE[name] = (w, host, h64)
     return _CACHE[name]
+
+
+def _rescale_margin(w, q, kv_cmp, kv, idx, cu, rows, first_block=64):
+    """Largest growth, in log2 units, of a (query, head)'s logit maximum past the maximum of
+    its first `first_block` candidates, in the order the forward takes them (compressed
+    rows in idx order, then the window)."""
+    bb, pp = O.token_positions(cu, q.shape[0])
+    starts, _ = O.sample_table(cu)
+    cu_cmp = O.cmp_seqlens(cu, w.ratio)
+    best = 0.0
+    for i, t in enumerate(rows):
+        cr, wr = O.attn_candidates(t, bb, pp, starts, cu_cmp, w.ratio, w.window,
+                                   None if idx is None else idx[i])
+        # compressed candidates padded to whole 64-row blocks before the window rows
+        X = np.concatenate([kv_cmp[cr], kv[wr]], axis=0)
+        if X.shape[0] == 0:
+            continue
+        lg = w.scale * (q[t] @ X.T) / np.log(2.0)
+        n_first = min(first_block, cr.size) if cr.size else min(first_block, wr.size)
+        best = max(best, float((lg.max(axis=1) - lg[:, :n_first].max(axis=1)).max()))
+    return best
 
 
 def _layer(w, host, backward=True):
@@ -94,18 +157,16 @@ def _announce(name, step):
     print(f"[gpu] case={name} step={step}", flush=True)
 
 
+def _wl(n):
+    return configs.workload(CASES[n][0], **CASES[n][1])
+
+
 def _idx_cases():
-    return [n for n in CASES if configs.workload(CASES[n][0], **CASES[n][1]).has_indexer
-            and dict(CASES[n][1]).get("mode", configs.WORKLOADS[CASES[n][0]].mode) == "sparse"]
+    return [n for n in CASES if _wl(n).has_indexer and _wl(n).mode == "sparse"]
 
 
 def _kl_cases():
-    out = []
-    for n in _idx_cases():
-        w = configs.workload(CASES[n][0], **CASES[n][1])
-        if w.teacher != "none":
-            out.append(n)
-    return out
+    return [n for n in _idx_cases() if _wl(n).teacher != "none"]
 
 
 # ------------------------------------------------------------------------- metadata
@@ -125,7 +186,7 @@ def test_metadata_and_compress(name):
     B.csa_compress(L.p, kv, cu, L.cu_cmp, L.kv_cmp)
     torch.cuda.synchronize()
     G.check("kv_cmp", G.back(L.kv_cmp[:Tc]), O.compress(h64["kv"], host["cu_seqlens"], w.ratio),
-            w.dtype)
+            _kind(name, w.dtype))
     assert torch.all(L.kv_cmp[Tc:] == 7.0), "rows beyond cu_cmp[B] were written"
     # validate_metadata accepts the packed batch
     st = torch.full((1,), -1, dtype=torch.int32, device="cuda")
@@ -419,18 +480,24 @@ def _random_e4m3(rng, shape):
     return ((s << 7) | (e << 3) | m).astype(np.uint8)
 
 
-@pytest.mark.parametrize("idx_dtype", ["bf16", "fp8"])
-def test_index_topk_fused_long_rows(idx_dtype):
-    """Rows of up to 4096 visible entries (the largest register footprint of the fused
-    kernel) in a two-sample batch, k not a multiple of 64; sampled rows against the oracle."""
+@pytest.mark.parametrize("idx_dtype,lengths,k", [
+    ("bf16", (16384, 2500), 1000),     # rows up to 4096 keys: one wave per token
+    ("fp8", (16384, 2500), 1000),
+    ("bf16", (40000, 3000), 2000),     # up to 10000 keys: a workgroup per token, 32 per lane
+    ("fp8", (70000, 5000), 2048),      # up to 17500 keys: 64 per lane
+])
+def test_index_topk_fused_long_rows(idx_dtype, lengths, k):
+    """Fused scores + top-k on long rows in a two-sample batch, k not always a multiple of
+    64: sampled rows against the oracle (selection and the selected scores), and the whole
+    selection and score matrix equal to those of the two separate calls."""
     from long_context_compressed_amd import binding as B
-    print(f"[gpu] case=index_topk_long dtype={idx_dtype}", flush=True)
+    print(f"[gpu] case=index_topk_long dtype={idx_dtype} lengths={lengths} k={k}", flush=True)
     rng = np.random.default_rng(11)
-    lengths = (16384, 2500)
     T = sum(lengths)
     cu = np.array([0, lengths[0], T], dtype=np.int64)
-    r, k, kcap = 4, 1000, 1024
-    n_cap = 16384 // r
+    r = 4
+    kcap = -(-k // 64) * 64
+    n_cap = max(lengths) // r
     cu_cmp = O.cmp_seqlens(cu, r)
     n_c = int(cu_cmp[-1])
     wts = (rng.standard_normal((T, 64)) / 8).astype(np.float32)
@@ -438,42 +505,62 @@ def test_index_topk_fused_long_rows(idx_dtype):
         q = torch.from_numpy(rng.standard_normal((T, 64, 128), dtype=np.float32)).to(torch.bfloat16)
         kk = torch.from_numpy(rng.standard_normal((n_c, 128), dtype=np.float32)
                               / np.sqrt(128)).to(torch.bfloat16)
-        q64, k64 = q.double().numpy(), kk.double().numpy()
         dq, dk, dqs, dks = q.cuda(), kk.cuda(), None, None
         code = B.CSA_BF16
     else:
         qc, kc = _random_e4m3(rng, (T, 64, 128)), _random_e4m3(rng, (n_c, 128))
         qs = rng.uniform(0.5, 2.0, (T, 64)).astype(np.float32)
         ks = rng.uniform(0.01, 0.05, (n_c,)).astype(np.float32)
-        q64, k64 = O.dequantize_fp8(qc, qs), O.dequantize_fp8(kc, ks)
         dq, dk = torch.from_numpy(qc).cuda(), torch.from_numpy(kc).cuda()
         dqs, dks = torch.from_numpy(qs).cuda(), torch.from_numpy(ks).cuda()
         code = B.CSA_FP8_E4M3
-    p = B.make_params(batch=2, total_tokens=T, max_seqlen=16384, ratio=r, window=128, topk=k,
-                      topk_cap=kcap, heads=64, head_dim=512, idx_heads=64, idx_dim=128,
+    p = B.make_params(batch=2, total_tokens=T, max_seqlen=max(lengths), ratio=r, window=128,
+                      topk=k, topk_cap=kcap, heads=64, head_dim=512, idx_heads=64, idx_dim=128,
                       scale=1.0 / np.sqrt(512), mode=B.CSA_SPARSE, teacher=B.CSA_TEACHER_SELECTED,
                       dtype=B.CSA_BF16, idx_dtype=code)
     cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
     cmp_d = torch.tensor(cu_cmp, dtype=torch.int32, device="cuda")
+    args = (p, dq, dqs, torch.from_numpy(wts).cuda(), dk, dks, cu_d, cmp_d)
     idx = torch.full((T, kcap), -7, dtype=torch.int32, device="cuda")
     sc = torch.full((T, n_cap), 12345.0, dtype=torch.float32, device="cuda")
-    B.csa_index_topk(p, dq, dqs, torch.from_numpy(wts).cuda(), dk, dks, cu_d, cmp_d, idx,
-                     scores=sc, scores_mode=1)
+    B.csa_index_topk(*args, idx, scores=sc, scores_mode=1)
     torch.cuda.synchronize()
-    rows = np.concatenate([np.arange(16384 - 8, 16384), [16383 - 4 * 1500, 4 * 1024 + 3,
-                           4 * 1000 + 7, 4 * 999 + 2, 4 * 700, 5000, 9999],
-                           16384 + np.array([0, 3, 4, 1500, 2499])])
-    ref = O.index_scores(q64, wts.astype(np.float64), k64, cu, r, n_cap, rows=rows)
+    L0 = lengths[0]
+    rows = [L0 - 8 + i for i in range(8)] + [L0 - 1 - 4 * 1500, 4 * k + 3, 4 * k - 1, 4 * k,
+                                            4 * (k - 1) + 2, L0 // 2, L0 // 3 + 1]
+    rows += [L0 + x for x in (0, 3, 4, lengths[1] // 2, lengths[1] - 1)]
+    rows = np.array(sorted(set(x for x in rows if 0 <= x < T)), dtype=np.int64)
+    if idx_dtype == "bf16":
+        q64 = q[torch.as_tensor(rows)].double().numpy()
+        k64 = kk.double().numpy()
+    else:
+        q64 = O.dequantize_fp8(qc[rows], qs[rows])
+        k64 = O.dequantize_fp8(kc, ks)
+    qv = np.zeros((T, 64, 128))
+    qv[rows] = q64
+    ref = O.index_scores(qv, wts.astype(np.float64), k64, cu, r, n_cap, rows=rows)
     got_i = idx.cpu().numpy()[rows]
     got_s = sc.cpu().numpy().astype(np.float64)[rows]
     for i, t_ in enumerate(rows):
-        row0 = int(cu_cmp[0 if t_ < 16384 else 1])
+        row0 = int(cu_cmp[0 if t_ < L0 else 1])
         _check_selection(got_i[i], ref[i], row0, k, 1e-4, (idx_dtype, int(t_)))
         sel = got_i[i][got_i[i] >= 0] - row0
         G.check(f"selected scores t={t_}", got_s[i][sel], ref[i][sel], "bf16")
         mask = np.ones(n_cap, bool)
         mask[sel] = False
         assert np.all(got_s[i][mask] == 12345.0), t_
+    # the same operands through the two separate calls: the same selection, and the fused
+    # call's every-visible-score mode writes the same score matrix
+    sc2 = torch.full_like(sc, 12345.0)
+    B.csa_index_scores(*args, sc2)
+    idx2 = torch.empty_like(idx)
+    B.csa_topk_select(p, sc2, cu_d, cmp_d, idx2)
+    sc3 = torch.full_like(sc, 12345.0)
+    idx3 = torch.empty_like(idx)
+    B.csa_index_topk(*args, idx3, scores=sc3, scores_mode=2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(idx, idx3)
+    assert torch.equal(sc2, sc3)
 
 
 # ------------------------------------------------------------------------- attention
@@ -522,8 +609,17 @@ def test_attn_fwd(name):
                                    h64.get("sink"), host["cu_seqlens"], w.ratio, w.window,
                                    w.scale, rows=rows)
     torch.cuda.synchronize()
-    G.check("O", G.back(L.out)[:n], Oref, w.dtype)
-    G.check("LSE", G.back(L.lse)[:n], Lref, w.dtype)
+    kind = _kind(name, w.dtype)
+    if "rescale" in name:
+        # the case reaches the lazy rescale: some (query, head) maximum grows past its first
+        # block's by more than the 2^8 the forward tolerates before moving its running max
+        mi = _mode_idx(w, idx)
+        margin = _rescale_margin(w, h64["q"], kv_cmp_r, h64["kv"], mi, host["cu_seqlens"], rows)
+        print(f"[gpu] {name}: largest growth past the first block {margin:.1f} log2 units",
+              flush=True)
+        assert margin > 12.0
+    G.check("O", G.back(L.out)[:n], Oref, kind)
+    G.check("LSE", G.back(L.lse)[:n], Lref, kind)
     # compressed-only normalizer: the same attention with an empty window and no sink
     bb, pp = O.token_positions(host["cu_seqlens"], w.total_tokens)
     if w.mode == "sparse":
@@ -539,7 +635,7 @@ def test_attn_fwd(name):
         mi = None if _mode_idx(w, idx) is None else idx[rc]
         _, Lc = O.sparse_attn_fwd(h64["q"], kv_cmp_r, h64["kv"], mi, None, host["cu_seqlens"],
                                   w.ratio, 0, w.scale, rows=rc)
-        G.check("LSE(compressed only)", got_c[has_c], Lc, w.dtype)
+        G.check("LSE(compressed only)", got_c[has_c], Lc, kind)
     if t_logits is not None:
         # cached compressed-candidate logits, slot order of the attention call
         ref_l = O.compressed_logits(h64["q"], kv_cmp_r, None if _mode_idx(w, idx) is None
@@ -549,7 +645,7 @@ def test_attn_fwd(name):
         got_f = np.concatenate([tl[t, :, :r.shape[1]].ravel() for t, r in zip(rows, ref_l)])
         ref_f = np.concatenate([r.ravel() for r in ref_l])
         assert got_f.size > 0
-        G.check("teacher logits cache", got_f, ref_f, w.dtype)
+        G.check("teacher logits cache", got_f, ref_f, kind)
     if n < w.total_tokens:
         assert torch.all(L.out[n:] == 0) and torch.all(L.lse[n:] == 0)
 
@@ -591,13 +687,14 @@ def test_attn_bwd(name):
                                             h64.get("sink"), host["cu_seqlens"], w.ratio, w.window,
                                             w.scale, O_r[:n], L_r[:n], dO[:n], rows=rows)
     torch.cuda.synchronize()
-    G.check("dq", G.back(L.dq)[:n], dq, w.dtype)
+    kind = _kind(name, w.dtype)
+    G.check("dq", G.back(L.dq)[:n], dq, kind)
     Tc = kv_cmp_r.shape[0]
     if w.mode != "window":
-        G.check("dkv_cmp", G.back(L.dkv_cmp)[:Tc], dkc, w.dtype)
-    G.check("dkv(window)", G.back(L.dkv), dkv, w.dtype)
+        G.check("dkv_cmp", G.back(L.dkv_cmp)[:Tc], dkc, kind)
+    G.check("dkv(window)", G.back(L.dkv), dkv, kind)
     if sink is not None:
-        G.check("dsink", G.back(L.dsink), dsink, w.dtype)
+        G.check("dsink", G.back(L.dsink), dsink, kind)
     if n < w.total_tokens:
         assert torch.all(L.dq[n:] == 0)
 
@@ -655,14 +752,23 @@ def test_indexer_kl(name, grads, from_fwd):
                                           kI64, host["cu_seqlens"], w.ratio, w.scale, w.teacher,
                                           gs, rows=rows)
     torch.cuda.synchronize()
+    if "rescale" in name and w.teacher == "dense":
+        # the dense teacher's per-head normalizer meets a key block whose logits exceed the
+        # first block's maximum by more than the 2^8 its running maximum tolerates
+        wd = dataclasses.replace(w, window=0)
+        margin = _rescale_margin(wd, h64["q"], kv_cmp_r, h64["kv"], None, host["cu_seqlens"],
+                                 rows)
+        print(f"[gpu] {name}: teacher logit growth past the first key block {margin:.1f} "
+              f"log2 units", flush=True)
+        assert margin > 12.0
     got_loss = float(L.loss.item())
     print(f"loss gpu={got_loss:.8e} ref={loss:.8e}", flush=True)
     assert abs(got_loss - loss) <= G.TOL_LOSS_REL * abs(loss)
-    G.check("kl", G.back(L.kl)[:n], kl, w.dtype if w.dtype == "f32" else "bf16")
+    G.check("kl", G.back(L.kl)[:n], kl, _kind(name, w.dtype) if w.dtype == "f32" else "bf16")
     if n < w.total_tokens:
         assert torch.all(L.kl[n:] == 0)
     if grads:
-        kind = "f32" if (w.dtype == "f32" and w.idx_dtype == "f32") else "bf16"
+        kind = _kind(name, "f32") if (w.dtype == "f32" and w.idx_dtype == "f32") else "bf16"
         G.check("dqI", G.back(L.dqI)[:n], dqI, kind)
         G.check("dw", G.back(L.dw)[:n], dw, kind)
         Tc = kI64.shape[0]
@@ -682,19 +788,27 @@ def _check_open(name, got, ref, bound):
     assert excess.max() <= 0, (name, float(excess.max()))
 
 
-@pytest.mark.parametrize("idx_dtype", ["bf16", "fp8"])
-def test_indexer_kl_dense_teacher_chunked(idx_dtype):
+@pytest.mark.parametrize("idx_dtype,boost,given", [("bf16", None, True), ("fp8", None, True),
+                                                   ("fp8", 8.0, True), ("bf16", None, False),
+                                                   ("fp8", None, False)])
+def test_indexer_kl_dense_teacher_chunked(idx_dtype, boost, given):
     """Dense-teacher loss on the tiled path across more than one 8192-query chunk: three
     samples starting at rows that are not multiples of 4, capacity padding, unit-variance
-    inputs (peaked teacher), with and without gradients, against the oracle."""
+    inputs (peaked teacher), with and without gradients, against the oracle.  With `boost`
+    the second half of every sample's kv rows is scaled so that the teacher normalizer's
+    running maximum is moved after its first key block.  given = False: no score matrix is
+    passed and the call forms the student scores itself."""
     from long_context_compressed_amd import binding as B
     w = configs.workload("csa128k_warmup_fp8", idx_dtype=idx_dtype, lengths=(4003, 2998, 2501),
                          total_tokens=9560, topk=64, topk_cap=64)
     host = synth_inputs.make_inputs(w, variant=0, strength=True)
+    if boost:
+        _boost_kv(host, boost)
     h64 = {k: synth_inputs.to_f64(v) for k, v in host.items() if isinstance(v, torch.Tensor)}
     h64["cu_seqlens"] = host["cu_seqlens"]
     h64["max_seqlen"] = host["max_seqlen"]
-    name = f"dense_teacher_{idx_dtype}"
+    name = f"dense_teacher_{idx_dtype}" + ("_rescale" if boost else "") + \
+        ("" if given else "_recomputed_scores")
     L = _layer(w, host, backward=True)
     assert L.ws_kl is not None and B.csa_workspace_size(L.p, B.CSA_OP_INDEXER_KL) > 0
     cu = _cu(host)
@@ -711,11 +825,19 @@ def test_indexer_kl_dense_teacher_chunked(idx_dtype):
     kl, loss, dqI, dw, dkI, open_bound = O.indexer_kl(
         h64["q"], kv_cmp_r, s32[:n], idx[:n], qI64, h64["w"], kI64, host["cu_seqlens"],
         w.ratio, w.scale, w.teacher, gs, rows=np.arange(n), relu_eps=2.0 ** -16)
+    if boost:
+        wd = dataclasses.replace(w, window=0)
+        margin = _rescale_margin(wd, h64["q"], kv_cmp_r, h64["kv"], None, host["cu_seqlens"],
+                                 np.arange(0, n, 7))
+        print(f"[gpu] {name}: teacher logit growth past the first key block {margin:.1f}",
+              flush=True)
+        assert margin > 12.0
     for grads in (True, False):
         _announce(name, f"indexer_kl grads={grads}")
         L.kl.fill_(float("nan"))
         L.dkI_cmp.zero_()
-        B.csa_indexer_kl(L.p, host["q"].cuda(), G.dev(kv_cmp_r, dt), torch.from_numpy(s32).cuda(),
+        B.csa_indexer_kl(L.p, host["q"].cuda(), G.dev(kv_cmp_r, dt),
+                         torch.from_numpy(s32).cuda() if given else None,
                          torch.from_numpy(idx.astype(np.int32)).cuda(), d["qI"], d["qI_scale"],
                          host["w"].cuda(), d["kI"], d["kI_scale"], cu, L.cu_cmp, gs, L.kl,
                          L.loss, L.dqI if grads else None, L.dw if grads else None,
@@ -733,44 +855,70 @@ def test_indexer_kl_dense_teacher_chunked(idx_dtype):
 
 
 # ------------------------------------------------------------------------- whole layer
+def _sets(a):
+    return [set(r[r >= 0].tolist()) for r in np.asarray(a)]
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_layer_end_to_end(name):
+    """The whole layer step (every call chained on the device) against the oracle's layer
+    chain with storage rounding (the chain holds compressed rows, rotated operands and the
+    saved output in the device dtype and scores / LSE in fp32, as the device buffers do).
+    Top-k sets then differ only where fp32 score sums meet an exact tie of the rounded
+    values: each differing row is checked to be such a near-tie, every per-query output is
+    compared on the rows whose sets agree, the loss over those rows to 1e-3, and the
+    shared-row gradients (sums over all queries) when every set agrees."""
     from long_context_compressed_amd.pipeline import to_device
     w, host, h64 = _case(name)
     _announce(name, "layer")
     L = _layer(w, host, backward=w.backward)
     dev = to_device(host)
     L.step(dev, dev["cu_seqlens"])
-    ref = O.layer_step(h64, w, rows=np.arange(int(host["cu_seqlens"][-1])))
-    torch.cuda.synchronize()
     n = int(host["cu_seqlens"][-1])
-    Tc = int(O.cmp_seqlens(host["cu_seqlens"], w.ratio)[-1])
-    flips = 0
+    ref = O.layer_step(h64, w, rows=np.arange(n), stored=True)
+    torch.cuda.synchronize()
+    kind = _kind(name, w.dtype)
+    k2 = _kind(name, "f32") if (w.dtype == "f32" and w.idx_dtype == "f32") else "bf16"
+    ok = np.ones(n, dtype=bool)
     if "idx" in ref:
-        flips = G.idx_sets_equal(L.idx.cpu().numpy()[:n], ref["idx"])
-        print(f"idx rows differing from the all-fp64 chain: {flips} / {n}", flush=True)
-        if w.dtype == "f32":
-            assert flips <= max(1, n // 200)
-    kind = w.dtype
-    if flips == 0:
-        G.check("O", G.back(L.out)[:n], ref["O"], kind)
-        G.check("LSE", G.back(L.lse)[:n], ref["LSE"], kind)
-        if "O_rot" in ref:
-            G.check("O_rot", G.back(L.out_rot)[:n], ref["O_rot"], kind)
-        if "loss" in ref:
-            print(f"loss gpu={L.loss.item():.8e} ref={ref['loss']:.8e}", flush=True)
+        got = L.idx.cpu().numpy()[:n]
+        gs, rs = _sets(got), _sets(ref["idx"])
+        ok = np.array([a == b for a, b in zip(gs, rs)], dtype=bool)
+        cu_cmp = O.cmp_seqlens(host["cu_seqlens"], w.ratio)
+        bb, _ = O.token_positions(host["cu_seqlens"], w.total_tokens)
+        # a differing set: the swapped entries lie within fp32 accumulation error of the k-th
+        # score (1e-5 of the row's largest |score|); with rotated indexer operands, whose
+        # device rotation (fp32) and the oracle's (fp64) may round one element a bf16 step
+        # apart, within the bf16 selection rule's 1e-3
+        rel = 1e-3 if w.rope_dim else 1e-5
+        for t in np.nonzero(~ok)[0]:
+            _check_selection(got[t], ref["scores"][t], int(cu_cmp[bb[t]]), w.topk, rel,
+                             (name, int(t)))
+        print(f"[gpu] idx rows differing from the oracle chain: {int((~ok).sum())} / {n}",
+              flush=True)
+        assert (~ok).sum() <= max(2, n // 200)
+    G.check("O", G.back(L.out)[:n][ok], ref["O"][ok], kind)
+    G.check("LSE", G.back(L.lse)[:n][ok], ref["LSE"][ok], kind)
+    if "O_rot" in ref:
+        G.check("O_rot", G.back(L.out_rot)[:n][ok], ref["O_rot"][ok], kind)
+    if "loss" in ref:
+        kl_ok = ok if w.teacher == "selected" else np.ones(n, dtype=bool)
+        got_kl = G.back(L.kl)[:n]
+        G.check("kl", got_kl[kl_ok], ref["kl"][kl_ok], kind if w.dtype == "f32" else "bf16")
+        lg, lr = float(got_kl[kl_ok].sum()), float(ref["kl"][kl_ok].sum())
+        print(f"loss over {int(kl_ok.sum())} rows gpu={lg:.8e} ref={lr:.8e}", flush=True)
+        assert abs(lg - lr) <= G.TOL_LOSS_REL * abs(lr)
+        if kl_ok.all():
             assert abs(L.loss.item() - ref["loss"]) <= G.TOL_LOSS_REL * abs(ref["loss"])
         if w.backward:
-            G.check("dq", G.back(L.dq)[:n], ref["dq"], kind)
+            G.check("dqI", G.back(L.dqI)[:n][kl_ok], ref["dqI"][kl_ok], k2)
+            G.check("dw", G.back(L.dw)[:n][kl_ok], ref["dw"][kl_ok], k2)
+    if w.backward:
+        G.check("dq", G.back(L.dq)[:n][ok], ref["dq"][ok], kind)
+        if ok.all():
             G.check("dkv", G.back(L.dkv), ref["dkv"], kind)
             if "dkI_tok" in ref:
-                k2 = "f32" if (w.dtype == "f32" and w.idx_dtype == "f32") else "bf16"
                 G.check("dkI_tok", G.back(L.dkI_tok), ref["dkI_tok"], k2)
-                G.check("dqI", G.back(L.dqI)[:n], ref["dqI"], k2)
-    else:
-        # near-tie flips change which rows are attended; the outputs stay close in norm
-        G.check("O", G.back(L.out)[:n], ref["O"], "bf16", rel_tol=5e-2)
-    assert Tc >= 0
 
 
 @pytest.mark.parametrize("name", ["tiny_f32_packed_tails_pad", "csa_bf16_thd_small"])

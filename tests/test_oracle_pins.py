@@ -826,3 +826,57 @@ def test_compressed_logits_normalize_to_compressed_lse_and_feed_the_teacher():
     _, lsed = O.sparse_attn_fwd(q, kc, kv_raw, None, None, cu, r, 0, scale, rows=rd)
     for i, t in enumerate(rd):
         assert np.allclose(logsumexp(dl[t], axis=1), lsed[i], rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- storage rounding
+def test_round_bf16_matches_torch_cast():
+    """The oracle's bf16 rounding equals torch's float32 -> bfloat16 cast (round to nearest,
+    ties to even), on wide magnitudes, exact halfway cases and subnormals."""
+    x = np.concatenate([RNG.standard_normal(50000) * s for s in (1e-30, 1e-3, 1, 1e4, 1e30)])
+    # halfway cases: bit 15 set and the lower 15 bits clear, both parities of bit 16
+    u = RNG.integers(0x00800000, 0x7F000000, 4000, dtype=np.uint32) & np.uint32(0xFFFF0000)
+    half = (u | np.uint32(0x8000)).view(np.float32).astype(np.float64)
+    x = np.concatenate([x, half, -half, [0.0, -0.0, 1e-40, -3e-39]])
+    ref = torch.tensor(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.round_bf16(x)
+    np.testing.assert_array_equal(got, ref)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+    s = O.store(np.array([np.inf, -np.inf, 1.0 + 2 ** -9]), "bf16")
+    assert np.isposinf(s[0]) and np.isneginf(s[1]) and s[2] == 1.0   # halfway to even
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_stored_chain_rounds_only_at_storage_points(dtype):
+    """The layer chain with storage rounding: its compressed rows are the rounded compressor
+    output; with float32 storage every result stays within float32 rounding of the float64
+    chain; with bfloat16 storage within a few bf16 steps (an error dropped elsewhere, or a
+    rounding applied to a step's arithmetic rather than to what it hands on, shows up)."""
+    from synth import configs
+    cfg = configs.workload("tiny_csa_f32_L256", heads=2, head_dim=8, idx_heads=2, idx_dim=4,
+                           window=5, topk=3, topk_cap=64, teacher="selected", dtype=dtype,
+                           idx_dtype=dtype)
+    lens = [23, 17]
+    rng = np.random.default_rng(41)
+    cu = _cu(lens)
+    T = int(cu[-1])
+    rnd = (lambda a: O.store(a, dtype))
+    inp = dict(cu_seqlens=cu, max_seqlen=max(lens),
+               q=rnd(rng.standard_normal((T, 2, 8))), kv=rnd(rng.standard_normal((T, 8))),
+               qI=rnd(rng.standard_normal((T, 2, 4))), kI_tok=rnd(rng.standard_normal((T, 4))),
+               w=rng.standard_normal((T, 2)).astype(np.float32).astype(np.float64),
+               dO=rnd(rng.standard_normal((T, 2, 8))))
+    ref = O.layer_step(inp, cfg)
+    st = O.layer_step(inp, cfg, stored=True)
+    np.testing.assert_array_equal(st["kv_cmp"], O.store(O.compress(inp["kv"], cu, 4), dtype))
+    np.testing.assert_array_equal(st["kI_cmp"], O.store(O.compress(inp["kI_tok"], cu, 4), dtype))
+    fin = np.isfinite(ref["scores"])
+    np.testing.assert_array_equal(np.isfinite(st["scores"]), fin)
+    assert np.array_equal(st["scores"][fin], st["scores"][fin].astype(np.float32))
+    np.testing.assert_array_equal(st["idx"], ref["idx"])   # no near-ties in this draw
+    rel = 2.0 ** -20 if dtype == "f32" else 2.0 ** -6
+    for key in ("O", "LSE", "kl", "dq", "dkv", "dqI", "dw", "dkI_tok"):
+        a, b = st[key], ref[key]
+        err = np.abs(a - b).max()
+        assert err <= rel * np.abs(b).max(), (key, err, np.abs(b).max())
+        if dtype == "bf16" and key in ("O", "dq", "dkv"):
+            assert err > 0, key          # the rounding reached this output
