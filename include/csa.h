@@ -290,6 +290,22 @@ csa_status_t csa_sparse_attn_bwd(const csa_params_t* p, const void* q, const voi
                                  float* dkv_cmp, float* dkv, float* dsink, void* ws,
                                  size_t ws_bytes, hipStream_t stream);
 
+/* csa_sparse_attn_bwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same operands, results and errors as csa_sparse_attn_bwd; its workspace is a static
+ * 256 MiB array of the library on each GPU (held from the library's first use on that GPU
+ * until the process ends), so the queries are processed in as many chunks as that needs.
+ * CSA_ERR_WORKSPACE when even the smallest chunk (csa_workspace_size_min) exceeds 256 MiB.
+ * The call allocates nothing.  All calls on one GPU share that GPU's array: calls that
+ * overlap in time on one GPU (two streams, two host threads) race and must be serialized
+ * by the caller.  Nothing carries over from one call to the next. */
+csa_status_t csa_sparse_attn_bwd_noalloc(const csa_params_t* p, const void* q,
+                                         const void* kv_cmp, const void* kv, const int32_t* idx,
+                                         const float* sink, const int32_t* cu_seqlens,
+                                         const int32_t* cu_cmp, const void* out, const float* lse,
+                                         const void* d_out, void* dq, float* dkv_cmp, float* dkv,
+                                         float* dsink, hipStream_t stream);
+
 /* Indexer KL auxiliary loss with its eager backward (section 3 loss equation; section
  * 8.2: the indexer-loss backward runs inside the forward, the loss scale is applied by
  * the caller through grad_scale).  C_t = idx row (CSA_TEACHER_SELECTED) or all visible

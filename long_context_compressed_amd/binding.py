@@ -66,6 +66,7 @@ _SIGS = {
     "csa_rope": ([_I32, _P, _P, _I64, _I32, _I32, _I32, _F, _I32, _I32, _P, _P], _I32),
     "csa_teacher_logits_stride": ([_PP], _I64),
     "csa_sparse_attn_bwd": ([_PP] + [_P] * 14 + [_P, _SZ, _P], _I32),
+    "csa_sparse_attn_bwd_noalloc": ([_PP] + [_P] * 14 + [_P], _I32),
     "csa_indexer_kl": ([_PP, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F,
                         _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
 }
@@ -242,6 +243,14 @@ def csa_sparse_attn_bwd(p, q, kv_cmp, kv, idx, sink, cu_seqlens, cu_cmp, out, ls
         ctypes.byref(p), _ptr(q), _ptr(kv_cmp), _ptr(kv), _ptr(idx), _ptr(sink), _ptr(cu_seqlens),
         _ptr(cu_cmp), _ptr(out), _ptr(lse), _ptr(d_out), _ptr(dq), _ptr(dkv_cmp), _ptr(dkv),
         _ptr(dsink), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def csa_sparse_attn_bwd_noalloc(p, q, kv_cmp, kv, idx, sink, cu_seqlens, cu_cmp, out, lse,
+                                d_out, dq, dkv_cmp, dkv, dsink, stream=None):
+    _check("csa_sparse_attn_bwd_noalloc", lib().csa_sparse_attn_bwd_noalloc(
+        ctypes.byref(p), _ptr(q), _ptr(kv_cmp), _ptr(kv), _ptr(idx), _ptr(sink), _ptr(cu_seqlens),
+        _ptr(cu_cmp), _ptr(out), _ptr(lse), _ptr(d_out), _ptr(dq), _ptr(dkv_cmp), _ptr(dkv),
+        _ptr(dsink), _stream(stream)))
 
 
 def csa_indexer_kl(p, q, kv_cmp, scores, idx, qI, qI_scale, w, kI_cmp, kI_scale, cu_seqlens,

@@ -303,6 +303,27 @@ csa_status_t csa_sparse_attn_bwd(const csa_params_t* p, const void* q, const voi
   return launched(csa::launch_attn_bwd(sh, io, stream));
 }
 
+csa_status_t csa_sparse_attn_bwd_noalloc(const csa_params_t* p, const void* q,
+                                         const void* kv_cmp, const void* kv, const int32_t* idx,
+                                         const float* sink, const int32_t* cu_seqlens,
+                                         const int32_t* cu_cmp, const void* out, const float* lse,
+                                         const void* d_out, void* dq, float* dkv_cmp, float* dkv,
+                                         float* dsink, hipStream_t stream) {
+  csa_status_t st = check_attn(p);
+  if (st) return st;
+  if (!q || !kv || !cu_seqlens || !cu_cmp || !out || !lse || !d_out || !dq || !dkv)
+    return CSA_ERR_NULL;
+  if (p->mode != CSA_WINDOW && (!kv_cmp || !dkv_cmp)) return CSA_ERR_NULL;
+  if (p->mode == CSA_SPARSE && !idx) return CSA_ERR_NULL;
+  const Shape sh = make_shape(p, cu_seqlens, cu_cmp);
+  if (csa::attn_bwd_workspace_min(sh) > csa::attn_bwd_scratch_bytes()) return CSA_ERR_WORKSPACE;
+  csa::AttnIO io = {};
+  io.q = q; io.kv_cmp = kv_cmp; io.kv = kv; io.idx = p->mode == CSA_SPARSE ? idx : nullptr;
+  io.sink = sink; io.o = out; io.lse = const_cast<float*>(lse); io.dout = d_out; io.dq = dq;
+  io.dkv_cmp = dkv_cmp; io.dkv = dkv; io.dsink = sink ? dsink : nullptr;
+  return launched(csa::launch_attn_bwd_noalloc(sh, io, stream));
+}
+
 csa_status_t csa_indexer_kl(const csa_params_t* p, const void* q, const void* kv_cmp,
                             const float* scores, int64_t ld_scores, const int32_t* idx,
                             const float* teacher_lse, const float* teacher_logits,

@@ -89,6 +89,9 @@ size_t attn_bwd_workspace(const Shape& sh);       // preferred size
 size_t attn_bwd_workspace_min(const Shape& sh);   // smallest size the call accepts
 hipError_t launch_attn_fwd(const Shape& sh, const AttnIO& io, hipStream_t s);
 hipError_t launch_attn_bwd(const Shape& sh, const AttnIO& io, hipStream_t s);
+// The backward with its workspace in the library's static per-device array (io.ws ignored).
+size_t attn_bwd_scratch_bytes();
+hipError_t launch_attn_bwd_noalloc(const Shape& sh, AttnIO io, hipStream_t s);
 
 struct KlIO {
   const void* q;
