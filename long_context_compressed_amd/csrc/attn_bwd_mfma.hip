@@ -7,6 +7,7 @@
 // one row is both), and the optional sink gradient.
 #include <math.h>
 
+#include "attn_bwd_keys.h"
 #include "attn_common.h"
 #include "csa_launch.h"
 #include "csr_build.h"
@@ -578,13 +579,29 @@ __global__ __launch_bounds__(256) void k_bwd_reduce_win(BwdArgs b, int u_lo) {
 namespace {
 
 struct BwdPlan {
-  int64_t n_slots, n_c_max, chunk, Tc_cap;
-  size_t off_pds, off_stage, off_nc, off_cnt, off_off, off_cur, off_list, total;
+  bool keys;   // shared-row gradients by the key-major pass (else staged rows + CSR sums)
+  int64_t n_slots, n_c_max, chunk, Tc_cap, cap;
+  size_t off_pds, off_stage, off_nc, off_cnt, off_off, off_cur, off_list;
+  size_t off_items, off_ipart, off_red, off_part, total;
 };
+
+// The key-major pass does dense masked products over every (query, row) pair a query sees,
+// where the staged path moves one 1 KiB row gradient per attended pair through HBM twice;
+// it is taken unless a query attends only a small share of the compressed rows it sees
+// (top-k well below the visible count), for all-visible and window-only layers, and while the
+// per-sample block tables fit.
+bool keys_path(const Shape& sh) {
+  const int64_t n_cap = sh.r > 0 ? sh.max_seqlen / sh.r : 0;
+  if (sh.mode == 2) return true;
+  if (n_cap / keys::kKeys + 1 > 2048) return false;
+  if (sh.mode == 1) return true;
+  return sh.k_cap <= 2048 && n_cap <= 6ll * sh.k_cap;
+}
 
 // Workspace layout for chunks of `chunk` query tokens.
 BwdPlan bwd_layout(const Shape& sh, int64_t chunk) {
-  BwdPlan p;
+  BwdPlan p = {};
+  p.keys = keys_path(sh);
   p.n_c_max = sh.mode == 0 ? sh.k_cap : (sh.mode == 1 ? sh.max_seqlen / sh.r : 0);
   p.n_slots = ((p.n_c_max + sh.W + kNB2 - 1) / kNB2) * kNB2;
   p.chunk = chunk;
@@ -592,41 +609,54 @@ BwdPlan bwd_layout(const Shape& sh, int64_t chunk) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t o = 0;
   p.off_pds = o;   o = al(o + (size_t)p.chunk * p.n_slots * 128 * 2);
-  p.off_stage = o; o = al(o + (size_t)p.chunk * p.n_slots * kD * 2);
   p.off_nc = o;    o = al(o + (size_t)sh.T * 4);
-  p.off_cnt = o;   o = al(o + (size_t)p.Tc_cap * 4);
-  p.off_off = o;   o = al(o + (size_t)p.Tc_cap * 4);
-  p.off_cur = o;   o = al(o + (size_t)p.Tc_cap * 4);
-  p.off_list = o;  o = al(o + (size_t)p.chunk * (p.n_c_max > 0 ? p.n_c_max : 1) * 4);
+  if (p.keys) {
+    const int n_cap = sh.mode == 2 ? 0 : sh.max_seqlen / sh.r;
+    p.cap = keys::item_cap(sh.mode, sh.B, (int)chunk, n_cap, sh.W);
+    p.off_cnt = o;   o = al(o + 128 * 4);   // 64 counters, then 256 zero bytes
+    p.off_items = o; o = al(o + (size_t)p.cap * 16);
+    p.off_ipart = o; o = al(o + (size_t)p.cap * 4);
+    p.off_red = o;   o = al(o + (size_t)p.cap * 16);
+    p.off_part = o;  o = al(o + (size_t)p.cap * keys::kKeys * kD * 4);
+  } else {
+    p.off_stage = o; o = al(o + (size_t)p.chunk * p.n_slots * kD * 2);
+    p.off_cnt = o;   o = al(o + (size_t)p.Tc_cap * 4);
+    p.off_off = o;   o = al(o + (size_t)p.Tc_cap * 4);
+    p.off_cur = o;   o = al(o + (size_t)p.Tc_cap * 4);
+    p.off_list = o;  o = al(o + (size_t)p.chunk * (p.n_c_max > 0 ? p.n_c_max : 1) * 4);
+  }
   p.total = o;
   return p;
 }
 
-// The largest chunk whose layout fits in `budget` bytes: whole multiples of the XCD token
-// mapping (8 * kChunk tokens) while that fits, else multiples of the CSR group, at least one
-// group (its total then exceeds a budget below the minimum; the caller checks).
+// The largest chunk whose layout fits in `budget` bytes (the layout grows with the chunk):
+// every query at once if that fits, else the largest whole multiple of the XCD token mapping
+// (8 * kChunk tokens), else of the CSR group; at least one group (its total then exceeds a
+// budget below the minimum; the caller checks).
 BwdPlan bwd_plan(const Shape& sh, size_t budget) {
   const int64_t T = sh.T > 0 ? sh.T : 1;
-  const BwdPlan one = bwd_layout(sh, 1);
-  const int64_t per_tok = (int64_t)(bwd_layout(sh, 2).total - one.total) > 0
-                              ? (int64_t)(bwd_layout(sh, 2).total - one.total) : 1;
-  int64_t ch = budget > one.total ? (int64_t)((budget - one.total) / per_tok) + 1 : 1;
-  if (ch >= T) ch = T;
-  else if (ch >= 8 * kChunk) ch = (ch / (8 * kChunk)) * (8 * kChunk);
-  else ch = (ch / kCsrGroup) * kCsrGroup;
-  if (ch < kCsrGroup) ch = kCsrGroup < T ? kCsrGroup : T;
-  BwdPlan p = bwd_layout(sh, ch);
-  while (p.total > budget && ch > kCsrGroup) {   // alignment slack of the layout
-    ch -= kCsrGroup;
-    p = bwd_layout(sh, ch);
-  }
-  return p;
+  BwdPlan p = bwd_layout(sh, T);
+  if (p.total <= budget || T <= kCsrGroup) return p;
+  auto largest = [&](int64_t unit, int64_t hi) {   // largest m * unit < hi that fits, or 0
+    int64_t lo = 0, up = (hi - 1) / unit;            // answer in [lo, up] units
+    while (lo < up) {
+      const int64_t mid = (lo + up + 1) / 2;
+      if (bwd_layout(sh, mid * unit).total <= budget) lo = mid;
+      else up = mid - 1;
+    }
+    return lo * unit;
+  };
+  int64_t ch = largest(8 * kChunk, T);
+  if (ch == 0) ch = largest(kCsrGroup, T < 8 * kChunk ? T : 8 * kChunk);
+  if (ch == 0) ch = kCsrGroup;
+  return bwd_layout(sh, ch);
 }
 
-// Preferred workspace: chunks of up to kStageBudget bytes of staging (one chunk for a 64K
-// batch: one launch tail and one CSR per kernel per step).
+// Preferred workspace: chunks of up to kStageBudget bytes of per-pair storage (one chunk for
+// a 64K batch: one launch tail per kernel per step).
 size_t bwd_preferred(const Shape& sh) {
-  const int64_t per_tok = bwd_layout(sh, 1).n_slots * (128 + kD) * 2;
+  const BwdPlan one = bwd_layout(sh, 1);
+  const int64_t per_tok = one.n_slots * (one.keys ? 128 * 2 : (128 + kD) * 2);
   int64_t ch = kStageBudget / per_tok;
   ch = (ch / (8 * kChunk)) * (8 * kChunk);
   if (ch < 8 * kChunk) ch = 8 * kChunk;
@@ -686,14 +716,52 @@ hipError_t launch_attn_bwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s
   b.mode = sh.mode;
   b.scale = sh.scale;
   b.scale_log2 = sh.scale * 1.44269504088896341f;
+  KeysArgs ka = {};
+  if (pl.keys) {
+    ka.q = b.q;
+    ka.dout = b.dout;
+    ka.pds = b.pds;
+    ka.idx = sh.mode == 0 ? io.idx : nullptr;
+    ka.nc = b.nc;
+    ka.cu = sh.cu;
+    ka.cu_cmp = sh.cu_cmp;
+    ka.counters = (int32_t*)(ws + pl.off_cnt);
+    ka.zeros = (const uint16_t*)(ws + pl.off_cnt + 64 * 4);
+    ka.items = (int4*)(ws + pl.off_items);
+    ka.item_part = (int32_t*)(ws + pl.off_ipart);
+    ka.red = (int4*)(ws + pl.off_red);
+    ka.part = (float*)(ws + pl.off_part);
+    ka.dkv_cmp = io.dkv_cmp;
+    ka.dkv = io.dkv;
+    ka.n_slots = pl.n_slots;
+    ka.cap = pl.cap;
+    ka.B = sh.B;
+    ka.r = sh.r;
+    ka.n_cap = sh.mode == 2 ? 0 : sh.max_seqlen / sh.r;
+    ka.W = sh.W;
+    ka.k_cap = sh.k_cap;
+    ka.mode = sh.mode;
+  }
   for (int64_t t0 = 0; t0 < sh.T; t0 += pl.chunk) {
     b.t0 = (int)t0;
     b.nT = (int)(sh.T - t0 < pl.chunk ? sh.T - t0 : pl.chunk);
     const int64_t grid = token_grid(b.nT);
+    if (pl.keys) {
+      ka.t0 = b.t0;
+      ka.nT = b.nT;
+      hipLaunchKernelGGL(k_bwd_fill_zero, dim3(1), dim3(256), 0, s, ka.counters, 128);
+      hipError_t e = launch_attn_bwd_keys(ka, s);
+      if (e != hipSuccess) return e;
+    }
     if (sh.mode != 0 || sh.k_cap <= kIdxLds)
       hipLaunchKernelGGL(k_attn_bwd_dq_mfma<true>, dim3((unsigned)grid), dim3(256), 0, s, b);
     else
       hipLaunchKernelGGL(k_attn_bwd_dq_mfma<false>, dim3((unsigned)grid), dim3(256), 0, s, b);
+    if (pl.keys) {
+      hipError_t e = launch_attn_bwd_keys_sums(ka, s);
+      if (e != hipSuccess) return e;
+      continue;
+    }
     hipLaunchKernelGGL(k_attn_bwd_dkv_mfma, dim3((unsigned)grid), dim3(256), 0, s, b);
     if (sh.mode != 2) {
       hipLaunchKernelGGL(k_bwd_fill_zero, dim3(64), dim3(256), 0, s, b.cnt, b.Tc_cap);

@@ -40,14 +40,27 @@ def test_workspace_sizes(lib):
     p = _params()
     assert B.csa_workspace_size(p, B.CSA_OP_ATTN_BWD) == 0          # scalar path: none
     assert B.csa_workspace_size(p, B.CSA_OP_ATTN_FWD) == 0
-    # bf16 H=64 D=512 backward: [scale*dS | P] (128 bf16) and a staged row gradient (512
-    # bf16) per (token, candidate slot) of a token chunk, slots = k_cap + W rounded up to 64
+    # bf16 H=64 D=512 backward: [scale*dS | P] (128 bf16) per (token, candidate slot) of a
+    # token chunk, slots = k_cap + W rounded up to 64.  Top-k 1024 of at most 250 visible
+    # rows: the rows' gradients are key-major products whose partial sums take at most
+    # (250 // 128 + 1) * (1000 // 256 + 1) + (1000 + 127) // 128 + 2 items of 256 KiB
     big = _params(heads=64, head_dim=512, dtype=B.CSA_BF16, topk=1024, topk_cap=1024,
-                  window=128, total_tokens=1000, max_seqlen=1000)
+                  window=128, total_tokens=1000, max_seqlen=1000, batch=1)
+    pds = 1000 * 1152 * 128 * 2
+    items = 2 * (3 + 1) + (1000 + 127) // 128 + 2
     n = B.csa_workspace_size(big, B.CSA_OP_ATTN_BWD)
-    assert 1000 * 1152 * (128 + 512) * 2 <= n <= 1000 * 1152 * (128 + 512) * 2 + 8 * 2**20
+    assert pds + items * 2**18 <= n <= pds + items * (2**18 + 64) + 2**20
     # the backward also takes any workspace down to one chunk of 16 queries
     m = B.csa_workspace_size_min(big, B.CSA_OP_ATTN_BWD)
+    items16 = 2 * (0 + 1) + (16 + 127) // 128 + 2
+    assert 16 * 1152 * 256 + items16 * 2**18 <= m <= 16 * 1152 * 256 + items16 * (2**18 + 64) + 2**20
+    # top-k 1024 of up to 25000 visible rows: one staged bf16 row gradient (512 values) per
+    # (token, slot) besides [scale*dS | P], summed per row through a CSR
+    sparse = _params(heads=64, head_dim=512, dtype=B.CSA_BF16, topk=1024, topk_cap=1024,
+                     window=128, total_tokens=1000, max_seqlen=100000, batch=1)
+    n = B.csa_workspace_size(sparse, B.CSA_OP_ATTN_BWD)
+    assert 1000 * 1152 * (128 + 512) * 2 <= n <= 1000 * 1152 * (128 + 512) * 2 + 8 * 2**20
+    m = B.csa_workspace_size_min(sparse, B.CSA_OP_ATTN_BWD)
     assert 16 * 1152 * (128 + 512) * 2 <= m <= 16 * 1152 * (128 + 512) * 2 + 2**20
     assert B.csa_workspace_size_min(p, B.CSA_OP_INDEXER_KL) == \
         B.csa_workspace_size(p, B.CSA_OP_INDEXER_KL)

@@ -62,6 +62,11 @@ CASES = {
                                                        teacher="none")),
     "rope_fp8_warmup_small": ("csa128k_warmup_fp8", dict(lengths=(1500,), total_tokens=1536,
                                                          topk=64, topk_cap=64, rope_dim=64)),
+    # top-k well below the visible rows (2600 // 4 = 650 > 6 x 64): the backward stages one
+    # row gradient per attended pair and sums them per row, instead of the key-major products
+    "csa_bf16_thd_staged": ("thd64k_csa_bf16", dict(lengths=(301, 515, 2600),
+                                                    total_tokens=3456, topk=32, topk_cap=64,
+                                                    draw=None)),
     # dense mode at ratio 4 (every visible compressed row + the window, no indexer) on the
     # matrix-core kernels
     "dense_bf16_thd_small": ("thd64k_csa_bf16", dict(mode="dense", teacher="none", idx_heads=0,
@@ -652,16 +657,45 @@ def test_attn_fwd(name):
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_attn_bwd(name):
+    _attn_bwd_check(name)
+
+
+def _repeat_rows(idx, cu, ratio):
+    """Every query with at least four selected rows lists its first row again in slot 2 and
+    its second row again in slot 3 (each listing is a candidate of its own)."""
+    idx = idx.copy()
+    n_rep = 0
+    for t in range(idx.shape[0]):
+        row = idx[t]
+        nc = int(np.argmax(row < 0)) if np.any(row < 0) else row.shape[0]
+        if nc >= 4:
+            row[2], row[3] = row[0], row[1]
+            n_rep += 1
+    assert n_rep > 0
+    return idx
+
+
+@pytest.mark.parametrize("name", ["csa_bf16_thd_small", "csa_bf16_thd_staged"])
+def test_attn_bwd_repeated_rows(name):
+    """A row listed twice in one query's idx row is two candidates: forward and backward
+    against the oracle on such idx rows (the key-major backward adds the later listings in
+    a separate pass)."""
+    _attn_bwd_check(name, lambda idx, host, w: _repeat_rows(idx, host["cu_seqlens"], w.ratio))
+
+
+def _attn_bwd_check(name, edit_idx=None):
     from long_context_compressed_amd import binding as B
     w, host, h64 = _case(name)
     if "dO" not in host:
         pytest.skip("forward-only workload")
-    _announce(name, "attn_bwd")
+    _announce(name, "attn_bwd" if edit_idx is None else "attn_bwd repeated rows")
     L = _layer(w, host, backward=True)
     cu = _cu(host)
     L.metadata(cu)
     dt = G.torch_dtype(w.dtype)
     kv_cmp_r, idx = _attn_inputs(w, host, h64)
+    if edit_idx is not None:
+        idx = edit_idx(idx, host, w)
     n = int(host["cu_seqlens"][-1])
     rows = np.arange(n)
     Oref, Lref = O.sparse_attn_fwd(h64["q"], kv_cmp_r, h64["kv"], _mode_idx(w, idx),
