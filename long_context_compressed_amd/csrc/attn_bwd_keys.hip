@@ -20,6 +20,8 @@
 // other listings when the planner's scan saw any.
 #include <math.h>
 
+#include <type_traits>
+
 #include "attn_bwd_keys.h"
 #include "attn_common.h"
 #include "csa_launch.h"
@@ -240,23 +242,30 @@ void k_attn_bwd_keys(KeysArgs a) {
     }
   };
   // k-step s (query s / 4, k-step s % 4) into buffer s % 3: wave w loads [q; dO] rows
-  // 4w .. 4w+3 of the k-step (1 KiB each, chunk-swizzled) and the dS|P columns of rows
-  // 16w .. 16w+15 (64 bytes each; lane l: row 16w + l/4, physical chunk l%4)
-  auto issue = [&](int s) {
-    const int tq = s >> 2, i = s & 3, buf = s % 3;
-    const int t = q0 + tq;
-    const uint16_t* src = (i < 2 ? a.q : a.dout) + ((int64_t)t * kH + 32 * (i & 1)) * kD;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int r = 4 * wave + jj;
-      dma16(src + (int64_t)r * kD + 8 * (lane ^ swz(r)), &Bs[buf][r][0]);
-    }
+  // 4w .. 4w+3 of the k-step (1 KiB each, chunk-swizzled; part jj < 4) and the dS|P columns of
+  // rows 16w .. 16w+15 (64 bytes each; lane l: row 16w + l/4, physical chunk l%4; part 4)
+  auto b_src = [&](int s) {
+    const int i = s & 3;
+    return (i < 2 ? a.q : a.dout) + ((int64_t)(q0 + (s >> 2)) * kH + 32 * (i & 1)) * kD;
+  };
+  auto issue_b = [&](int s, const uint16_t* src, int jj) {
+    const int r = 4 * wave + jj;
+    dma16(src + (int64_t)r * kD + 8 * (lane ^ swz(r)), &Bs[s % 3][r][0]);
+  };
+  auto a_src = [&](int s) {
+    const int tq = s >> 2, i = s & 3;
     const int sl = slot_s[tq & 1][16 * wave + (lane >> 2)];
     const int lc = (lane & 3) ^ (lane >> 4);
-    const uint16_t* as = (sl >= 0 && sl != 0x7fffffff)
-                             ? a.pds + ((int64_t)(t - a.t0) * a.n_slots + sl) * 128 + 32 * i + 8 * lc
-                             : a.zeros;
-    dma16(as, &As[buf][16 * wave][0]);
+    return (sl >= 0 && sl != 0x7fffffff)
+               ? a.pds + ((int64_t)(q0 + tq - a.t0) * a.n_slots + sl) * 128 + 32 * i + 8 * lc
+               : a.zeros;
+  };
+  auto issue_a = [&](int s, const uint16_t* src) { dma16(src, &As[s % 3][16 * wave][0]); };
+  auto issue = [&](int s) {
+    const uint16_t* src = b_src(s);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) issue_b(s, src, jj);
+    issue_a(s, a_src(s));
   };
 
   // B operand: [q; dO] rows 8g .. 8g+7 of the k-step at d = 64w + 16nt + c16, read transposed;
@@ -278,7 +287,10 @@ void k_attn_bwd_keys(KeysArgs a) {
   __syncthreads();
   issue(0);
   if (S > 1) issue(1);
-  for (int s = 0; s < S; ++s) {
+  // k-step s; MORE: k-step s + 2 exists (its loads are issued between this step's MFMAs, so
+  // that a load waiting for the address unit overlaps the MFMAs in flight)
+  auto body = [&](auto more_c, int s) {
+    constexpr bool kMore = decltype(more_c)::value;
     const int tq = s >> 2, i = s & 3, buf = s % 3;
     // every wave issues 5 loads per k-step: all but the next k-step's are done
     if (s + 1 < S) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
@@ -286,19 +298,28 @@ void k_attn_bwd_keys(KeysArgs a) {
     __syncthreads();
     if (i == 0 && tq + 1 < nq) prep0(tq + 1);
     if (i == 1 && tq + 1 < nq) prep1(tq + 1);
-    if (s + 2 < S) issue(s + 2);
-    bf16x8 bv[4];
+    const uint16_t* bsrc = kMore ? b_src(s + 2) : nullptr;
+    const uint16_t* asrc = kMore ? a_src(s + 2) : nullptr;
+    bf16x8 bv[4], av[8];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
       bv[nt] = join8(ld_tr(&Bs[buf][trr][troff + (lo_s ^ (16 * nt))]),
                      ld_tr(&Bs[buf][trr + 4][troff + (hi_s ^ (16 * nt))]));
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const bf16x8 av = ld16(&As[buf][16 * mt + c16][aoff]);
+    for (int mt = 0; mt < 8; ++mt) av[mt] = ld16(&As[buf][16 * mt + c16][aoff]);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma16(av, bv[nt], acc[mt][nt]);
+    for (int mt = 0; mt < 8; ++mt) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma16(av[mt], bv[nt], acc[mt][nt]);
+      if (kMore && mt < 4) issue_b(s + 2, bsrc, mt);
+      if (kMore && mt == 4) issue_a(s + 2, asrc);
     }
-  }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int s = 0;
+  for (; s + 2 < S; ++s) body(std::true_type(), s);
+  for (; s < S; ++s) body(std::false_type(), s);
   // rows 16mt + 4g + i, d = 64w + 16nt + c16
   float* dst = part >= 0 ? a.part + (int64_t)part * kKeys * kD
                          : (kind == kKindWin ? a.dkv : a.dkv_cmp) + (int64_t)key0 * kD;
