@@ -129,9 +129,14 @@ struct KeysArgs {
   float* dkv;
   int64_t n_slots, cap;
   int t0, nT, B, r, n_cap, W, k_cap, mode;
+  int D;    // width of the gradient rows (and of the partial rows)
+  int KC;   // coefficients per (query, slot): 128 (attention: dS | P) or 64 (indexer: E)
 };
 hipError_t launch_attn_bwd_keys(const KeysArgs& a, hipStream_t s);       // the work items
 hipError_t launch_attn_bwd_keys_sums(const KeysArgs& a, hipStream_t s);  // sums, reduction
+// Indexer-key gradients: dkI[j] += sum_t sum_h E[t, h, j] qI[t, h] (q = qI [T, 64, 128],
+// pds = E [nT, n_slots, 64] bf16, dkv_cmp = dkI, D = 128, KC = 64, W = 0).
+hipError_t launch_kl_keys_sums(const KeysArgs& a, hipStream_t s);
 #endif
 
 }  // namespace csa

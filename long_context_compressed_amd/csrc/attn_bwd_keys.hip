@@ -339,39 +339,47 @@ void k_attn_bwd_keys(KeysArgs a) {
 }
 
 // ---- blocks with several items: rows += sum of their partial slots, in slot order.
-// Work unit = (block record, 8 rows); lane: row 8u' + tid / 32, d = 16 (tid % 32) .. +15.
+// Work unit = (block record, 8 rows); lane: row 8u' + tid / 32, columns (tid % 32) D/32 ..
+// (D = 512 or 128: 4 or 1 float4 per lane).
 __global__ __launch_bounds__(256) void k_attn_bwd_keys_reduce(KeysArgs a) {
   const int n_units = a.counters[1] * 16;
+  const int nv4 = a.D / 128;
   for (int w = blockIdx.x; w < n_units; w += gridDim.x) {
     const int4 rd = a.red[w >> 4];
     const int key0 = rd.x, nkeys = rd.y & 0xff, kind = rd.y >> 8, pf = rd.z, np = rd.w;
-    const int row = 8 * (w & 15) + (threadIdx.x >> 5), d = 16 * (threadIdx.x & 31);
+    const int row = 8 * (w & 15) + (threadIdx.x >> 5), d = nv4 * 4 * (threadIdx.x & 31);
     if (row >= nkeys || pf < 0 || pf + np > a.cap) continue;
     float4 s[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) s[v] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int p = 0; p < np; ++p) {
       const float4* src =
-          reinterpret_cast<const float4*>(a.part + ((int64_t)(pf + p) * kKeys + row) * kD + d);
+          reinterpret_cast<const float4*>(a.part + ((int64_t)(pf + p) * kKeys + row) * a.D + d);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float4 x = src[v];
-        s[v].x += x.x; s[v].y += x.y; s[v].z += x.z; s[v].w += x.w;
+        if (v < nv4) {
+          const float4 x = src[v];
+          s[v].x += x.x; s[v].y += x.y; s[v].z += x.z; s[v].w += x.w;
+        }
       }
     }
     float4* o = reinterpret_cast<float4*>((kind == kKindWin ? a.dkv : a.dkv_cmp) +
-                                          (int64_t)(key0 + row) * kD + d);
+                                          (int64_t)(key0 + row) * a.D + d);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float4 x = o[v];
-      x.x += s[v].x; x.y += s[v].y; x.z += s[v].z; x.w += s[v].w;
-      o[v] = x;
+      if (v < nv4) {
+        float4 x = o[v];
+        x.x += s[v].x; x.y += s[v].y; x.z += s[v].z; x.w += s[v].w;
+        o[v] = x;
+      }
     }
   }
 }
 
 // ---- rows listed more than once in a query's idx row: the key-major pass took each such row
 // at its first slot; add the contributions of the later slots (rare; only when flagged).
+// Coefficient k of a slot multiplies row k of [q_t; dO_t] (KC = 128: the attention's dS | P)
+// or row k of qI_t (KC = 64: the indexer loss's E).
 __global__ __launch_bounds__(256) void k_attn_bwd_keys_dups(KeysArgs a) {
   __shared__ int32_t row_s[2048];
   __shared__ int32_t dup_s[2048];
@@ -396,20 +404,176 @@ __global__ __launch_bounds__(256) void k_attn_bwd_keys_dups(KeysArgs a) {
     }
     __syncthreads();
     const int nd = n_dup;
-    const uint16_t* qt = a.q + (int64_t)t * kH * kD;
-    const uint16_t* gt = a.dout + (int64_t)t * kH * kD;
+    const uint16_t* bt = a.q + (int64_t)t * 64 * a.D;
+    const uint16_t* gt = a.KC == 128 ? a.dout + (int64_t)t * 64 * a.D : nullptr;
     for (int e = 0; e < nd; ++e) {
       const int c = dup_s[e], j = row_s[c];
-      const uint16_t* ps = a.pds + ((int64_t)tl * a.n_slots + c) * 128;
-      for (int d = tid; d < kD; d += 256) {
+      const uint16_t* ps = a.pds + ((int64_t)tl * a.n_slots + c) * a.KC;
+      for (int d = tid; d < a.D; d += 256) {
         float s = 0.f;
-        for (int h = 0; h < kH; ++h)
-          s += bf2f(ps[h]) * bf2f(qt[h * kD + d]) + bf2f(ps[kH + h]) * bf2f(gt[h * kD + d]);
-        atomicAdd(a.dkv_cmp + (int64_t)j * kD + d, s);
+        for (int h = 0; h < 64; ++h) {
+          s += bf2f(ps[h]) * bf2f(bt[h * a.D + d]);
+          if (gt) s += bf2f(ps[64 + h]) * bf2f(gt[h * a.D + d]);
+        }
+        atomicAdd(a.dkv_cmp + (int64_t)j * a.D + d, s);
       }
     }
     __syncthreads();
   }
+}
+
+// ---- indexer-key gradients, one work item per workgroup: dkI[j] += sum_t E[t, :, j] qI_t for
+// the item's 128 rows and queries (the same items, slot maps and partial slots as the
+// attention's compressed rows, no window); per query two k-steps of 32 heads: the qI rows
+// 32i .. 32i+31 (256 bytes each) and the rows' 64-byte E pieces, three k-steps in flight.
+// 4 waves, wave w owns d = 32w .. 32w+31 of all 128 rows.
+template <int KI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_kl_keys(KeysArgs a) {
+  constexpr int kDI = 128;
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[3][32][kDI];    // qI k-step rows
+  __shared__ __attribute__((aligned(16))) uint16_t As[3][kKeys][32];  // E of the rows
+  __shared__ __attribute__((aligned(16))) int32_t idx_s[KI > 0 ? 256 * KI : 1];
+  __shared__ int32_t slot_s[2][kKeys];
+  __shared__ int32_t nc_s[kCq];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int n_items = a.counters[0];
+  const int per = (n_items + 7) >> 3;
+  const int jb = (int)(blockIdx.x >> 3);
+  if (jb >= per) return;
+  const int item = (int)(blockIdx.x & 7) * per + jb;
+  if (item >= n_items) return;
+  const int4 it = a.items[item];
+  const int key0 = it.x, nkeys = it.y & 0xff, kind = it.y >> 8, q0 = it.z, nq = it.w;
+  const int part = a.item_part[item];
+  if (part >= a.cap || nq <= 0 || nq > kCq) return;
+  TokenInfo ti;
+  token_info_wave(a.cu, a.B, q0, ti, a.cu_cmp);
+  const int s0 = ti.start, c0 = ti.c0;
+  for (int i = tid; i < nq; i += 256) nc_s[i] = a.nc[q0 + i];
+
+  auto prep0 = [&](int tq) {
+    if (KI > 0 && kind == kKindSel) {
+      const int32_t* row = a.idx + (int64_t)(q0 + tq) * a.k_cap;
+#pragma unroll
+      for (int e = 0; e < KI; ++e) {
+        const int base = 64 * (4 * e + wave);
+        if (base < a.k_cap) dma4(row + base + lane, &idx_s[base]);
+      }
+      if (tid < kKeys) slot_s[tq & 1][tid] = 0x7fffffff;
+    }
+  };
+  auto prep1 = [&](int tq) {
+    const int t = q0 + tq, p = t - s0, nct = nc_s[tq];
+    if (kind == kKindSel) {
+      if (KI > 0) {
+        for (int c = tid; c < nct; c += 256) {
+          const int j = idx_s[c] - key0;
+          if (j >= 0 && j < nkeys) {
+            const int old = atomicMin(&slot_s[tq & 1][j], c);
+            if (old != 0x7fffffff) a.counters[2] = 1;   // a row listed twice
+          }
+        }
+      }
+    } else if (tid < kKeys) {
+      int s = -1;
+      if (tid < nkeys) {
+        const int jl = key0 - c0 + tid, nv = min((p + 1) / a.r, a.n_cap);
+        if (jl < nv) s = jl;
+      }
+      slot_s[tq & 1][tid] = s;
+    }
+  };
+  // k-step s (query s / 2, heads 32 (s % 2) ..) into buffer s % 3.  Parts 0, 1: qI rows
+  // 8w + 4jj .. +3 (lane l: row + l/16, physical chunk l%16); parts 2, 3: the 64-byte E pieces
+  // of rows 32w + 16jj .. +15 (lane l: row + l/4, physical chunk l%4)
+  auto b_src = [&](int s) { return a.q + ((int64_t)(q0 + (s >> 1)) * 64 + 32 * (s & 1)) * kDI; };
+  auto issue_b = [&](int s, const uint16_t* src, int jj) {
+    const int r0 = 8 * wave + 4 * jj, r = r0 + (lane >> 4);
+    dma16(src + (int64_t)r * kDI + 8 * ((lane & 15) ^ swz(r)), &Bs[s % 3][r0][0]);
+  };
+  auto a_src = [&](int s, int jj) {
+    const int tq = s >> 1, i = s & 1;
+    const int sl = slot_s[tq & 1][32 * wave + 16 * jj + (lane >> 2)];
+    const int lc = (lane & 3) ^ (lane >> 4);
+    return (sl >= 0 && sl != 0x7fffffff)
+               ? a.pds + ((int64_t)(q0 + tq - a.t0) * a.n_slots + sl) * 64 + 32 * i + 8 * lc
+               : a.zeros;
+  };
+  auto issue_a = [&](int s, const uint16_t* src, int jj) {
+    dma16(src, &As[s % 3][32 * wave + 16 * jj][0]);
+  };
+  auto issue = [&](int s) {
+    const uint16_t* src = b_src(s);
+    issue_b(s, src, 0);
+    issue_b(s, src, 1);
+    issue_a(s, a_src(s, 0), 0);
+    issue_a(s, a_src(s, 1), 1);
+  };
+
+  const int trr = 8 * g + (c16 >> 2), tre = (c16 & 3) >> 1, troff = 4 * (c16 & 1);
+  const int lo_s = 8 * ((4 * wave + tre) ^ swz(trr)), hi_s = 8 * ((4 * wave + tre) ^ swz(trr + 4));
+  const int aoff = 8 * (g ^ (c16 >> 2));
+  f32x4 acc[8][2];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // The loads of k-step s + 2 are issued in k-step s, so the slot map of query tq + 2 is
+  // formed in query tq's k-steps (idx row loaded in the first, mapped in the second) and
+  // first read in query tq + 1's first k-step: maps of queries 0 and 1 before the loop.
+  const int S = 2 * nq;
+  for (int q = 0; q < 2 && q < nq; ++q) {
+    prep0(q);
+    wait_vmem();
+    __syncthreads();
+    prep1(q);
+    __syncthreads();
+  }
+  issue(0);
+  if (S > 1) issue(1);
+  auto body = [&](auto more_c, int s) {
+    constexpr bool kMore = decltype(more_c)::value;
+    const int tq = s >> 1, i = s & 1, buf = s % 3;
+    // every wave issues 4 loads per k-step (an idx row's loads come before them): all but
+    // the next k-step's are done
+    if (s + 1 < S) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else wait_vmem();
+    __syncthreads();
+    if (i == 0 && tq + 2 < nq) prep0(tq + 2);
+    if (i == 1 && tq + 2 < nq) prep1(tq + 2);
+    if (kMore) issue(s + 2);
+    bf16x8 bv[2], av[8];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      bv[nt] = join8(ld_tr(&Bs[buf][trr][troff + (lo_s ^ (16 * nt))]),
+                     ld_tr(&Bs[buf][trr + 4][troff + (hi_s ^ (16 * nt))]));
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) av[mt] = ld16(&As[buf][16 * mt + c16][aoff]);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16(av[mt], bv[nt], acc[mt][nt]);
+    }
+  };
+  int s = 0;
+  for (; s + 2 < S; ++s) body(std::true_type(), s);
+  for (; s < S; ++s) body(std::false_type(), s);
+  // rows 16mt + 4g + i, d = 32w + 16nt + c16
+  float* dst = part >= 0 ? a.part + (int64_t)part * kKeys * kDI : a.dkv_cmp + (int64_t)key0 * kDI;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * mt + 4 * g + i;
+      if (row >= nkeys) continue;
+      float* o = dst + (int64_t)row * kDI + 32 * wave + c16;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        if (part >= 0) o[16 * nt] = acc[mt][nt][i];
+        else o[16 * nt] += acc[mt][nt][i];
+      }
+    }
 }
 
 hipError_t launch_attn_bwd_keys(const KeysArgs& a, hipStream_t s) {
@@ -425,6 +589,20 @@ hipError_t launch_attn_bwd_keys_sums(const KeysArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_attn_bwd_keys<2>, dim3((unsigned)grid), dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL(k_attn_bwd_keys<4>, dim3((unsigned)grid), dim3(512), 0, s, a);
+  const int64_t rgrid = a.cap * 16 < 2048 ? a.cap * 16 : 2048;
+  hipLaunchKernelGGL(k_attn_bwd_keys_reduce, dim3((unsigned)(rgrid > 0 ? rgrid : 1)), dim3(256), 0, s, a);
+  if (a.mode == 0) hipLaunchKernelGGL(k_attn_bwd_keys_dups, dim3(1024), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kl_keys_sums(const KeysArgs& a, hipStream_t s) {
+  const int64_t grid = ((a.cap + 7) / 8) * 8;
+  if (a.mode != 0)
+    hipLaunchKernelGGL(k_kl_keys<0>, dim3((unsigned)grid), dim3(256), 0, s, a);
+  else if (a.k_cap <= 1024)
+    hipLaunchKernelGGL(k_kl_keys<4>, dim3((unsigned)grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_kl_keys<8>, dim3((unsigned)grid), dim3(256), 0, s, a);
   const int64_t rgrid = a.cap * 16 < 2048 ? a.cap * 16 : 2048;
   hipLaunchKernelGGL(k_attn_bwd_keys_reduce, dim3((unsigned)(rgrid > 0 ? rgrid : 1)), dim3(256), 0, s, a);
   if (a.mode == 0) hipLaunchKernelGGL(k_attn_bwd_keys_dups, dim3(1024), dim3(256), 0, s, a);

@@ -741,6 +741,8 @@ hipError_t launch_attn_bwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s
     ka.W = sh.W;
     ka.k_cap = sh.k_cap;
     ka.mode = sh.mode;
+    ka.D = kD;
+    ka.KC = 128;
   }
   for (int64_t t0 = 0; t0 < sh.T; t0 += pl.chunk) {
     b.t0 = (int)t0;

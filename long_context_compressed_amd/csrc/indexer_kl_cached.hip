@@ -18,15 +18,15 @@
 //     rows gathered into swizzled LDS by direct global->LDS loads one block ahead);
 //   * E = g w 1[z>0], dw += g relu(z); dqI += E kI (E reused from registers as the A
 //     operand, key rows read transposed);
-//   * dkI^T = qI^T E^T over all 64 heads (both operands read transposed from LDS) is
-//     written as one bf16 row per (query, slot) to a staging buffer; a CSR of the
-//     compressed rows then sums each row's staged vectors in fp32.  Plain stores and an
-//     owner-side sum replace fp32 atomics, which run at a fraction of the store bandwidth.
+//   * E (bf16, 64 heads) is written per (query, slot), 128 bytes; the key gradient
+//     dkI[j] = sum_t sum_h E[t,h,j] qI[t,h] is then formed key-major (k_kl_keys: blocks of
+//     128 compressed rows against the queries that see them, on MFMA, sums in registers),
+//     with no per-pair key-gradient vector and no fp32 atomics.
 #include <math.h>
 
 #include "attn_common.h"
+#include "attn_bwd_keys.h"
 #include "csa_launch.h"
-#include "csr_build.h"
 
 #pragma clang diagnostic ignored "-Winline-asm"
 
@@ -40,8 +40,8 @@ constexpr int kHT = 64;     // teacher heads
 constexpr int kHI = 64;     // indexer heads
 constexpr int kDI = 128;    // indexer width
 constexpr int kNB = 64;     // slots per block
-constexpr int kES = 72;     // bf16 row stride of the E tile
-constexpr int64_t kStageBudget = 16ll << 30;   // bytes of staging per chunk
+constexpr int kEST = 72;    // bf16 row stride of the E tile (slot-major, 64 heads + pad)
+constexpr int64_t kStageBudget = 16ll << 30;   // bytes of E per chunk
 constexpr int kIdxLds = 2048;                   // idx entries of a query staged in LDS
 
 struct KlcArgs {
@@ -60,7 +60,7 @@ struct KlcArgs {
   float* kl;
   float* dqI;
   float* dw;
-  uint16_t* stage;          // [chunk][k_slots][128] bf16
+  uint16_t* es;             // [chunk][k_slots][64] bf16: E of every (query, slot)
   int32_t* nc;              // [T] candidate count
   int64_t k_slots;
   int t0, nT;
@@ -68,8 +68,8 @@ struct KlcArgs {
 };
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// at most 4 vector memory operations outstanding (they complete in issue order)
-__device__ __forceinline__ void wait_vmem_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
+// at most 2 vector memory operations outstanding (they complete in issue order)
+__device__ __forceinline__ void wait_vmem_2() { asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); }
 
 __device__ __forceinline__ void dma_rows16(const void* src, const void* lds) {
   const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
@@ -116,8 +116,7 @@ void k_kl_cached(KlcArgs a) {
   __shared__ int32_t idx_s[IDX_LDS ? kIdxLds : 1];
   __shared__ float sc_s[IDX_LDS ? kIdxLds : 1];   // student scores of the slots
   __shared__ __attribute__((aligned(16))) uint16_t KIt[2][kNB][kDI];   // swizzled 256-byte rows
-  __shared__ __attribute__((aligned(16))) uint16_t QIt[kHI][kDI];      // swizzled 256-byte rows
-  __shared__ __attribute__((aligned(16))) uint16_t Es[kHI][kES];
+  __shared__ __attribute__((aligned(16))) uint16_t EsT[kNB][kEST];
   __shared__ float Pp[4][kNB];
   __shared__ float gw_s[4][kNB];
   __shared__ float lse2_s[kHT];
@@ -169,8 +168,7 @@ void k_kl_cached(KlcArgs a) {
   };
 
   // ---- loads of the query's resident operands, issued before the student scores so that
-  // their latencies overlap: qI^T B operand of z, the qI tile for dkI (into LDS), weights,
-  // teacher lse
+  // their latencies overlap: qI^T B operand of z, weights, teacher lse
   bf16x8 qib[2][4];   // heads 32hh + 16nt + c16, d = 32ks + 8g .. +7
   float wv[2];
   if (a.grads) {
@@ -180,15 +178,6 @@ void k_kl_cached(KlcArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) qib[nt][ks] = ld16(src + 32 * ks);
       wv[nt] = a.w[(int64_t)t * kHI + 32 * hh + 16 * nt + c16];
-    }
-    // QIt[h][chunk ^ swz(h)] (16-byte chunks of 256-byte rows) by direct loads: wave w
-    // fills rows 16w .. 16w+15, four per instruction (lane l: physical chunk l % 16 of row
-    // 4i + l / 16); complete at the wait before the block loop
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 16 * wave + 4 * i + (lane >> 4);
-      dma_rows16(a.qI + ((int64_t)t * kHI + h) * kDI + 8 * ((lane & 15) ^ swz(h)),
-                 &QIt[16 * wave + 4 * i][0]);
     }
   }
   const float tlse_v = (a.tlse && tid < kHT) ? a.tlse[(int64_t)t * kHT + tid] : 0.f;
@@ -307,9 +296,6 @@ void k_kl_cached(KlcArgs a) {
   //  2 nd + (c16 & 3) / 2, element 4 (c16 & 1) within it; row bits 0-3 = 4g + c16/4 (mod 16)
   const int trr = 4 * g + (c16 >> 2);
   const int tre = (c16 & 3) >> 1, troff = 4 * (c16 & 1);
-  //  dkI^T operands: qI^T A (rows = heads 32ks + 8g + c16/4 (+4), chunk 2 md + e),
-  //  E B (rows = heads, columns = slots 16 wave + 4 (c16 & 3))
-  const int rq_lo = 8 * g + (c16 >> 2);
 
   int rid_cur = row_of(0), rid_nxt = row_of(1);
   float sc_cur = score_of(0), sc_nxt = score_of(1);
@@ -358,8 +344,8 @@ void k_kl_cached(KlcArgs a) {
     }
     // key rows of this block, issued during the previous block; the only younger memory
     // operations are that block's logit loads (already consumed above) and, if this wave
-    // staged any slot of it, its 4 dkI row stores, which may stay in flight
-    if (IDX_LDS && a.grads && b > 0 && kNB * (b - 1) + 16 * wave < n_c) wait_vmem_4();
+    // wrote E of any slot of it, its 2 E stores, which may stay in flight
+    if (IDX_LDS && a.grads && b > 0 && kNB * (b - 1) + 16 * wave < n_c) wait_vmem_2();
     else wait_vmem();
     __syncthreads();
     // the other key buffer was last read before the previous block's second barrier
@@ -398,7 +384,7 @@ void k_kl_cached(KlcArgs a) {
           z[mt][1] = mfma16(av, qib[1][ks], z[mt][1]);
         }
       }
-      // ---- E = g w 1[z > 0]; dw += g relu(z); E (bf16) to LDS as [head][slot]
+      // ---- E = g w 1[z > 0]; dw += g relu(z); E (bf16) to LDS as [slot][head]
       uint32_t ew[2][4];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -414,8 +400,12 @@ void k_kl_cached(KlcArgs a) {
           }
           ew[nt][2 * mt] = pack_bf16x2(e[0], e[1]);
           ew[nt][2 * mt + 1] = pack_bf16x2(e[2], e[3]);
-          *reinterpret_cast<uint2*>(&Es[32 * hh + 16 * nt + c16][32 * ch + 16 * mt + 4 * g]) =
-              make_uint2(ew[nt][2 * mt], ew[nt][2 * mt + 1]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t wd = ew[nt][2 * mt + (i >> 1)];
+            EsT[32 * ch + 16 * mt + 4 * g + i][32 * hh + 16 * nt + c16] =
+                (uint16_t)((i & 1) ? (wd >> 16) : (wd & 0xffffu));
+          }
         }
       }
       // ---- dqI[h][d] += sum_c E[h][c] kI[c][d]: k-slot order {4g..4g+3, 16+4g..16+4g+3}
@@ -437,43 +427,15 @@ void k_kl_cached(KlcArgs a) {
     }
     __syncthreads();
     if (a.grads) {
-      // ---- dkI^T[d][c] = sum_h qI[h][d] E[h][c]: wave w takes slots 16w .. 16w+15, all d
-      f32x4 dk[8];
-#pragma unroll
-      for (int md = 0; md < 8; ++md) dk[md] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int r_lo = 32 * ks + rq_lo, r_hi = r_lo + 4;
-        const bf16x8 eb = join8(ld_tr(&Es[r_lo][16 * wave + 4 * (c16 & 3)]),
-                                ld_tr(&Es[r_hi][16 * wave + 4 * (c16 & 3)]));
-#pragma unroll
-        for (int md = 0; md < 8; ++md) {
-          const int kq = 2 * md + tre;
-          const bf16x8 qa = join8(ld_tr(&QIt[r_lo][8 * (kq ^ swz(r_lo)) + troff]),
-                                  ld_tr(&QIt[r_hi][8 * (kq ^ swz(r_hi)) + troff]));
-          dk[md] = mfma16(qa, eb, dk[md]);
-        }
-      }
-      // lane: slot 16 wave + c16, d = 16 md + 4g .. +3 -> bf16 staging row of (t, slot).
-      // Lanes g and g ^ 1 (same slot) swap half of each md pair, so that every lane stores
-      // 8 consecutive d (16 bytes): even g keeps d 32m + 4g .. +3 of md = 2m and takes its
-      // neighbour's next four; odd g keeps d 32m + 16 + 4g .. +3 of md = 2m + 1 and takes the
-      // four before them.
-      const int slot = kNB * b + 16 * wave + c16;
-      const bool odd = g & 1;
-      uint16_t* dst = a.stage + ((int64_t)tl * a.k_slots + slot) * kDI;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint2 e = make_uint2(pack_bf16x2(dk[2 * m][0], dk[2 * m][1]),
-                                   pack_bf16x2(dk[2 * m][2], dk[2 * m][3]));
-        const uint2 o = make_uint2(pack_bf16x2(dk[2 * m + 1][0], dk[2 * m + 1][1]),
-                                   pack_bf16x2(dk[2 * m + 1][2], dk[2 * m + 1][3]));
-        const uint2 give = odd ? e : o;
-        const uint2 got = make_uint2((uint32_t)__shfl_xor((int)give.x, 16, 64),
-                                     (uint32_t)__shfl_xor((int)give.y, 16, 64));
-        const uint4 v = odd ? make_uint4(got.x, got.y, o.x, o.y) : make_uint4(e.x, e.y, got.x, got.y);
-        const int d0 = odd ? 32 * m + 16 + 4 * (g - 1) : 32 * m + 4 * g;
-        if (slot < n_c) *reinterpret_cast<uint4*>(dst + d0) = v;
+      // ---- E rows of the block's slots (thread: slot tid / 4, heads 16 (tid % 4) .. +15):
+      // two 16-byte stores from the slot-major LDS tile
+      const int sl = tid >> 2, hq4 = 16 * (tid & 3), slot = kNB * b + sl;
+      if (slot < n_c) {
+        const uint4 e0 = *reinterpret_cast<const uint4*>(&EsT[sl][hq4]);
+        const uint4 e1 = *reinterpret_cast<const uint4*>(&EsT[sl][hq4 + 8]);
+        uint4* dst = reinterpret_cast<uint4*>(a.es + ((int64_t)tl * a.k_slots + slot) * kHI + hq4);
+        dst[0] = e0;
+        dst[1] = e1;
       }
     }
     rid_cur = rid_nxt;
@@ -525,152 +487,52 @@ void k_kl_cached(KlcArgs a) {
   for (int e = tid; e < kHI * kDI / 4; e += 256) dst[e] = src[e];
 }
 
-// ---- CSR of the compressed rows over a chunk's (query, slot) pairs, and the owner sums
+// ---- workspace plan and launch
 namespace {
-
-struct CsrArgs {
-  const int32_t* idx;
-  const int32_t* cu;
-  const int32_t* cu_cmp;
-  const int32_t* nc;
-  int32_t* cnt;
-  int32_t* off;
-  int32_t* cur;
-  int32_t* list;
-  const uint16_t* stage;
-  float* dst;
-  int64_t k_slots;
-  int t0, nT, B, r, n_cap, k_cap, n_rows;
-};
-
-template <bool FILL>
-__global__ __launch_bounds__(256) void k_csr_pairs(CsrArgs c) {
-  CsrBuild g;
-  g.idx = c.idx; g.cu = c.cu; g.cu_cmp = c.cu_cmp; g.nc = c.nc; g.cnt = c.cnt; g.cur = c.cur;
-  g.list = c.list; g.slots = c.k_slots; g.t0 = c.t0; g.nT = c.nT; g.B = c.B; g.r = c.r;
-  g.n_cap = c.n_cap; g.k_cap = c.k_cap;
-  csr_group_pass<FILL>(g);
-}
 
 __global__ __launch_bounds__(256) void k_fill_zero_i32(int32_t* __restrict__ p, int n) {
   for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
 }
 
-// exclusive scan of cnt into off and cur (one workgroup of 1024 lanes)
-__global__ __launch_bounds__(1024) void k_csr_scan(CsrArgs c) {
-  __shared__ int part[1024];
-  const int n = c.n_rows;
-  const int per = (n + 1023) / 1024;
-  const int lo = threadIdx.x * per, hi = min(n, lo + per);
-  int s = 0;
-  for (int i = lo; i < hi; ++i) s += c.cnt[i];
-  part[threadIdx.x] = s;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  int run = part[threadIdx.x] - s;
-  for (int i = lo; i < hi; ++i) {
-    c.off[i] = run;
-    c.cur[i] = run;
-    run += c.cnt[i];
-  }
-}
-
-// dst[j, :] += sum of the staged bf16 rows listed for j.  One workgroup per row; wave w takes
-// list entries 64w .. 64w + 63, then 64w + 256 .., each batch read with one coalesced load
-// and broadcast from registers.  Sixteen lanes cover one 256-byte row (16 bytes each), so
-// one load instruction reads four rows and eight are kept in flight (32 rows per wave).
-__global__ __launch_bounds__(256) void k_csr_reduce(CsrArgs c) {
-  __shared__ float part[4][kDI];
-  const int j = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = c.cnt[j];
-  if (n == 0) return;
-  const int32_t* lst = c.list + c.off[j];
-  const int sub = lane >> 4, ch = lane & 15;   // row within a group of four, 16-byte chunk
-  float acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int base = 64 * wave; base < n; base += 256) {
-    const int my = base + lane < n ? lst[base + lane] : 0;
-    const int m = min(64, n - base);
-    for (int k = 0; k < m; k += 32) {
-      uint4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int x = k + 4 * u + sub;   // < 64
-        const int e = __shfl(my, x, 64);
-        v[u] = x < m ? *reinterpret_cast<const uint4*>(c.stage + (int64_t)e * kDI + 8 * ch)
-                     : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        float f[8];
-        load8(reinterpret_cast<const uint16_t*>(&v[u]), f);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += f[i];
-      }
-    }
-  }
-  // lanes of the same chunk hold partial sums of the same eight elements
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    acc[i] += __shfl_xor(acc[i], 16, 64);
-    acc[i] += __shfl_xor(acc[i], 32, 64);
-  }
-  if (sub == 0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) part[wave][8 * ch + i] = acc[i];
-  }
-  __syncthreads();
-  if (wave == 0 && lane < kDI / 4) {
-    float4* d = reinterpret_cast<float4*>(c.dst + (int64_t)j * kDI + 4 * lane);
-    float4 o = *d;
-    float s4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int x = 4 * lane + i;
-      s4[i] = (part[0][x] + part[1][x]) + (part[2][x] + part[3][x]);
-    }
-    o.x += s4[0]; o.y += s4[1]; o.z += s4[2]; o.w += s4[3];
-    *d = o;
-  }
-}
-
 struct KlcPlan {
-  int64_t k_slots, chunk, rows_cap;
-  size_t off_stage, off_nc, off_cnt, off_off, off_cur, off_list, total;
+  int64_t k_slots, chunk, cap;
+  size_t off_es, off_nc, off_cnt, off_items, off_ipart, off_red, off_part, total;
 };
 
 bool klc_handles(const Shape& sh) {
-  return sh.H == kHT && sh.HI == kHI && sh.dI == kDI && sh.idx_dtype == 1 && sh.r > 0 &&
-         ((sh.teacher == 1 && sh.mode == 0) || (sh.teacher == 2 && sh.mode == 1));
+  if (!(sh.H == kHT && sh.HI == kHI && sh.dI == kDI && sh.idx_dtype == 1 && sh.r > 0 &&
+        ((sh.teacher == 1 && sh.mode == 0) || (sh.teacher == 2 && sh.mode == 1))))
+    return false;
+  // the key-major key gradients: idx rows held in LDS, per-sample block tables
+  const int64_t n_cap = sh.max_seqlen / sh.r;
+  return (sh.mode == 1 || sh.k_cap <= 2048) && n_cap / keys::kKeys + 1 <= 2048;
 }
 
-KlcPlan klc_plan(const Shape& sh) {
+KlcPlan klc_layout(const Shape& sh, int64_t chunk) {
   KlcPlan p;
   p.k_slots = sh.mode == 0 ? sh.k_cap : sh.max_seqlen / sh.r;
   if (p.k_slots < 1) p.k_slots = 1;
-  const int64_t per_tok = p.k_slots * kDI * 2;
-  int64_t ch = kStageBudget / per_tok;
-  ch = (ch / (8 * kChunk)) * (8 * kChunk);
-  if (ch < 8 * kChunk) ch = 8 * kChunk;
-  p.chunk = ch < sh.T ? ch : sh.T;
-  p.rows_cap = sh.T / sh.r + 1;
+  p.chunk = chunk;
+  p.cap = keys::item_cap(sh.mode, sh.B, (int)chunk, sh.max_seqlen / sh.r, 0);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t o = 0;
-  p.off_stage = o; o = al(o + (size_t)p.chunk * p.k_slots * kDI * 2);
+  p.off_es = o;    o = al(o + (size_t)p.chunk * p.k_slots * kHI * 2);
   p.off_nc = o;    o = al(o + (size_t)sh.T * 4);
-  p.off_cnt = o;   o = al(o + (size_t)p.rows_cap * 4);
-  p.off_off = o;   o = al(o + (size_t)p.rows_cap * 4);
-  p.off_cur = o;   o = al(o + (size_t)p.rows_cap * 4);
-  p.off_list = o;  o = al(o + (size_t)p.chunk * p.k_slots * 4);
+  p.off_cnt = o;   o = al(o + 128 * 4);   // 64 counters, then 256 zero bytes
+  p.off_items = o; o = al(o + (size_t)p.cap * 16);
+  p.off_ipart = o; o = al(o + (size_t)p.cap * 4);
+  p.off_red = o;   o = al(o + (size_t)p.cap * 16);
+  p.off_part = o;  o = al(o + (size_t)p.cap * keys::kKeys * kDI * 4);
   p.total = o;
   return p;
+}
+
+KlcPlan klc_plan(const Shape& sh) {
+  const int64_t per_tok = (sh.mode == 0 ? sh.k_cap : sh.max_seqlen / sh.r) * kHI * 2;
+  int64_t ch = kStageBudget / (per_tok > 0 ? per_tok : 1);
+  ch = (ch / (8 * kChunk)) * (8 * kChunk);
+  if (ch < 8 * kChunk) ch = 8 * kChunk;
+  return klc_layout(sh, ch < sh.T ? ch : (sh.T > 0 ? sh.T : 1));
 }
 
 }  // namespace
@@ -684,6 +546,7 @@ hipError_t launch_indexer_kl_cached(const Shape& sh, const KlIO& io, hipStream_t
   if (!io.t_logits || !klc_handles(sh)) return hipSuccess;
   *handled = true;
   const KlcPlan pl = klc_plan(sh);
+  if (pl.total > io.ws_bytes) return hipErrorInvalidValue;   // host-checked
   char* ws = (char*)io.ws;
   KlcArgs a;
   a.tl = io.t_logits;
@@ -701,7 +564,7 @@ hipError_t launch_indexer_kl_cached(const Shape& sh, const KlIO& io, hipStream_t
   a.kl = io.kl;
   a.dqI = io.dqI;
   a.dw = io.dw;
-  a.stage = (uint16_t*)(ws + pl.off_stage);
+  a.es = (uint16_t*)(ws + pl.off_es);
   a.nc = (int32_t*)(ws + pl.off_nc);
   a.k_slots = pl.k_slots;
   a.B = sh.B;
@@ -710,36 +573,45 @@ hipError_t launch_indexer_kl_cached(const Shape& sh, const KlIO& io, hipStream_t
   a.n_cap = sh.max_seqlen / sh.r;
   a.k_cap = sh.k_cap;
   a.grads = io.dqI != nullptr;
-  CsrArgs c;
-  c.idx = a.idx;
-  c.cu = sh.cu;
-  c.cu_cmp = sh.cu_cmp;
-  c.nc = a.nc;
-  c.cnt = (int32_t*)(ws + pl.off_cnt);
-  c.off = (int32_t*)(ws + pl.off_off);
-  c.cur = (int32_t*)(ws + pl.off_cur);
-  c.list = (int32_t*)(ws + pl.off_list);
-  c.stage = a.stage;
-  c.dst = io.dkI;
-  c.k_slots = pl.k_slots;
-  c.B = sh.B;
-  c.r = sh.r;
-  c.n_cap = a.n_cap;
-  c.k_cap = sh.k_cap;
-  c.n_rows = (int)pl.rows_cap;
+  KeysArgs k = {};
+  k.q = a.qI;
+  k.pds = a.es;
+  k.idx = a.idx;
+  k.nc = a.nc;
+  k.cu = sh.cu;
+  k.cu_cmp = sh.cu_cmp;
+  k.counters = (int32_t*)(ws + pl.off_cnt);
+  k.zeros = (const uint16_t*)(ws + pl.off_cnt + 64 * 4);
+  k.items = (int4*)(ws + pl.off_items);
+  k.item_part = (int32_t*)(ws + pl.off_ipart);
+  k.red = (int4*)(ws + pl.off_red);
+  k.part = (float*)(ws + pl.off_part);
+  k.dkv_cmp = io.dkI;
+  k.n_slots = pl.k_slots;
+  k.cap = pl.cap;
+  k.B = sh.B;
+  k.r = sh.r;
+  k.n_cap = a.n_cap;
+  k.W = 0;
+  k.k_cap = sh.k_cap;
+  k.mode = sh.mode;
+  k.D = kDI;
+  k.KC = kHI;
   for (int64_t t0 = 0; t0 < sh.T; t0 += pl.chunk) {
-    a.t0 = c.t0 = (int)t0;
-    a.nT = c.nT = (int)(sh.T - t0 < pl.chunk ? sh.T - t0 : pl.chunk);
+    a.t0 = k.t0 = (int)t0;
+    a.nT = k.nT = (int)(sh.T - t0 < pl.chunk ? sh.T - t0 : pl.chunk);
+    if (a.grads) {
+      hipLaunchKernelGGL(k_fill_zero_i32, dim3(1), dim3(256), 0, s, k.counters, 128);
+      hipError_t e = launch_attn_bwd_keys(k, s);
+      if (e != hipSuccess) return e;
+    }
     if (sh.k_cap <= kIdxLds)
       hipLaunchKernelGGL(k_kl_cached<true>, dim3((unsigned)token_grid(a.nT)), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL(k_kl_cached<false>, dim3((unsigned)token_grid(a.nT)), dim3(256), 0, s, a);
     if (a.grads) {
-      hipLaunchKernelGGL(k_fill_zero_i32, dim3(64), dim3(256), 0, s, c.cnt, c.n_rows);
-      hipLaunchKernelGGL(k_csr_pairs<false>, dim3(csr_grid(c.nT)), dim3(256), 0, s, c);
-      hipLaunchKernelGGL(k_csr_scan, dim3(1), dim3(1024), 0, s, c);
-      hipLaunchKernelGGL(k_csr_pairs<true>, dim3(csr_grid(c.nT)), dim3(256), 0, s, c);
-      hipLaunchKernelGGL(k_csr_reduce, dim3(c.n_rows), dim3(256), 0, s, c);
+      hipError_t e = launch_kl_keys_sums(k, s);
+      if (e != hipSuccess) return e;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
