@@ -17,13 +17,14 @@
 //                  ahead) and feeds all 4 queries.  Pass 1: per-head online log-sum-exp
 //                  of the teacher and the student log-sum-exp; pass 2: P (head mean), Q,
 //                  KL_t and g = grad_scale (Q - P), written to the workspace.
-//   k_kld_queries  the same 4-query groups, one query per wave with its qI resident; each
-//                  64-key block of kI is staged once into LDS for the 4 queries; z^T, E =
-//                  g w 1[z > 0] (kept in registers as the A operand), dw and dqI = E kI.
-//   k_kld_keys     one workgroup per (4 key blocks, query range), one block per wave; each
-//                  query's qI tile is staged once into LDS for the 4 blocks; z, E and
-//                  dkI += E^T qI accumulate in registers over the range, one fp32 atomic add
-//                  per key element at the end.
+//   k_kld_queries  the same 4-query groups, two waves per query (32 indexer heads each)
+//                  with its qI resident; each 64-key block of kI is staged once into LDS for
+//                  the 4 queries; z^T, E = g w 1[z > 0] (kept in registers as the A operand),
+//                  dw and dqI = E kI.
+//   k_kld_keys     one workgroup per (4 key blocks, query range), two waves per block (32
+//                  indexer heads each); each query's qI tile is staged once into LDS for the 4
+//                  blocks; z, E and dkI += E^T qI accumulate in registers over the range, one
+//                  fp32 atomic add per key element and head half at the end.
 // Queries are processed in chunks of kChunkRows (the workspace holds g for one chunk).
 #include <math.h>
 
@@ -335,10 +336,12 @@ void k_kld_teacher(KldArgs a) {
 // ---------------------------------------------------------------------------- dkI
 // Workgroup (x, y): 4 key blocks of 64 rows of one sample (regular groups start at
 // 256-aligned rows and stop at the sample end; group tc_groups + b holds the first
-// unaligned rows of sample b), wave w owning block w; queries y kRange .. of the chunk from
-// the first one that sees the group's first key.  Each query's indexer query tile is staged
-// once into LDS (double-buffered, fetched a query ahead) for the 4 blocks.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// unaligned rows of sample b); 8 waves, wave w owning block w / 2 for indexer heads
+// 32 (w % 2) .. + 31 (two waves per SIMD; each adds its head half of the block's dkI);
+// queries y kRange .. of the chunk from the first one that sees the group's first key.  Each
+// query's indexer query tile is staged once into LDS (double-buffered, fetched a query
+// ahead) for the 4 blocks.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_kld_keys(KldArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t QIt[2][kHI][kIS];
   __shared__ __attribute__((aligned(16))) uint8_t QI8[2][kHI][kI8S];
@@ -347,6 +350,7 @@ void k_kld_keys(KldArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
+  const int kb = wave >> 1, hh = wave & 1;
   constexpr int kGroup = 4 * kKB;
   const int Tc = a.cu_cmp[a.B];
   int r_lo, r_hi, b;
@@ -368,20 +372,19 @@ void k_kld_keys(KldArgs a) {
   const int q_lo = max(max(t_min, a.t_lo + kRange * (int)blockIdx.y), s_b);
   const int q_hi = min(min(e_b, a.t_hi), a.t_lo + kRange * ((int)blockIdx.y + 1));
   if (q_lo >= q_hi) return;
-  // this wave's block: keys jw .. jw + nk - 1 (local), rows r_lo + 64 wave ..
-  const int jw = jl0 + kKB * wave;
-  const int nk = max(0, min(kKB, r_hi - (r_lo + kKB * wave)));
+  // this wave's block: keys jw .. jw + nk - 1 (local), rows r_lo + 64 kb ..
+  const int jw = jl0 + kKB * kb;
+  const int nk = max(0, min(kKB, r_hi - (r_lo + kKB * kb)));
 
-  // this wave's key block: bf16 rows (or fp8 codes), rows past nk zero; every load of a
-  // lane is issued before its first store (a loop storing each chunk before loading the
-  // next waits one load latency per chunk)
+  // the block's bf16 rows (or fp8 codes), rows past nk zero, loaded by its two waves (rows
+  // 32 hh .. 32 hh + 31 each); every load of a lane is issued before its first store
   {
-    constexpr int kPL = kKB * (kDI / 8) / 64;   // 16-byte chunks per lane
+    constexpr int kPL = (kKB / 2) * (kDI / 8) / 64;   // 16-byte chunks per lane
     uint4 kv[kPL];
 #pragma unroll
     for (int u = 0; u < kPL; ++u) {
-      const int e = lane + 64 * u, row = e >> 4, ch = e & 15;
-      const int64_t src = (int64_t)(r_lo + kKB * wave + row) * kDI;
+      const int e = lane + 64 * u, row = 32 * hh + (e >> 4), ch = e & 15;
+      const int64_t src = (int64_t)(r_lo + kKB * kb + row) * kDI;
       kv[u] = make_uint4(0, 0, 0, 0);
       if (row < nk) {
         if (!a.fp8) kv[u] = *reinterpret_cast<const uint4*>((const uint16_t*)a.kI + src + 8 * ch);
@@ -390,15 +393,15 @@ void k_kld_keys(KldArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < kPL; ++u) {
-      const int e = lane + 64 * u, row = e >> 4, ch = e & 15;
-      if (!a.fp8) *reinterpret_cast<uint4*>(&KIt[wave][row][8 * ch]) = kv[u];
-      else if (ch < 8) *reinterpret_cast<uint4*>(&KI8[wave][row][16 * ch]) = kv[u];
+      const int e = lane + 64 * u, row = 32 * hh + (e >> 4), ch = e & 15;
+      if (!a.fp8) *reinterpret_cast<uint4*>(&KIt[kb][row][8 * ch]) = kv[u];
+      else if (ch < 8) *reinterpret_cast<uint4*>(&KI8[kb][row][16 * ch]) = kv[u];
     }
   }
 
-  // query tiles: 16 KiB of bf16 rows (4 chunks per thread) and 8 KiB of fp8 codes (2)
-  uint4 pq[4], pq8[2];
-  float pg[4], pw[4][4];   // the fetched query's g of the wave's keys 16 nt + c16, its w
+  // query tiles: 16 KiB of bf16 rows (2 chunks per thread) and 8 KiB of fp8 codes (1)
+  uint4 pq[2], pq8;
+  float pg[4], pw[2][4];   // the fetched query's g of the wave's keys 16 nt + c16, its w
   auto fetch = [&](int tq) {
     const int nvq = min((tq - s_b + 1) / a.r, a.n_cap);
     const float* grq = a.g + (int64_t)(tq - a.t_lo) * a.n_cap + jw;
@@ -408,105 +411,97 @@ void k_kld_keys(KldArgs a) {
       pg[nt] = (kj < nk && jw + kj < nvq) ? grq[kj] : 0.f;
     }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pw[mt][i] = a.w[(int64_t)tq * kHI + 16 * mt + 4 * g + i];
+      for (int i = 0; i < 4; ++i) pw[m2][i] = a.w[(int64_t)tq * kHI + 32 * hh + 16 * m2 + 4 * g + i];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = tid + 256 * u, hh = e >> 4, ch = e & 15;
-      pq[u] = *reinterpret_cast<const uint4*>(a.qI16 + ((int64_t)(tq - a.q16_t0) * kHI + hh) * kDI + 8 * ch);
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + 512 * u, hr = e >> 4, ch = e & 15;
+      pq[u] = *reinterpret_cast<const uint4*>(a.qI16 + ((int64_t)(tq - a.q16_t0) * kHI + hr) * kDI + 8 * ch);
     }
     if (a.fp8) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = tid + 256 * u, hh = e >> 3, ch = e & 7;
-        pq8[u] = *reinterpret_cast<const uint4*>((const uint8_t*)a.qI + ((int64_t)tq * kHI + hh) * kDI + 16 * ch);
-      }
+      const int hr = tid >> 3, ch = tid & 7;
+      pq8 = *reinterpret_cast<const uint4*>((const uint8_t*)a.qI + ((int64_t)tq * kHI + hr) * kDI + 16 * ch);
     }
   };
   auto commit = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = tid + 256 * u, hh = e >> 4, ch = e & 15;
-      *reinterpret_cast<uint4*>(&QIt[buf][hh][8 * ch]) = pq[u];
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + 512 * u, hr = e >> 4, ch = e & 15;
+      *reinterpret_cast<uint4*>(&QIt[buf][hr][8 * ch]) = pq[u];
     }
     if (a.fp8) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = tid + 256 * u, hh = e >> 3, ch = e & 7;
-        *reinterpret_cast<uint4*>(&QI8[buf][hh][16 * ch]) = pq8[u];
-      }
+      const int hr = tid >> 3, ch = tid & 7;
+      *reinterpret_cast<uint4*>(&QI8[buf][hr][16 * ch]) = pq8;
     }
   };
 
-  // dkI partial sums: acc[nt][dt] = keys 16 nt + 4 g + i of the wave's block, d 16 dt + c16
+  // dkI partial sums over this wave's heads: acc[nt][dt] = keys 16 nt + 4 g + i of the
+  // wave's block, d 16 dt + c16
   f32x4 acc[4][8];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int jr = c16 >> 2, jc = 4 * (c16 & 3);
+  const int ks = hh;   // k-step of the dkI product: head tiles 2 ks, 2 ks + 1
 
   fetch(q_lo);
   commit(0);
   for (int tq = q_lo; tq < q_hi; ++tq) {
     const int buf = (tq - q_lo) & 1;
     __syncthreads();
-    float gvs[4], wv[4][4];
+    float gvs[4], wv[2][4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) gvs[nt] = pg[nt];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wv[mt][i] = pw[mt][i];
+      for (int i = 0; i < 4; ++i) wv[m2][i] = pw[m2][i];
     if (tq + 1 < q_hi) fetch(tq + 1);
     const int nv_t = min((tq - s_b + 1) / a.r, a.n_cap);
     if (nk > 0 && nv_t > jw) {
-      // z[head 16 mt + 4 g + i][key 16 nt + c16] (the ReLU mask needs only its sign, so fp8
-      // codes need no scales), then E = g w 1[z > 0] as bf16 A operands of the dkI product:
-      // k-step ks takes head tiles 2 ks (k-slots 8g..8g+3) and 2 ks + 1 (8g+4..8g+7); the qI
-      // rows are read transposed in the same order
+      // z[head 16 mt + 4 g + i][key 16 nt + c16] for the wave's head tiles mt = 2 ks, 2 ks + 1
+      // (the ReLU mask needs only its sign, so fp8 codes need no scales), then E = g w
+      // 1[z > 0] as the bf16 A operand of the dkI product over those 32 heads; the qI rows
+      // are read transposed in the same order
+      bf16x8 qbt[8];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        // qI^T B operands of this k-step, shared by the 4 key tiles
-        bf16x8 qbt[8];
+      for (int dt = 0; dt < 8; ++dt)
+        qbt[dt] = join8(ld_tr(&QIt[buf][32 * ks + 4 * g + jr][16 * dt + jc]),
+                        ld_tr(&QIt[buf][32 * ks + 16 + 4 * g + jr][16 * dt + jc]));
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          qbt[dt] = join8(ld_tr(&QIt[buf][32 * ks + 4 * g + jr][16 * dt + jc]),
-                          ld_tr(&QIt[buf][32 * ks + 16 + 4 * g + jr][16 * dt + jc]));
+      for (int nt = 0; nt < 4; ++nt) {
+        const float gv = gvs[nt];
+        uint32_t e4[4];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const float gv = gvs[nt];
-          uint32_t e4[4];
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int mt = 2 * ks + h2;
+          f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (!a.fp8) {
 #pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const int mt = 2 * ks + h2;
-            f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (!a.fp8) {
-#pragma unroll
-              for (int kk = 0; kk < 4; ++kk)
-                z = mfma16(ld16(&QIt[buf][16 * mt + c16][32 * kk + 8 * g]),
-                           ld16(&KIt[wave][16 * nt + c16][32 * kk + 8 * g]), z);
-            } else {
-              const uint4* qp = reinterpret_cast<const uint4*>(&QI8[buf][16 * mt + c16][32 * g]);
-              const uint4* kp = reinterpret_cast<const uint4*>(&KI8[wave][16 * nt + c16][32 * g]);
-              const uint4 q0 = qp[0], q1 = qp[1], k0 = kp[0], k1 = kp[1];
-              z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  i32x8{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w},
-                  i32x8{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w},
-                  z, 0, 0, 0, 127, 0, 127);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; i += 2) {
-              const float e0 = z[i] > 0.f ? gv * wv[mt][i] : 0.f;
-              const float e1 = z[i + 1] > 0.f ? gv * wv[mt][i + 1] : 0.f;
-              e4[2 * h2 + (i >> 1)] = pack_bf16x2(e0, e1);
-            }
+            for (int kk = 0; kk < 4; ++kk)
+              z = mfma16(ld16(&QIt[buf][16 * mt + c16][32 * kk + 8 * g]),
+                         ld16(&KIt[kb][16 * nt + c16][32 * kk + 8 * g]), z);
+          } else {
+            const uint4* qp = reinterpret_cast<const uint4*>(&QI8[buf][16 * mt + c16][32 * g]);
+            const uint4* kp = reinterpret_cast<const uint4*>(&KI8[kb][16 * nt + c16][32 * g]);
+            const uint4 q0 = qp[0], q1 = qp[1], k0 = kp[0], k1 = kp[1];
+            z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                i32x8{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w},
+                i32x8{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w},
+                z, 0, 0, 0, 127, 0, 127);
           }
-          const bf16x8 ea = __builtin_bit_cast(bf16x8, make_uint4(e4[0], e4[1], e4[2], e4[3]));
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = mfma16(ea, qbt[dt], acc[nt][dt]);
+          for (int i = 0; i < 4; i += 2) {
+            const float e0 = z[i] > 0.f ? gv * wv[h2][i] : 0.f;
+            const float e1 = z[i + 1] > 0.f ? gv * wv[h2][i + 1] : 0.f;
+            e4[2 * h2 + (i >> 1)] = pack_bf16x2(e0, e1);
+          }
         }
+        const bf16x8 ea = __builtin_bit_cast(bf16x8, make_uint4(e4[0], e4[1], e4[2], e4[3]));
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = mfma16(ea, qbt[dt], acc[nt][dt]);
       }
     }
     if (tq + 1 < q_hi) commit(buf ^ 1);
@@ -520,13 +515,15 @@ void k_kld_keys(KldArgs a) {
       if (kj < nk) {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
-          atomicAdd(a.dkI + (int64_t)(r_lo + kKB * wave + kj) * kDI + 16 * dt + c16, acc[nt][dt][i]);
+          atomicAdd(a.dkI + (int64_t)(r_lo + kKB * kb + kj) * kDI + 16 * dt + c16, acc[nt][dt][i]);
       }
     }
 }
 
 // ---------------------------------------------------------------------------- dqI, dw
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// 8 waves: wave w serves query w / 2 of the group with indexer heads 32 (w % 2) .. + 31, so two
+// waves share each SIMD and one's ReLU/E arithmetic overlaps the other's MFMAs.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_kld_queries(KldArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t KIt[2][kKB][kIS];
   __shared__ __attribute__((aligned(16))) uint8_t KI8[2][kKB][kI8S];
@@ -534,31 +531,33 @@ void k_kld_queries(KldArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
+  const int qw = wave >> 1, hh = wave & 1;
   if ((int)blockIdx.x < kChunkRows / 4) {   // capacity padding rows: dqI = 0, dw = 0
-    const int u = a.t_lo + 4 * blockIdx.x + wave;
+    const int u = a.t_lo + 4 * blockIdx.x + qw;
     if (u < a.t_hi && u >= a.cu[a.B]) {
-      for (int e = lane; e < kHI * kDI; e += 64) a.dqI[(int64_t)u * kHI * kDI + e] = 0.f;
-      a.dw[(int64_t)u * kHI + lane] = 0.f;
+      for (int e = lane; e < kHI * kDI / 2; e += 64)
+        a.dqI[(int64_t)u * kHI * kDI + hh * (kHI * kDI / 2) + e] = 0.f;
+      if (lane < kHI / 2) a.dw[(int64_t)u * kHI + 32 * hh + lane] = 0.f;
     }
   }
   int t_first, n_tok;
   TokenInfo ti;
   if (!query_group(a, blockIdx.x, t_first, n_tok, ti)) return;
-  const bool active = wave < n_tok;
-  const int t = t_first + (active ? wave : 0);
+  const bool active = qw < n_tok;
+  const int t = t_first + (active ? qw : 0);
   const int row0 = a.cu_cmp[ti.b];
-  const int nv_w = active ? min((ti.p + wave + 1) / a.r, a.n_cap) : 0;
+  const int nv_w = active ? min((ti.p + qw + 1) / a.r, a.n_cap) : 0;
   const int nv_max = min((ti.p + n_tok) / a.r, a.n_cap);
   const int nblk = (nv_max + kKB - 1) / kKB;
   const float* grow = a.g + (int64_t)(t - a.t_lo) * a.n_cap;
 
-  // resident: qI^T as B operands (heads 16 nt + c16), head weights, fp8 row scales
-  bf16x8 qb[4][4];
-  i32x8 q8[4];
-  float wv[4], qsc[4];
+  // resident: qI^T as B operands (heads 32 hh + 16 nt + c16), head weights, fp8 row scales
+  bf16x8 qb[2][4];
+  i32x8 q8[2];
+  float wv[2], qsc[2];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int h = 16 * nt + c16;
+  for (int nt = 0; nt < 2; ++nt) {
+    const int h = 32 * hh + 16 * nt + c16;
     wv[nt] = a.w[(int64_t)t * kHI + h];
     if (!a.fp8) {
 #pragma unroll
@@ -572,17 +571,17 @@ void k_kld_queries(KldArgs a) {
     }
   }
 
-  // kI block jb: 64 rows of 16-byte chunks, 4 per thread (bf16 rows: the fp8 path reads the
-  // dequantized copy), fp8 codes 2 per thread and the row scales; rows past the last visible
+  // kI block jb: 64 rows of 16-byte chunks, 2 per thread (bf16 rows: the fp8 path reads the
+  // dequantized copy), fp8 codes 1 per thread and the row scales; rows past the last visible
   // key repeat row0 (finite; their g is 0)
-  uint4 pre[4], pre8[2];
+  uint4 pre[2], pre8;
   float pre_s = 0.f;
   float pre_g[4][4];   // g of keys 16 mt + 4 g + i of the fetched block (0 past nv_w)
   const uint16_t* kI16 = a.fp8 ? a.kI16 : (const uint16_t*)a.kI;
   auto fetch = [&](int jb) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = tid + 256 * u, row = e >> 4, ch = e & 15;
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + 512 * u, row = e >> 4, ch = e & 15;
       const int key = kKB * jb + row;
       pre[u] = *reinterpret_cast<const uint4*>(kI16 + (int64_t)(row0 + (key < nv_max ? key : 0)) * kDI + 8 * ch);
     }
@@ -594,40 +593,34 @@ void k_kld_queries(KldArgs a) {
         pre_g[mt][i] = j < nv_w ? grow[j] : 0.f;
       }
     if (a.fp8) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = tid + 256 * u, row = e >> 3, ch = e & 7;
-        const int key = kKB * jb + row;
-        pre8[u] = *reinterpret_cast<const uint4*>((const uint8_t*)a.kI + (int64_t)(row0 + (key < nv_max ? key : 0)) * kDI + 16 * ch);
-      }
+      const int row = tid >> 3, ch = tid & 7;
+      const int key = kKB * jb + row;
+      pre8 = *reinterpret_cast<const uint4*>((const uint8_t*)a.kI + (int64_t)(row0 + (key < nv_max ? key : 0)) * kDI + 16 * ch);
       if (tid < kKB) {
-        const int key = kKB * jb + tid;
-        pre_s = a.kI_scale[row0 + (key < nv_max ? key : 0)];
+        const int k2 = kKB * jb + tid;
+        pre_s = a.kI_scale[row0 + (k2 < nv_max ? k2 : 0)];
       }
     }
   };
   auto commit = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = tid + 256 * u, row = e >> 4, ch = e & 15;
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + 512 * u, row = e >> 4, ch = e & 15;
       *reinterpret_cast<uint4*>(&KIt[buf][row][8 * ch]) = pre[u];
     }
     if (a.fp8) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = tid + 256 * u, row = e >> 3, ch = e & 7;
-        *reinterpret_cast<uint4*>(&KI8[buf][row][16 * ch]) = pre8[u];
-      }
+      const int row = tid >> 3, ch = tid & 7;
+      *reinterpret_cast<uint4*>(&KI8[buf][row][16 * ch]) = pre8;
       if (tid < kKB) ksc_s[buf][tid] = pre_s;
     }
   };
 
-  f32x4 acc[4][8];   // dqI: heads 16 nt + 4 g + i, d 16 dt + c16
+  f32x4 acc[2][8];   // dqI: heads 32 hh + 16 nt + 4 g + i, d 16 dt + c16
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
+  for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float dwp[4] = {0.f, 0.f, 0.f, 0.f};
+  float dwp[2] = {0.f, 0.f};
   const int jr = c16 >> 2, jc = 4 * (c16 & 3);
 
   if (nblk > 0) {
@@ -645,18 +638,18 @@ void k_kld_queries(KldArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) gk[mt][i] = pre_g[mt][i];
     if (jb + 1 < nblk) fetch(jb + 1);
-    // z^T[key 16 mt + 4 g + i][head 16 nt + c16]; E as the A operand of dqI = E kI with
-    // k-step ks over key tiles 2 ks (k-slots 8g..8g+3) and 2 ks + 1 (8g+4..8g+7)
+    // z^T[key 16 mt + 4 g + i][head 32 hh + 16 nt + c16]; E as the A operand of dqI = E kI
+    // with k-step ks over key tiles 2 ks (k-slots 8g..8g+3) and 2 ks + 1 (8g+4..8g+7)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      // kI^T B operands of this k-step, shared by the 4 head tiles
+      // kI^T B operands of this k-step, shared by the 2 head tiles
       bf16x8 kbt[8];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
         kbt[dt] = join8(ld_tr(&KIt[buf][32 * ks + 4 * g + jr][16 * dt + jc]),
                         ld_tr(&KIt[buf][32 * ks + 16 + 4 * g + jr][16 * dt + jc]));
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < 2; ++nt) {
         uint32_t e4[4];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
@@ -693,16 +686,16 @@ void k_kld_queries(KldArgs a) {
   }
   if (!active) return;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < 2; ++nt) {
     float v = dwp[nt];
     v += __shfl_xor(v, 16, 64);
     v += __shfl_xor(v, 32, 64);
-    if (g == 0) a.dw[(int64_t)t * kHI + 16 * nt + c16] = v;
+    if (g == 0) a.dw[(int64_t)t * kHI + 32 * hh + 16 * nt + c16] = v;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        a.dqI[((int64_t)t * kHI + 16 * nt + 4 * g + i) * kDI + 16 * dt + c16] = acc[nt][dt][i];
+        a.dqI[((int64_t)t * kHI + 32 * hh + 16 * nt + 4 * g + i) * kDI + 16 * dt + c16] = acc[nt][dt][i];
   }
 }
 
@@ -814,7 +807,7 @@ hipError_t launch_indexer_kl_dense(const Shape& sh, const KlIO& io, hipStream_t 
     if (!grads) continue;
     a.dqI = io.dqI;
     a.dw = io.dw;
-    hipLaunchKernelGGL(k_kld_queries, dim3(kChunkRows / 4 + sh.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_kld_queries, dim3(kChunkRows / 4 + sh.B), dim3(512), 0, s, a);
     if (a.fp8) {
       const int64_t n = (int64_t)(a.t_hi - a.t_lo) * kHI * (kDI / 8);
       hipLaunchKernelGGL(k_kld_dequant, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
@@ -822,7 +815,7 @@ hipError_t launch_indexer_kl_dense(const Shape& sh, const KlIO& io, hipStream_t 
                          (int64_t)(a.t_hi - a.t_lo) * kHI, (const int32_t*)nullptr, q16);
       a.q16_t0 = a.t_lo;   // the copy holds rows t - t_lo
     }
-    hipLaunchKernelGGL(k_kld_keys, dim3(a.tc_blocks + sh.B, kChunkRows / kRange), dim3(256), 0,
+    hipLaunchKernelGGL(k_kld_keys, dim3(a.tc_blocks + sh.B, kChunkRows / kRange), dim3(512), 0,
                        s, a);
   }
   return hipGetLastError();
