@@ -6,20 +6,21 @@
 // forward returns O, the log-sum-exp and, optionally, the log-sum-exp over the compressed
 // candidates alone (the normalizer of the selected-set indexer teacher, section 3).
 //
-// Design: one workgroup of 4 waves per query token (one per SIMD, 512 registers each);
-// candidates are processed in blocks of 64 rows, double-buffered in LDS.
+// Design: one workgroup of 8 waves per query token (two per SIMD, so one wave's gathers,
+// softmax and waits overlap the other's MFMAs; 256 registers each); candidates are processed
+// in blocks of 64 rows, double-buffered in LDS.
 //   * Rows are gathered with direct global->LDS loads (global_load_lds_dwordx4, one 1 KiB
 //     row per wave instruction) one block ahead, spread over the S^T k-steps so that they
 //     land while the current block computes; the query's idx row is staged in LDS once.
 //     LDS rows are 1 KiB with a 16-byte chunk swizzle, so both the row-segment reads of
 //     S = Q K^T and the transposed reads of P V are bank-conflict free.
-//   * S^T: wave (hh, ch) computes heads 32hh..32hh+31 against candidates 32ch..32ch+31 of
+//   * S^T: wave (hh, ch) computes heads 16hh..16hh+15 against candidates 32ch..32ch+31 of
 //     the block on v_mfma_f32_16x16x32_bf16 (A = row segments from LDS, B = the query's Q
-//     resident in registers); every row segment read from LDS feeds two MFMAs.
+//     of its 16 heads resident in registers).
 //   * Online softmax per head with a lazily rescaled running max: the max is only moved
 //     when it grows by more than 2^8, so most blocks skip the O rescale.  P (bf16) goes to
 //     LDS.
-//   * O^T: wave w owns d = 128w..128w+127 for all 64 heads: A = the row tile read transposed
+//   * O^T: wave w owns d = 64w..64w+63 for all 64 heads: A = the row tile read transposed
 //     (ds_read_b64_tr_b16), B = P^T from LDS.
 //   * O is normalised, transposed through LDS and written with full-row 16-byte stores.
 // Tokens map to workgroups so that each XCD walks contiguous 256-token chunks (its L2 then
@@ -42,7 +43,8 @@ constexpr int kNB = 64;        // candidates per block
 constexpr int kPS = 72;        // P tile row stride (bf16)
 constexpr float kLazy = 8.f;   // growth (log2 units) of the running max tolerated before rescaling
 constexpr int kIdxLds = 2048;    // idx entries of a query staged in LDS
-constexpr int kFwdWaves = 4;   // one wave per SIMD: each wave holds Q (32 heads) and 1/4 of O
+constexpr int kFwdWaves = 8;   // two waves per SIMD: each holds Q of 16 heads and 1/8 of O
+constexpr int kFwdHeadGroups = 4;
 
 struct FwdArgs {
   const uint16_t* q;
@@ -85,29 +87,29 @@ __device__ __forceinline__ void dma_row16_s(uint64_t row, uint32_t lane_off, uin
 
 }  // namespace
 
-// NW waves per query: NW/2 candidate groups of CPW = 128/NW candidates for S^T, and d slices
-// of DPW = 512/NW columns for O^T.
+// NW waves per query: NHG head groups of HPW = 64/NHG heads times NCH = NW/NHG candidate
+// groups of CPW = 64/NCH candidates for S^T, and d slices of DPW = 512/NW columns for O^T.
 // IDX_LDS: the query's idx row (k_cap <= kIdxLds) is staged in LDS once, so that the block
 // loop reads its next slots from LDS instead of issuing a global load per block.
-template <int NW, bool IDX_LDS>
+template <int NW, int NHG, bool IDX_LDS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void k_attn_fwd_mfma(FwdArgs a) {
-  constexpr int NT = NW * 64, NCH = NW / 2, CPW = kNB / NCH, MQ = CPW / 16, DPW = kD / NW,
-                MP = DPW / 16, RPW = kNB / NW;
+  constexpr int NT = NW * 64, NCH = NW / NHG, CPW = kNB / NCH, MQ = CPW / 16, DPW = kD / NW,
+                MP = DPW / 16, RPW = kNB / NW, HPW = kH / NHG, NT2 = HPW / 16;
   __shared__ __attribute__((aligned(16))) uint16_t tile[2][kNB][kD];
   __shared__ __attribute__((aligned(16))) uint16_t Ps[kH][kPS];
   __shared__ float mx_s[NCH][kH];
   __shared__ float alpha_s[kH];
   __shared__ float lsum_s[NCH][kH], lsnap_s[NCH][kH];
   __shared__ float mrun_s[kH], msnap_s[kH], fin_s[kH];
-  __shared__ int resc_s[2];
+  __shared__ int resc_s[NHG];
   __shared__ int s_tmp;
   __shared__ float2 rope_s[kD / 2];   // cos, sin of the output rotation's pairs
   __shared__ int32_t idx_s[IDX_LDS ? kIdxLds : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int hh = wave & 1, ch = wave >> 1;
+  const int hh = wave % NHG, ch = wave / NHG;   // head group, candidate group
   const int t = token_of_block(blockIdx.x);
   if (t >= a.T) return;
 
@@ -125,15 +127,15 @@ void k_attn_fwd_mfma(FwdArgs a) {
   }
   // the idx row first (into registers; to LDS once Q is in flight), so the first block's
   // gather waits for the idx loads alone, then Q^T as the B operand:
-  // qb[nt][ks] = Q[32hh + 16nt + c16][32ks + 8g .. +7]
+  // qb[nt][ks] = Q[HPW hh + 16nt + c16][32ks + 8g .. +7]
   const int32_t* idx_t = a.mode == 0 ? a.idx + (int64_t)t * a.k_cap : nullptr;
   int iv[IDX_LDS ? kIdxLds / NT : 1];
   if (IDX_LDS && a.mode == 0) load_idx_regs(idx_t, a.k_cap, iv);
-  bf16x8 qb[2][16];
+  bf16x8 qb[NT2][16];
   {
-    const uint16_t* qt = a.q + ((int64_t)t * kH + 32 * hh + c16) * kD + 8 * g;
+    const uint16_t* qt = a.q + ((int64_t)t * kH + HPW * hh + c16) * kD + 8 * g;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NT2; ++nt)
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) qb[nt][ks] = ld16(qt + 16 * nt * kD + 32 * ks);
   }
@@ -178,8 +180,12 @@ void k_attn_fwd_mfma(FwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) o[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  float m_run[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
-  float m_snap[2] = {-INFINITY, -INFINITY}, l_snap[2] = {0.f, 0.f};
+  float m_run[NT2], l_part[NT2], m_snap[NT2], l_snap[NT2];
+#pragma unroll
+  for (int nt = 0; nt < NT2; ++nt) {
+    m_run[nt] = m_snap[nt] = -INFINITY;
+    l_part[nt] = l_snap[nt] = 0.f;
+  }
 
   // row-segment reads of S^T: logical chunk 4ks + g of row CPW ch + 16 mq + c16 sits at
   // physical chunk 16 (ks / 4) + ((4 (ks % 4) + g) ^ swz(c16))
@@ -187,10 +193,11 @@ void k_attn_fwd_mfma(FwdArgs a) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) eq[q] = 8 * ((4 * q + g) ^ swz(c16));
   // transposed reads of P V: logical chunk DPW/8 wave + 2 mt + (c16 & 3) / 2 of rows
-  // 32ks + 8g + c16/4 (lo) and +4 (hi); 8 ((2 mt + e) ^ s) = 16 mt ^ 8 (e ^ s)
+  // 32ks + 8g + c16/4 (lo) and +4 (hi), at physical chunk (DPW/8 wave + e + 2 mt) ^ s; the
+  // three terms occupy disjoint bits, so 8 (that) = 8 ((DPW/8 wave + e) ^ s) ^ 16 mt
   const int tr_e = (c16 & 3) >> 1, tr_off = 4 * (c16 & 1);
-  const int klo = 8 * (tr_e ^ swz(8 * (g & 1) + (c16 >> 2)));
-  const int khi = 8 * (tr_e ^ swz(8 * (g & 1) + 4 + (c16 >> 2)));
+  const int klo = 8 * (((DPW / 8) * wave + tr_e) ^ swz(8 * (g & 1) + (c16 >> 2)));
+  const int khi = 8 * (((DPW / 8) * wave + tr_e) ^ swz(8 * (g & 1) + 4 + (c16 >> 2)));
 
   // row id of slot 64 b + lane: >= 0 compressed row, <= -2 raw row -2 - id, -1 none
   auto rid_of = [&](int b, int raw) {
@@ -220,7 +227,7 @@ void k_attn_fwd_mfma(FwdArgs a) {
   // the next block's rows are gathered one per S^T k-step, so the loads overlap the MFMAs
   // instead of stalling the wave at the block start: lane l holds the source of slot l, row
   // RPW wave + j is read with two lane reads; swz(row) depends on the row's low 4 bits only
-  static_assert(RPW == 16, "one row per S^T k-step");
+  static_assert(RPW == 16 || RPW == 8, "one row per one or two S^T k-steps");
   const uint32_t lane16 = 16u * (uint32_t)lane;
   const uint32_t tile_lds = (uint32_t)(uintptr_t)&tile[0][0][0];
   auto row_addr = [&](int rid) {
@@ -245,14 +252,16 @@ void k_attn_fwd_mfma(FwdArgs a) {
       const int r = RPW * wave + j;
       const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)nsrc, r);
       const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(nsrc >> 32), r);
-      dma_row16_s(((uint64_t)hi << 32) | lo, lane16 ^ (16u * swz(j)), nlds + j * (kD * 2));
+      dma_row16_s(((uint64_t)hi << 32) | lo, lane16 ^ (16u * swz(RPW * wave + j)), nlds + j * (kD * 2));
     };
     const int raw_nn = raw_of(b + 2);   // consumed after this block's final wait
 
-    // ---- S^T: candidates CPW ch + 16 mq + 4g + i, heads 32hh + 16nt + c16
-    f32x4 st[MQ][2];
+    // ---- S^T: candidates CPW ch + 16 mq + 4g + i, heads HPW hh + 16nt + c16
+    f32x4 st[MQ][NT2];
 #pragma unroll
-    for (int mq = 0; mq < MQ; ++mq) st[mq][0] = st[mq][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mq = 0; mq < MQ; ++mq)
+#pragma unroll
+      for (int nt = 0; nt < NT2; ++nt) st[mq][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
       // operands read kPre k-steps ahead of the MFMAs that consume them
       const uint16_t* rb = &tile[buf][CPW * ch + c16][0];
@@ -267,11 +276,10 @@ void k_attn_fwd_mfma(FwdArgs a) {
       for (int ks = 0; ks < 16; ++ks) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mq = 0; mq < MQ; ++mq) {
-          st[mq][0] = mfma16(av[ks % kPre][mq], qb[0][ks], st[mq][0]);
-          st[mq][1] = mfma16(av[ks % kPre][mq], qb[1][ks], st[mq][1]);
-        }
-        if (more) gather(ks);
+        for (int mq = 0; mq < MQ; ++mq)
+#pragma unroll
+          for (int nt = 0; nt < NT2; ++nt) st[mq][nt] = mfma16(av[ks % kPre][mq], qb[nt][ks], st[mq][nt]);
+        if (more && (RPW == 16 || (ks & 1))) gather(RPW == 16 ? ks : ks >> 1);
         if (ks + kPre < 16) {
 #pragma unroll
           for (int mq = 0; mq < MQ; ++mq) av[ks % kPre][mq] = seg(ks + kPre, mq);
@@ -283,8 +291,8 @@ void k_attn_fwd_mfma(FwdArgs a) {
     // consecutive slots of one head)
     if (a.t_logits && kNB * b < cs.n_cs) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float* dst = a.t_logits + ((int64_t)t * kH + 32 * hh + 16 * nt + c16) * a.ld_t +
+      for (int nt = 0; nt < NT2; ++nt) {
+        float* dst = a.t_logits + ((int64_t)t * kH + HPW * hh + 16 * nt + c16) * a.ld_t +
                      kNB * b + CPW * ch + 4 * g;
 #pragma unroll
         for (int mq = 0; mq < MQ; ++mq)
@@ -293,9 +301,9 @@ void k_attn_fwd_mfma(FwdArgs a) {
     }
     // candidate validity of this lane's slots
     const uint32_t vbits = (uint32_t)(valid >> (CPW * ch + 4 * g));
-    float s[2][4 * MQ];
+    float s[NT2][4 * MQ];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT2; ++nt) {
       float mloc = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 4 * MQ; ++j) {
@@ -305,15 +313,15 @@ void k_attn_fwd_mfma(FwdArgs a) {
       }
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      if (g == 0) mx_s[ch][32 * hh + 16 * nt + c16] = mloc;
+      if (g == 0) mx_s[ch][HPW * hh + 16 * nt + c16] = mloc;
     }
     __syncthreads();
 
     // ---- softmax of this block: P (bf16) and the per-head rescale factors
     bool any_resc = false;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int h = 32 * hh + 16 * nt + c16;
+    for (int nt = 0; nt < NT2; ++nt) {
+      const int h = HPW * hh + 16 * nt + c16;
       float mb = mx_s[0][h];
 #pragma unroll
       for (int c = 1; c < NCH; ++c) mb = fmaxf(mb, mx_s[c][h]);
@@ -348,7 +356,10 @@ void k_attn_fwd_mfma(FwdArgs a) {
     __syncthreads();
 
     // ---- O^T[d, h] = alpha_h O^T + V^T P^T over this block
-    if (resc_s[0] | resc_s[1]) {
+    bool resc = false;
+#pragma unroll
+    for (int k = 0; k < NHG; ++k) resc = resc || resc_s[k];
+    if (resc) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const float al = alpha_s[16 * nt + c16];
@@ -359,8 +370,8 @@ void k_attn_fwd_mfma(FwdArgs a) {
     {
       // unit u = (ks, mt) = (u / MP, u % MP); its transposed row reads are issued two units
       // ahead of its MFMAs, the P^T operands of k-step 1 during unit 0
-      const uint16_t* vb = &tile[buf][8 * g + (c16 >> 2)][DPW * wave + tr_off];
-      static_assert(DPW <= 128, "the transposed-read swizzle covers 16 chunks of a d slice");
+      const uint16_t* vb = &tile[buf][8 * g + (c16 >> 2)][tr_off];
+      static_assert(DPW % 16 == 0 && DPW <= 128, "d slices of whole 16-column tiles");
       auto tr_lo = [&](int u) { return ld_tr(vb + 32 * (u / MP) * kD + ((16 * (u % MP)) ^ klo)); };
       auto tr_hi = [&](int u) { return ld_tr(vb + (32 * (u / MP) + 4) * kD + ((16 * (u % MP)) ^ khi)); };
       bf16x8 pb[2][4];
@@ -398,14 +409,14 @@ void k_attn_fwd_mfma(FwdArgs a) {
 
   // ---- finalize: per-head normalizers (with the optional sink), lse, lse_cmp
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < NT2; ++nt) {
     float lt = l_part[nt], ls = l_snap[nt];
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
     ls += __shfl_xor(ls, 16, 64);
     ls += __shfl_xor(ls, 32, 64);
     if (g == 0) {
-      const int h = 32 * hh + 16 * nt + c16;
+      const int h = HPW * hh + 16 * nt + c16;
       lsum_s[ch][h] = lt;
       lsnap_s[ch][h] = ls;
       if (ch == 0) {
@@ -521,10 +532,10 @@ hipError_t launch_attn_fwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s
   a.mode = sh.mode;
   a.scale_log2 = sh.scale * 1.44269504088896341f;
   if (sh.mode != 0 || sh.k_cap <= kIdxLds)
-    hipLaunchKernelGGL((k_attn_fwd_mfma<kFwdWaves, true>), dim3((unsigned)token_grid(sh.T)),
+    hipLaunchKernelGGL((k_attn_fwd_mfma<kFwdWaves, kFwdHeadGroups, true>), dim3((unsigned)token_grid(sh.T)),
                        dim3(kFwdWaves * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((k_attn_fwd_mfma<kFwdWaves, false>), dim3((unsigned)token_grid(sh.T)),
+    hipLaunchKernelGGL((k_attn_fwd_mfma<kFwdWaves, kFwdHeadGroups, false>), dim3((unsigned)token_grid(sh.T)),
                        dim3(kFwdWaves * 64), 0, s, a);
   return hipGetLastError();
 }
