@@ -6,7 +6,7 @@
 // already formed by the dq pass, the gradient of a shared row x is
 //   d row_x = sum_t sum_h (scale dS[t,h,x] q[t,h] + P[t,h,x] dO[t,h]),
 // a contraction over (query, head, {dS, P}) of the per-query operand [q_t; dO_t]
-// (128 x 512).  Here it runs as a dense masked product per work item: a block of up to 128
+// (128 x 512).  Here it runs as a dense masked product per work item: a block of up to kb
 // consecutive rows of one sample (compressed rows, or raw window rows) against a range of
 // up to kCq consecutive queries of that sample; the (query, row) pairs a query does not
 // attend contribute zero.  Items of one block write fp32 partial sums that a reduction adds
@@ -27,7 +27,7 @@
 namespace csa {
 namespace keys {
 
-constexpr int kKeys = 128;   // rows per item
+constexpr int kKeysMax = 256;   // rows per item: kb = 128 (attention) or 256 (indexer keys)
 constexpr int kCq = 256;     // queries per item
 
 // Item kinds: compressed rows of a CSA_SPARSE layer (slots found in the idx row), compressed
@@ -48,58 +48,58 @@ CSA_HD inline SampleChunk sample_chunk(int s0, int L, int t0, int nT) {
   return sc;
 }
 
-// ---- compressed rows: block k holds local rows [128k, 128k + 128) of the rows visible to
-// some query of the chunk; query p sees rows < min((p + 1) / r, n_cap).
+// ---- compressed rows: block k holds local rows [kb k, kb (k + 1)) of the rows visible to some
+// query of the chunk; query p sees rows < min((p + 1) / r, n_cap).
 CSA_HD inline int cmp_rows(const SampleChunk& sc, int r, int n_cap) {
   const int v = sc.pb / r;
   return v < n_cap ? v : n_cap;
 }
-CSA_HD inline int cmp_blocks(const SampleChunk& sc, int r, int n_cap) {
-  return (cmp_rows(sc, r, n_cap) + kKeys - 1) / kKeys;
+CSA_HD inline int cmp_blocks(const SampleChunk& sc, int r, int n_cap, int kb) {
+  return (cmp_rows(sc, r, n_cap) + kb - 1) / kb;
 }
 CSA_HD inline int n_chunks(const SampleChunk& sc) { return (sc.pb - sc.pa + kCq - 1) / kCq; }
-// first query of the chunk that sees row 128k
-CSA_HD inline int cmp_qlo(const SampleChunk& sc, int r, int k) {
-  const int f = r * (kKeys * k + 1) - 1;
+// first query of the chunk that sees row kb k
+CSA_HD inline int cmp_qlo(const SampleChunk& sc, int r, int k, int kb) {
+  const int f = r * (kb * k + 1) - 1;
   return f > sc.pa ? f : sc.pa;
 }
 // first query chunk (of kCq queries from pa) holding a query that sees block k
-CSA_HD inline int cmp_clo(const SampleChunk& sc, int r, int k) {
-  return (cmp_qlo(sc, r, k) - sc.pa) / kCq;
+CSA_HD inline int cmp_clo(const SampleChunk& sc, int r, int k, int kb) {
+  return (cmp_qlo(sc, r, k, kb) - sc.pa) / kCq;
 }
 
-// ---- window rows: block m holds local raw rows [128m, 128m + 128); row u is seen by the
+// ---- window rows: block m holds local raw rows [kb m, kb (m + 1)); row u is seen by the
 // queries u .. u + W - 1 of its sample.
-CSA_HD inline int win_mlo(const SampleChunk& sc, int W) {
+CSA_HD inline int win_mlo(const SampleChunk& sc, int W, int kb) {
   const int u = sc.pa - W + 1;
-  return (u > 0 ? u : 0) / kKeys;
+  return (u > 0 ? u : 0) / kb;
 }
-CSA_HD inline int win_mhi(const SampleChunk& sc) { return (sc.pb + kKeys - 1) / kKeys; }
+CSA_HD inline int win_mhi(const SampleChunk& sc, int kb) { return (sc.pb + kb - 1) / kb; }
 struct WinBlock {
   int nk, qlo, qhi, pieces;
 };
-CSA_HD inline WinBlock win_block(const SampleChunk& sc, int W, int m) {
+CSA_HD inline WinBlock win_block(const SampleChunk& sc, int W, int m, int kb) {
   WinBlock wb;
-  wb.nk = sc.L - kKeys * m < kKeys ? sc.L - kKeys * m : kKeys;
-  wb.qlo = kKeys * m > sc.pa ? kKeys * m : sc.pa;
-  const int e = kKeys * m + wb.nk - 1 + W;
+  wb.nk = sc.L - kb * m < kb ? sc.L - kb * m : kb;
+  wb.qlo = kb * m > sc.pa ? kb * m : sc.pa;
+  const int e = kb * m + wb.nk - 1 + W;
   wb.qhi = e < sc.pb ? e : sc.pb;
   wb.pieces = wb.qhi > wb.qlo ? (wb.qhi - wb.qlo + kCq - 1) / kCq : 0;
   return wb;
 }
 
 // Upper bound on the items of one chunk of nT queries (B samples, rows per sample at most
-// n_cap compressed rows, window W); partial slots and reduction records are at most as many.
-// Compressed: every sample has at most n_cap / 128 + 1 blocks, each in at most
-// (its queries in the chunk) / kCq + 1 items.  Window: a sample's blocks that its chunk
-// queries see number at most (its queries + W - 1) / 128 + 2, each in at most
-// ceil((127 + W) / kCq) items.
-CSA_HD inline int64_t item_cap(int mode, int B, int nT, int n_cap, int W) {
+// n_cap compressed rows, window W, blocks of kb rows); partial slots and reduction records are
+// at most as many.  Compressed: every sample has at most n_cap / kb + 1 blocks, each in at
+// most (its queries in the chunk) / kCq + 1 items.  Window: a sample's blocks that its chunk
+// queries see number at most (its queries + W - 1) / kb + 2, each in at most
+// ceil((kb - 1 + W) / kCq) items.
+CSA_HD inline int64_t item_cap(int mode, int B, int nT, int n_cap, int W, int kb) {
   const int64_t bc = B < nT ? B : nT;
   int64_t n = 0;
-  if (mode != 2) n += (int64_t)(n_cap / kKeys + 1) * ((int64_t)nT / kCq + bc);
+  if (mode != 2) n += (int64_t)(n_cap / kb + 1) * ((int64_t)nT / kCq + bc);
   if (W > 0)
-    n += (((int64_t)nT + bc * (W - 1)) / kKeys + 2 * bc) * ((kKeys - 1 + W + kCq - 1) / kCq);
+    n += (((int64_t)nT + bc * (W - 1)) / kb + 2 * bc) * ((kb - 1 + W + kCq - 1) / kCq);
   return n;
 }
 
@@ -120,15 +120,16 @@ struct KeysArgs {
   const int32_t* cu;
   const int32_t* cu_cmp;
   const uint16_t* zeros;    // >= 16 zero bytes
-  int4* items;              // [cap] key0, nkeys | kind << 8, first query, queries
+  int4* items;              // [cap] key0, nkeys | kind << 16, first query, queries
   int32_t* item_part;       // [cap] partial slot of the item, -1: added directly
-  int4* red;                // [cap] key0, nkeys | kind << 8, first partial slot, slots
-  float* part;              // [cap, 128, 512]
+  int4* red;                // [cap] key0, nkeys | kind << 16, first partial slot, slots
+  float* part;              // [cap, kb, D]
   int32_t* counters;        // [0] items, [1] reduction records, [2] repeated-row flag (zeroed)
   float* dkv_cmp;
   float* dkv;
   int64_t n_slots, cap;
   int t0, nT, B, r, n_cap, W, k_cap, mode;
+  int kb;   // rows per block: 128 (attention) or 256 (indexer keys)
   int D;    // width of the gradient rows (and of the partial rows)
   int KC;   // coefficients per (query, slot): 128 (attention: dS | P) or 64 (indexer: E)
 };

@@ -92,13 +92,13 @@ __global__ __launch_bounds__(256) void k_attn_bwd_keys_plan(KeysArgs a) {
     if (sc.pa >= sc.pb) continue;
     if (a.mode != 2) {
       const int c0 = a.cu_cmp[b];
-      const int rows = cmp_rows(sc, a.r, a.n_cap), nblk = cmp_blocks(sc, a.r, a.n_cap);
+      const int rows = cmp_rows(sc, a.r, a.n_cap), nblk = cmp_blocks(sc, a.r, a.n_cap, a.kb);
       const int nch = n_chunks(sc);
       const int kind = a.mode == 0 ? kKindSel : kKindDense;
       for (int k0 = 0; k0 < nblk; k0 += 256) {
         const int k = k0 + tid;
         const bool in = k < nblk;
-        const int clo = in ? cmp_clo(sc, a.r, k) : 0;
+        const int clo = in ? cmp_clo(sc, a.r, k, a.kb) : 0;
         const int ni = in ? nch - clo : 0, v = ni >= 2 ? ni : 0;
         int tot, rtot;
         const int pre = wg_scan(v, sc_s, tot);
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_keys_plan(KeysArgs a) {
           pbase_s[k] = v > 0 ? n_parts + pre : -1;
         }
         if (v > 0 && n_red + rpre < cap)
-          a.red[n_red + rpre] = make_int4(c0 + kKeys * k, min(kKeys, rows - kKeys * k) | (kind << 8),
+          a.red[n_red + rpre] = make_int4(c0 + a.kb * k, min(a.kb, rows - a.kb * k) | (kind << 16),
                                           n_parts + pre, ni);
         n_parts += tot;
         n_red += rtot;
@@ -131,9 +131,9 @@ __global__ __launch_bounds__(256) void k_attn_bwd_keys_plan(KeysArgs a) {
         for (int k = 0; k < K; ++k) {
           const int64_t e = (int64_t)n_items + pre + k;
           if (e >= cap) break;
-          const int qa = max(cmp_qlo(sc, a.r, k), sc.pa + kCq * c);
+          const int qa = max(cmp_qlo(sc, a.r, k, a.kb), sc.pa + kCq * c);
           const int qb = min(sc.pb, sc.pa + kCq * (c + 1));
-          a.items[e] = make_int4(c0 + kKeys * k, min(kKeys, rows - kKeys * k) | (kind << 8),
+          a.items[e] = make_int4(c0 + a.kb * k, min(a.kb, rows - a.kb * k) | (kind << 16),
                                  s0 + qa, qb - qa);
           a.item_part[e] = pbase_s[k] >= 0 ? pbase_s[k] + (c - clo_s[k]) : -1;
         }
@@ -142,11 +142,11 @@ __global__ __launch_bounds__(256) void k_attn_bwd_keys_plan(KeysArgs a) {
       __syncthreads();   // clo_s and pbase_s are rewritten for the next sample
     }
     if (a.W > 0) {
-      const int mlo = win_mlo(sc, a.W), nm = win_mhi(sc) - mlo;
+      const int mlo = win_mlo(sc, a.W, a.kb), nm = win_mhi(sc, a.kb) - mlo;
       for (int m0 = 0; m0 < nm; m0 += 256) {
         const int m = mlo + m0 + tid;
         WinBlock wb = {0, 0, 0, 0};
-        if (m0 + tid < nm) wb = win_block(sc, a.W, m);
+        if (m0 + tid < nm) wb = win_block(sc, a.W, m, a.kb);
         const int np = wb.pieces, v = np >= 2 ? np : 0;
         int tot, ptot, rtot;
         const int pre = wg_scan(np, sc_s, tot);
@@ -156,12 +156,12 @@ __global__ __launch_bounds__(256) void k_attn_bwd_keys_plan(KeysArgs a) {
           const int64_t e = (int64_t)n_items + pre + e2;
           if (e >= cap) break;
           const int qa = wb.qlo + kCq * e2;
-          a.items[e] = make_int4(s0 + kKeys * m, wb.nk | (kKindWin << 8), s0 + qa,
+          a.items[e] = make_int4(s0 + a.kb * m, wb.nk | (kKindWin << 16), s0 + qa,
                                  min(kCq, wb.qhi - qa));
           a.item_part[e] = v > 0 ? n_parts + ppre + e2 : -1;
         }
         if (v > 0 && n_red + rpre < cap)
-          a.red[n_red + rpre] = make_int4(s0 + kKeys * m, wb.nk | (kKindWin << 8), n_parts + ppre, np);
+          a.red[n_red + rpre] = make_int4(s0 + a.kb * m, wb.nk | (kKindWin << 16), n_parts + ppre, np);
         n_items += tot;
         n_parts += ptot;
         n_red += rtot;
@@ -179,6 +179,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_keys_plan(KeysArgs a) {
 template <int KI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_attn_bwd_keys(KeysArgs a) {
+  constexpr int kKeys = 128;   // rows per block (a.kb)
   __shared__ __attribute__((aligned(16))) uint16_t Bs[3][32][kD];     // [q; dO] k-step rows
   __shared__ __attribute__((aligned(16))) uint16_t As[3][kKeys][32];  // dS|P of the rows
   __shared__ __attribute__((aligned(16))) int32_t idx_s[KI > 0 ? 512 * KI : 1];
@@ -194,7 +195,7 @@ void k_attn_bwd_keys(KeysArgs a) {
   const int item = (int)(blockIdx.x & 7) * per + jb;
   if (item >= n_items) return;
   const int4 it = a.items[item];
-  const int key0 = it.x, nkeys = it.y & 0xff, kind = it.y >> 8, q0 = it.z, nq = it.w;
+  const int key0 = it.x, nkeys = it.y & 0xffff, kind = it.y >> 16, q0 = it.z, nq = it.w;
   const int part = a.item_part[item];
   if (part >= a.cap || nq <= 0 || nq > kCq) return;
   TokenInfo ti;
@@ -342,19 +343,20 @@ void k_attn_bwd_keys(KeysArgs a) {
 // Work unit = (block record, 8 rows); lane: row 8u' + tid / 32, columns (tid % 32) D/32 ..
 // (D = 512 or 128: 4 or 1 float4 per lane).
 __global__ __launch_bounds__(256) void k_attn_bwd_keys_reduce(KeysArgs a) {
-  const int n_units = a.counters[1] * 16;
+  const int kUnits = a.kb / 8;
+  const int n_units = a.counters[1] * kUnits;
   const int nv4 = a.D / 128;
   for (int w = blockIdx.x; w < n_units; w += gridDim.x) {
-    const int4 rd = a.red[w >> 4];
-    const int key0 = rd.x, nkeys = rd.y & 0xff, kind = rd.y >> 8, pf = rd.z, np = rd.w;
-    const int row = 8 * (w & 15) + (threadIdx.x >> 5), d = nv4 * 4 * (threadIdx.x & 31);
+    const int4 rd = a.red[w / kUnits];
+    const int key0 = rd.x, nkeys = rd.y & 0xffff, kind = rd.y >> 16, pf = rd.z, np = rd.w;
+    const int row = 8 * (w % kUnits) + (threadIdx.x >> 5), d = nv4 * 4 * (threadIdx.x & 31);
     if (row >= nkeys || pf < 0 || pf + np > a.cap) continue;
     float4 s[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) s[v] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int p = 0; p < np; ++p) {
       const float4* src =
-          reinterpret_cast<const float4*>(a.part + ((int64_t)(pf + p) * kKeys + row) * a.D + d);
+          reinterpret_cast<const float4*>(a.part + ((int64_t)(pf + p) * a.kb + row) * a.D + d);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         if (v < nv4) {
@@ -423,14 +425,14 @@ __global__ __launch_bounds__(256) void k_attn_bwd_keys_dups(KeysArgs a) {
 }
 
 // ---- indexer-key gradients, one work item per workgroup: dkI[j] += sum_t E[t, :, j] qI_t for
-// the item's 128 rows and queries (the same items, slot maps and partial slots as the
+// the item's 256 rows and queries (the same items, slot maps and partial slots as the
 // attention's compressed rows, no window); per query two k-steps of 32 heads: the qI rows
 // 32i .. 32i+31 (256 bytes each) and the rows' 64-byte E pieces, three k-steps in flight.
-// 4 waves, wave w owns d = 32w .. 32w+31 of all 128 rows.
+// 4 waves, wave w owns d = 32w .. 32w+31 of all 256 rows.
 template <int KI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_kl_keys(KeysArgs a) {
-  constexpr int kDI = 128;
+  constexpr int kDI = 128, kKeys = 256;   // rows per block (a.kb)
   __shared__ __attribute__((aligned(16))) uint16_t Bs[3][32][kDI];    // qI k-step rows
   __shared__ __attribute__((aligned(16))) uint16_t As[3][kKeys][32];  // E of the rows
   __shared__ __attribute__((aligned(16))) int32_t idx_s[KI > 0 ? 256 * KI : 1];
@@ -445,7 +447,7 @@ void k_kl_keys(KeysArgs a) {
   const int item = (int)(blockIdx.x & 7) * per + jb;
   if (item >= n_items) return;
   const int4 it = a.items[item];
-  const int key0 = it.x, nkeys = it.y & 0xff, kind = it.y >> 8, q0 = it.z, nq = it.w;
+  const int key0 = it.x, nkeys = it.y & 0xffff, kind = it.y >> 16, q0 = it.z, nq = it.w;
   const int part = a.item_part[item];
   if (part >= a.cap || nq <= 0 || nq > kCq) return;
   TokenInfo ti;
@@ -485,9 +487,9 @@ void k_kl_keys(KeysArgs a) {
       slot_s[tq & 1][tid] = s;
     }
   };
-  // k-step s (query s / 2, heads 32 (s % 2) ..) into buffer s % 3.  Parts 0, 1: qI rows
-  // 8w + 4jj .. +3 (lane l: row + l/16, physical chunk l%16); parts 2, 3: the 64-byte E pieces
-  // of rows 32w + 16jj .. +15 (lane l: row + l/4, physical chunk l%4)
+  // k-step s (query s / 2, heads 32 (s % 2) ..) into buffer s % 3.  qI parts 0, 1: rows
+  // 8w + 4jj .. +3 (lane l: row + l/16, physical chunk l%16); E parts 0 .. 3: the 64-byte E
+  // pieces of rows 64w + 16jj .. +15 (lane l: row + l/4, physical chunk l%4)
   auto b_src = [&](int s) { return a.q + ((int64_t)(q0 + (s >> 1)) * 64 + 32 * (s & 1)) * kDI; };
   auto issue_b = [&](int s, const uint16_t* src, int jj) {
     const int r0 = 8 * wave + 4 * jj, r = r0 + (lane >> 4);
@@ -495,29 +497,29 @@ void k_kl_keys(KeysArgs a) {
   };
   auto a_src = [&](int s, int jj) {
     const int tq = s >> 1, i = s & 1;
-    const int sl = slot_s[tq & 1][32 * wave + 16 * jj + (lane >> 2)];
+    const int sl = slot_s[tq & 1][64 * wave + 16 * jj + (lane >> 2)];
     const int lc = (lane & 3) ^ (lane >> 4);
     return (sl >= 0 && sl != 0x7fffffff)
                ? a.pds + ((int64_t)(q0 + tq - a.t0) * a.n_slots + sl) * 64 + 32 * i + 8 * lc
                : a.zeros;
   };
   auto issue_a = [&](int s, const uint16_t* src, int jj) {
-    dma16(src, &As[s % 3][32 * wave + 16 * jj][0]);
+    dma16(src, &As[s % 3][64 * wave + 16 * jj][0]);
   };
   auto issue = [&](int s) {
     const uint16_t* src = b_src(s);
     issue_b(s, src, 0);
     issue_b(s, src, 1);
-    issue_a(s, a_src(s, 0), 0);
-    issue_a(s, a_src(s, 1), 1);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) issue_a(s, a_src(s, jj), jj);
   };
 
   const int trr = 8 * g + (c16 >> 2), tre = (c16 & 3) >> 1, troff = 4 * (c16 & 1);
   const int lo_s = 8 * ((4 * wave + tre) ^ swz(trr)), hi_s = 8 * ((4 * wave + tre) ^ swz(trr + 4));
   const int aoff = 8 * (g ^ (c16 >> 2));
-  f32x4 acc[8][2];
+  f32x4 acc[16][2];
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < 16; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // The loads of k-step s + 2 are issued in k-step s, so the slot map of query tq + 2 is
   // formed in query tq's k-steps (idx row loaded in the first, mapped in the second) and
@@ -535,25 +537,24 @@ void k_kl_keys(KeysArgs a) {
   auto body = [&](auto more_c, int s) {
     constexpr bool kMore = decltype(more_c)::value;
     const int tq = s >> 1, i = s & 1, buf = s % 3;
-    // every wave issues 4 loads per k-step (an idx row's loads come before them): all but
+    // every wave issues 6 loads per k-step (an idx row's loads come before them): all but
     // the next k-step's are done
-    if (s + 1 < S) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    if (s + 1 < S) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
     else wait_vmem();
     __syncthreads();
     if (i == 0 && tq + 2 < nq) prep0(tq + 2);
     if (i == 1 && tq + 2 < nq) prep1(tq + 2);
     if (kMore) issue(s + 2);
-    bf16x8 bv[2], av[8];
+    bf16x8 bv[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
       bv[nt] = join8(ld_tr(&Bs[buf][trr][troff + (lo_s ^ (16 * nt))]),
                      ld_tr(&Bs[buf][trr + 4][troff + (hi_s ^ (16 * nt))]));
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) av[mt] = ld16(&As[buf][16 * mt + c16][aoff]);
+    for (int mt = 0; mt < 16; ++mt) {
+      const bf16x8 av = ld16(&As[buf][16 * mt + c16][aoff]);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16(av[mt], bv[nt], acc[mt][nt]);
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16(av, bv[nt], acc[mt][nt]);
     }
   };
   int s = 0;
@@ -562,7 +563,7 @@ void k_kl_keys(KeysArgs a) {
   // rows 16mt + 4g + i, d = 32w + 16nt + c16
   float* dst = part >= 0 ? a.part + (int64_t)part * kKeys * kDI : a.dkv_cmp + (int64_t)key0 * kDI;
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+  for (int mt = 0; mt < 16; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * mt + 4 * g + i;
@@ -582,6 +583,7 @@ hipError_t launch_attn_bwd_keys(const KeysArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_attn_bwd_keys_sums(const KeysArgs& a, hipStream_t s) {
+  if (a.kb != 128) return hipErrorInvalidValue;
   const int64_t grid = ((a.cap + 7) / 8) * 8;
   if (a.mode != 0)
     hipLaunchKernelGGL(k_attn_bwd_keys<0>, dim3((unsigned)grid), dim3(512), 0, s, a);
@@ -589,13 +591,14 @@ hipError_t launch_attn_bwd_keys_sums(const KeysArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_attn_bwd_keys<2>, dim3((unsigned)grid), dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL(k_attn_bwd_keys<4>, dim3((unsigned)grid), dim3(512), 0, s, a);
-  const int64_t rgrid = a.cap * 16 < 2048 ? a.cap * 16 : 2048;
+  const int64_t rgrid = a.cap * (a.kb / 8) < 2048 ? a.cap * (a.kb / 8) : 2048;
   hipLaunchKernelGGL(k_attn_bwd_keys_reduce, dim3((unsigned)(rgrid > 0 ? rgrid : 1)), dim3(256), 0, s, a);
   if (a.mode == 0) hipLaunchKernelGGL(k_attn_bwd_keys_dups, dim3(1024), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_kl_keys_sums(const KeysArgs& a, hipStream_t s) {
+  if (a.kb != 256) return hipErrorInvalidValue;
   const int64_t grid = ((a.cap + 7) / 8) * 8;
   if (a.mode != 0)
     hipLaunchKernelGGL(k_kl_keys<0>, dim3((unsigned)grid), dim3(256), 0, s, a);
@@ -603,7 +606,7 @@ hipError_t launch_kl_keys_sums(const KeysArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_kl_keys<4>, dim3((unsigned)grid), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(k_kl_keys<8>, dim3((unsigned)grid), dim3(256), 0, s, a);
-  const int64_t rgrid = a.cap * 16 < 2048 ? a.cap * 16 : 2048;
+  const int64_t rgrid = a.cap * (a.kb / 8) < 2048 ? a.cap * (a.kb / 8) : 2048;
   hipLaunchKernelGGL(k_attn_bwd_keys_reduce, dim3((unsigned)(rgrid > 0 ? rgrid : 1)), dim3(256), 0, s, a);
   if (a.mode == 0) hipLaunchKernelGGL(k_attn_bwd_keys_dups, dim3(1024), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -593,7 +593,7 @@ struct BwdPlan {
 bool keys_path(const Shape& sh) {
   const int64_t n_cap = sh.r > 0 ? sh.max_seqlen / sh.r : 0;
   if (sh.mode == 2) return true;
-  if (n_cap / keys::kKeys + 1 > 2048) return false;
+  if (n_cap / 128 + 1 > 2048) return false;
   if (sh.mode == 1) return true;
   return sh.k_cap <= 2048 && n_cap <= 6ll * sh.k_cap;
 }
@@ -612,12 +612,12 @@ BwdPlan bwd_layout(const Shape& sh, int64_t chunk) {
   p.off_nc = o;    o = al(o + (size_t)sh.T * 4);
   if (p.keys) {
     const int n_cap = sh.mode == 2 ? 0 : sh.max_seqlen / sh.r;
-    p.cap = keys::item_cap(sh.mode, sh.B, (int)chunk, n_cap, sh.W);
+    p.cap = keys::item_cap(sh.mode, sh.B, (int)chunk, n_cap, sh.W, 128);
     p.off_cnt = o;   o = al(o + 128 * 4);   // 64 counters, then 256 zero bytes
     p.off_items = o; o = al(o + (size_t)p.cap * 16);
     p.off_ipart = o; o = al(o + (size_t)p.cap * 4);
     p.off_red = o;   o = al(o + (size_t)p.cap * 16);
-    p.off_part = o;  o = al(o + (size_t)p.cap * keys::kKeys * kD * 4);
+    p.off_part = o;  o = al(o + (size_t)p.cap * 128 * kD * 4);
   } else {
     p.off_stage = o; o = al(o + (size_t)p.chunk * p.n_slots * kD * 2);
     p.off_cnt = o;   o = al(o + (size_t)p.Tc_cap * 4);
@@ -743,6 +743,7 @@ hipError_t launch_attn_bwd_mfma(const Shape& sh, const AttnIO& io, hipStream_t s
     ka.mode = sh.mode;
     ka.D = kD;
     ka.KC = 128;
+    ka.kb = 128;
   }
   for (int64_t t0 = 0; t0 < sh.T; t0 += pl.chunk) {
     b.t0 = (int)t0;

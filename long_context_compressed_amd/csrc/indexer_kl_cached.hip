@@ -505,7 +505,7 @@ bool klc_handles(const Shape& sh) {
     return false;
   // the key-major key gradients: idx rows held in LDS, per-sample block tables
   const int64_t n_cap = sh.max_seqlen / sh.r;
-  return (sh.mode == 1 || sh.k_cap <= 2048) && n_cap / keys::kKeys + 1 <= 2048;
+  return (sh.mode == 1 || sh.k_cap <= 2048) && n_cap / 256 + 1 <= 2048;
 }
 
 KlcPlan klc_layout(const Shape& sh, int64_t chunk) {
@@ -513,7 +513,7 @@ KlcPlan klc_layout(const Shape& sh, int64_t chunk) {
   p.k_slots = sh.mode == 0 ? sh.k_cap : sh.max_seqlen / sh.r;
   if (p.k_slots < 1) p.k_slots = 1;
   p.chunk = chunk;
-  p.cap = keys::item_cap(sh.mode, sh.B, (int)chunk, sh.max_seqlen / sh.r, 0);
+  p.cap = keys::item_cap(sh.mode, sh.B, (int)chunk, sh.max_seqlen / sh.r, 0, 256);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t o = 0;
   p.off_es = o;    o = al(o + (size_t)p.chunk * p.k_slots * kHI * 2);
@@ -522,7 +522,7 @@ KlcPlan klc_layout(const Shape& sh, int64_t chunk) {
   p.off_items = o; o = al(o + (size_t)p.cap * 16);
   p.off_ipart = o; o = al(o + (size_t)p.cap * 4);
   p.off_red = o;   o = al(o + (size_t)p.cap * 16);
-  p.off_part = o;  o = al(o + (size_t)p.cap * keys::kKeys * kDI * 4);
+  p.off_part = o;  o = al(o + (size_t)p.cap * 256 * kDI * 4);
   p.total = o;
   return p;
 }
@@ -597,6 +597,7 @@ hipError_t launch_indexer_kl_cached(const Shape& sh, const KlIO& io, hipStream_t
   k.mode = sh.mode;
   k.D = kDI;
   k.KC = kHI;
+  k.kb = 256;
   for (int64_t t0 = 0; t0 < sh.T; t0 += pl.chunk) {
     a.t0 = k.t0 = (int)t0;
     a.nT = k.nT = (int)(sh.T - t0 < pl.chunk ? sh.T - t0 : pl.chunk);
