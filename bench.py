@@ -68,11 +68,11 @@ def parse():
 
 # kernels of each multi-kernel ABI call, by the demangled name prefix rocprofv3 reports
 CALL_KERNELS = {
-    "attn_bwd": ("k_attn_bwd_dq_mfma", "k_attn_bwd_dkv_mfma", "k_bwd_fill_zero", "k_bwd_csr_pass",
-                 "k_bwd_csr_scan", "k_bwd_reduce_cmp", "k_bwd_reduce_win", "k_attn_bwd_generic"),
+    "attn_bwd": ("k_attn_bwd_dq_mfma", "k_attn_bwd_keys", "k_attn_bwd_keys_dups",
+                 "k_attn_bwd_dkv_mfma", "k_bwd_fill_zero", "k_bwd_csr_pass", "k_bwd_csr_scan",
+                 "k_bwd_reduce_cmp", "k_bwd_reduce_win", "k_attn_bwd_generic"),
     "attn_fwd": ("k_attn_fwd_mfma", "k_attn_fwd_generic"),
-    "indexer_kl": ("k_kl_cached", "k_fill_zero_i32", "k_csr_pairs", "k_csr_scan", "k_csr_reduce",
-                   "k_indexer_kl_mfma", "k_kl_generic", "k_sum", "k_kld_teacher",
+    "indexer_kl": ("k_kl_cached", "k_kl_keys", "k_fill_zero_i32", "k_indexer_kl_mfma", "k_kl_generic", "k_sum", "k_kld_teacher",
                    "k_kld_queries", "k_kld_keys", "k_kld_dequant"),
     "index_topk": ("k_index_topk",),
     "index_scores": ("k_index_scores_mfma", "k_index_scores_generic"),
@@ -84,6 +84,10 @@ CALL_KERNELS = {
     "compress_bwd (kv + kI)": ("k_compress_bwd",),
     "rope (all operands)": ("k_rope",),
 }
+# kernels launched by more than one call (the key-major planner and partial-sum reduction of the
+# attention backward and the indexer loss): each dispatch belongs to the call whose own kernel
+# was dispatched last before it (both calls open with a fill kernel of their own)
+SHARED_KERNELS = ("k_attn_bwd_keys_plan", "k_attn_bwd_keys_reduce")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "thd64k_csa_bf16_traffic.md")
 
 
@@ -155,10 +159,15 @@ def summarize_pmc(fetch_dir, write_dir, copy_bytes):
         copies = [v for _, n, _, v in rows if "copyBuffer" in n]
         factor = copy_bytes / (max(copies) * 1024.0)
         per_call = {}
-        for _, n, _, v in rows:
-            for call, ks in CALL_KERNELS.items():
-                if n in ks:
-                    per_call[call] = per_call.get(call, 0.0) + v * 1024.0 * factor
+        current = None
+        for _, n, _, v in sorted(rows):
+            call = next((c for c, ks in CALL_KERNELS.items() if n in ks), None)
+            if call is not None:
+                current = call
+            elif n in SHARED_KERNELS:
+                call = current
+            if call is not None:
+                per_call[call] = per_call.get(call, 0.0) + v * 1024.0 * factor
         res[label] = {"factor": factor, "copy_kib": max(copies), "per_call_bytes": per_call}
     return res
 
