@@ -68,8 +68,9 @@ struct KlcArgs {
 };
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// at most 2 vector memory operations outstanding (they complete in issue order)
-__device__ __forceinline__ void wait_vmem_2() { asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); }
+// at most 4 or 6 vector memory operations outstanding (they complete in issue order)
+__device__ __forceinline__ void wait_vmem_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
+__device__ __forceinline__ void wait_vmem_6() { asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); }
 
 __device__ __forceinline__ void dma_rows16(const void* src, const void* lds) {
   const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
@@ -106,7 +107,8 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 
 }  // namespace
 
-// IDX_LDS: the query's idx row and its student scores (k_cap <= kIdxLds) are staged in LDS,
+// IDX_LDS: the query's idx row and its student scores (C_t of at most kIdxLds slots: k_cap
+// for the selected teacher, max_seqlen / ratio for the dense one) are staged in LDS,
 // so that the block loop's only global loads are the cached logits and the key rows, neither
 // needed in the block that issues it (a load consumed right away would make the wave wait
 // for every older memory operation, the previous block's staged stores included).
@@ -116,6 +118,7 @@ void k_kl_cached(KlcArgs a) {
   __shared__ int32_t idx_s[IDX_LDS ? kIdxLds : 1];
   __shared__ float sc_s[IDX_LDS ? kIdxLds : 1];   // student scores of the slots
   __shared__ __attribute__((aligned(16))) uint16_t KIt[2][kNB][kDI];   // swizzled 256-byte rows
+  __shared__ __attribute__((aligned(16))) uint16_t QIs[kHI][kDI];      // the query's qI, swizzled
   __shared__ __attribute__((aligned(16))) uint16_t EsT[kNB][kEST];
   __shared__ float Pp[4][kNB];
   __shared__ float gw_s[4][kNB];
@@ -168,24 +171,27 @@ void k_kl_cached(KlcArgs a) {
   };
 
   // ---- loads of the query's resident operands, issued before the student scores so that
-  // their latencies overlap: qI^T B operand of z, weights, teacher lse
-  bf16x8 qib[2][4];   // heads 32hh + 16nt + c16, d = 32ks + 8g .. +7
+  // their latencies overlap: qI (the B operand of z; into LDS, wave w rows 16w .. 16w+15, 4
+  // rows per instruction: lane l fills physical chunk l % 16 of row 4i + l / 16), weights,
+  // teacher lse
   float wv[2];
   if (a.grads) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const uint16_t* src = a.qI + ((int64_t)t * kHI + 32 * hh + 16 * nt + c16) * kDI + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qib[nt][ks] = ld16(src + 32 * ks);
-      wv[nt] = a.w[(int64_t)t * kHI + 32 * hh + 16 * nt + c16];
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * wave + 4 * i + (lane >> 4);
+      dma_rows16(a.qI + ((int64_t)t * kHI + r) * kDI + 8 * ((lane & 15) ^ swz(r)),
+                 &QIs[16 * wave + 4 * i][0]);
     }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) wv[nt] = a.w[(int64_t)t * kHI + 32 * hh + 16 * nt + c16];
   }
   const float tlse_v = (a.tlse && tid < kHT) ? a.tlse[(int64_t)t * kHT + tid] : 0.f;
 
   // ---- student log-sum-exp over C_t.  With up to kIdxLds slots the scores are read once,
   // all loads in flight together, and kept in LDS for the block loop (-inf marks a slot
   // outside C_t or the visible range); longer rows read them where they are used.
-  const bool sc_lds = IDX_LDS && n_c <= kIdxLds;
+  // (IDX_LDS is launched only where every C_t has at most kIdxLds slots)
+  constexpr bool sc_lds = IDX_LDS;
   float mx = -INFINITY;
   if (sc_lds) {
     constexpr int kPT = (IDX_LDS ? kIdxLds : 256) / 256;
@@ -303,25 +309,29 @@ void k_kl_cached(KlcArgs a) {
   wait_vmem();
   __syncthreads();
 
-  // cached teacher logits of a block: thread = (heads 4 hq .. +3, slots 4 sq .. +3), read a
-  // block ahead (the logits come from HBM; reading them where they are used would expose
-  // that latency once per block)
+  // cached teacher logits of a block: thread = (heads 4 hq .. +3, slots 4 sq .. +3), read two
+  // blocks ahead (the logits come from HBM: with one block in flight per workgroup the loss
+  // ran at the rate that a block's worth of loads per workgroup sustains at HBM latency, well
+  // below the bandwidth).  Three register sets take turns (block b reads set b % 3 and loads
+  // set (b + 2) % 3), so no set is copied while its loads are in flight, and every block
+  // issues exactly 4 loads (past the last block they repeat it), so the waits can count them.
   const int hq = tid >> 4, sq = tid & 15;
   auto load_logits = [&](int b, f32x4 (&v)[4]) {
+    const int bb = b < nblk ? b : nblk - 1;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      v[k] = b < nblk ? *reinterpret_cast<const f32x4*>(tl_t + (int64_t)(4 * hq + k) * a.ld_t +
-                                                        kNB * b + 4 * sq)
-                      : f32x4{0.f, 0.f, 0.f, 0.f};
+      v[k] = *reinterpret_cast<const f32x4*>(tl_t + (int64_t)(4 * hq + k) * a.ld_t + kNB * bb +
+                                             4 * sq);
   };
-  f32x4 lg_cur[4], lg_nxt[4];
-  load_logits(0, lg_cur);
+  f32x4 lg_a[4], lg_b[4], lg_c[4];
+  load_logits(0, lg_a);
+  load_logits(1, lg_b);
   // block 0's logits complete before the loop, so that inside it the waits for the logits
-  // count only the previous block's younger loads and stores
+  // count only younger loads and stores
 #pragma unroll
-  for (int k = 0; k < 4; ++k) asm volatile("" :: "v"(lg_cur[k]));
+  for (int k = 0; k < 4; ++k) asm volatile("" :: "v"(lg_a[k]));
 
-  for (int b = 0; b < nblk; ++b) {
+  auto block = [&](int b, f32x4 (&lg_cur)[4], f32x4 (&lg_ld)[4]) {
     const int buf = b & 1;
     const int rid_nn = row_of(b + 2);
 
@@ -342,15 +352,16 @@ void k_kl_cached(KlcArgs a) {
       }
       if (g == 0) *reinterpret_cast<f32x4*>(&Pp[wave][4 * sq]) = f32x4{pj[0], pj[1], pj[2], pj[3]};
     }
-    // key rows of this block, issued during the previous block; the only younger memory
-    // operations are that block's logit loads (already consumed above) and, if this wave
-    // wrote E of any slot of it, its 2 E stores, which may stay in flight
-    if (IDX_LDS && a.grads && b > 0 && kNB * (b - 1) + 16 * wave < n_c) wait_vmem_2();
-    else wait_vmem();
+    // key rows of this block, issued during the previous block; younger than them are that
+    // block's 4 logit loads (for block b + 1, left in flight) and, if this wave wrote E of
+    // any slot of it, its 2 E stores (block 0: its rows were waited for before the loop)
+    if (!IDX_LDS) wait_vmem();
+    else if (a.grads && b > 0 && kNB * (b - 1) + 16 * wave < n_c) wait_vmem_6();
+    else wait_vmem_4();
     __syncthreads();
     // the other key buffer was last read before the previous block's second barrier
     if (b + 1 < nblk) issue(rid_nxt, buf ^ 1);
-    load_logits(b + 1, lg_nxt);
+    load_logits(b + 2, lg_ld);
     const float sc_nn = score_of(b + 2);   // used two blocks on
 
     // ---- per slot (lane l = slot 64 b + l): P, Q, KL and g; g w per wave in LDS
@@ -380,8 +391,10 @@ void k_kl_cached(KlcArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const bf16x8 av = ld16(rp + za[ks]);
-          z[mt][0] = mfma16(av, qib[0][ks], z[mt][0]);
-          z[mt][1] = mfma16(av, qib[1][ks], z[mt][1]);
+          // B: qI of heads 32hh + 16nt + c16 (row bits 0-3 = c16), d = 32ks + 8g .. +7
+          const int qc = 8 * ((4 * ks + g) ^ swz(c16));
+          z[mt][0] = mfma16(av, ld16(&QIs[32 * hh + c16][qc]), z[mt][0]);
+          z[mt][1] = mfma16(av, ld16(&QIs[32 * hh + 16 + c16][qc]), z[mt][1]);
         }
       }
       // ---- E = g w 1[z > 0]; dw += g relu(z); E (bf16) to LDS as [slot][head]
@@ -442,9 +455,17 @@ void k_kl_cached(KlcArgs a) {
     rid_nxt = rid_nn;
     sc_cur = sc_nxt;
     sc_nxt = sc_nn;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) lg_cur[k] = lg_nxt[k];
+  };
+  // whole rounds of three blocks, then the one or two left (no block of a round is
+  // conditional, so the waits for the logits can count the loads issued after them)
+  int b = 0;
+  for (; b + 2 < nblk; b += 3) {
+    block(b, lg_a, lg_c);
+    block(b + 1, lg_b, lg_a);
+    block(b + 2, lg_c, lg_b);
   }
+  if (b < nblk) block(b, lg_a, lg_c);
+  if (b + 1 < nblk) block(b + 1, lg_b, lg_a);
 
   // ---- outputs: kl, dw, dqI (the two slot halves ch = 0, 1 summed through LDS)
   if (wave == 0) {
@@ -606,7 +627,7 @@ hipError_t launch_indexer_kl_cached(const Shape& sh, const KlIO& io, hipStream_t
       hipError_t e = launch_attn_bwd_keys(k, s);
       if (e != hipSuccess) return e;
     }
-    if (sh.k_cap <= kIdxLds)
+    if ((sh.mode == 0 ? (int64_t)sh.k_cap : a.n_cap) <= kIdxLds)
       hipLaunchKernelGGL(k_kl_cached<true>, dim3((unsigned)token_grid(a.nT)), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL(k_kl_cached<false>, dim3((unsigned)token_grid(a.nT)), dim3(256), 0, s, a);

@@ -397,6 +397,38 @@ def test_topk_ties_signed_zero_and_long_rows():
             assert np.all(got[i][n:] == -1)
 
 
+def test_topk_many_rows_per_wave_with_padding():
+    """Rows of up to 4096 visible scores over several samples and capacity padding: each
+    wave of the stand-alone kernel walks many rows (light, heavy and padding rows mixed), so
+    every row's selection must come out of the row it was loaded for."""
+    from long_context_compressed_amd import binding as B
+    lengths, pad, k, kcap = (9001, 301, 11999, 7), 499, 1024, 1088
+    print(f"[gpu] case=topk_many_rows lengths={lengths} pad={pad} k={k}", flush=True)
+    rng = np.random.default_rng(11)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    T = int(cu[-1]) + pad
+    max_len = max(lengths)
+    n_cap = max_len // 4
+    s = rng.standard_normal((T, n_cap)).astype(np.float32)
+    s[1::7, ::5] = 0.0                       # ties in some rows
+    p = B.make_params(batch=len(lengths), total_tokens=T, max_seqlen=max_len, ratio=4,
+                      window=1, topk=k, topk_cap=kcap, heads=1, head_dim=8, idx_heads=1,
+                      idx_dim=8, scale=1.0, mode=0, teacher=0, dtype=1, idx_dtype=1)
+    idx = torch.full((T, kcap), 7, dtype=torch.int32, device="cuda")
+    cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    cmp_d = torch.empty(len(lengths) + 1, dtype=torch.int32, device="cuda")
+    B.csa_cmp_seqlens(cu_d, len(lengths), 4, cmp_d)
+    B.csa_topk_select(p, torch.from_numpy(s).cuda(), cu_d, cmp_d, idx)
+    got = idx.cpu().numpy()
+    assert np.all(got[int(cu[-1]):] == -1), "padding rows"
+    rows = np.unique(np.concatenate([np.arange(0, T, 5), np.arange(int(cu[-1]) - 40, T)]))
+    ref = O.topk_select(s[rows], cu, 4, k, kcap, T, rows=rows)
+    for i, t in enumerate(rows):
+        n = int((ref[i] >= 0).sum())
+        assert np.array_equal(got[t][:n], np.sort(ref[i][:n])), t
+        assert np.all(got[t][n:] == -1), t
+
+
 def _check_selection(got, ref_scores, row0, k, rel_tol, tag):
     """`got` (one idx row) against fp64 oracle scores of the same query: the min(k, n_vis)
     selected rows ascending, -1 after them, and the set equal to the oracle's top-k except
@@ -748,15 +780,31 @@ def _kl_variants():
 def test_indexer_kl(name, grads, from_fwd):
     """from_fwd: "none" (teacher recomputed), "lse" (teacher normalizer from the GPU
     forward), "cache" (normalizer and teacher logits from the GPU forward)."""
+    _indexer_kl_check(name, grads, from_fwd)
+
+
+@pytest.mark.parametrize("name", ["csa_bf16_thd_small", "csa_bf16_thd_staged"])
+def test_indexer_kl_repeated_rows(name):
+    """A row listed twice in one query's idx row is two members of C_t: loss and gradients
+    from the cached teacher against the oracle on such idx rows (the key-major key gradient
+    adds the later listings in a separate pass, from the same E records)."""
+    _indexer_kl_check(name, True, "cache",
+                      lambda idx, host, w: _repeat_rows(idx, host["cu_seqlens"], w.ratio))
+
+
+def _indexer_kl_check(name, grads, from_fwd, edit_idx=None):
     from long_context_compressed_amd import binding as B
     w, host, h64 = _case(name)
-    _announce(name, f"indexer_kl grads={grads} from_fwd={from_fwd}")
+    _announce(name, f"indexer_kl grads={grads} from_fwd={from_fwd}" +
+              ("" if edit_idx is None else " repeated rows"))
     fwd_lse = from_fwd != "none"
     L = _layer(w, host, backward=True)
     cu = _cu(host)
     L.metadata(cu)
     dt = G.torch_dtype(w.dtype)
     kv_cmp_r, idx = _attn_inputs(w, host, h64)
+    if edit_idx is not None:
+        idx = edit_idx(idx, host, w)
     d, qI64, kI64 = _indexer_inputs(w, host, h64)
     sc = O.index_scores(qI64, h64["w"], kI64, host["cu_seqlens"], w.ratio, L.n_cap)
     s32 = np.where(np.isfinite(sc), sc, 0.0).astype(np.float32)
