@@ -397,13 +397,14 @@ def test_topk_ties_signed_zero_and_long_rows():
             assert np.all(got[i][n:] == -1)
 
 
-def test_topk_many_rows_per_wave_with_padding():
-    """Rows of up to 4096 visible scores over several samples and capacity padding: each
-    wave of the stand-alone kernel walks many rows (light, heavy and padding rows mixed), so
-    every row's selection must come out of the row it was loaded for."""
+def test_topk_mixed_rows_with_padding():
+    """Rows of up to 4096 visible scores (the wave kernel's largest register footprint) over
+    several samples and capacity padding: light rows (every visible row selected), heavy rows
+    with and without ties, and padding rows (-1) in one launch, bit-exact against the oracle
+    on every fifth row and on the rows around the end of the packed batch."""
     from long_context_compressed_amd import binding as B
     lengths, pad, k, kcap = (9001, 301, 11999, 7), 499, 1024, 1088
-    print(f"[gpu] case=topk_many_rows lengths={lengths} pad={pad} k={k}", flush=True)
+    print(f"[gpu] case=topk_mixed_rows lengths={lengths} pad={pad} k={k}", flush=True)
     rng = np.random.default_rng(11)
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
     T = int(cu[-1]) + pad
