@@ -10,7 +10,7 @@
 // consecutive rows of one sample (compressed rows, or raw window rows) against a range of
 // up to kCq consecutive queries of that sample; the (query, row) pairs a query does not
 // attend contribute zero.  Items of one block write fp32 partial sums that a reduction adds
-// in a fixed order (one item: added directly), so the result does not depend on scheduling.
+// in a fixed order, so the result does not depend on scheduling.
 //
 // This file holds the enumeration of the work items, shared by the device planner and the
 // host bound on their number.
@@ -121,7 +121,7 @@ struct KeysArgs {
   const int32_t* cu_cmp;
   const uint16_t* zeros;    // >= 16 zero bytes
   int4* items;              // [cap] key0, nkeys | kind << 16, first query, queries
-  int32_t* item_part;       // [cap] partial slot of the item, -1: added directly
+  int32_t* item_part;       // [cap] partial slot of the item
   int4* red;                // [cap] key0, nkeys | kind << 16, first partial slot, slots
   float* part;              // [cap, kb, D]
   int32_t* counters;        // [0] items, [1] reduction records, [2] repeated-row flag (zeroed)

@@ -12,8 +12,9 @@
 // dS|P slot are loaded global -> LDS, four k-steps of 32 per query, three k-steps in flight.
 // Rows the query does not attend load zeros.  No per-pair row gradient is ever stored: the
 // workgroup keeps its 128 x 512 fp32 sums in registers for all its queries and writes them
-// once (to the row gradient directly when the block has one item, else to a partial slot that
-// k_attn_bwd_keys_reduce adds in item order).
+// once, with plain stores, to a partial slot that k_attn_bwd_keys_reduce adds to the rows in
+// item order (also for a block with one item: a read-modify-write of the rows here would wait
+// out one memory round trip per value).
 //
 // A row listed twice in one query's idx row (allowed by the sparse layout: each listing is a
 // candidate of its own) is taken once here, at its first slot; k_attn_bwd_keys_dups adds the
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_keys_plan(KeysArgs a) {
         const int k = k0 + tid;
         const bool in = k < nblk;
         const int clo = in ? cmp_clo(sc, a.r, k, a.kb) : 0;
-        const int ni = in ? nch - clo : 0, v = ni >= 2 ? ni : 0;
+        const int ni = in ? nch - clo : 0, v = ni;
         int tot, rtot;
         const int pre = wg_scan(v, sc_s, tot);
         const int rpre = wg_scan(v > 0 ? 1 : 0, sc_s, rtot);
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_keys_plan(KeysArgs a) {
         const int m = mlo + m0 + tid;
         WinBlock wb = {0, 0, 0, 0};
         if (m0 + tid < nm) wb = win_block(sc, a.W, m, a.kb);
-        const int np = wb.pieces, v = np >= 2 ? np : 0;
+        const int np = wb.pieces, v = np;
         int tot, ptot, rtot;
         const int pre = wg_scan(np, sc_s, tot);
         const int ppre = wg_scan(v, sc_s, ptot);
@@ -197,7 +198,7 @@ void k_attn_bwd_keys(KeysArgs a) {
   const int4 it = a.items[item];
   const int key0 = it.x, nkeys = it.y & 0xffff, kind = it.y >> 16, q0 = it.z, nq = it.w;
   const int part = a.item_part[item];
-  if (part >= a.cap || nq <= 0 || nq > kCq) return;
+  if (part < 0 || part >= a.cap || nq <= 0 || nq > kCq) return;
   TokenInfo ti;
   token_info_wave(a.cu, a.B, q0, ti, kind == kKindWin ? nullptr : a.cu_cmp);
   const int s0 = ti.start, c0 = ti.c0;
@@ -322,8 +323,7 @@ void k_attn_bwd_keys(KeysArgs a) {
   for (; s + 2 < S; ++s) body(std::true_type(), s);
   for (; s < S; ++s) body(std::false_type(), s);
   // rows 16mt + 4g + i, d = 64w + 16nt + c16
-  float* dst = part >= 0 ? a.part + (int64_t)part * kKeys * kD
-                         : (kind == kKindWin ? a.dkv : a.dkv_cmp) + (int64_t)key0 * kD;
+  float* dst = a.part + (int64_t)part * kKeys * kD;
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -332,14 +332,11 @@ void k_attn_bwd_keys(KeysArgs a) {
       if (row >= nkeys) continue;
       float* o = dst + (int64_t)row * kD + 64 * wave + c16;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        if (part >= 0) o[16 * nt] = acc[mt][nt][i];
-        else o[16 * nt] += acc[mt][nt][i];
-      }
+      for (int nt = 0; nt < 4; ++nt) o[16 * nt] = acc[mt][nt][i];
     }
 }
 
-// ---- blocks with several items: rows += sum of their partial slots, in slot order.
+// ---- every block: rows += sum of its partial slots, in slot order.
 // Work unit = (block record, 8 rows); lane: row 8u' + tid / 32, columns (tid % 32) D/32 ..
 // (D = 512 or 128: 4 or 1 float4 per lane).
 __global__ __launch_bounds__(256) void k_attn_bwd_keys_reduce(KeysArgs a) {
@@ -449,7 +446,7 @@ void k_kl_keys(KeysArgs a) {
   const int4 it = a.items[item];
   const int key0 = it.x, nkeys = it.y & 0xffff, kind = it.y >> 16, q0 = it.z, nq = it.w;
   const int part = a.item_part[item];
-  if (part >= a.cap || nq <= 0 || nq > kCq) return;
+  if (part < 0 || part >= a.cap || nq <= 0 || nq > kCq) return;
   TokenInfo ti;
   token_info_wave(a.cu, a.B, q0, ti, a.cu_cmp);
   const int s0 = ti.start, c0 = ti.c0;
@@ -561,7 +558,7 @@ void k_kl_keys(KeysArgs a) {
   for (; s + 2 < S; ++s) body(std::true_type(), s);
   for (; s < S; ++s) body(std::false_type(), s);
   // rows 16mt + 4g + i, d = 32w + 16nt + c16
-  float* dst = part >= 0 ? a.part + (int64_t)part * kKeys * kDI : a.dkv_cmp + (int64_t)key0 * kDI;
+  float* dst = a.part + (int64_t)part * kKeys * kDI;
 #pragma unroll
   for (int mt = 0; mt < 16; ++mt)
 #pragma unroll
@@ -570,10 +567,7 @@ void k_kl_keys(KeysArgs a) {
       if (row >= nkeys) continue;
       float* o = dst + (int64_t)row * kDI + 32 * wave + c16;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        if (part >= 0) o[16 * nt] = acc[mt][nt][i];
-        else o[16 * nt] += acc[mt][nt][i];
-      }
+      for (int nt = 0; nt < 2; ++nt) o[16 * nt] = acc[mt][nt][i];
     }
 }
 
