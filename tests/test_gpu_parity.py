@@ -937,6 +937,67 @@ def test_indexer_kl_dense_teacher_chunked(idx_dtype, boost, given):
             _check_open("dkI_cmp", G.back(L.dkI_cmp)[:kI64.shape[0]], dkI, open_bound[2])
 
 
+def test_indexer_kl_dense_teacher_from_cache():
+    """The cached-teacher loss with the dense teacher (CSA_DENSE attention: C_t = every visible
+    compressed row): the forward keeps every visible row's logits in visible order, the loss
+    reads them instead of recomputing the teacher, and the key-major key gradient runs over the
+    dense kind of rows.  Unit-variance inputs (peaked teacher), capacity padding, against the
+    oracle with its open-ReLU bound."""
+    from long_context_compressed_amd import binding as B
+    w = configs.workload("thd64k_csa_bf16", mode="dense", teacher="dense", lengths=(301, 515, 1027),
+                         total_tokens=1856, draw=None)
+    host = synth_inputs.make_inputs(w, variant=0, strength=True)
+    h64 = {k: synth_inputs.to_f64(v) for k, v in host.items() if isinstance(v, torch.Tensor)}
+    h64["cu_seqlens"] = host["cu_seqlens"]
+    h64["max_seqlen"] = host["max_seqlen"]
+    _announce("dense_teacher_bf16_cached", "attn_fwd + indexer_kl from the teacher cache")
+    L = _layer(w, host, backward=True)
+    cu = _cu(host)
+    L.metadata(cu)
+    dt = G.torch_dtype(w.dtype)
+    kv_cmp_r, _ = _attn_inputs(w, host, h64)
+    d, qI64, kI64 = _indexer_inputs(w, host, h64)
+    sc = O.index_scores(qI64, h64["w"], kI64, host["cu_seqlens"], w.ratio, L.n_cap)
+    s32 = np.where(np.isfinite(sc), sc, 0.0).astype(np.float32)
+    ld_t = B.csa_teacher_logits_stride(L.p)
+    assert ld_t >= L.n_cap and ld_t % 64 == 0
+    t_logits = torch.full((w.total_tokens, w.heads, ld_t), float("nan"), device="cuda")
+    kvc = G.dev(kv_cmp_r, dt)
+    B.csa_sparse_attn_fwd(L.p, host["q"].cuda(), kvc, host["kv"].cuda(), None, None, cu,
+                          L.cu_cmp, L.out, L.lse, None, ws=L.ws_fwd, t_logits=t_logits)
+    n_ws = B.csa_workspace_size(L.p, B.CSA_OP_INDEXER_KL_CACHED)
+    ws = torch.empty(n_ws, dtype=torch.uint8, device="cuda")
+    gs = 0.5
+    n = int(host["cu_seqlens"][-1])
+    # (the layer object allocates the loss buffers only for the sparse phase)
+    T, HI, dI = w.total_tokens, w.idx_heads, w.idx_dim
+    kl_d = torch.empty(T, device="cuda")
+    loss_d = torch.empty(1, device="cuda")
+    dqI_d = torch.empty(T, HI, dI, device="cuda")
+    dw_d = torch.empty(T, HI, device="cuda")
+    dkI_d = torch.empty(L.tc_cap, dI, device="cuda")
+    kl, loss, dqI, dw, dkI, open_bound = O.indexer_kl(
+        h64["q"], kv_cmp_r, s32[:n], None, qI64, h64["w"], kI64, host["cu_seqlens"], w.ratio,
+        w.scale, w.teacher, gs, rows=np.arange(n), relu_eps=2.0 ** -16)
+    for grads in (True, False):
+        kl_d.fill_(float("nan"))
+        dkI_d.zero_()
+        B.csa_indexer_kl(L.p, host["q"].cuda(), kvc, torch.from_numpy(s32).cuda(), None, d["qI"],
+                         d["qI_scale"], host["w"].cuda(), d["kI"], d["kI_scale"], cu, L.cu_cmp,
+                         gs, kl_d, loss_d, dqI_d if grads else None, dw_d if grads else None,
+                         dkI_d if grads else None, ws, None, teacher_logits=t_logits)
+        torch.cuda.synchronize()
+        got_loss = float(loss_d.item())
+        print(f"[gpu] grads={grads} loss gpu={got_loss:.8e} ref={loss:.8e}", flush=True)
+        assert abs(got_loss - loss) <= G.TOL_LOSS_REL * abs(loss)
+        G.check("kl", G.back(kl_d)[:n], kl, "bf16")
+        assert torch.all(kl_d[n:] == 0)
+        if grads:
+            _check_open("dqI", G.back(dqI_d)[:n], dqI, open_bound[0])
+            _check_open("dw", G.back(dw_d)[:n], dw, open_bound[1])
+            _check_open("dkI_cmp", G.back(dkI_d)[:kI64.shape[0]], dkI, open_bound[2])
+
+
 # ------------------------------------------------------------------------- whole layer
 def _sets(a):
     return [set(r[r >= 0].tolist()) for r in np.asarray(a)]
