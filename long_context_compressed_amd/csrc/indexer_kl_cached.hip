@@ -68,9 +68,8 @@ struct KlcArgs {
 };
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// at most 4 or 6 vector memory operations outstanding (they complete in issue order)
-__device__ __forceinline__ void wait_vmem_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
-__device__ __forceinline__ void wait_vmem_6() { asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); }
+// at most 2 vector memory operations outstanding (they complete in issue order)
+__device__ __forceinline__ void wait_vmem_2() { asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); }
 
 __device__ __forceinline__ void dma_rows16(const void* src, const void* lds) {
   const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
@@ -120,7 +119,7 @@ void k_kl_cached(KlcArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t KIt[2][kNB][kDI];   // swizzled 256-byte rows
   __shared__ __attribute__((aligned(16))) uint16_t QIs[kHI][kDI];      // the query's qI, swizzled
   __shared__ __attribute__((aligned(16))) uint16_t EsT[kNB][kEST];
-  __shared__ float Pp[4][kNB];
+  __shared__ float Pp[2][4][kNB];   // per block parity: each wave's head-partial P of the slots
   __shared__ float gw_s[4][kNB];
   __shared__ float lse2_s[kHT];
   __shared__ double red_d[4];
@@ -309,12 +308,12 @@ void k_kl_cached(KlcArgs a) {
   wait_vmem();
   __syncthreads();
 
-  // cached teacher logits of a block: thread = (heads 4 hq .. +3, slots 4 sq .. +3), read two
-  // blocks ahead (the logits come from HBM: with one block in flight per workgroup the loss
-  // ran at the rate that a block's worth of loads per workgroup sustains at HBM latency, well
-  // below the bandwidth).  Three register sets take turns (block b reads set b % 3 and loads
-  // set (b + 2) % 3), so no set is copied while its loads are in flight, and every block
-  // issues exactly 4 loads (past the last block they repeat it), so the waits can count them.
+  // cached teacher logits of a block: thread = (heads 4 hq .. +3, slots 4 sq .. +3).  Block b
+  // loads block b + 1's right after its first barrier and turns them into block b + 1's P at
+  // its end, behind its own products.  Two register sets take turns over pairs of blocks, so no
+  // set is copied while its loads are in flight (a rotating copy made every block end wait for
+  // all its loads, and so did a student score that could come from global memory); past the
+  // last block the loads repeat it, so every block issues the same loads.
   const int hq = tid >> 4, sq = tid & 15;
   auto load_logits = [&](int b, f32x4 (&v)[4]) {
     const int bb = b < nblk ? b : nblk - 1;
@@ -323,52 +322,56 @@ void k_kl_cached(KlcArgs a) {
       v[k] = *reinterpret_cast<const f32x4*>(tl_t + (int64_t)(4 * hq + k) * a.ld_t + kNB * bb +
                                              4 * sq);
   };
-  f32x4 lg_a[4], lg_b[4], lg_c[4];
+  f32x4 lg_a[4], lg_b[4];
   load_logits(0, lg_a);
-  load_logits(1, lg_b);
-  // block 0's logits complete before the loop, so that inside it the waits for the logits
-  // count only younger loads and stores
+  // block 0's logits complete before its P is formed
 #pragma unroll
   for (int k = 0; k < 4; ++k) asm volatile("" :: "v"(lg_a[k]));
 
-  auto block = [&](int b, f32x4 (&lg_cur)[4], f32x4 (&lg_ld)[4]) {
+  // ---- teacher probabilities of block b's slots from its logits: this wave's 16 heads, per
+  // slot, into Pp[b & 1][wave] (block b + 1's are formed at the end of block b, while block b's
+  // products are still in flight, so that they are off the path to block b + 1's first barrier)
+  auto teacher_p = [&](int b, const f32x4 (&lg)[4]) {
+    float pj[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float l2 = lse2_s[4 * hq + k];
+      const f32x4 v = lg[k];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pj[i] += __builtin_amdgcn_exp2f(v[i] * 1.44269504088896341f - l2);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pj[i] += __shfl_xor(pj[i], 16, 64);
+      pj[i] += __shfl_xor(pj[i], 32, 64);
+    }
+    if (g == 0) *reinterpret_cast<f32x4*>(&Pp[b & 1][wave][4 * sq]) = f32x4{pj[0], pj[1], pj[2], pj[3]};
+  };
+  teacher_p(0, lg_a);
+
+  // block b: its logits' P is in Pp[b & 1]; lg_ld receives block b + 1's logits, whose P
+  // this block forms at its end
+  auto block = [&](int b, f32x4 (&lg_ld)[4]) {
     const int buf = b & 1;
     const int rid_nn = row_of(b + 2);
-
-    // ---- teacher probabilities of this block's slots
-    {
-      float pj[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float l2 = lse2_s[4 * hq + k];
-        const f32x4 v = lg_cur[k];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pj[i] += __builtin_amdgcn_exp2f(v[i] * 1.44269504088896341f - l2);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pj[i] += __shfl_xor(pj[i], 16, 64);
-        pj[i] += __shfl_xor(pj[i], 32, 64);
-      }
-      if (g == 0) *reinterpret_cast<f32x4*>(&Pp[wave][4 * sq]) = f32x4{pj[0], pj[1], pj[2], pj[3]};
-    }
     // key rows of this block, issued during the previous block; younger than them are that
-    // block's 4 logit loads (for block b + 1, left in flight) and, if this wave wrote E of
-    // any slot of it, its 2 E stores (block 0: its rows were waited for before the loop)
-    if (!IDX_LDS) wait_vmem();
-    else if (a.grads && b > 0 && kNB * (b - 1) + 16 * wave < n_c) wait_vmem_6();
-    else wait_vmem_4();
+    // block's logit loads (consumed at its end) and, if this wave wrote E of any slot of it,
+    // its 2 E stores, which may stay in flight (block 0: its rows were waited for before the
+    // loop)
+    if (IDX_LDS && a.grads && b > 0 && kNB * (b - 1) + 16 * wave < n_c) wait_vmem_2();
+    else wait_vmem();
     __syncthreads();
     // the other key buffer was last read before the previous block's second barrier
     if (b + 1 < nblk) issue(rid_nxt, buf ^ 1);
-    load_logits(b + 2, lg_ld);
+    load_logits(b + 1, lg_ld);
     const float sc_nn = score_of(b + 2);   // used two blocks on
 
     // ---- per slot (lane l = slot 64 b + l): P, Q, KL and g; g w per wave in LDS
     float gl;
     {
       const bool in = rid_cur >= 0;
-      const float P = ((Pp[0][lane] + Pp[1][lane]) + (Pp[2][lane] + Pp[3][lane])) * (1.f / kHT);
+      const float P = ((Pp[buf][0][lane] + Pp[buf][1][lane]) + (Pp[buf][2][lane] + Pp[buf][3][lane])) *
+                      (1.f / kHT);
       const float logQ = sc_cur - lseS;
       const float Q = in ? expf(logQ) : 0.f;
       // log P - log Q = log(P * s_S) - (s - m_S): no cancellation of two logs of the
@@ -438,6 +441,8 @@ void k_kl_cached(KlcArgs a) {
         }
       }
     }
+    // Pp[buf ^ 1] was last read before this block's first barrier
+    if (b + 1 < nblk) teacher_p(b + 1, lg_ld);
     __syncthreads();
     if (a.grads) {
       // ---- E rows of the block's slots (thread: slot tid / 4, heads 16 (tid % 4) .. +15):
@@ -456,16 +461,13 @@ void k_kl_cached(KlcArgs a) {
     sc_cur = sc_nxt;
     sc_nxt = sc_nn;
   };
-  // whole rounds of three blocks, then the one or two left (no block of a round is
-  // conditional, so the waits for the logits can count the loads issued after them)
+  // pairs of blocks, then the one left
   int b = 0;
-  for (; b + 2 < nblk; b += 3) {
-    block(b, lg_a, lg_c);
-    block(b + 1, lg_b, lg_a);
-    block(b + 2, lg_c, lg_b);
+  for (; b + 1 < nblk; b += 2) {
+    block(b, lg_b);
+    block(b + 1, lg_a);
   }
-  if (b < nblk) block(b, lg_a, lg_c);
-  if (b + 1 < nblk) block(b + 1, lg_b, lg_a);
+  if (b < nblk) block(b, lg_b);
 
   // ---- outputs: kl, dw, dqI (the two slot halves ch = 0, 1 summed through LDS)
   if (wave == 0) {
@@ -480,7 +482,7 @@ void k_kl_cached(KlcArgs a) {
     float d2 = dw_acc[nt];
     d2 += __shfl_xor(d2, 16, 64);
     d2 += __shfl_xor(d2, 32, 64);
-    if (g == 0) Pp[ch][32 * hh + 16 * nt + c16] = d2;
+    if (g == 0) Pp[0][ch][32 * hh + 16 * nt + c16] = d2;
   }
   if (ch == 0) {
 #pragma unroll
@@ -502,7 +504,7 @@ void k_kl_cached(KlcArgs a) {
           dqs[(32 * hh + 16 * nt + 4 * g + i) * kDI + 16 * nd + c16] += dq[nt][nd][i];
   }
   __syncthreads();
-  if (tid < kHI) a.dw[(int64_t)t * kHI + tid] = Pp[0][tid] + Pp[1][tid];
+  if (tid < kHI) a.dw[(int64_t)t * kHI + tid] = Pp[0][0][tid] + Pp[0][1][tid];
   float4* dst = reinterpret_cast<float4*>(a.dqI + (int64_t)t * kHI * kDI);
   const float4* src = reinterpret_cast<const float4*>(dqs);
   for (int e = tid; e < kHI * kDI / 4; e += 256) dst[e] = src[e];
