@@ -68,6 +68,8 @@ struct FwdArgs {
 };
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// at most 2 vector memory operations outstanding (they complete in issue order)
+__device__ __forceinline__ void wait_vmem_2() { asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); }
 
 // One 16-byte-per-lane global -> LDS load (global_load_lds_dwordx4); lane l's 16 bytes land
 // at LDS byte offset lds + 16 l.  Issued through asm so that the compiler does not order the
@@ -289,7 +291,8 @@ void k_attn_fwd_mfma(FwdArgs a) {
     }
     // compressed blocks: keep the logits for the indexer teacher (16-byte stores of four
     // consecutive slots of one head)
-    if (a.t_logits && kNB * b < cs.n_cs) {
+    const bool t_store = a.t_logits && kNB * b < cs.n_cs;
+    if (t_store) {
 #pragma unroll
       for (int nt = 0; nt < NT2; ++nt) {
         float* dst = a.t_logits + ((int64_t)t * kH + HPW * hh + 16 * nt + c16) * a.ld_t +
@@ -401,7 +404,11 @@ void k_attn_fwd_mfma(FwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vmem();
+    // the next block's rows, gathered in the S^T loop: younger than them are only this block's
+    // teacher-logit stores (NT2 x MQ = 2 per lane), which may stay in flight
+    static_assert(NT2 * MQ == 2, "the wait below counts the teacher-logit stores");
+    if (t_store) wait_vmem_2();
+    else wait_vmem();
     __syncthreads();
     rid_cur = rid_nxt;
     rid_nxt = rid_of(b + 2, raw_nn);
